@@ -1,0 +1,160 @@
+/*
+ * kan.h - C ABI of the MI355X (gfx950) B-spline KAN layer library.
+ *
+ * The layer (InKAN project page, "What is a KAN?"): every edge (j, i) carries a
+ * learned cubic B-spline phi_ji, and output j sums them over the inputs,
+ *
+ *     y[b, j] = sum_i sum_m C[j, i, m] * B_m(x[b, i])
+ *             + has_base * sum_i W_base[j, i] * silu(x[b, i]),
+ *
+ * with B_m, m = 0 .. G+2, the uniform cubic B-splines of a grid of G equal
+ * intervals on [lo, hi] extended by 3 knots on each side (knots
+ * t_r = lo + (r - 3) h, h = (hi - lo) / G, r = 0 .. G+6).  The residual
+ * W_base * silu(x) branch is optional and is not on the pages.  Training
+ * backward ("same optimizer, same training loop", InKAN page, "Why InKAN?"):
+ *
+ *     dx[b, i]      = sum_j dy[b, j] * (sum_m C[j, i, m] * B'_m(x[b, i])
+ *                                       + W_base[j, i] * silu'(x[b, i]))
+ *     dC[j, i, m]   = sum_b dy[b, j] * B_m(x[b, i])
+ *     dW_base[j, i] = sum_b dy[b, j] * silu(x[b, i])
+ *
+ * An input outside the extended grid [t_0, t_{G+6}) has every B_m = 0 and
+ * contributes through the base branch only; the layer never clamps x.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Layouts are row-major and contiguous: x [N, I]; C [O, I, G+3] with m
+ *   fastest; W_base [O, I]; y, dy [N, O]; dx [N, I]; dC [O, I, G+3];
+ *   dW_base [O, I].
+ * - x, C and W_base share one storage dtype (KAN_F32 or KAN_BF16); y, dy, dx,
+ *   dC and dW_base are always float32.  Arithmetic accumulates in float32.
+ * - Tensor pointers are DEVICE pointers, 16-byte aligned.  `desc` and `grid`
+ *   are HOST pointers, read during the call only.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *   is enqueued asynchronously on it; nothing synchronises the host.
+ * - The caller owns every buffer.  The library allocates and frees no device
+ *   memory and keeps no pointer after returning.  Scratch space is the
+ *   caller's workspace of at least kan_workspace_size() bytes, 256-byte aligned.
+ * - Outputs are overwritten, never accumulated into.  Outputs must not overlap
+ *   inputs or each other (KAN_ERR_ALIAS).
+ * - Every argument is validated before any device work: a call that returns
+ *   an error has enqueued nothing.  A launch failure returns KAN_ERR_HIP.
+ * - Results are deterministic: the same inputs give bitwise-identical outputs
+ *   on every call (no floating-point atomics anywhere).
+ * - The library holds no mutable global state; concurrent calls on different
+ *   streams with disjoint outputs are safe.
+ */
+#ifndef KAN_H
+#define KAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KAN_ABI_VERSION 1
+
+typedef enum {
+    KAN_OK = 0,
+    KAN_ERR_NULL = -1,        /* a required pointer is NULL, or a forbidden one is not */
+    KAN_ERR_SHAPE = -2,       /* N < 0, I < 1, O < 1, or a size beyond the index range */
+    KAN_ERR_GRID = -3,        /* G < 1, lo >= hi, or lo / hi not finite */
+    KAN_ERR_DTYPE = -4,       /* dtype not KAN_F32 / KAN_BF16 */
+    KAN_ERR_ALIGN = -5,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
+    KAN_ERR_WORKSPACE = -6,   /* workspace smaller than kan_workspace_size() */
+    KAN_ERR_HIP = -7,         /* a HIP launch failed */
+    KAN_ERR_UNSUPPORTED = -8, /* degree != 3, bad variant / has_base / pass value */
+    KAN_ERR_ALIAS = -9        /* an output overlaps an input or another output */
+} kan_status_t;
+
+typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
+
+/* Kernel family.  AUTO picks per shape and dtype.  MFMA runs the contraction
+ * over the dense basis (I*(G+3+has_base) wide) on the matrix cores, with the
+ * basis generated in LDS and never written to memory.  GATHER touches only the
+ * 4 non-zero basis functions per input (InKAN page, "Why InKAN?": local
+ * 4-basis lookup) on the vector ALUs. */
+typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 2 } kan_variant_t;
+
+typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;
+
+/* Grid: G intervals on [lo, hi]; degree must be 3 (cubic, InKAN page). */
+typedef struct {
+    float lo;
+    float hi;
+    int32_t G;
+    int32_t degree;
+} kan_grid_t;
+
+/* One layer.  N rows may be 0 (forward and dx are then no-ops; dC and dW_base
+ * are filled with zeros). */
+typedef struct {
+    int64_t N;
+    int64_t I;
+    int64_t O;
+    kan_grid_t grid;
+    int32_t dtype;     /* kan_dtype_t: storage of x, C, W_base */
+    int32_t has_base;  /* 0 or 1 */
+    int32_t variant;   /* kan_variant_t */
+    int32_t flags;     /* 0 or KAN_FLAG_PREPARED */
+} kan_desc_t;
+
+/* The workspace already holds this pass's packed operands, written by
+ * kan_prepare (or by the last kan_forward / kan_backward without this flag)
+ * for the same desc, C, W_base (and dy, for the backward pass); the call then
+ * skips packing and launches only the contraction kernels.  The caller must
+ * not have changed those inputs since. */
+#define KAN_FLAG_PREPARED 1
+
+/* KAN_ABI_VERSION of the loaded library. */
+int kan_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* kan_status_string(int status);
+
+/* Bytes of workspace a pass needs (0 if none; SIZE_MAX if `desc` is invalid).
+ * `pass` is kan_pass_t. */
+size_t kan_workspace_size(const kan_desc_t* desc, int pass);
+
+/* Packs what a pass reads into the workspace: for the MFMA variant the
+ * coefficient operand C' = [C | W_base] per input, zero-padded to the tile
+ * grid (forward: [O][I*(G+3+has_base)]; backward: its transpose), and for the
+ * backward pass also dy rounded to the storage dtype in both orientations.
+ * dy may be NULL for the forward pass.  A no-op for the GATHER variant. */
+int kan_prepare(const kan_desc_t* desc, int pass, const void* C, const void* W_base,
+                const float* dy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward: y [N, O] float32.  x, C, W_base in desc->dtype; W_base must be NULL
+ * exactly when has_base == 0. */
+int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
+                float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward.  dy [N, O] float32 in.  dx [N, I], dC [O, I, G+3] and dW_base
+ * [O, I] are float32 outputs; each may be NULL to skip it (dW_base must be
+ * NULL when has_base == 0).  dC and dW_base are sums over all N rows, reduced
+ * in a fixed order without atomics (FlashKAT abstract: atomic gradient
+ * accumulation is what slows the backward pass). */
+int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
+                 const float* dy, float* dx, float* dC, float* dW_base,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* The span / local-basis step on its own, for checking the device basis.
+ * x [n] in `dtype`; B and dB [n, G+3] float32 outputs (either may be NULL):
+ * B[k, m] = B_m(x[k]) and dB[k, m] = dB_m/dx(x[k]), computed from the 4
+ * non-zero pieces of the knot span that holds x[k] (InKAN page, "Why InKAN?":
+ * stable piecewise evaluation, local 4-basis lookup) and written densely. */
+int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
+                   float* B, float* dB, void* stream);
+
+/* float32 -> bfloat16, round to nearest even (NaN stays NaN).  n elements;
+ * `out` receives the 16-bit patterns.  Used between bf16 layers, where a
+ * float32 layer output becomes the next layer's bf16 input. */
+int kan_cast_f32_to_bf16(const float* in, void* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAN_H */

@@ -1,0 +1,299 @@
+// C ABI of the KAN layer library: argument validation, the per-call plan and
+// workspace layout, and kernel dispatch.  Every check runs before the first
+// launch, so a call that fails has enqueued nothing.  No C++ exception leaves
+// this file; there is no mutable global state.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kan_internal.h"
+
+namespace kan {
+
+namespace {
+
+constexpr int64_t kIndexLimit = (int64_t(1) << 31) - 4096;  // keeps 32-bit tile math safe
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
+
+}  // namespace
+
+int make_plan(const kan_desc_t* d, Plan* p) {
+    if (!d || !p) return KAN_ERR_NULL;
+    if (d->N < 0 || d->I < 1 || d->O < 1) return KAN_ERR_SHAPE;
+    if (d->grid.degree != 3) return KAN_ERR_UNSUPPORTED;
+    if (d->grid.G < 1 || d->grid.G > 4096) return KAN_ERR_GRID;
+    if (!isfinite(d->grid.lo) || !isfinite(d->grid.hi) || !(d->grid.lo < d->grid.hi))
+        return KAN_ERR_GRID;
+    if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
+    if (d->has_base != 0 && d->has_base != 1) return KAN_ERR_UNSUPPORTED;
+    if (d->variant < KAN_VARIANT_AUTO || d->variant > KAN_VARIANT_GATHER) return KAN_ERR_UNSUPPORTED;
+    if (d->flags != 0 && d->flags != KAN_FLAG_PREPARED) return KAN_ERR_UNSUPPORTED;
+
+    Plan q;
+    memset(&q, 0, sizeof(q));
+    q.N = d->N;
+    q.I = d->I;
+    q.O = d->O;
+    q.G = d->grid.G;
+    q.K = q.G + 3;
+    q.base = d->has_base;
+    q.Kb = q.K + q.base;
+    q.dtype = d->dtype;
+    q.esize = d->dtype == KAN_F32 ? 4 : 2;
+    if (q.N > kIndexLimit || q.O > kIndexLimit || q.I * q.Kb > kIndexLimit) return KAN_ERR_SHAPE;
+    const double lo = d->grid.lo, hi = d->grid.hi;
+    q.gk.scale = (float)((double)q.G / (hi - lo));
+    q.gk.shift = (float)(3.0 - lo * (double)q.G / (hi - lo));
+    q.gk.G = q.G;
+
+    // The dx epilogue keeps whole inputs inside one 256-wide tile.  AUTO: bf16
+    // runs on the matrix cores; float32 takes the local gather kernels (the
+    // dense contraction would execute (G+3+base)/(4+base) times the useful
+    // work at the float32 matrix rate, which equals the vector rate, and the
+    // gather forward accumulates in float64).
+    const bool mfma_ok = q.Kb <= kTileN;
+    if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
+    if (d->variant == KAN_VARIANT_GATHER) q.variant = KAN_VARIANT_GATHER;
+    else if (d->variant == KAN_VARIANT_MFMA) q.variant = KAN_VARIANT_MFMA;
+    else q.variant = (mfma_ok && q.dtype == KAN_BF16) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
+
+    if (q.variant == KAN_VARIANT_MFMA) {
+        q.BK = kTileKBytes / q.esize;
+        q.IKb = q.I * q.Kb;
+        q.Opad = round_up(q.O, kTileN);
+        q.Npad = round_up(std::max<int64_t>(q.N, 1), kTileM);
+        q.Kf = round_up(q.IKb, q.BK);
+        q.Qn = kTileN / q.Kb;
+        q.tiles_dx = (q.I + q.Qn - 1) / q.Qn;
+        q.rowsT = round_up((q.tiles_dx - 1) * q.Qn * q.Kb + kTileN, q.BK);
+        size_t off = 0;
+        auto take = [&](size_t bytes, size_t* o, size_t* sz) {
+            *o = off;
+            *sz = bytes;
+            off += (size_t)round_up((int64_t)bytes, 256);
+        };
+        take((size_t)(q.Opad * q.Kf) * q.esize, &q.off_cp, &q.sz_cp);
+        q.ws_fwd = off;
+        off = 0;
+        take((size_t)(q.rowsT * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
+        take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
+        take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
+        q.ws_bwd = off;
+    }
+    *p = q;
+    return KAN_OK;
+}
+
+}  // namespace kan
+
+using namespace kan;
+
+extern "C" {
+
+int kan_abi_version(void) { return KAN_ABI_VERSION; }
+
+const char* kan_status_string(int status) {
+    switch (status) {
+        case KAN_OK: return "ok";
+        case KAN_ERR_NULL: return "required pointer is NULL (or a forbidden one is not)";
+        case KAN_ERR_SHAPE: return "invalid shape";
+        case KAN_ERR_GRID: return "invalid grid (G < 1 or > 4096, lo >= hi, or non-finite)";
+        case KAN_ERR_DTYPE: return "unsupported dtype";
+        case KAN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, workspace 256)";
+        case KAN_ERR_WORKSPACE: return "workspace too small";
+        case KAN_ERR_HIP: return "HIP launch failed";
+        case KAN_ERR_UNSUPPORTED: return "unsupported option (degree, variant, flags, pass)";
+        case KAN_ERR_ALIAS: return "an output overlaps an input or another output";
+        default: return "unknown status";
+    }
+}
+
+size_t kan_workspace_size(const kan_desc_t* desc, int pass) {
+    Plan p;
+    if (make_plan(desc, &p) != KAN_OK) return SIZE_MAX;
+    if (pass != KAN_PASS_FORWARD && pass != KAN_PASS_BACKWARD) return SIZE_MAX;
+    if (p.variant != KAN_VARIANT_MFMA) return 0;
+    return pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
+}
+
+static int check_ws(const Plan& p, int pass, const void* ws, size_t ws_bytes) {
+    if (p.variant != KAN_VARIANT_MFMA) return KAN_OK;
+    const size_t need = pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
+    if (ws_bytes < need) return KAN_ERR_WORKSPACE;
+    if (need > 0 && !ws) return KAN_ERR_NULL;
+    if (ws && !aligned(ws, 256)) return KAN_ERR_ALIGN;
+    return KAN_OK;
+}
+
+static char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+static int prepare_impl(const Plan& p, int pass, const void* C, const void* W, const float* dy,
+                        void* ws, hipStream_t s) {
+    if (p.variant != KAN_VARIANT_MFMA) return KAN_OK;
+    hipError_t e = hipSuccess;
+    if (pass == KAN_PASS_FORWARD) {
+        e = launch_pack_fwd(p, C, W, ws_at(ws, p.off_cp), s);
+    } else {
+        e = launch_pack_bwd(p, C, W, ws_at(ws, p.off_cpt), s);
+        if (e == hipSuccess && p.N > 0)
+            e = launch_prep_dy(p, dy, ws_at(ws, p.off_dyp), ws_at(ws, p.off_dyt), s);
+    }
+    return status_of(e);
+}
+
+int kan_prepare(const kan_desc_t* desc, int pass, const void* C, const void* W_base,
+                const float* dy, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int st = make_plan(desc, &p);
+    if (st != KAN_OK) return st;
+    if (pass != KAN_PASS_FORWARD && pass != KAN_PASS_BACKWARD) return KAN_ERR_UNSUPPORTED;
+    if (!C) return KAN_ERR_NULL;
+    if ((W_base != nullptr) != (p.base == 1)) return KAN_ERR_NULL;
+    if (pass == KAN_PASS_BACKWARD && p.N > 0 && !dy) return KAN_ERR_NULL;
+    if (!aligned(C, 16) || (W_base && !aligned(W_base, 16)) || (dy && !aligned(dy, 16)))
+        return KAN_ERR_ALIGN;
+    if ((st = check_ws(p, pass, ws, ws_bytes)) != KAN_OK) return st;
+    const size_t wsn = pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
+    const Range wr{ws, p.variant == KAN_VARIANT_MFMA ? wsn : 0};
+    const Range in[] = {{C, (size_t)(p.O * p.I * p.K) * p.esize},
+                        {W_base, (size_t)(p.O * p.I) * p.esize},
+                        {dy, pass == KAN_PASS_BACKWARD ? (size_t)(p.N * p.O) * 4 : 0}};
+    for (const Range& r : in)
+        if (overlap(wr, r)) return KAN_ERR_ALIAS;
+    (void)hipGetLastError();
+    return prepare_impl(p, pass, C, W_base, dy, ws, (hipStream_t)stream);
+}
+
+int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
+                float* y, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int st = make_plan(desc, &p);
+    if (st != KAN_OK) return st;
+    if (!C || (p.N > 0 && (!x || !y))) return KAN_ERR_NULL;
+    if ((W_base != nullptr) != (p.base == 1)) return KAN_ERR_NULL;
+    const void* fptrs[] = {x, C, W_base, y};
+    for (const void* q : fptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    if ((st = check_ws(p, KAN_PASS_FORWARD, ws, ws_bytes)) != KAN_OK) return st;
+    const Range out{y, (size_t)(p.N * p.O) * 4};
+    const Range wr{ws, p.variant == KAN_VARIANT_MFMA ? p.ws_fwd : 0};
+    const Range in[] = {{x, (size_t)(p.N * p.I) * p.esize},
+                        {C, (size_t)(p.O * p.I * p.K) * p.esize},
+                        {W_base, (size_t)(p.O * p.I) * p.esize}};
+    for (const Range& r : in)
+        if (overlap(out, r) || overlap(wr, r)) return KAN_ERR_ALIAS;
+    if (overlap(out, wr)) return KAN_ERR_ALIAS;
+    if (p.N == 0) return KAN_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (p.variant == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, s));
+    if (!(desc->flags & KAN_FLAG_PREPARED)) {
+        st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
+        if (st != KAN_OK) return st;
+    }
+    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp), y, s));
+}
+
+int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
+                 const float* dy, float* dx, float* dC, float* dW, void* ws, size_t ws_bytes,
+                 void* stream) {
+    Plan p;
+    int st = make_plan(desc, &p);
+    if (st != KAN_OK) return st;
+    if (!C || (p.N > 0 && (!x || !dy))) return KAN_ERR_NULL;
+    if ((W_base != nullptr) != (p.base == 1)) return KAN_ERR_NULL;
+    if (dW && !p.base) return KAN_ERR_NULL;
+    const void* ptrs[] = {x, C, W_base, dy, dx, dC, dW};
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    if ((st = check_ws(p, KAN_PASS_BACKWARD, ws, ws_bytes)) != KAN_OK) return st;
+    const Range outs[] = {{dx, (size_t)(p.N * p.I) * 4},
+                          {dC, (size_t)(p.O * p.I * p.K) * 4},
+                          {dW, (size_t)(p.O * p.I) * 4},
+                          {ws, p.variant == KAN_VARIANT_MFMA ? p.ws_bwd : 0}};
+    const Range ins[] = {{x, (size_t)(p.N * p.I) * p.esize},
+                         {C, (size_t)(p.O * p.I * p.K) * p.esize},
+                         {W_base, (size_t)(p.O * p.I) * p.esize},
+                         {dy, (size_t)(p.N * p.O) * 4}};
+    for (int a = 0; a < 4; ++a) {
+        for (const Range& r : ins)
+            if (overlap(outs[a], r)) return KAN_ERR_ALIAS;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outs[a], outs[b])) return KAN_ERR_ALIAS;
+    }
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (p.N == 0) {  // empty batch: the gradient sums are zero, dx is empty
+        hipError_t e = hipSuccess;
+        if (dC) e = launch_fill_zero(dC, p.O * p.I * p.K, s);
+        if (e == hipSuccess && dW) e = launch_fill_zero(dW, p.O * p.I, s);
+        return status_of(e);
+    }
+    if (p.variant == KAN_VARIANT_GATHER) {
+        hipError_t e = hipSuccess;
+        if (dx) e = launch_gather_dx(p, x, C, W_base, dy, dx, s);
+        if (e == hipSuccess && (dC || dW)) e = launch_gather_dc(p, x, dy, dC, dW, s);
+        return status_of(e);
+    }
+    if (!(desc->flags & KAN_FLAG_PREPARED)) {
+        st = prepare_impl(p, KAN_PASS_BACKWARD, C, W_base, dy, ws, s);
+        if (st != KAN_OK) return st;
+    }
+    hipError_t e = hipSuccess;
+    if (dx) e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt), dx, s);
+    if (e == hipSuccess && (dC || dW)) e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), dC, dW, s);
+    return status_of(e);
+}
+
+int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
+                   float* dB, void* stream) {
+    if (!grid) return KAN_ERR_NULL;
+    kan_desc_t d;
+    memset(&d, 0, sizeof(d));
+    d.N = n < 0 ? -1 : 1;
+    d.I = 1;
+    d.O = 1;
+    d.grid = *grid;
+    d.dtype = dtype;
+    Plan p;
+    int st = make_plan(&d, &p);
+    if (st != KAN_OK) return st;
+    if (n > kIndexLimit / (p.K > 0 ? p.K : 1)) return KAN_ERR_SHAPE;
+    if (n == 0) return KAN_OK;
+    if (!x || (!B && !dB)) return KAN_ERR_NULL;
+    if (!aligned(x, 16) || (B && !aligned(B, 16)) || (dB && !aligned(dB, 16))) return KAN_ERR_ALIGN;
+    const size_t ob = (size_t)n * p.K * 4;
+    const Range rx{x, (size_t)n * p.esize}, rb{B, ob}, rd{dB, ob};
+    if (overlap(rx, rb) || overlap(rx, rd) || overlap(rb, rd)) return KAN_ERR_ALIAS;
+    (void)hipGetLastError();
+    return status_of(launch_basis_eval(p.gk, n, dtype, x, B, dB, (hipStream_t)stream));
+}
+
+int kan_cast_f32_to_bf16(const float* in, void* out, int64_t n, void* stream) {
+    if (n < 0) return KAN_ERR_SHAPE;
+    if (n == 0) return KAN_OK;
+    if (!in || !out) return KAN_ERR_NULL;
+    if (!aligned(in, 16) || !aligned(out, 16)) return KAN_ERR_ALIGN;
+    if (overlap(Range{in, (size_t)n * 4}, Range{out, (size_t)n * 2})) return KAN_ERR_ALIAS;
+    (void)hipGetLastError();
+    return status_of(launch_cast_bf16(in, static_cast<uint16_t*>(out), n, (hipStream_t)stream));
+}
+
+}  // extern "C"

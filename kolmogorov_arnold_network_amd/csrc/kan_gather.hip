@@ -1,0 +1,419 @@
+// Local 4-basis kernels on the vector ALUs (gfx950), plus the standalone basis
+// evaluation, the bf16 cast and a zero fill.
+//
+// "Local 4-basis lookup instead of dense K-basis computation" (InKAN project
+// page, "Why InKAN?"): for each (row b, input i) only the span s and the four
+// pieces b0..b3 are formed; the contraction then gathers the coefficients
+// C[j, i, s-3 .. s].  All arithmetic is float32 and every reduction runs in a
+// fixed order without atomics.
+#include "kan_internal.h"
+
+namespace kan {
+
+namespace {
+
+// Per (b, i): span-relative coefficient index base and the four weights with
+// the out-of-range ones set to zero, so the inner loops can clamp the index
+// and multiply unconditionally.
+struct Rec {
+    int m0;          // s - 3: index of the coefficient that b0 multiplies
+    float w[4];      // b_r (or derivative) for m = m0 + r; 0 where m is outside [0, K-1]
+    float base;      // silu(x) or silu'(x)
+};
+
+template <bool DERIV>
+__device__ __forceinline__ Rec make_rec(float xv, const GridK& g) {
+    Rec r;
+    float u;
+    const int s = span_u(xv, g, u);
+    float w0, w1, w2, w3;
+    if (DERIV) dpieces(u, g.scale, w0, w1, w2, w3);
+    else pieces(u, w0, w1, w2, w3);
+    r.m0 = s - 3;
+    const int K = g.G + 3;
+    r.w[0] = (r.m0 >= 0 && r.m0 < K) ? w0 : 0.0f;
+    r.w[1] = (r.m0 + 1 >= 0 && r.m0 + 1 < K) ? w1 : 0.0f;
+    r.w[2] = (r.m0 + 2 >= 0 && r.m0 + 2 < K) ? w2 : 0.0f;
+    r.w[3] = (r.m0 + 3 >= 0 && r.m0 + 3 < K) ? w3 : 0.0f;
+    r.base = DERIV ? silu_prime(xv) : silu(xv);
+    return r;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// ---------------------------------------------------------------------------
+// Standalone basis: dense B[k, m] and dB[k, m] from the local pieces.
+template <typename TS>
+__global__ void basis_eval_kernel(GridK g, int64_t n, const TS* __restrict__ x,
+                                  float* __restrict__ B, float* __restrict__ dB) {
+    const int K = g.G + 3;
+    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const float xv = load_f(x, k);
+        float u;
+        const int s = span_u(xv, g, u);
+        float b[4], d[4];
+        pieces(u, b[0], b[1], b[2], b[3]);
+        dpieces(u, g.scale, d[0], d[1], d[2], d[3]);
+        for (int m = 0; m < K; ++m) {
+            const int r = m - (s - 3);
+            const bool in = r >= 0 && r < 4;
+            const int rr = clampi(r, 0, 3);
+            if (B) B[k * K + m] = in ? b[rr] : 0.0f;
+            if (dB) dB[k * K + m] = in ? d[rr] : 0.0f;
+        }
+    }
+}
+
+__global__ void cast_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
+    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x)
+        out[k] = f2bf(in[k]);
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x)
+        p[k] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  Block: 64 rows x 64 outputs; thread: 4 rows x 4 consecutive outputs.
+// Inputs advance in chunks of 4; the chunk's coefficients sit in LDS as
+// Cs[i][m][j] so that C[j..j+3, i, m] is one 16-byte read.  Each input's
+// five-term partial phi_ji(x_i) is formed in float32 and added into a float64
+// accumulator: a chain of KAN layers feeds y through B' of the next layer,
+// which amplifies forward rounding error about tenfold, and float64 adds cost
+// the same as float32 FMAs on the vector ALU.
+constexpr int GF_TB = 64, GF_TJ = 64, GF_IC = 4;
+
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, int O, int base,
+                                                         const TS* __restrict__ x,
+                                                         const TS* __restrict__ C,
+                                                         const TS* __restrict__ W,
+                                                         float* __restrict__ y) {
+    extern __shared__ float4 smem4[];
+    float* smem = reinterpret_cast<float*>(smem4);
+    const int K = g.G + 3;
+    float* Cs = smem;                                  // [IC][K][TJ]
+    float* Ws = Cs + GF_IC * K * GF_TJ;                // [IC][TJ]
+    Rec* Rs = reinterpret_cast<Rec*>(Ws + GF_IC * GF_TJ);  // [IC][TB]
+
+    const int t = threadIdx.x;
+    const int jq = t % 16, rq = t / 16;
+    const int b0 = blockIdx.x * GF_TB, j0 = blockIdx.y * GF_TJ;
+    double acc[4][4] = {};
+
+    for (int i0 = 0; i0 < I; i0 += GF_IC) {
+        const int nic = min(GF_IC, I - i0);
+        __syncthreads();
+        // coefficients: C[j0 + jj, i0 + ii, m] -> Cs[ii][m][jj]
+        for (int e = t; e < GF_TJ * GF_IC * K; e += 256) {
+            const int jj = e / (GF_IC * K), rem = e % (GF_IC * K);
+            const int ii = rem / K, m = rem % K;
+            const int j = j0 + jj, i = i0 + ii;
+            Cs[(ii * K + m) * GF_TJ + jj] =
+                (j < O && ii < nic) ? load_f(C, ((int64_t)j * I + i) * K + m) : 0.0f;
+        }
+        for (int e = t; e < GF_TJ * GF_IC; e += 256) {
+            const int jj = e / GF_IC, ii = e % GF_IC;
+            const int j = j0 + jj, i = i0 + ii;
+            Ws[ii * GF_TJ + jj] = (base && j < O && ii < nic) ? load_f(W, (int64_t)j * I + i) : 0.0f;
+        }
+        for (int e = t; e < GF_TB * GF_IC; e += 256) {
+            const int bb = e / GF_IC, ii = e % GF_IC;
+            const int b = b0 + bb, i = i0 + ii;
+            Rec r;
+            if (b < N && ii < nic) {
+                r = make_rec<false>(load_f(x, (int64_t)b * I + i), g);
+                if (!base) r.base = 0.0f;
+            } else {
+                r.m0 = 0;
+                r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0.0f;
+                r.base = 0.0f;
+            }
+            Rs[ii * GF_TB + bb] = r;
+        }
+        __syncthreads();
+        for (int ii = 0; ii < nic; ++ii) {
+            const float4 wv = *reinterpret_cast<const float4*>(&Ws[ii * GF_TJ + 4 * jq]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const Rec r = Rs[ii * GF_TB + rq + 16 * p];
+                float a0 = r.base * wv.x, a1 = r.base * wv.y, a2 = r.base * wv.z, a3 = r.base * wv.w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = clampi(r.m0 + q, 0, K - 1);
+                    const float4 c = *reinterpret_cast<const float4*>(&Cs[(ii * K + m) * GF_TJ + 4 * jq]);
+                    a0 = __builtin_fmaf(r.w[q], c.x, a0);
+                    a1 = __builtin_fmaf(r.w[q], c.y, a1);
+                    a2 = __builtin_fmaf(r.w[q], c.z, a2);
+                    a3 = __builtin_fmaf(r.w[q], c.w, a3);
+                }
+                acc[p][0] += (double)a0;
+                acc[p][1] += (double)a1;
+                acc[p][2] += (double)a2;
+                acc[p][3] += (double)a3;
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int b = b0 + rq + 16 * p;
+        if (b >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + 4 * jq + q;
+            if (j < O) y[(int64_t)b * O + j] = (float)acc[p][q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dx.  Block: 64 rows x 16 inputs; thread: 4 rows x 1 input.  The reduction
+// runs over outputs j in chunks of 16 with dy and C staged in LDS.
+constexpr int GX_TB = 64, GX_TI = 16, GX_JC = 16;
+
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, int O, int base,
+                                                        const TS* __restrict__ x,
+                                                        const TS* __restrict__ C,
+                                                        const TS* __restrict__ W,
+                                                        const float* __restrict__ dy,
+                                                        float* __restrict__ dx) {
+    extern __shared__ float4 smem4[];
+    float* smem = reinterpret_cast<float*>(smem4);
+    const int K = g.G + 3;
+    float* Ds = smem;                               // [TB][JC]
+    float* Cs = Ds + GX_TB * GX_JC;                  // [TI][K][JC]
+    float* Ws = Cs + GX_TI * K * GX_JC;              // [TI][JC]
+
+    const int t = threadIdx.x;
+    const int il = t % GX_TI, rq = t / GX_TI;
+    const int b0 = blockIdx.x * GX_TB, i0 = blockIdx.y * GX_TI;
+    const int i = i0 + il;
+    Rec rec[4];
+    int mi[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int b = b0 + rq + 16 * p;
+        if (b < N && i < I) {
+            rec[p] = make_rec<true>(load_f(x, (int64_t)b * I + i), g);
+            if (!base) rec[p].base = 0.0f;
+        } else {
+            rec[p].m0 = 0;
+            rec[p].w[0] = rec[p].w[1] = rec[p].w[2] = rec[p].w[3] = 0.0f;
+            rec[p].base = 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mi[p][q] = clampi(rec[p].m0 + q, 0, K - 1);
+    }
+    float Q[4][5] = {};
+    for (int jc = 0; jc < O; jc += GX_JC) {
+        __syncthreads();
+        for (int e = t; e < GX_TB * GX_JC; e += 256) {
+            const int bb = e / GX_JC, jj = e % GX_JC;
+            const int b = b0 + bb, j = jc + jj;
+            Ds[bb * GX_JC + jj] = (b < N && j < O) ? dy[(int64_t)b * O + j] : 0.0f;
+        }
+        for (int e = t; e < GX_JC * GX_TI * K; e += 256) {
+            const int jj = e / (GX_TI * K), rem = e % (GX_TI * K);
+            const int ii = rem / K, m = rem % K;
+            const int j = jc + jj, ig = i0 + ii;
+            Cs[(ii * K + m) * GX_JC + jj] =
+                (j < O && ig < I) ? load_f(C, ((int64_t)j * I + ig) * K + m) : 0.0f;
+        }
+        for (int e = t; e < GX_JC * GX_TI; e += 256) {
+            const int jj = e / GX_TI, ii = e % GX_TI;
+            const int j = jc + jj, ig = i0 + ii;
+            Ws[ii * GX_JC + jj] = (base && j < O && ig < I) ? load_f(W, (int64_t)j * I + ig) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < GX_JC; jj += 4) {
+            const float4 wv = *reinterpret_cast<const float4*>(&Ws[il * GX_JC + jj]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float4 d = *reinterpret_cast<const float4*>(&Ds[(rq + 16 * p) * GX_JC + jj]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 c = *reinterpret_cast<const float4*>(&Cs[(il * K + mi[p][q]) * GX_JC + jj]);
+                    Q[p][q] = __builtin_fmaf(d.x, c.x, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.y, c.y, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.z, c.z, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.w, c.w, Q[p][q]);
+                }
+                Q[p][4] = __builtin_fmaf(d.x, wv.x, Q[p][4]);
+                Q[p][4] = __builtin_fmaf(d.y, wv.y, Q[p][4]);
+                Q[p][4] = __builtin_fmaf(d.z, wv.z, Q[p][4]);
+                Q[p][4] = __builtin_fmaf(d.w, wv.w, Q[p][4]);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int b = b0 + rq + 16 * p;
+        if (b >= N || i >= I) continue;
+        float v = Q[p][4] * rec[p].base;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v = __builtin_fmaf(Q[p][q], rec[p].w[q], v);
+        dx[(int64_t)b * I + i] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dC, dW_base.  Block owns 16 inputs x 16 outputs and sweeps every row in a
+// fixed order; thread (i, j) keeps its K spline accumulators in a private LDS
+// column (no other thread touches them, so there is no atomic and the sum
+// order is the row order).
+constexpr int GC_TI = 16, GC_TJ = 16, GC_RB = 64;
+
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_dc_kernel(GridK g, int N, int I, int O, int base,
+                                                        const TS* __restrict__ x,
+                                                        const float* __restrict__ dy,
+                                                        float* __restrict__ dC,
+                                                        float* __restrict__ dW) {
+    extern __shared__ float4 smem4[];
+    float* smem = reinterpret_cast<float*>(smem4);
+    const int K = g.G + 3;
+    float* Acc = smem;                                // [K][256]
+    float* Ds = Acc + K * 256;                        // [RB][TJ]
+    Rec* Rs = reinterpret_cast<Rec*>(Ds + GC_RB * GC_TJ);  // [RB][TI]
+
+    const int t = threadIdx.x;
+    const int il = t % GC_TI, jl = t / GC_TI;
+    const int i0 = blockIdx.x * GC_TI, j0 = blockIdx.y * GC_TJ;
+    for (int m = 0; m < K; ++m) Acc[m * 256 + t] = 0.0f;
+    float accw = 0.0f;
+    for (int r0 = 0; r0 < N; r0 += GC_RB) {
+        __syncthreads();
+        for (int e = t; e < GC_RB * GC_TJ; e += 256) {
+            const int bb = e / GC_TJ, jj = e % GC_TJ;
+            const int b = r0 + bb, j = j0 + jj;
+            Ds[bb * GC_TJ + jj] = (b < N && j < O) ? dy[(int64_t)b * O + j] : 0.0f;
+        }
+        for (int e = t; e < GC_RB * GC_TI; e += 256) {
+            const int bb = e / GC_TI, ii = e % GC_TI;
+            const int b = r0 + bb, i = i0 + ii;
+            Rec r;
+            if (b < N && i < I) {
+                r = make_rec<false>(load_f(x, (int64_t)b * I + i), g);
+            } else {
+                r.m0 = 0;
+                r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0.0f;
+                r.base = 0.0f;
+            }
+            Rs[bb * GC_TI + ii] = r;
+        }
+        __syncthreads();
+        const int nb = min(GC_RB, N - r0);
+        for (int bb = 0; bb < nb; ++bb) {
+            const float d = Ds[bb * GC_TJ + jl];
+            const Rec r = Rs[bb * GC_TI + il];
+            accw = __builtin_fmaf(d, r.base, accw);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = clampi(r.m0 + q, 0, K - 1);
+                Acc[m * 256 + t] = __builtin_fmaf(d, r.w[q], Acc[m * 256 + t]);
+            }
+        }
+    }
+    const int i = i0 + il, j = j0 + jl;
+    if (i < I && j < O) {
+        if (dC)
+            for (int m = 0; m < K; ++m) dC[((int64_t)j * I + i) * K + m] = Acc[m * 256 + t];
+        if (dW && base) dW[(int64_t)j * I + i] = accw;
+    }
+}
+
+int grid1d(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 8192); }
+
+// Dynamic LDS beyond 64 KiB (gfx950 has 160 KiB per workgroup) must be requested.
+template <typename Kern>
+hipError_t allow_lds(Kern k, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace
+
+hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
+                             float* dB, hipStream_t s) {
+    if (dtype == KAN_F32)
+        hipLaunchKernelGGL(basis_eval_kernel<float>, dim3(grid1d(n)), dim3(256), 0, s, g, n,
+                           static_cast<const float*>(x), B, dB);
+    else
+        hipLaunchKernelGGL(basis_eval_kernel<uint16_t>, dim3(grid1d(n)), dim3(256), 0, s, g, n,
+                           static_cast<const uint16_t*>(x), B, dB);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid1d(n)), dim3(256), 0, s, in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid1d(n)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+template <typename TS>
+static hipError_t gather_fwd_t(const Plan& p, const void* x, const void* C, const void* W,
+                               float* y, hipStream_t s) {
+    const size_t lds = (size_t)(GF_IC * p.K * GF_TJ + GF_IC * GF_TJ) * 4 + GF_IC * GF_TB * sizeof(Rec);
+    dim3 grid((unsigned)((p.N + GF_TB - 1) / GF_TB), (unsigned)((p.O + GF_TJ - 1) / GF_TJ));
+    hipError_t e = allow_lds(gather_fwd_kernel<TS>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_fwd_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+                       (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
+                       static_cast<const TS*>(W), y);
+    return hipGetLastError();
+}
+
+template <typename TS>
+static hipError_t gather_dx_t(const Plan& p, const void* x, const void* C, const void* W,
+                              const float* dy, float* dx, hipStream_t s) {
+    const size_t lds = (size_t)(GX_TB * GX_JC + GX_TI * p.K * GX_JC + GX_TI * GX_JC) * 4;
+    dim3 grid((unsigned)((p.N + GX_TB - 1) / GX_TB), (unsigned)((p.I + GX_TI - 1) / GX_TI));
+    hipError_t e = allow_lds(gather_dx_kernel<TS>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_dx_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+                       (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
+                       static_cast<const TS*>(W), dy, dx);
+    return hipGetLastError();
+}
+
+template <typename TS>
+static hipError_t gather_dc_t(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
+                              hipStream_t s) {
+    const size_t lds = (size_t)(p.K * 256 + GC_RB * GC_TJ) * 4 + GC_RB * GC_TI * sizeof(Rec);
+    dim3 grid((unsigned)((p.I + GC_TI - 1) / GC_TI), (unsigned)((p.O + GC_TJ - 1) / GC_TJ));
+    hipError_t e = allow_lds(gather_dc_kernel<TS>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_dc_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+                       (int)p.O, p.base, static_cast<const TS*>(x), dy, dC, dW);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
+                             float* y, hipStream_t s) {
+    return p.dtype == KAN_F32 ? gather_fwd_t<float>(p, x, C, W, y, s)
+                              : gather_fwd_t<uint16_t>(p, x, C, W, y, s);
+}
+hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
+                            const float* dy, float* dx, hipStream_t s) {
+    return p.dtype == KAN_F32 ? gather_dx_t<float>(p, x, C, W, dy, dx, s)
+                              : gather_dx_t<uint16_t>(p, x, C, W, dy, dx, s);
+}
+hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
+                            hipStream_t s) {
+    return p.dtype == KAN_F32 ? gather_dc_t<float>(p, x, dy, dC, dW, s)
+                              : gather_dc_t<uint16_t>(p, x, dy, dC, dW, s);
+}
+
+}  // namespace kan

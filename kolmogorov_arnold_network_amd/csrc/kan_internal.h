@@ -1,0 +1,77 @@
+// Host-side plan of one KAN layer call and the kernel launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kan.h"
+#include "kan_device.h"
+
+namespace kan {
+
+// MFMA tile geometry (both dtypes): 256 x 256 output tile per workgroup of
+// 4 waves (2 x 2, 128 x 128 each), k-tiles of 128 bytes per row (64 bf16 or
+// 32 float) staged in LDS with a 144-byte row pitch, two stages.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kTileKBytes = 128;
+constexpr int kThreads = 256;
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+struct Plan {
+    int64_t N, I, O;
+    int G, K, Kb;        // K = G+3 spline functions; Kb = K + has_base columns per input
+    int base;
+    int dtype;           // KAN_F32 / KAN_BF16
+    int variant;         // resolved: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
+    int esize;           // bytes per stored element (4 or 2)
+    GridK gk;
+
+    // MFMA geometry
+    int BK;              // elements per k-tile (128 bytes)
+    int64_t IKb;         // I * Kb: width of the dense basis
+    int64_t Opad;        // O rounded up to the tile (rows of the packed C')
+    int64_t Npad;        // N rounded up to the tile
+    int64_t Kf;          // forward contraction length: IKb rounded up to BK
+    int Qn;              // inputs per n-tile of the dx contraction (floor(256 / Kb))
+    int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I / Qn)
+    int64_t rowsT;       // rows of the transposed packed C' (covers the last dx tile)
+
+    // workspace layout (bytes); forward uses [off_cp, +sz_cp)
+    size_t off_cp, sz_cp;      // C' packed [Opad][Kf]
+    size_t off_cpt, sz_cpt;    // C'^T packed [rowsT][Opad]
+    size_t off_dyp, sz_dyp;    // dy in storage dtype [Npad][Opad]
+    size_t off_dyt, sz_dyt;    // dy^T in storage dtype [Opad][Npad]
+    size_t ws_fwd, ws_bwd;
+};
+
+// Builds the plan; returns KAN_OK or the validation error for `desc` alone.
+int make_plan(const kan_desc_t* desc, Plan* p);
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
+                             float* dB, hipStream_t s);
+hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
+                             float* y, hipStream_t s);
+hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
+                            const float* dy, float* dx, hipStream_t s);
+hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
+                            hipStream_t s);
+
+hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
+hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s);
+hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s);
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s);
+hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
+                          float* dx, hipStream_t s);
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
+                          hipStream_t s);
+
+}  // namespace kan

@@ -1,0 +1,644 @@
+// Dense-basis KAN contractions on the gfx950 matrix cores.
+//
+// With C' = [C | W_base] per input (Kb = G+3+has_base columns per input) and
+// Phi'(x) the dense basis row [B_0(x_i) .. B_{G+2}(x_i), silu(x_i)] per input,
+// the three contractions of a training step are GEMMs over generated or
+// packed operands:
+//
+//   forward  y   [N, O]      = Phi'[N, I*Kb]  . C'^T          (k = (i, m))
+//   dx       P   [N, I*Kb]   = dy [N, O]      . C'            (k = j), then
+//            dx[b, i] = sum_m P[b, i, m] B'_m(x[b, i]) + P[b, i, K] silu'(x[b, i])
+//   dC, dW   dC' [O, I*Kb]   = dy^T [O, N]    . Phi'[N, I*Kb] (k = b)
+//
+// Phi' is generated tile by tile in LDS from x (span, 4 pieces, silu: InKAN
+// project page, "Why InKAN?") and is never written to memory (UKAN / warpKAN
+// abstract: the memory saving of not materialising the basis).  The dC'
+// reduction over the batch is owned by one workgroup per output tile and runs
+// in a fixed order without atomics (FlashKAT abstract: atomic gradient
+// accumulation and memory stalls are what slow the backward pass).
+//
+// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2 waves of
+// 128 x 128 = 8 x 8 MFMA fragments of 16 x 16), k-tiles of 128 bytes per row
+// (64 bf16 / 32 float), two LDS stages of A and B with a 144-byte row pitch.
+// bf16 uses v_mfma_f32_16x16x32_bf16, float uses v_mfma_f32_16x16x4_f32;
+// both accumulate in float32.  Each lane reads 16 contiguous bytes of k per
+// fragment row, so A and B share one lane -> k assignment and the k order
+// inside a step does not matter.
+#include <string.h>
+
+#include <algorithm>
+
+#include "kan_internal.h"
+
+namespace kan {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PITCH = 144;                     // bytes per LDS tile row (128 data + 16 pad)
+constexpr int TILE_BYTES = 256 * PITCH;        // one 256-row operand tile
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // A + B
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;     // two stages: 147456 bytes
+constexpr int DX_PITCH = 260;                  // floats per row of the dx epilogue staging
+
+template <typename TS> struct Traits;
+template <> struct Traits<uint16_t> {          // bf16 storage
+    static constexpr int ES = 2;
+    static constexpr int BK = 64;
+    __device__ static void mma(f32x4& acc, const uint4& a, const uint4& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+    __device__ static void put(char* p, float v) { *reinterpret_cast<uint16_t*>(p) = f2bf(v); }
+};
+template <> struct Traits<float> {
+    static constexpr int ES = 4;
+    static constexpr int BK = 32;
+    __device__ static void mma(f32x4& acc, const uint4& a, const uint4& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    }
+    __device__ static void put(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
+};
+
+struct GemmArgs {
+    int tiles_m, tiles_n, nkt, group_m;
+    const char* a;       // loaded A operand (row-major [rows][k]), or null
+    int64_t lda;         // bytes per row
+    const char* b;       // loaded B operand, or null
+    int64_t ldb;
+    const void* x;       // generator input x [N, I]
+    GridK g;
+    int N, I, O, K, Kb, base, Qn;
+    int64_t IKb;
+    float* out0;         // y, dx or dC
+    float* out1;         // dW_base
+};
+
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  Give every XCD a contiguous range of tile ids, and walk
+// ids in groups of `group_m` tile rows so that the workgroups resident on one
+// XCD share their B tiles (and their A tiles across the group).
+__device__ __forceinline__ void tile_coords(const GemmArgs& a, int& tm, int& tn) {
+    const int total = a.tiles_m * a.tiles_n;
+    const int bid = blockIdx.x;
+    const int nfull = total / 8, rem = total % 8;
+    const int xcd = bid % 8, slot = bid / 8;
+    const int id = xcd * nfull + min(xcd, rem) + slot;
+    const int per_group = a.group_m * a.tiles_n;
+    const int grp = id / per_group;
+    const int first_m = grp * a.group_m;
+    const int gm = min(a.tiles_m - first_m, a.group_m);
+    const int r = id - grp * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+// Operand copied from a packed row-major array: rows [r0, r0+256), k-tile kt
+// = bytes [128 kt, 128 kt + 128) of each row.  8 threads read one row's 128
+// bytes (coalesced); the tile goes through registers into LDS.
+struct LoadOp {
+    const char* base;
+    int64_t ld;
+    uint4 reg[8];
+    __device__ LoadOp(const char* p, int64_t r0, int64_t ld_) : base(p + r0 * ld_), ld(ld_) {}
+    __device__ __forceinline__ void fetch(int kt) {
+        const int t = threadIdx.x, c = t & 7, r = t >> 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            reg[q] = *reinterpret_cast<const uint4*>(base + (int64_t)(r + 32 * q) * ld +
+                                                     (int64_t)kt * 128 + c * 16);
+    }
+    __device__ __forceinline__ void store(char* S, int) {
+        const int t = threadIdx.x, c = t & 7, r = t >> 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<uint4*>(S + (r + 32 * q) * PITCH + c * 16) = reg[q];
+    }
+};
+
+// Forward A operand Phi'[b, (i, m)]: thread t owns row b = m0 + t of the tile
+// and writes that row only (zero fill, then the <= 4 spline values and the
+// silu value of every input that meets the k-tile), so no barrier is needed
+// between the two.
+template <typename TS>
+struct GenFwdA {
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int MAXIN = BK / 4 + 2;   // inputs meeting one k-tile (Kb >= 4)
+    const TS* x;
+    int b, i_first, nin;
+    bool row_ok;
+    float xr[MAXIN];
+    __device__ GenFwdA(const GemmArgs& a, int tm) {
+        x = static_cast<const TS*>(a.x);
+        b = tm * 256 + threadIdx.x;
+        row_ok = b < a.N;
+    }
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        const int k0 = kt * BK;
+        i_first = k0 / a.Kb;
+        const int i_last = min((k0 + BK - 1) / a.Kb, a.I - 1);
+        nin = i_last - i_first + 1;
+#pragma unroll
+        for (int q = 0; q < MAXIN; ++q)
+            if (q < nin && row_ok) xr[q] = load_f(x, (int64_t)b * a.I + i_first + q);
+    }
+    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
+        char* row = S + threadIdx.x * PITCH;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(0, 0, 0, 0);
+        if (!row_ok) return;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int q = 0; q < MAXIN; ++q) {
+            if (q < nin) {
+                const float xv = xr[q];
+                float u;
+                const int s = span_u(xv, a.g, u);
+                float bb[4];
+                pieces(u, bb[0], bb[1], bb[2], bb[3]);
+                const int cb = (i_first + q) * a.Kb - k0;   // tile column of (i, m = 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = s - 3 + r;
+                    const int col = cb + m;
+                    if (m >= 0 && m < a.K && col >= 0 && col < BK)
+                        Traits<TS>::put(row + col * Traits<TS>::ES, bb[r]);
+                }
+                if (a.base) {
+                    const int col = cb + a.K;
+                    if (col >= 0 && col < BK) Traits<TS>::put(row + col * Traits<TS>::ES, silu(xv));
+                }
+            }
+        }
+    }
+};
+
+// dC B operand Phi'^T[(i, m), b]: tile rows are the 256 packed columns
+// n0 .. n0+255 of Phi', k runs over the batch.  Thread t handles row
+// b = k0 + (t % BK) and the inputs slot, slot + NS, ... of the tile
+// (slot = t / BK).  The whole tile is zero-filled, then (after a barrier)
+// the non-zeros are scattered.
+template <typename TS>
+struct GenDcB {
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int NS = 256 / BK;                     // input slots
+    static constexpr int MAXQ = (256 / 4 + 2 + NS - 1) / NS;
+    const TS* x;
+    int n0, i_first, nin, bl, slot;
+    float xr[MAXQ];
+    __device__ GenDcB(const GemmArgs& a, int tn) {
+        x = static_cast<const TS*>(a.x);
+        n0 = tn * 256;
+        i_first = n0 / a.Kb;
+        const int i_last = min((n0 + 255) / a.Kb, a.I - 1);
+        nin = i_last - i_first + 1;
+        bl = threadIdx.x % BK;
+        slot = threadIdx.x / BK;
+    }
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        const int b = kt * BK + bl;
+        const bool ok = b < a.N;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            const int il = slot + NS * q;
+            if (il < nin && ok) xr[q] = load_f(x, (int64_t)b * a.I + i_first + il);
+        }
+    }
+    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
+        {
+            char* row = S + threadIdx.x * PITCH;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+        const int b = kt * BK + bl;
+        if (b >= a.N) return;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            const int il = slot + NS * q;
+            if (il < nin) {
+                const float xv = xr[q];
+                float u;
+                const int s = span_u(xv, a.g, u);
+                float bb[4];
+                pieces(u, bb[0], bb[1], bb[2], bb[3]);
+                const int rb = (i_first + il) * a.Kb - n0;   // tile row of (i, m = 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = s - 3 + r;
+                    const int row = rb + m;
+                    if (m >= 0 && m < a.K && row >= 0 && row < 256)
+                        Traits<TS>::put(S + row * PITCH + bl * Traits<TS>::ES, bb[r]);
+                }
+                if (a.base) {
+                    const int row = rb + a.K;
+                    if (row >= 0 && row < 256)
+                        Traits<TS>::put(S + row * PITCH + bl * Traits<TS>::ES, silu(xv));
+                }
+            }
+        }
+    }
+};
+
+// Loaded operands wrapped to the generator interface.
+struct LoadA {
+    LoadOp op;
+    __device__ LoadA(const GemmArgs& a, int tm, int) : op(a.a, (int64_t)tm * 256, a.lda) {}
+    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
+    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
+};
+struct LoadB {                       // rows n0 = tn * 256
+    LoadOp op;
+    __device__ LoadB(const GemmArgs& a, int, int tn) : op(a.b, (int64_t)tn * 256, a.ldb) {}
+    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
+    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
+};
+struct LoadBdx {                     // rows n0 = tn * Qn * Kb: whole inputs per tile
+    LoadOp op;
+    __device__ LoadBdx(const GemmArgs& a, int, int tn)
+        : op(a.b, (int64_t)tn * a.Qn * a.Kb, a.ldb) {}
+    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
+    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
+};
+template <typename TS>
+struct GenA {
+    GenFwdA<TS> g;
+    __device__ GenA(const GemmArgs& a, int tm, int) : g(a, tm) {}
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) { g.fetch(a, kt); }
+    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) { g.store(a, S, kt); }
+};
+template <typename TS>
+struct GenB {
+    GenDcB<TS> g;
+    __device__ GenB(const GemmArgs& a, int, int tn) : g(a, tn) {}
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) { g.fetch(a, kt); }
+    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) { g.store(a, S, kt); }
+};
+
+typedef f32x4 Acc[8][8];
+
+// ---- epilogues ----
+// acc[fi][fj][r] holds D[wm + 16 fi + 4 (lane / 16) + r][wn + 16 fj + lane % 16].
+struct EpiY {
+    template <typename TS>
+    __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char*) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int r0 = tm * 256 + (wave >> 1) * 128 + 4 * (lane >> 4);
+        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 15);
+#pragma unroll
+        for (int fi = 0; fi < 8; ++fi)
+#pragma unroll
+            for (int fj = 0; fj < 8; ++fj) {
+                const int col = c0 + 16 * fj;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = r0 + 16 * fi + r;
+                    if (row < a.N && col < a.O) a.out0[(int64_t)row * a.O + col] = acc[fi][fj][r];
+                }
+            }
+    }
+};
+
+struct EpiDC {
+    template <typename TS>
+    __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char*) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int r0 = tm * 256 + (wave >> 1) * 128 + 4 * (lane >> 4);
+        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 15);
+#pragma unroll
+        for (int fj = 0; fj < 8; ++fj) {
+            const int n = c0 + 16 * fj;
+            if (n >= a.IKb) continue;
+            const int i = n / a.Kb, m = n - i * a.Kb;
+            const bool spline = m < a.K;
+            if (spline ? !a.out0 : !a.out1) continue;
+#pragma unroll
+            for (int fi = 0; fi < 8; ++fi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = r0 + 16 * fi + r;
+                    if (j >= a.O) continue;
+                    if (spline) a.out0[((int64_t)j * a.I + i) * a.K + m] = acc[fi][fj][r];
+                    else a.out1[(int64_t)j * a.I + i] = acc[fi][fj][r];
+                }
+        }
+    }
+};
+
+// dx: the P tile is staged through LDS in two phases.  In phase h every wave
+// writes its fragment rows 4h .. 4h+3 (64 of its 128 rows), so the staging
+// area holds 128 tile rows: LDS row (wave / 2) * 64 + rr is tile row
+// (wave / 2) * 128 + 64 h + rr.  Then each (row, input) pair of those rows
+// contracts its <= 4 spline columns with B' and its silu column with silu'.
+struct EpiDX {
+    template <typename TS>
+    __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char* lds) {
+        float* P = reinterpret_cast<float*>(lds);
+        const TS* x = static_cast<const TS*>(a.x);
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        const int i0 = tn * a.Qn;
+        const int nin = min(a.Qn, a.I - i0);
+        const int cw = (wave & 1) * 128 + (lane & 15);
+        const int rw = (wave >> 1) * 64 + 4 * (lane >> 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int fj = 0; fj < 8; ++fj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        P[(rw + 16 * f + r) * DX_PITCH + cw + 16 * fj] = acc[4 * h + f][fj][r];
+            __syncthreads();
+#pragma unroll 1
+            for (int e = t; e < 128 * nin; e += 256) {
+                const int rl = e / nin, il = e - rl * nin;
+                const int b = tm * 256 + (rl >> 6) * 128 + 64 * h + (rl & 63);
+                const int i = i0 + il;
+                if (b < a.N) {
+                    const float xv = load_f(x, (int64_t)b * a.I + i);
+                    float u;
+                    const int s = span_u(xv, a.g, u);
+                    float d[4];
+                    dpieces(u, a.g.scale, d[0], d[1], d[2], d[3]);
+                    const float* prow = P + rl * DX_PITCH + il * a.Kb;
+                    float v = a.base ? prow[a.K] * silu_prime(xv) : 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = s - 3 + r;
+                        if (m >= 0 && m < a.K) v = __builtin_fmaf(prow[m], d[r], v);
+                    }
+                    a.out0[(int64_t)b * a.I + i] = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+};
+
+// ---- the contraction kernel ----
+template <typename TS, class AOp, class BOp, class Epi>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
+    extern __shared__ uint4 lds4[];
+    char* lds = reinterpret_cast<char*>(lds4);
+    int tm, tn;
+    tile_coords(args, tm, tn);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+    AOp A(args, tm, tn);
+    BOp B(args, tm, tn);
+    Acc acc;
+#pragma unroll
+    for (int fi = 0; fi < 8; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 8; ++fj) acc[fi][fj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    A.fetch(args, 0);
+    B.fetch(args, 0);
+    A.store(args, lds, 0);
+    B.store(args, lds + TILE_BYTES, 0);
+    __syncthreads();
+    const int arow = (wm + (lane & 15)) * PITCH + (lane >> 4) * 16;
+    const int brow = (wn + (lane & 15)) * PITCH + (lane >> 4) * 16;
+    // MFMAs over one staged k-tile: 2 k-steps of 64 bytes per row.
+    auto compute = [&](const char* As, const char* Bs) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 bf[8];
+#pragma unroll
+            for (int f = 0; f < 8; ++f)
+                bf[f] = *reinterpret_cast<const uint4*>(Bs + brow + f * 16 * PITCH + ks * 64);
+#pragma unroll
+            for (int fi = 0; fi < 8; ++fi) {
+                const uint4 af = *reinterpret_cast<const uint4*>(As + arow + fi * 16 * PITCH + ks * 64);
+#pragma unroll
+                for (int fj = 0; fj < 8; ++fj) Traits<TS>::mma(acc[fi][fj], af, bf[fj]);
+            }
+            // keep one k-step of fragments live at a time (bounds register use)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // The last k-tile is peeled so that fetch/store are unconditional in the
+    // loop and the staging registers die at each store.
+    for (int kt = 0; kt + 1 < args.nkt; ++kt) {
+        const int cur = kt & 1;
+        A.fetch(args, kt + 1);
+        B.fetch(args, kt + 1);
+        const char* As = lds + cur * STAGE_BYTES;
+        compute(As, As + TILE_BYTES);
+        char* Sn = lds + (cur ^ 1) * STAGE_BYTES;
+        A.store(args, Sn, kt + 1);
+        B.store(args, Sn + TILE_BYTES, kt + 1);
+        __syncthreads();
+    }
+    {
+        const char* As = lds + ((args.nkt - 1) & 1) * STAGE_BYTES;
+        compute(As, As + TILE_BYTES);
+        __syncthreads();
+    }
+    Epi::template run<TS>(args, acc, tm, tn, lds);
+}
+
+// ---- packing ----
+// C'[j][k], k = i * Kb + m: C[j, i, m] for m < K, W_base[j, i] for m = K; zero
+// outside [0, O) x [0, I*Kb).  One block row per j, 4 consecutive k per thread.
+template <typename TS>
+__global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
+                                TS* __restrict__ cp, int O, int I, int K, int Kb, int64_t Kf,
+                                int64_t Opad) {
+    const int64_t IKb = (int64_t)I * Kb;
+    for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
+    TS* dst = cp + j * Kf;
+    for (int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k0 < Kf;
+         k0 += (int64_t)gridDim.x * blockDim.x * 4) {
+        int i = (int)(k0 / Kb), m = (int)(k0 - (int64_t)i * Kb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t k = k0 + e;
+            TS v = TS(0);
+            if (j < O && k < IKb)
+                v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
+            if (k < Kf) dst[k] = v;
+            if (++m == Kb) { m = 0; ++i; }
+        }
+    }
+    }
+}
+
+// Transposed C'^T[k][j] for k < rowsT, j < Opad, through a 64 x 64 LDS tile.
+template <typename TS>
+__global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
+                                TS* __restrict__ cpt, int O, int I, int K, int Kb,
+                                int64_t rowsT, int64_t Opad) {
+    __shared__ TS tile[64][65];
+    const int64_t k0 = (int64_t)blockIdx.x * 64;
+    const int j0 = blockIdx.y * 64;
+    const int64_t IKb = (int64_t)I * Kb;
+    const int t = threadIdx.x;
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int jj = e / 64, kk = e % 64;
+        const int j = j0 + jj;
+        const int64_t k = k0 + kk;
+        TS v = TS(0);
+        if (j < O && k < IKb) {
+            const int i = (int)(k / Kb), m = (int)(k - (int64_t)i * Kb);
+            v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
+        }
+        tile[jj][kk] = v;
+    }
+    __syncthreads();
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int kk = e / 64, jj = e % 64;
+        const int64_t k = k0 + kk;
+        if (k < rowsT) cpt[k * Opad + j0 + jj] = tile[jj][kk];
+    }
+}
+
+template <typename TS> __device__ __forceinline__ TS to_store(float v);
+template <> __device__ __forceinline__ float to_store<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { return f2bf(v); }
+
+// dy (float32 [N, O]) -> dyp [Npad][Opad] and dyT [Opad][Npad] in the storage
+// dtype, zero-padded; 64 x 64 tiles through LDS.
+template <typename TS>
+__global__ void prep_dy_kernel(const float* __restrict__ dy, TS* __restrict__ dyp,
+                               TS* __restrict__ dyt, int N, int O, int64_t Npad, int64_t Opad) {
+    __shared__ TS tile[64][65];
+    const int64_t b0 = (int64_t)blockIdx.x * 64;
+    const int64_t j0 = (int64_t)blockIdx.y * 64;
+    const int t = threadIdx.x;
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int bb = e / 64, jj = e % 64;
+        const int64_t b = b0 + bb, j = j0 + jj;
+        const TS v = (b < N && j < O) ? to_store<TS>(dy[b * O + j]) : TS(0);
+        dyp[b * Opad + j] = v;
+        tile[bb][jj] = v;
+    }
+    __syncthreads();
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int jj = e / 64, bb = e % 64;
+        dyt[(j0 + jj) * Npad + b0 + bb] = tile[bb][jj];
+    }
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <typename TS, class AOp, class BOp, class Epi>
+hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
+    auto kern = gemm_kernel<TS, AOp, BOp, Epi>;
+    hipError_t e = set_lds(kern, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+GemmArgs base_args(const Plan& p, const void* x) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.g = p.gk;
+    a.N = (int)p.N;
+    a.I = (int)p.I;
+    a.O = (int)p.O;
+    a.K = p.K;
+    a.Kb = p.Kb;
+    a.base = p.base;
+    a.Qn = p.Qn;
+    a.IKb = p.IKb;
+    a.group_m = 16;
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s) {
+    const int64_t per_block = 256 * 4;
+    dim3 grid((unsigned)std::min<int64_t>((p.Kf + per_block - 1) / per_block, 65535),
+              (unsigned)std::min<int64_t>(p.Opad, 65535));
+    if (p.dtype == KAN_F32)
+        hipLaunchKernelGGL(pack_fwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
+                           static_cast<const float*>(W), static_cast<float*>(cp), (int)p.O, (int)p.I,
+                           p.K, p.Kb, p.Kf, p.Opad);
+    else
+        hipLaunchKernelGGL(pack_fwd_kernel<uint16_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(W),
+                           static_cast<uint16_t*>(cp), (int)p.O, (int)p.I, p.K, p.Kb, p.Kf, p.Opad);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s) {
+    dim3 grid((unsigned)((p.rowsT + 63) / 64), (unsigned)(p.Opad / 64));
+    if (p.dtype == KAN_F32)
+        hipLaunchKernelGGL(pack_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
+                           static_cast<const float*>(W), static_cast<float*>(cpt), (int)p.O, (int)p.I,
+                           p.K, p.Kb, p.rowsT, p.Opad);
+    else
+        hipLaunchKernelGGL(pack_bwd_kernel<uint16_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(W),
+                           static_cast<uint16_t*>(cpt), (int)p.O, (int)p.I, p.K, p.Kb, p.rowsT, p.Opad);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s) {
+    dim3 grid((unsigned)(p.Npad / 64), (unsigned)(p.Opad / 64));
+    if (p.dtype == KAN_F32)
+        hipLaunchKernelGGL(prep_dy_kernel<float>, grid, dim3(256), 0, s, dy, static_cast<float*>(dyp),
+                           static_cast<float*>(dyt), (int)p.N, (int)p.O, p.Npad, p.Opad);
+    else
+        hipLaunchKernelGGL(prep_dy_kernel<uint16_t>, grid, dim3(256), 0, s, dy,
+                           static_cast<uint16_t*>(dyp), static_cast<uint16_t*>(dyt), (int)p.N, (int)p.O,
+                           p.Npad, p.Opad);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s) {
+    GemmArgs a = base_args(p, x);
+    a.tiles_m = (int)(p.Npad / 256);
+    a.tiles_n = (int)(p.Opad / 256);
+    a.b = static_cast<const char*>(cp);
+    a.ldb = p.Kf * p.esize;
+    a.nkt = (int)(p.Kf / p.BK);
+    a.out0 = y;
+    if (p.dtype == KAN_F32) return run_gemm<float, GenA<float>, LoadB, EpiY>(a, s);
+    return run_gemm<uint16_t, GenA<uint16_t>, LoadB, EpiY>(a, s);
+}
+
+hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
+                          float* dx, hipStream_t s) {
+    GemmArgs a = base_args(p, x);
+    a.tiles_m = (int)(p.Npad / 256);
+    a.tiles_n = (int)p.tiles_dx;
+    a.a = static_cast<const char*>(dyp);
+    a.lda = p.Opad * p.esize;
+    a.b = static_cast<const char*>(cpt);
+    a.ldb = p.Opad * p.esize;
+    a.nkt = (int)(p.Opad / p.BK);
+    a.out0 = dx;
+    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, LoadBdx, EpiDX>(a, s);
+    return run_gemm<uint16_t, LoadA, LoadBdx, EpiDX>(a, s);
+}
+
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
+                          hipStream_t s) {
+    GemmArgs a = base_args(p, x);
+    a.tiles_m = (int)(p.Opad / 256);
+    a.tiles_n = (int)((p.IKb + 255) / 256);
+    a.a = static_cast<const char*>(dyt);
+    a.lda = p.Npad * p.esize;
+    a.nkt = (int)(p.Npad / p.BK);
+    a.out0 = dC;
+    a.out1 = dW;
+    a.group_m = 2;
+    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, GenB<float>, EpiDC>(a, s);
+    return run_gemm<uint16_t, LoadA, GenB<uint16_t>, EpiDC>(a, s);
+}
+
+}  // namespace kan

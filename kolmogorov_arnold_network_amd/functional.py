@@ -1,0 +1,139 @@
+"""Torch-facing wrappers of the C entry points, under the same names.
+
+Each wrapper checks dtype / device / contiguity, allocates the outputs and the
+workspace with torch (device memory only), and passes raw pointers plus the
+current HIP stream to the library.  No arithmetic of the layer happens here.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float32: L.KAN_F32, torch.bfloat16: L.KAN_BF16}
+_VARIANTS = {"auto": L.KAN_VARIANT_AUTO, "mfma": L.KAN_VARIANT_MFMA, "gather": L.KAN_VARIANT_GATHER}
+
+
+def _variant(v):
+    return _VARIANTS[v] if isinstance(v, str) else int(v)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_tensor(t, name, dtypes, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def layer_desc(x, C, W, grid, variant="auto", flags=0):
+    """``kan_desc_t`` for ``x [N, I]``, ``C [O, I, G+3]``, ``W [O, I]`` or None."""
+    lo, hi, G = grid
+    N, I = x.shape
+    O, I2, K = C.shape
+    if I2 != I or K != G + 3:
+        raise ValueError("C must be [O, I, G+3] = [%d, %d, %d], got %s" % (O, I, G + 3, tuple(C.shape)))
+    if W is not None and tuple(W.shape) != (O, I):
+        raise ValueError("W_base must be [O, I]")
+    if x.dtype != C.dtype or (W is not None and W.dtype != C.dtype):
+        raise ValueError("x, C and W_base must share one dtype")
+    return L.make_desc(N, I, O, lo, hi, G, _DTYPES[x.dtype], W is not None, _variant(variant), flags)
+
+
+def kan_workspace_size(desc, pass_):
+    n = L.lib().kan_workspace_size(ctypes.byref(desc), int(pass_))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid layer description")
+    return int(n)
+
+
+def workspace(desc, pass_, device):
+    """A fresh device workspace for one pass (torch allocator; 512-byte aligned)."""
+    n = kan_workspace_size(desc, pass_)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None):
+    """Packs the pass's operands into a workspace; returns ``(ws, ws_bytes)``."""
+    desc = layer_desc(x, C, W, grid, variant)
+    if ws is None:
+        ws = workspace(desc, pass_, C.device)
+    buf, n = ws
+    L.check(L.lib().kan_prepare(ctypes.byref(desc), int(pass_), _ptr(C), _ptr(W), _ptr(dy),
+                                _ptr(buf), n, _stream(C)), "kan_prepare")
+    return ws
+
+
+def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None):
+    """``y [N, O]`` float32 of one KAN layer."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    _check_tensor(W, "W_base", _DTYPES, x.device)
+    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_PREPARED if prepared else 0)
+    if ws is None:
+        ws = workspace(desc, L.KAN_PASS_FORWARD, x.device)
+    buf, n = ws
+    y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
+                                                device=x.device)
+    _check_tensor(y, "y", (torch.float32,), x.device)
+    L.check(L.lib().kan_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(W), _ptr(y), _ptr(buf),
+                                n, _stream(x)), "kan_forward")
+    return y
+
+
+def kan_backward(x, C, W, dy, grid, need_dx=True, need_dC=True, need_dW=True, variant="auto",
+                 ws=None, prepared=False):
+    """``(dx [N, I], dC [O, I, G+3], dW_base [O, I])`` float32; unrequested ones are None."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    _check_tensor(W, "W_base", _DTYPES, x.device)
+    _check_tensor(dy, "dy", (torch.float32,), x.device)
+    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_PREPARED if prepared else 0)
+    if tuple(dy.shape) != (x.shape[0], C.shape[0]):
+        raise ValueError("dy must be [N, O]")
+    if ws is None:
+        ws = workspace(desc, L.KAN_PASS_BACKWARD, x.device)
+    buf, n = ws
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty(x.shape, **f32) if need_dx else None
+    dC = torch.empty(C.shape, **f32) if need_dC else None
+    dW = torch.empty(W.shape, **f32) if (need_dW and W is not None) else None
+    L.check(L.lib().kan_backward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(W), _ptr(dy), _ptr(dx),
+                                 _ptr(dC), _ptr(dW), _ptr(buf), n, _stream(x)), "kan_backward")
+    return dx, dC, dW
+
+
+def kan_basis_eval(x, grid, need_B=True, need_dB=True):
+    """Dense ``B [n, G+3]`` and ``dB [n, G+3]`` of a 1-D tensor of inputs."""
+    _check_tensor(x, "x", _DTYPES)
+    lo, hi, G = grid
+    g = L.kan_grid_t(float(lo), float(hi), int(G), 3)
+    n = x.numel()
+    B = torch.empty((n, G + 3), dtype=torch.float32, device=x.device) if need_B else None
+    dB = torch.empty((n, G + 3), dtype=torch.float32, device=x.device) if need_dB else None
+    L.check(L.lib().kan_basis_eval(ctypes.byref(g), n, _DTYPES[x.dtype], _ptr(x), _ptr(B), _ptr(dB),
+                                   _stream(x)), "kan_basis_eval")
+    return B, dB
+
+
+def kan_cast_f32_to_bf16(t, out=None):
+    """Round-to-nearest-even float32 -> bfloat16 on the device."""
+    _check_tensor(t, "input", (torch.float32,))
+    o = out if out is not None else torch.empty(t.shape, dtype=torch.bfloat16, device=t.device)
+    L.check(L.lib().kan_cast_f32_to_bf16(_ptr(t), _ptr(o), t.numel(), _stream(t)),
+            "kan_cast_f32_to_bf16")
+    return o

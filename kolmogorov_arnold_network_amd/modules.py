@@ -1,0 +1,111 @@
+"""``KANLayer`` / ``KANNetwork``: torch modules over the HIP library.
+
+"KANLayer(in, out) replaces nn.Linear(in, out). Same interface, same
+optimizer, same training loop" (InKAN project page, "Why InKAN?"): the layer
+takes ``[..., in_features]`` and returns ``[..., out_features]``, and its
+parameters are plain tensors that any torch optimizer updates.  Autograd
+calls ``kan_backward``; torch only accumulates the returned gradients.
+"""
+
+import math
+
+import torch
+
+from . import functional as F
+
+
+class KANFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, C, W, lo, hi, G, variant):
+        ctx.grid = (lo, hi, G)
+        ctx.variant = variant
+        ctx.has_base = W is not None
+        ctx.save_for_backward(x, C, W)
+        return F.kan_forward(x, C, W, (lo, hi, G), variant)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, C, W = ctx.saved_tensors
+        need_x, need_C, need_W = ctx.needs_input_grad[:3]
+        dx, dC, dW = F.kan_backward(x, C, W, dy.contiguous().float(), ctx.grid, need_dx=need_x,
+                                    need_dC=need_C, need_dW=need_W and ctx.has_base,
+                                    variant=ctx.variant)
+        if dx is not None and dx.dtype != x.dtype:
+            dx = dx.to(x.dtype)
+        if dC is not None and dC.dtype != C.dtype:
+            dC = dC.to(C.dtype)
+        if dW is not None and dW.dtype != W.dtype:
+            dW = dW.to(W.dtype)
+        return dx, dC, dW, None, None, None, None
+
+
+class CastBF16(torch.autograd.Function):
+    """float32 -> bfloat16 on the device; the gradient passes through as float32."""
+
+    @staticmethod
+    def forward(ctx, t):
+        return F.kan_cast_f32_to_bf16(t.contiguous())
+
+    @staticmethod
+    def backward(ctx, g):
+        return g.float()
+
+
+class KANLayer(torch.nn.Module):
+    """One KAN layer: ``y_j = sum_i phi_ji(x_i)`` with cubic B-spline ``phi_ji``.
+
+    Parameters: ``coef [out, in, grid_size + 3]`` and, with ``base=True``,
+    ``base_weight [out, in]`` for the ``W_base * silu(x)`` branch.  ``dtype``
+    (float32 or bfloat16) is the storage of inputs and parameters; outputs
+    and gradients are computed in float32.
+    """
+
+    def __init__(self, in_features, out_features, grid_size=8, grid_range=(-1.0, 1.0), base=True,
+                 dtype=torch.float32, device=None, variant="auto", coef_std=0.1):
+        super().__init__()
+        self.in_features = int(in_features)
+        self.out_features = int(out_features)
+        self.grid_size = int(grid_size)
+        self.grid_range = (float(grid_range[0]), float(grid_range[1]))
+        self.variant = variant
+        fk = dict(dtype=dtype, device=device)
+        self.coef = torch.nn.Parameter(
+            torch.randn(out_features, in_features, grid_size + 3, **fk) * coef_std)
+        if base:
+            self.base_weight = torch.nn.Parameter(
+                torch.randn(out_features, in_features, **fk) / math.sqrt(in_features))
+        else:
+            self.register_parameter("base_weight", None)
+
+    @property
+    def grid(self):
+        return (self.grid_range[0], self.grid_range[1], self.grid_size)
+
+    def forward(self, x):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features)
+        if x2.dtype != self.coef.dtype:
+            x2 = CastBF16.apply(x2) if self.coef.dtype == torch.bfloat16 else x2.to(self.coef.dtype)
+        x2 = x2.contiguous()
+        y = KANFunction.apply(x2, self.coef, self.base_weight, self.grid_range[0],
+                              self.grid_range[1], self.grid_size, self.variant)
+        return y.reshape(*lead, self.out_features)
+
+    def extra_repr(self):
+        return "in=%d, out=%d, grid_size=%d, range=%s, base=%s, dtype=%s" % (
+            self.in_features, self.out_features, self.grid_size, self.grid_range,
+            self.base_weight is not None, self.coef.dtype)
+
+
+class KANNetwork(torch.nn.Module):
+    """A chain of ``KANLayer`` with nothing in between (InKAN "Quick Start")."""
+
+    def __init__(self, widths, **kw):
+        super().__init__()
+        self.layers = torch.nn.ModuleList(
+            KANLayer(widths[l], widths[l + 1], **kw) for l in range(len(widths) - 1))
+
+    def forward(self, x):
+        for layer in self.layers:
+            x = layer(x)
+        return x

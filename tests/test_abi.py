@@ -1,0 +1,198 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+``include/kan.h`` declares, and returns each validation error before any
+device work (pointers here are fake addresses that are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kan_testutil import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kan.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    from kolmogorov_arnold_network_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kan_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_lists_the_binding_exports():
+    assert declared_functions() == sorted(
+        __import__("kolmogorov_arnold_network_amd._lib", fromlist=["EXPORTS"]).EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    from kolmogorov_arnold_network_amd._build import LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_version_and_status_strings(L):
+    assert L.lib().kan_abi_version() == L.ABI_VERSION == 1
+    for code in range(0, -10, -1):
+        s = L.status_string(code)
+        assert s and s != "unknown status"
+    assert L.status_string(42) == "unknown status"
+
+
+def test_struct_layout(L):
+    assert ctypes.sizeof(L.kan_grid_t) == 16
+    assert ctypes.sizeof(L.kan_desc_t) == 3 * 8 + 16 + 4 * 4
+
+
+# fake, 256-aligned, non-overlapping device addresses (never dereferenced)
+X, C, W, Y, WS, DY, DX, DC, DW = [0x100000000 * (k + 1) for k in range(9)]
+
+
+def desc(L, **kw):
+    a = dict(N=64, I=16, O=8, lo=-1.0, hi=1.0, G=8, dtype=L.KAN_F32, has_base=1,
+             variant=L.KAN_VARIANT_MFMA, flags=0)
+    a.update(kw)
+    return L.make_desc(**a)
+
+
+def fwd(L, d, x=X, c=C, w=W, y=Y, ws=WS, nbytes=None):
+    if nbytes is None:
+        nbytes = L.lib().kan_workspace_size(ctypes.byref(d), L.KAN_PASS_FORWARD)
+    return L.lib().kan_forward(ctypes.byref(d), x, c, w, y, ws, nbytes, None)
+
+
+def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
+    if nbytes is None:
+        nbytes = L.lib().kan_workspace_size(ctypes.byref(d), L.KAN_PASS_BACKWARD)
+    return L.lib().kan_backward(ctypes.byref(d), x, c, w, dy, dx, dc, dw, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), "SHAPE"), (dict(I=0), "SHAPE"), (dict(O=0), "SHAPE"), (dict(N=1 << 40), "SHAPE"),
+    (dict(G=0), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
+    (dict(lo=2.0, hi=1.0), "GRID"), (dict(lo=float("nan")), "GRID"), (dict(hi=float("inf")), "GRID"),
+    (dict(degree=2), "UNSUPPORTED"), (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
+    (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
+    (dict(G=254, variant=2 - 1), "UNSUPPORTED"),     # Kb = 258 > 256: no MFMA tile
+])
+def test_bad_descriptors(L, kw, code):
+    d = desc(L, **kw)
+    want = getattr(L, "KAN_ERR_" + code)
+    assert fwd(L, d, nbytes=1 << 40) == want
+    assert bwd(L, d, nbytes=1 << 40) == want
+    assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == ctypes.c_size_t(-1).value
+
+
+def test_null_desc(L):
+    lib = L.lib()
+    assert lib.kan_forward(None, X, C, W, Y, WS, 1 << 30, None) == L.KAN_ERR_NULL
+    assert lib.kan_backward(None, X, C, W, DY, DX, DC, DW, WS, 1 << 30, None) == L.KAN_ERR_NULL
+    assert lib.kan_workspace_size(None, 0) == ctypes.c_size_t(-1).value
+
+
+def test_forward_pointer_checks(L):
+    d = desc(L)
+    assert fwd(L, d, x=None) == L.KAN_ERR_NULL
+    assert fwd(L, d, y=None) == L.KAN_ERR_NULL
+    assert fwd(L, d, c=None) == L.KAN_ERR_NULL
+    assert fwd(L, d, w=None) == L.KAN_ERR_NULL                     # has_base=1 needs W
+    assert fwd(L, desc(L, has_base=0)) == L.KAN_ERR_NULL          # has_base=0 forbids W
+    assert fwd(L, d, x=X + 8) == L.KAN_ERR_ALIGN
+    assert fwd(L, d, y=Y + 4) == L.KAN_ERR_ALIGN
+    assert fwd(L, d, ws=WS + 128) == L.KAN_ERR_ALIGN
+    assert fwd(L, d, nbytes=16) == L.KAN_ERR_WORKSPACE
+    assert fwd(L, d, ws=None) == L.KAN_ERR_NULL
+    assert fwd(L, d, y=X + 64) == L.KAN_ERR_ALIAS
+    assert fwd(L, d, y=C) == L.KAN_ERR_ALIAS
+    assert fwd(L, d, ws=Y) == L.KAN_ERR_ALIAS
+
+
+def test_backward_pointer_checks(L):
+    d = desc(L)
+    assert bwd(L, d, dy=None) == L.KAN_ERR_NULL
+    assert bwd(L, d, x=None) == L.KAN_ERR_NULL
+    assert bwd(L, desc(L, has_base=0), w=None) == L.KAN_ERR_NULL  # dW given without base
+    assert bwd(L, d, dy=DY + 2) == L.KAN_ERR_ALIGN
+    assert bwd(L, d, dc=DC + 4) == L.KAN_ERR_ALIGN
+    assert bwd(L, d, nbytes=0) == L.KAN_ERR_WORKSPACE
+    assert bwd(L, d, dx=DC) == L.KAN_ERR_ALIAS
+    assert bwd(L, d, dw=DY) == L.KAN_ERR_ALIAS
+    assert bwd(L, d, dc=X) == L.KAN_ERR_ALIAS
+    assert bwd(L, d, ws=DX) == L.KAN_ERR_ALIAS
+
+
+def test_empty_batch_forward_returns_ok_without_launch(L):
+    assert fwd(L, desc(L, N=0)) == L.KAN_OK
+
+
+def test_workspace_sizes(L):
+    ws = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 0)
+    wb = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 1)
+    assert ws(variant=L.KAN_VARIANT_GATHER) == 0 and wb(variant=L.KAN_VARIANT_GATHER) == 0
+    # MFMA forward: packed C' [O padded to 256][I*Kb padded to the k-tile]
+    r = lambda a, b: (a + b - 1) // b * b
+    for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
+        for (N, I, O, G, base) in [(64, 16, 8, 8, 1), (1000, 777, 300, 20, 0), (5, 3, 2, 1, 1)]:
+            Kb = G + 3 + base
+            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == r(r(O, 256) * r(I * Kb, bk) * es, 256)
+            Qn = 256 // Kb
+            tiles = (I + Qn - 1) // Qn
+            rowsT = r((tiles - 1) * Qn * Kb + 256, bk)
+            Op, Np = r(O, 256), r(N, 256)
+            want = r(rowsT * Op * es, 256) + 2 * r(Np * Op * es, 256)
+            assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
+    # auto: bf16 on the matrix cores, float32 on the gather kernels, and the gather
+    # kernels whenever an input's columns exceed one tile
+    assert ws(G=254, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == 0
+    assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
+    assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ws(variant=L.KAN_VARIANT_MFMA,
+                                                                   dtype=L.KAN_BF16) > 0
+
+
+def test_prepare_checks(L):
+    d = desc(L)
+    lib = L.lib()
+    assert lib.kan_prepare(ctypes.byref(d), 5, C, W, DY, WS, 1 << 30, None) == L.KAN_ERR_UNSUPPORTED
+    assert lib.kan_prepare(ctypes.byref(d), 0, None, W, None, WS, 1 << 30, None) == L.KAN_ERR_NULL
+    assert lib.kan_prepare(ctypes.byref(d), 1, C, W, None, WS, 1 << 30, None) == L.KAN_ERR_NULL
+    assert lib.kan_prepare(ctypes.byref(d), 0, C, W, None, C, 1 << 30, None) == L.KAN_ERR_ALIAS
+
+
+def test_basis_and_cast_checks(L):
+    lib = L.lib()
+    g = L.kan_grid_t(-1.0, 1.0, 8, 3)
+    assert lib.kan_basis_eval(None, 4, 0, X, Y, DY, None) == L.KAN_ERR_NULL
+    assert lib.kan_basis_eval(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 0, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
+    assert lib.kan_basis_eval(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 1)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
+    assert lib.kan_basis_eval(ctypes.byref(g), -1, 0, X, Y, None, None) == L.KAN_ERR_SHAPE
+    assert lib.kan_basis_eval(ctypes.byref(g), 0, 0, X, Y, None, None) == L.KAN_OK
+    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X, None, None, None) == L.KAN_ERR_NULL
+    assert lib.kan_basis_eval(ctypes.byref(g), 4, 3, X, Y, None, None) == L.KAN_ERR_DTYPE
+    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X + 4, Y, None, None) == L.KAN_ERR_ALIGN
+    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X, X, None, None) == L.KAN_ERR_ALIAS
+    assert lib.kan_cast_f32_to_bf16(X, Y, -1, None) == L.KAN_ERR_SHAPE
+    assert lib.kan_cast_f32_to_bf16(X, Y, 0, None) == L.KAN_OK
+    assert lib.kan_cast_f32_to_bf16(None, Y, 4, None) == L.KAN_ERR_NULL
+    assert lib.kan_cast_f32_to_bf16(X + 2, Y, 4, None) == L.KAN_ERR_ALIGN
+    assert lib.kan_cast_f32_to_bf16(X, X + 16, 8, None) == L.KAN_ERR_ALIAS
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from kolmogorov_arnold_network_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,365 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Tolerances: float32 path, normwise max relative error <= 1e-5 per output
+tensor; bf16-input / float32-accumulate path, relative Frobenius error <= 1e-2
+per output tensor.  Small shapes are compared element by element in full;
+the full-size workloads are compared on seeded samples of rows (y, dx: a row
+depends only on the same row of the inputs) and of (j, i) pairs (dC, dW: each
+entry is its own sum over all rows), which the oracle computes one by one.
+"""
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from kan_testutil import TOL_BF16, TOL_F32, ensure_built, metric, rel_fro, rel_inf, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def F():
+    ensure_built()
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from kolmogorov_arnold_network_amd import functional
+    return functional
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# basis step alone
+@pytest.mark.parametrize("G", [1, 5, 8, 20, 50])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_basis_kernel(F, G, dtype):
+    claims = json.load(open(os.path.join(GOLD, "inkan_claims.json")))
+    lo, hi = -1.0, 1.0
+    h = (hi - lo) / G
+    rng = np.random.default_rng(G)
+    x = np.concatenate([rng.uniform(lo - 4 * h, hi + 4 * h, 200000),
+                        lo + (np.arange(G + 7) - 3) * h, [lo, hi, 0.0, lo - 1e-7, hi + 1e-7]])
+    x = x.astype(np.float32)
+    if dtype == "bf16":
+        x = wl.to_bf16_values(x)
+    say("basis G=%d dtype=%s n=%d" % (G, dtype, x.size))
+    B, dB = F.kan_basis_eval(to_dev(x, dtype), (lo, hi, G))
+    _sync()
+    B, dB = _np(B), _np(dB)
+    ref = oracle.basis(x.astype(np.float64), lo, hi, G)
+    dref = oracle.basis_derivative(x.astype(np.float64), lo, hi, G)
+    tol = 2 * claims["basis_float32_abs_accuracy"]
+    assert np.max(np.abs(B - ref)) <= tol
+    assert B.min() >= 0.0                                    # non-negative, bitwise
+    assert np.count_nonzero(B, axis=1).max() <= claims["support_intervals"]
+    assert np.max(np.abs(dB - dref)) <= tol * 4 * (G / (hi - lo))
+
+
+# ---------------------------------------------------------------------------
+# small ragged layers, every variant, in full
+SMALL = [  # N, I, O, G, base
+    (1, 1, 1, 1, True), (37, 5, 3, 8, False), (300, 29, 17, 5, True), (513, 64, 260, 20, True),
+    (100, 13, 7, 50, False), (257, 40, 300, 8, True), (64, 256, 31, 3, True), (20, 3, 513, 12, False),
+]
+
+
+def _layer_on_gpu(F, d, variant):
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    dt = d["dtype"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, Wt, dyt = to_dev(x, dt), to_dev(C, dt), to_dev(W, dt), to_dev(dy, "f32")
+    y = F.kan_forward(xt, Ct, Wt, grid, variant)
+    dx, dC, dW = F.kan_backward(xt, Ct, Wt, dyt, grid, variant=variant)
+    _sync()
+    return _np(y), _np(dx), _np(dC), _np(dW)
+
+
+def _layer_oracle(d):
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    y = oracle.layer_forward(x, C, W, *grid)
+    dx, dC, dW = oracle.layer_backward(x, C, W, dy, *grid)
+    return y, dx, dC, dW
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=["x".join(map(str, s)) for s in SMALL])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["mfma", "gather"])
+def test_small_layer(F, shape, dtype, variant):
+    N, I, O, G, base = shape
+    say("small layer %s dtype=%s variant=%s" % (shape, dtype, variant))
+    d = wl.random_layer(N, I, O, G, dtype=dtype, base=base, seed=N + I + O + G)
+    got = _layer_on_gpu(F, d, variant)
+    ref = _layer_oracle(d)
+    err, tol = metric(dtype)
+    for name, a, r in zip(("y", "dx", "dC", "dW"), got, ref):
+        if r is None:
+            assert a is None
+            continue
+        e = err(a, r)
+        assert e <= tol, "%s error %.3e > %.0e" % (name, e, tol)
+
+
+def test_deterministic_and_prepared(F):
+    import torch
+    d = wl.random_layer(700, 48, 300, 8, dtype="bf16", base=True, seed=5)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, Wt, dyt = to_dev(x, "bf16"), to_dev(C, "bf16"), to_dev(W, "bf16"), to_dev(dy, "f32")
+    say("determinism bf16 700x48x300")
+    outs = []
+    for _ in range(3):
+        outs.append((F.kan_forward(xt, Ct, Wt, grid, "mfma"),) +
+                    F.kan_backward(xt, Ct, Wt, dyt, grid, variant="mfma"))
+    _sync()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+    # pre-packed workspaces give the same bits
+    from kolmogorov_arnold_network_amd import _lib as L
+    wsf = F.kan_prepare(xt, Ct, Wt, grid, L.KAN_PASS_FORWARD, variant="mfma")
+    y2 = F.kan_forward(xt, Ct, Wt, grid, "mfma", ws=wsf, prepared=True)
+    wsb = F.kan_prepare(xt, Ct, Wt, grid, L.KAN_PASS_BACKWARD, dy=dyt, variant="mfma")
+    b2 = F.kan_backward(xt, Ct, Wt, dyt, grid, variant="mfma", ws=wsb, prepared=True)
+    _sync()
+    assert torch.equal(y2, outs[0][0])
+    for a, b in zip(b2, outs[0][1:]):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("variant", ["mfma", "gather"])
+def test_empty_batch(F, variant):
+    import torch
+    say("empty batch", variant)
+    C = torch.randn(5, 7, 11, device="cuda:0")
+    W = torch.randn(5, 7, device="cuda:0")
+    x = torch.empty(0, 7, device="cuda:0")
+    y = F.kan_forward(x, C, W, (-1.0, 1.0, 8), variant)
+    dx, dC, dW = F.kan_backward(x, C, W, torch.empty(0, 5, device="cuda:0"), (-1.0, 1.0, 8),
+                                variant=variant)
+    _sync()
+    assert y.shape == (0, 5) and dx.shape == (0, 7)
+    assert torch.count_nonzero(dC) == 0 and torch.count_nonzero(dW) == 0
+
+
+@pytest.mark.parametrize("variant", ["mfma", "gather"])
+def test_output_guards_and_nonfinite_inputs(F, variant):
+    """Outputs written exactly in place (NaN canaries around them stay NaN);
+    non-finite inputs neither crash nor disturb other rows."""
+    import ctypes
+    import torch
+    from kolmogorov_arnold_network_amd import _lib as L
+    say("guards", variant)
+    N, I, O, G = 130, 21, 19, 8
+    d = wl.random_layer(N, I, O, G, dtype="f32", base=True, seed=11)
+    (C, W), x, dy = d["layers"][0], d["x"].copy(), d["dy"]
+    bad_rows = [3, 77]
+    x[3, 4], x[77, 0] = np.nan, np.inf
+    dev = "cuda:0"
+    xt, Ct, Wt, dyt = to_dev(x, "f32"), to_dev(C, "f32"), to_dev(W, "f32"), to_dev(dy, "f32")
+    G4 = 64  # guard floats each side (keeps 16-byte alignment)
+
+    def guarded(n):
+        buf = torch.full((n + 2 * G4,), float("nan"), device=dev)
+        return buf, buf[G4:G4 + n]
+
+    yb, y = guarded(N * O)
+    dxb, dx = guarded(N * I)
+    dCb, dC = guarded(O * I * (G + 3))
+    dWb, dW = guarded(O * I)
+    desc = F.layer_desc(xt, Ct, Wt, (-1.0, 1.0, G), variant)
+    wsf, nf = F.workspace(desc, 0, dev)
+    wsb, nb = F.workspace(desc, 1, dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L.check(L.lib().kan_forward(ctypes.byref(desc), p(xt), p(Ct), p(Wt), p(y), p(wsf), nf, s), "fwd")
+    L.check(L.lib().kan_backward(ctypes.byref(desc), p(xt), p(Ct), p(Wt), p(dyt), p(dx), p(dC), p(dW),
+                                 p(wsb), nb, s), "bwd")
+    _sync()
+    for buf in (yb, dxb, dCb, dWb):
+        assert torch.isnan(buf[:G4]).all() and torch.isnan(buf[-G4:]).all()
+    ok = np.setdiff1d(np.arange(N), bad_rows)
+    ref_y = oracle.layer_forward(x[ok], C, W, -1.0, 1.0, G)
+    assert rel_inf(_np(y).reshape(N, O)[ok], ref_y) <= TOL_F32
+    ref_dx = oracle.layer_backward(x[ok], C, W, dy[ok], -1.0, 1.0, G, need=("dx",))[0]
+    assert rel_inf(_np(dx).reshape(N, I)[ok], ref_dx) <= TOL_F32
+    # the spline part of dC never sees the bad inputs: their basis is empty
+    xc = x.copy()
+    xc[3, 4] = xc[77, 0] = 1e6
+    ref_dC = oracle.layer_backward(xc, C, W, dy, -1.0, 1.0, G, need=("dC",))[1]
+    assert rel_inf(_np(dC).reshape(O, I, G + 3), ref_dC) <= TOL_F32
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+def run_net_gpu(F, d, variant="auto"):
+    """Forward + backward of the whole chain through the C ABI."""
+    import torch
+    dt = d["dtype"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xs = [to_dev(d["x"], dt)]
+    Ls = [(to_dev(C, dt), to_dev(W, dt)) for C, W in d["layers"]]
+    for li, (Ct, Wt) in enumerate(Ls):
+        y = F.kan_forward(xs[-1], Ct, Wt, grid, variant)
+        if li + 1 < len(Ls):
+            y = F.kan_cast_f32_to_bf16(y) if dt == "bf16" else y
+        xs.append(y)
+    g = to_dev(d["dy"], "f32")
+    grads = [None] * len(Ls)
+    for li in range(len(Ls) - 1, -1, -1):
+        Ct, Wt = Ls[li]
+        dx, dC, dW = F.kan_backward(xs[li], Ct, Wt, g, grid, variant=variant)
+        grads[li] = (dC, dW)
+        g = dx
+    torch.cuda.synchronize()
+    return xs[-1], g, grads
+
+
+def check_net(F, d, rows=None, pairs=64, variant="auto", seed=0):
+    name = d["name"]
+    lo, hi, G = d["lo"], d["hi"], d["G"]
+    layers = d["layers"]
+    bf = d["dtype"] == "bf16"
+    err, tol = metric(d["dtype"])
+    say("workload %s G=%d N=%d variant=%s: GPU" % (name, G, d["N"], variant))
+    y, dx0, grads = run_net_gpu(F, d, variant)
+    N = d["N"]
+    R = np.arange(N) if rows is None else wl.sample_indices(N, rows, seed)
+    say("workload %s: oracle rows=%d" % (name, len(R)))
+    acts = oracle.network_forward(d["x"][R], layers, lo, hi, G, bf16_between=bf)
+    dxr, _ = oracle.network_backward(acts, layers, d["dy"][R], lo, hi, G)
+    errs = {"y": err(_np(y)[R], acts[-1]), "dx0": err(_np(dx0)[R], dxr)}
+    # per-layer coefficient gradients on sampled (j, i) pairs over all rows
+    nl = len(layers)
+    for li in range(nl):
+        C, W = layers[li]
+        O, I = C.shape[0], C.shape[1]
+        P = wl.sample_pairs(O, I, pairs, seed + li)
+        xin = _layer_input_columns(d, li, np.unique(P[:, 1]))
+        gin = _upstream_columns(d, li, np.unique(P[:, 0]))
+        dCp = np.zeros((len(P), G + 3))
+        dWp = np.zeros(len(P))
+        for k, (j, i) in enumerate(P):
+            c, w = oracle.coef_grad_pairs(xin[i][:, None], gin[j][:, None], [[0, 0]], lo, hi, G,
+                                          W is not None)
+            dCp[k] = c[0]
+            if W is not None:
+                dWp[k] = w[0]
+        gC = _np(grads[li][0]).reshape(O, I, G + 3)[P[:, 0], P[:, 1]]
+        errs["dC%d" % li] = err(gC, dCp)
+        if W is not None:
+            errs["dW%d" % li] = err(_np(grads[li][1])[P[:, 0], P[:, 1]], dWp)
+    say("workload %s errors: %s" % (name, " ".join("%s=%.2e" % kv for kv in errs.items())))
+    for k, e in errs.items():
+        assert e <= tol, "%s: %s error %.3e > %.0e" % (name, k, e, tol)
+
+
+def _layer_input_columns(d, li, cols):
+    """Columns of layer li's input over every row (layer 0: x; layer 1: the
+    first layer's output columns, bf16-rounded for bf16 networks)."""
+    if li == 0:
+        return {int(i): d["x"][:, i].astype(np.float64) for i in cols}
+    assert li == 1
+    C0, W0 = d["layers"][0]
+    lo, hi, G = d["lo"], d["hi"], d["G"]
+    cols = np.asarray(cols)
+    y = oracle.layer_forward(d["x"], C0[cols], None if W0 is None else W0[cols], lo, hi, G)
+    if d["dtype"] == "bf16":
+        y = oracle.round_bf16(y)
+    return {int(c): y[:, k] for k, c in enumerate(cols)}
+
+
+def _upstream_columns(d, li, cols):
+    """Columns of the gradient arriving at layer li's output, over every row."""
+    nl = len(d["layers"])
+    if li == nl - 1:
+        return {int(j): d["dy"][:, j].astype(np.float64) for j in cols}
+    assert li == 0 and nl == 2
+    # dy at layer 0's output = dx of layer 1; input column j of layer 1 needs
+    # only x1[:, j], C1[:, j, :], W1[:, j]
+    C1, W1 = d["layers"][1]
+    lo, hi, G = d["lo"], d["hi"], d["G"]
+    x1 = _layer_input_columns(d, 1, cols)
+    out = {}
+    for j in cols:
+        j = int(j)
+        dxj, _, _ = oracle.layer_backward(x1[j][:, None], C1[:, j:j + 1, :],
+                                          None if W1 is None else W1[:, j:j + 1], d["dy"],
+                                          lo, hi, G, need=("dx",))
+        out[j] = dxj[:, 0]
+    return out
+
+
+@pytest.mark.parametrize("variant", ["mfma", "gather"])
+def test_workload_c1(F, variant):
+    check_net(F, wl.make_workload("c1"), rows=None, pairs=32, variant=variant)
+
+
+def check_layers(F, d, variant):
+    """Each layer of a chain on its own, in full: a layer's input and its
+    upstream gradient are the oracle's own intermediates rounded to the
+    storage dtype, so only that layer's kernels are measured."""
+    lo, hi, G = d["lo"], d["hi"], d["G"]
+    layers = d["layers"]
+    dt = d["dtype"]
+    err, tol = metric(dt)
+    acts = oracle.network_forward(d["x"], layers, lo, hi, G, bf16_between=dt == "bf16")
+    ups = [None] * len(layers)
+    g = d["dy"].astype(np.float64)
+    for li in range(len(layers) - 1, -1, -1):
+        ups[li] = g
+        g = oracle.layer_backward(acts[li], *layers[li], g, lo, hi, G, need=("dx",))[0]
+    for li, (C, W) in enumerate(layers):
+        xl = acts[li].astype(np.float32)
+        gl = ups[li].astype(np.float32)
+        say("layer %d of %s on its own, variant=%s" % (li, d["name"], variant))
+        one = dict(d, x=xl, dy=gl, layers=[(C, W)])
+        got = _layer_on_gpu(F, one, variant)
+        ref = _layer_oracle(one)
+        errs = {k: err(a, r) for k, a, r in zip(("y", "dx", "dC", "dW"), got, ref) if r is not None}
+        say("  errors: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+        for k, e in errs.items():
+            assert e <= tol, "layer %d %s error %.3e > %.0e" % (li, k, e, tol)
+
+
+@pytest.mark.parametrize("variant", ["auto", "gather"])
+def test_workload_c2(F, variant):
+    check_net(F, wl.make_workload("c2"), rows=None, pairs=256, variant=variant)
+
+
+@pytest.mark.parametrize("variant", ["mfma", "gather"])
+def test_workload_c2_per_layer(F, variant):
+    check_layers(F, wl.make_workload("c2"), variant)
+
+
+@pytest.mark.parametrize("G", [8, 20, 50])
+@pytest.mark.parametrize("variant", ["auto", "mfma"])
+def test_workload_c3(F, G, variant):
+    check_net(F, wl.make_workload("c3", G=G), rows=256, pairs=128, variant=variant)
+
+
+def test_workload_c4(F):
+    check_net(F, wl.make_workload("c4"), rows=128, pairs=96)
+
+
+def test_workload_c5(F):
+    check_net(F, wl.make_workload("c5"), rows=64, pairs=128)
