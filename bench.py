@@ -1,0 +1,299 @@
+"""Benchmark: one KAN layer training step (forward + backward) on one MI355X.
+
+A step is the whole hot path over one batch: pack the coefficient operand,
+forward contraction (basis generated in LDS), pack the transposed operand and
+dy, dx contraction with its B' epilogue, and the batch-reduction contraction
+for dC and dW_base.  Inputs are seeded synthetic tensors resident in HBM
+before timing starts.  Prints one JSON line.
+
+Default workload: one layer 4096 -> 4096, 65536 rows, G = 20 cubic, bf16 x /
+C / W_base, float32 accumulation, silu base branch.  Other workloads:
+``--workload c1 .. c5`` (c2 and c4 are two-layer chains).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KAN layer fwd+bwd rows/sec and GFLOP/s; % of MFMA/HBM roofline, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA (fp32: = vector fp32)
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_TEXT = {
+    "c1": "KAN layer 8->4, 32 rows, G=8 cubic on [-1,1], fp32, no base branch",
+    "c2": "KAN net 784->64->10, 1024 rows, G=8 cubic on [-1,1], fp32, silu base branch",
+    "c3": "KAN layer 1024->1024, 8192 rows, cubic on [-1,1], fp32, no base branch",
+    "c4": "KAN channel mixer 768->3072->768, 12608 rows (64 x 197 tokens), G=5 cubic, bf16 "
+          "x/C/W_base, fp32 accumulate, silu base branch",
+    "c5": "KAN layer 4096->4096, 65536 rows, G=20 cubic on [-1,1], bf16 x/C/W_base, fp32 "
+          "accumulate, silu base branch",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--G", type=int, default=None, help="grid size (c3 only: 8, 20 or 50)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "gather"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=None)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device copy of BYTES bytes (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": src.numel() * 4}))
+
+
+def stage_names(nl):
+    out = []
+    for l in range(nl):
+        out += ["L%d.pack_fwd" % l, "L%d.fwd" % l] + (["L%d.cast" % l] if l + 1 < nl else [])
+    for l in range(nl - 1, -1, -1):
+        out += ["L%d.pack_bwd" % l, "L%d.dx" % l, "L%d.dC" % l]
+    return out
+
+
+def main():
+    args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the KAN layer path here has no multi-GPU "
+              "mode (data-parallel sharding over rows is described in DESIGN.md); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from kolmogorov_arnold_network_amd import _lib as L
+    from kolmogorov_arnold_network_amd import functional as F
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.make_workload(args.workload, G=args.G)
+    G, lo, hi = d["G"], d["lo"], d["hi"]
+    grid = (lo, hi, G)
+    dt = d["dtype"]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    N = d["N"]
+    widths = d["widths"]
+    nl = len(widths) - 1
+    base = d["base"]
+
+    def dev_t(a, dtype):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dtype)
+
+    x0 = dev_t(d["x"], tdt)
+    layers = [(dev_t(C, tdt), dev_t(W, tdt)) for C, W in d["layers"]]
+    dy = dev_t(d["dy"], torch.float32)
+    # per-layer buffers, workspaces and descriptors, allocated once
+    ys = [torch.empty((N, widths[l + 1]), dtype=torch.float32, device=dev) for l in range(nl)]
+    # a float32 chain reads the previous layer's output in place; a bf16 chain
+    # rounds it into a bf16 buffer first
+    xs = [x0] + [torch.empty((N, widths[l + 1]), dtype=tdt, device=dev) if dt == "bf16" else ys[l]
+                 for l in range(nl - 1)]
+    gx = [torch.empty((N, widths[l]), dtype=torch.float32, device=dev) for l in range(nl)]
+    gC = [torch.empty_like(C, dtype=torch.float32) for C, _ in layers]
+    gW = [None if W is None else torch.empty_like(W, dtype=torch.float32) for _, W in layers]
+    descs, wsf, wsb, descs_p = [], [], [], []
+    for l, (C, W) in enumerate(layers):
+        dsc = F.layer_desc(xs[l], C, W, grid, args.variant)
+        descs.append(dsc)
+        dp = F.layer_desc(xs[l], C, W, grid, args.variant, L.KAN_FLAG_PREPARED)
+        descs_p.append(dp)
+        wsf.append(F.workspace(dsc, L.KAN_PASS_FORWARD, dev))
+        wsb.append(F.workspace(dsc, L.KAN_PASS_BACKWARD, dev))
+    lib = L.lib()
+    import ctypes
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    S = ctypes.c_void_p(stream.cuda_stream)
+    names = stage_names(nl)
+    events = None
+
+    def rec(k):
+        if events is not None:
+            events[k].record(stream)
+
+    def step():
+        k = 0
+        rec(k)
+        for l, (C, W) in enumerate(layers):
+            dsc = ctypes.byref(descs[l])
+            buf, n = wsf[l]
+            L.check(lib.kan_prepare(dsc, 0, P(C), P(W), None, P(buf), n, S), "prepare fwd")
+            k += 1; rec(k)
+            L.check(lib.kan_forward(ctypes.byref(descs_p[l]), P(xs[l]), P(C), P(W), P(ys[l]), P(buf),
+                                    n, S), "forward")
+            k += 1; rec(k)
+            if l + 1 < nl:
+                if dt == "bf16":
+                    L.check(lib.kan_cast_f32_to_bf16(P(ys[l]), P(xs[l + 1]), ys[l].numel(), S), "cast")
+                k += 1; rec(k)
+        g = dy
+        for l in range(nl - 1, -1, -1):
+            C, W = layers[l]
+            dsc = ctypes.byref(descs[l])
+            dpp = ctypes.byref(descs_p[l])
+            buf, n = wsb[l]
+            L.check(lib.kan_prepare(dsc, 1, P(C), P(W), P(g), P(buf), n, S), "prepare bwd")
+            k += 1; rec(k)
+            L.check(lib.kan_backward(dpp, P(xs[l]), P(C), P(W), P(g), P(gx[l]), None, None, P(buf), n,
+                                     S), "backward dx")
+            k += 1; rec(k)
+            L.check(lib.kan_backward(dpp, P(xs[l]), P(C), P(W), P(g), None, P(gC[l]), P(gW[l]),
+                                     P(buf), n, S), "backward dC")
+            k += 1; rec(k)
+            g = gx[l]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_step_events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        per_step_events.append(events)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    events = None
+    stage_ms = {nm: 0.0 for nm in names}
+    for evs in per_step_events:
+        for k, nm in enumerate(names):
+            stage_ms[nm] += evs[k].elapsed_time(evs[k + 1]) / args.steps
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # work counts: algorithmic = the 4 non-zero basis functions (+ silu) per input
+    # in each of the three contractions; executed = the dense I*(G+3+base) basis
+    Kb = G + 3 + (1 if base else 0)
+    alg = exe = 0.0
+    for l in range(nl):
+        I, O = widths[l], widths[l + 1]
+        alg += 6.0 * N * I * O * (4 + (1 if base else 0))
+        exe += 6.0 * N * I * O * Kb
+    gemm_stages = [nm for nm in names if nm.split(".")[1] in ("fwd", "dx", "dC")]
+    dom = max(gemm_stages, key=lambda nm: stage_ms[nm])
+    dl = int(dom[1])
+    I, O = widths[dl], widths[dl + 1]
+    alg_dom = 2.0 * N * I * O * (4 + (1 if base else 0))
+    exe_dom = 2.0 * N * I * O * Kb
+    mfma_path = args.variant == "mfma" or (args.variant == "auto" and dt == "bf16")
+    peak = PEAK_TFLOPS[dt]
+    t_dom = stage_ms[dom] * 1e-3
+    roof = {
+        "bound": "mfma" if mfma_path else "alu",
+        "kernel": dom,
+        "achieved": alg_dom / t_dom / 1e12,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": alg_dom / t_dom / 1e12 / peak,
+        "traffic": None,
+        "executed_achieved": exe_dom / t_dom / 1e12 if mfma_path else None,
+        "executed_frac": exe_dom / t_dom / 1e12 / peak if mfma_path else None,
+        "dominant_ms": stage_ms[dom],
+    }
+    tr = read_traffic(args.workload, dom.split(".")[1])
+    if tr is not None:
+        roof["traffic"] = tr
+    out = {
+        "metric": METRIC,
+        "value": N * 1e3 / ms_per_step,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + (" (G=%d)" % G if args.workload == "c3" else ""),
+                   "name": args.workload, "rows": N, "widths": widths, "G": G,
+                   "base_branch": base, "variant": args.variant},
+        "gflops_algorithmic": alg / (ms_per_step * 1e-3) / 1e9,
+        "gflops_executed": exe / (ms_per_step * 1e-3) / 1e9,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
+    print(json.dumps(out))
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc", "kan_mfma.hip")
+    if kv.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(d, rows=None):
+    """The float64 NumPy oracle on a bounded sample of the same workload: y, dx
+    and the sample rows' own dC / dW_base contributions, timed on the host."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    N = d["N"]
+    default_rows = {"c1": 32, "c2": 1024, "c3": 1024, "c4": 1024, "c5": 512}
+    n = min(N, rows or default_rows[d["name"]])
+    R = wl.sample_indices(N, n, 99)
+    lo, hi, G = d["lo"], d["hi"], d["G"]
+    bf = d["dtype"] == "bf16"
+    t0 = time.perf_counter()
+    acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf)
+    oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G)
+    dt = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d rows: forward and backward (dx, and the rows' own dC/dW_base "
+                      "contributions) in float64 NumPy, %.1f s; CPU %s" % (n, N, dt, model)}
+
+
+if __name__ == "__main__":
+    main()
