@@ -18,12 +18,15 @@
 // accumulation and memory stalls are what slow the backward pass).
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2 waves of
-// 128 x 128 = 8 x 8 MFMA fragments of 16 x 16), k-tiles of 128 bytes per row
+// 128 x 128 = 4 x 4 MFMA blocks of 32 x 32), k-tiles of 128 bytes per row
 // (64 bf16 / 32 float), two LDS stages of A and B with a 144-byte row pitch.
-// bf16 uses v_mfma_f32_16x16x32_bf16, float uses v_mfma_f32_16x16x4_f32;
-// both accumulate in float32.  Each lane reads 16 contiguous bytes of k per
-// fragment row, so A and B share one lane -> k assignment and the k order
-// inside a step does not matter.
+// bf16 uses v_mfma_f32_32x32x16_bf16, float uses v_mfma_f32_32x32x2_f32;
+// both accumulate in float32.  The 32 x 32 blocks keep each accumulator in
+// one 16-register tuple, which the register allocator leaves in place (16 x
+// 16 blocks made it shuttle accumulators between register files every
+// k-tile).  Each lane reads 16 contiguous bytes of k per fragment row, so A
+// and B share one lane -> k assignment and the k order inside a step does
+// not matter.
 #include <string.h>
 
 #include <algorithm>
@@ -35,7 +38,7 @@ namespace kan {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int PITCH = 144;                     // bytes per LDS tile row (128 data + 16 pad)
 constexpr int TILE_BYTES = 256 * PITCH;        // one 256-row operand tile
@@ -47,20 +50,26 @@ template <typename TS> struct Traits;
 template <> struct Traits<uint16_t> {          // bf16 storage
     static constexpr int ES = 2;
     static constexpr int BK = 64;
-    __device__ static void mma(f32x4& acc, const uint4& a, const uint4& b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+    // one 32-byte k-step per row: 16 bf16
+    __device__ static void mma(f32x16& acc, const uint4& a, const uint4& b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     }
-    __device__ static void put(char* p, float v) { *reinterpret_cast<uint16_t*>(p) = f2bf(v); }
+    // v_cvt_pk_bf16_f32: round to nearest even
+    __device__ static void put(char* p, float v) {
+        *reinterpret_cast<uint16_t*>(p) = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
 };
 template <> struct Traits<float> {
     static constexpr int ES = 4;
     static constexpr int BK = 32;
-    __device__ static void mma(f32x4& acc, const uint4& a, const uint4& b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    // one 32-byte k-step per row: 8 floats, lane half h holds k = 4h .. 4h+3;
+    // MFMA e pairs k = e (lanes 0-31) with k = 4 + e (lanes 32-63)
+    __device__ static void mma(f32x16& acc, const uint4& a, const uint4& b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
     }
     __device__ static void put(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
 };
@@ -98,205 +107,217 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& a, int& tm, int& tn)
     tn = r / gm;
 }
 
+// ---- operands ----
+// Every operand has three hooks, called by the k-loop:
+//   fetch(kt)     start the global loads of k-tile kt into the `next` slot
+//                 (a copied operand: the tile itself; a generated one: the x
+//                 values it needs)
+//   store(S, kt)  write k-tile kt into LDS tile S from the `current` slot
+//   rotate()      next -> current
+// A tile is fetched two k-tiles ahead of its store, so its loads have two
+// k-tiles of MFMA work to arrive.  The workgroup has 8 waves (2 per SIMD, so
+// one wave's vector work runs while the other's MFMAs execute), arranged
+// 4 x 2 over the 256 x 256 tile; wave w owns rows 64 (w / 2) .. +64 and
+// columns 128 (w % 2) .. +128.
+constexpr int NTHR = 512;
+
 // Operand copied from a packed row-major array: rows [r0, r0+256), k-tile kt
 // = bytes [128 kt, 128 kt + 128) of each row.  8 threads read one row's 128
 // bytes (coalesced); the tile goes through registers into LDS.
 struct LoadOp {
-    const char* base;
+    const char* base;    // this thread's row and 16-byte column in the tile
     int64_t ld;
-    uint4 reg[8];
-    __device__ LoadOp(const char* p, int64_t r0, int64_t ld_) : base(p + r0 * ld_), ld(ld_) {}
-    __device__ __forceinline__ void fetch(int kt) {
-        const int t = threadIdx.x, c = t & 7, r = t >> 3;
+    uint4 cur[4], nxt[4];
+    __device__ LoadOp(const char* p, int64_t r0, int64_t ld_)
+        : base(p + (r0 + (threadIdx.x >> 3)) * ld_ + (threadIdx.x & 7) * 16), ld(ld_) {}
+    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) {
+        const char* p = base + (int64_t)kt * 128;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            reg[q] = *reinterpret_cast<const uint4*>(base + (int64_t)(r + 32 * q) * ld +
-                                                     (int64_t)kt * 128 + c * 16);
+        for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const uint4*>(p + (int64_t)(64 * q) * ld);
     }
-    __device__ __forceinline__ void store(char* S, int) {
+    __device__ __forceinline__ void store(const GemmArgs&, char* S, int) {
         const int t = threadIdx.x, c = t & 7, r = t >> 3;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<uint4*>(S + (r + 32 * q) * PITCH + c * 16) = reg[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(S + (r + 64 * q) * PITCH + c * 16) = cur[q];
+    }
+    __device__ __forceinline__ void rotate() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
     }
 };
+struct LoadA : LoadOp {                // rows m0 = tm * 256
+    __device__ LoadA(const GemmArgs& a, int tm, int) : LoadOp(a.a, (int64_t)tm * 256, a.lda) {}
+};
+struct LoadB : LoadOp {                // rows n0 = tn * 256
+    __device__ LoadB(const GemmArgs& a, int, int tn) : LoadOp(a.b, (int64_t)tn * 256, a.ldb) {}
+};
+struct LoadBdx : LoadOp {              // rows n0 = tn * Qn * Kb: whole inputs per tile
+    __device__ LoadBdx(const GemmArgs& a, int, int tn)
+        : LoadOp(a.b, (int64_t)tn * a.Qn * a.Kb, a.ldb) {}
+};
 
-// Forward A operand Phi'[b, (i, m)]: thread t owns row b = m0 + t of the tile
-// and writes that row only (zero fill, then the <= 4 spline values and the
-// silu value of every input that meets the k-tile), so no barrier is needed
-// between the two.
-template <typename TS>
-struct GenFwdA {
+// Forward A operand Phi'[b, (i, m)]: thread t (< 256) owns row b = m0 + t of
+// the tile and writes that row only (zero fill, then the <= 4 spline values
+// and the silu value of every input that meets the k-tile), so no barrier is
+// needed between the two; threads 256 .. 511 (one wave per SIMD) do not
+// generate.  NIN (inputs meeting one k-tile) is a compile-time bound, x loads
+// are clamped in bounds, and writes that fall outside the tile go to the row's
+// 16 pad bytes, which no fragment read touches: no divergent branches.
+template <typename TS, int NIN>
+struct GenA {
     static constexpr int BK = Traits<TS>::BK;
-    static constexpr int MAXIN = BK / 4 + 2;   // inputs meeting one k-tile (Kb >= 4)
+    static constexpr int ES = Traits<TS>::ES;
     const TS* x;
-    int b, i_first, nin;
-    bool row_ok;
-    float xr[MAXIN];
-    __device__ GenFwdA(const GemmArgs& a, int tm) {
+    int64_t xrow;
+    bool row_ok, active;
+    int i_cur, i_nxt;
+    float xr[NIN], xn[NIN];
+    __device__ GenA(const GemmArgs& a, int tm, int) {
         x = static_cast<const TS*>(a.x);
-        b = tm * 256 + threadIdx.x;
+        active = threadIdx.x < 256;
+        const int b = tm * 256 + (threadIdx.x & 255);
         row_ok = b < a.N;
+        xrow = (int64_t)min(b, a.N - 1) * a.I;
     }
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
-        const int k0 = kt * BK;
-        i_first = k0 / a.Kb;
-        const int i_last = min((k0 + BK - 1) / a.Kb, a.I - 1);
-        nin = i_last - i_first + 1;
+        i_nxt = (unsigned)(kt * BK) / (unsigned)a.Kb;
+        if (!active) return;
 #pragma unroll
-        for (int q = 0; q < MAXIN; ++q)
-            if (q < nin && row_ok) xr[q] = load_f(x, (int64_t)b * a.I + i_first + q);
+        for (int q = 0; q < NIN; ++q) xn[q] = load_f(x, xrow + min(i_nxt + q, a.I - 1));
+    }
+    __device__ __forceinline__ void rotate() {
+        i_cur = i_nxt;
+#pragma unroll
+        for (int q = 0; q < NIN; ++q) xr[q] = xn[q];
     }
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
+        if (!active) return;
         char* row = S + threadIdx.x * PITCH;
 #pragma unroll
         for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(0, 0, 0, 0);
-        if (!row_ok) return;
         const int k0 = kt * BK;
 #pragma unroll
-        for (int q = 0; q < MAXIN; ++q) {
-            if (q < nin) {
-                const float xv = xr[q];
-                float u;
-                const int s = span_u(xv, a.g, u);
-                float bb[4];
-                pieces(u, bb[0], bb[1], bb[2], bb[3]);
-                const int cb = (i_first + q) * a.Kb - k0;   // tile column of (i, m = 0)
+        for (int q = 0; q < NIN; ++q) {
+            const int i = i_cur + q;
+            const bool ok = row_ok & (i < a.I);
+            const int cb = i * a.Kb - k0;             // tile column of (i, m = 0)
+            const float xv = xr[q];
+            float u;
+            const int s = span_u(xv, a.g, u);
+            float bb[4];
+            pieces(u, bb[0], bb[1], bb[2], bb[3]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = s - 3 + r;
-                    const int col = cb + m;
-                    if (m >= 0 && m < a.K && col >= 0 && col < BK)
-                        Traits<TS>::put(row + col * Traits<TS>::ES, bb[r]);
-                }
-                if (a.base) {
-                    const int col = cb + a.K;
-                    if (col >= 0 && col < BK) Traits<TS>::put(row + col * Traits<TS>::ES, silu(xv));
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = s - 3 + r;
+                const int col = cb + m;
+                const bool v = ok & (m >= 0) & (m < a.K) & (col >= 0) & (col < BK);
+                Traits<TS>::put(row + (v ? col : BK) * ES, bb[r]);
             }
+            const int cs = cb + a.K;                  // silu column, uniform
+            if (a.base && cs >= 0 && cs < BK)
+                Traits<TS>::put(row + (ok ? cs : BK) * ES, silu(xv));
         }
     }
 };
 
 // dC B operand Phi'^T[(i, m), b]: tile rows are the 256 packed columns
-// n0 .. n0+255 of Phi', k runs over the batch.  Thread t handles row
-// b = k0 + (t % BK) and the inputs slot, slot + NS, ... of the tile
-// (slot = t / BK).  The whole tile is zero-filled, then (after a barrier)
-// the non-zeros are scattered.
-template <typename TS>
-struct GenDcB {
+// n0 .. n0+255 of Phi', k runs over the batch.  Lane l of wave w handles row
+// b = k0 + (l % BK) of the k-tile and the tile inputs w + 8 j (the fp32 tile,
+// 32 rows deep, puts two inputs in one wave instruction).  Wave w also zero
+// fills the tile rows of exactly those inputs before scattering into them,
+// so the zero fill and the scatter of a row come from one wave, in order,
+// and need no barrier.  ZR = ceil(Kb / 8) zero-fill instructions per input;
+// writes outside the tile go to the pad bytes of row 0.
+template <typename TS, int NQ, int ZR>
+struct GenB {
     static constexpr int BK = Traits<TS>::BK;
-    static constexpr int NS = 256 / BK;                     // input slots
-    static constexpr int MAXQ = (256 / 4 + 2 + NS - 1) / NS;
+    static constexpr int ES = Traits<TS>::ES;
+    static constexpr int LPW = 64 / BK;                  // inputs per wave instruction
     const TS* x;
-    int n0, i_first, nin, bl, slot;
-    float xr[MAXQ];
-    __device__ GenDcB(const GemmArgs& a, int tn) {
+    int n0, i_first, bl, islot, wave, lane;
+    float xr[NQ], xn[NQ];
+    __device__ GenB(const GemmArgs& a, int, int tn) {
         x = static_cast<const TS*>(a.x);
         n0 = tn * 256;
-        i_first = n0 / a.Kb;
-        const int i_last = min((n0 + 255) / a.Kb, a.I - 1);
-        nin = i_last - i_first + 1;
-        bl = threadIdx.x % BK;
-        slot = threadIdx.x / BK;
+        i_first = (unsigned)n0 / (unsigned)a.Kb;
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        bl = lane % BK;
+        islot = wave + 8 * (lane / BK);                  // first tile input of this lane
     }
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
-        const int b = kt * BK + bl;
-        const bool ok = b < a.N;
+        const int64_t brow = (int64_t)min(kt * BK + bl, a.N - 1) * a.I;
 #pragma unroll
-        for (int q = 0; q < MAXQ; ++q) {
-            const int il = slot + NS * q;
-            if (il < nin && ok) xr[q] = load_f(x, (int64_t)b * a.I + i_first + il);
-        }
+        for (int q = 0; q < NQ; ++q)
+            xn[q] = load_f(x, brow + min(i_first + islot + 8 * LPW * q, a.I - 1));
+    }
+    __device__ __forceinline__ void rotate() {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) xr[q] = xn[q];
     }
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
-        {
-            char* row = S + threadIdx.x * PITCH;
+        // zero the rows of this wave's inputs: 8 rows of 128 bytes per instruction
 #pragma unroll
-            for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < NQ * LPW; ++j) {
+            const int rb = (i_first + wave + 8 * j) * a.Kb - n0;
+#pragma unroll
+            for (int z = 0; z < ZR; ++z) {
+                const int rr = 8 * z + (lane >> 3);
+                const int row = rb + rr;
+                const bool v = (rr < a.Kb) & (row >= 0) & (row < 256);
+                *reinterpret_cast<uint4*>(v ? S + row * PITCH + (lane & 7) * 16 : S + 128) =
+                    make_uint4(0, 0, 0, 0);
+            }
         }
-        __syncthreads();
-        const int b = kt * BK + bl;
-        if (b >= a.N) return;
+        const bool b_ok = kt * BK + bl < a.N;
+        char* colp = S + bl * ES;
 #pragma unroll
-        for (int q = 0; q < MAXQ; ++q) {
-            const int il = slot + NS * q;
-            if (il < nin) {
-                const float xv = xr[q];
-                float u;
-                const int s = span_u(xv, a.g, u);
-                float bb[4];
-                pieces(u, bb[0], bb[1], bb[2], bb[3]);
-                const int rb = (i_first + il) * a.Kb - n0;   // tile row of (i, m = 0)
+        for (int q = 0; q < NQ; ++q) {
+            const int i = i_first + islot + 8 * LPW * q;
+            const bool ok = b_ok & (i < a.I);
+            const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
+            const float xv = xr[q];
+            float u;
+            const int s = span_u(xv, a.g, u);
+            float bb[4];
+            pieces(u, bb[0], bb[1], bb[2], bb[3]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = s - 3 + r;
-                    const int row = rb + m;
-                    if (m >= 0 && m < a.K && row >= 0 && row < 256)
-                        Traits<TS>::put(S + row * PITCH + bl * Traits<TS>::ES, bb[r]);
-                }
-                if (a.base) {
-                    const int row = rb + a.K;
-                    if (row >= 0 && row < 256)
-                        Traits<TS>::put(S + row * PITCH + bl * Traits<TS>::ES, silu(xv));
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = s - 3 + r;
+                const int row = rb + m;
+                const bool v = ok & (m >= 0) & (m < a.K) & (row >= 0) & (row < 256);
+                Traits<TS>::put(v ? colp + row * PITCH : S + 128, bb[r]);
+            }
+            if (a.base) {
+                const int row = rb + a.K;
+                const bool v = ok & (row >= 0) & (row < 256);
+                Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
             }
         }
     }
 };
 
-// Loaded operands wrapped to the generator interface.
-struct LoadA {
-    LoadOp op;
-    __device__ LoadA(const GemmArgs& a, int tm, int) : op(a.a, (int64_t)tm * 256, a.lda) {}
-    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
-    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
-};
-struct LoadB {                       // rows n0 = tn * 256
-    LoadOp op;
-    __device__ LoadB(const GemmArgs& a, int, int tn) : op(a.b, (int64_t)tn * 256, a.ldb) {}
-    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
-    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
-};
-struct LoadBdx {                     // rows n0 = tn * Qn * Kb: whole inputs per tile
-    LoadOp op;
-    __device__ LoadBdx(const GemmArgs& a, int, int tn)
-        : op(a.b, (int64_t)tn * a.Qn * a.Kb, a.ldb) {}
-    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) { op.fetch(kt); }
-    __device__ __forceinline__ void store(const GemmArgs&, char* S, int kt) { op.store(S, kt); }
-};
-template <typename TS>
-struct GenA {
-    GenFwdA<TS> g;
-    __device__ GenA(const GemmArgs& a, int tm, int) : g(a, tm) {}
-    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) { g.fetch(a, kt); }
-    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) { g.store(a, S, kt); }
-};
-template <typename TS>
-struct GenB {
-    GenDcB<TS> g;
-    __device__ GenB(const GemmArgs& a, int, int tn) : g(a, tn) {}
-    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) { g.fetch(a, kt); }
-    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) { g.store(a, S, kt); }
-};
-
-typedef f32x4 Acc[8][8];
+typedef f32x16 Acc[2][4];
 
 // ---- epilogues ----
-// acc[fi][fj][r] holds D[wm + 16 fi + 4 (lane / 16) + r][wn + 16 fj + lane % 16].
+// acc[fi][fj][r] holds D[wm + 32 fi + 8 (r / 4) + 4 (lane / 32) + r % 4][wn + 32 fj + lane % 32]
+// with wm = 64 (wave / 2), wn = 128 (wave % 2).
+__device__ __forceinline__ int acc_row(int fi, int r) { return 32 * fi + 8 * (r >> 2) + (r & 3); }
+
 struct EpiY {
     template <typename TS>
     __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char*) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int r0 = tm * 256 + (wave >> 1) * 128 + 4 * (lane >> 4);
-        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 15);
+        const int r0 = tm * 256 + (wave >> 1) * 64 + 4 * (lane >> 5);
+        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 31);
 #pragma unroll
-        for (int fi = 0; fi < 8; ++fi)
+        for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
-            for (int fj = 0; fj < 8; ++fj) {
-                const int col = c0 + 16 * fj;
+            for (int fj = 0; fj < 4; ++fj) {
+                const int col = c0 + 32 * fj;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = r0 + 16 * fi + r;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + acc_row(fi, r);
                     if (row < a.N && col < a.O) a.out0[(int64_t)row * a.O + col] = acc[fi][fj][r];
                 }
             }
@@ -307,20 +328,20 @@ struct EpiDC {
     template <typename TS>
     __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char*) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int r0 = tm * 256 + (wave >> 1) * 128 + 4 * (lane >> 4);
-        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 15);
+        const int r0 = tm * 256 + (wave >> 1) * 64 + 4 * (lane >> 5);
+        const int c0 = tn * 256 + (wave & 1) * 128 + (lane & 31);
 #pragma unroll
-        for (int fj = 0; fj < 8; ++fj) {
-            const int n = c0 + 16 * fj;
+        for (int fj = 0; fj < 4; ++fj) {
+            const int n = c0 + 32 * fj;
             if (n >= a.IKb) continue;
             const int i = n / a.Kb, m = n - i * a.Kb;
             const bool spline = m < a.K;
             if (spline ? !a.out0 : !a.out1) continue;
 #pragma unroll
-            for (int fi = 0; fi < 8; ++fi)
+            for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = r0 + 16 * fi + r;
+                for (int r = 0; r < 16; ++r) {
+                    const int j = r0 + acc_row(fi, r);
                     if (j >= a.O) continue;
                     if (spline) a.out0[((int64_t)j * a.I + i) * a.K + m] = acc[fi][fj][r];
                     else a.out1[(int64_t)j * a.I + i] = acc[fi][fj][r];
@@ -329,11 +350,11 @@ struct EpiDC {
     }
 };
 
-// dx: the P tile is staged through LDS in two phases.  In phase h every wave
-// writes its fragment rows 4h .. 4h+3 (64 of its 128 rows), so the staging
-// area holds 128 tile rows: LDS row (wave / 2) * 64 + rr is tile row
-// (wave / 2) * 128 + 64 h + rr.  Then each (row, input) pair of those rows
-// contracts its <= 4 spline columns with B' and its silu column with silu'.
+// dx: the P tile is staged through LDS in two phases of 128 rows.  In phase h
+// every wave writes its accumulator block fi = h (32 of its 64 rows): LDS row
+// (wave / 2) * 32 + rr is tile row (wave / 2) * 64 + 32 h + rr.  Then each
+// (row, input) pair of those rows contracts its <= 4 spline columns with B'
+// and its silu column with silu'.
 struct EpiDX {
     template <typename TS>
     __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char* lds) {
@@ -342,22 +363,20 @@ struct EpiDX {
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
         const int i0 = tn * a.Qn;
         const int nin = min(a.Qn, a.I - i0);
-        const int cw = (wave & 1) * 128 + (lane & 15);
-        const int rw = (wave >> 1) * 64 + 4 * (lane >> 4);
+        const int cw = (wave & 1) * 128 + (lane & 31);
+        const int rw = (wave >> 1) * 32 + 4 * (lane >> 5);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int fj = 0; fj < 4; ++fj)
 #pragma unroll
-                for (int fj = 0; fj < 8; ++fj)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        P[(rw + 16 * f + r) * DX_PITCH + cw + 16 * fj] = acc[4 * h + f][fj][r];
+                for (int r = 0; r < 16; ++r)
+                    P[(rw + acc_row(0, r)) * DX_PITCH + cw + 32 * fj] = acc[h][fj][r];
             __syncthreads();
 #pragma unroll 1
-            for (int e = t; e < 128 * nin; e += 256) {
+            for (int e = t; e < 128 * nin; e += NTHR) {
                 const int rl = e / nin, il = e - rl * nin;
-                const int b = tm * 256 + (rl >> 6) * 128 + 64 * h + (rl & 63);
+                const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
                 const int i = i0 + il;
                 if (b < a.N) {
                     const float xv = load_f(x, (int64_t)b * a.I + i);
@@ -382,64 +401,81 @@ struct EpiDX {
 
 // ---- the contraction kernel ----
 template <typename TS, class AOp, class BOp, class Epi>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     extern __shared__ uint4 lds4[];
     char* lds = reinterpret_cast<char*>(lds4);
     int tm, tn;
     tile_coords(args, tm, tn);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     AOp A(args, tm, tn);
     BOp B(args, tm, tn);
     Acc acc;
 #pragma unroll
-    for (int fi = 0; fi < 8; ++fi)
+    for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
-        for (int fj = 0; fj < 8; ++fj) acc[fi][fj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fi][fj][r] = 0.0f;
 
-    A.fetch(args, 0);
-    B.fetch(args, 0);
-    A.store(args, lds, 0);
-    B.store(args, lds + TILE_BYTES, 0);
-    __syncthreads();
-    const int arow = (wm + (lane & 15)) * PITCH + (lane >> 4) * 16;
-    const int brow = (wn + (lane & 15)) * PITCH + (lane >> 4) * 16;
-    // MFMAs over one staged k-tile: 2 k-steps of 64 bytes per row.
+    const int arow = (wm + (lane & 31)) * PITCH + (lane >> 5) * 16;
+    const int brow = (wn + (lane & 31)) * PITCH + (lane >> 5) * 16;
+    // MFMAs over one staged k-tile: 4 k-steps of 32 bytes per row.
     auto compute = [&](const char* As, const char* Bs) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint4 bf[8];
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 fa[2], fb[4];
 #pragma unroll
-            for (int f = 0; f < 8; ++f)
-                bf[f] = *reinterpret_cast<const uint4*>(Bs + brow + f * 16 * PITCH + ks * 64);
+            for (int f = 0; f < 4; ++f)
+                fb[f] = *reinterpret_cast<const uint4*>(Bs + brow + f * 32 * PITCH + ks * 32);
 #pragma unroll
-            for (int fi = 0; fi < 8; ++fi) {
-                const uint4 af = *reinterpret_cast<const uint4*>(As + arow + fi * 16 * PITCH + ks * 64);
+            for (int f = 0; f < 2; ++f)
+                fa[f] = *reinterpret_cast<const uint4*>(As + arow + f * 32 * PITCH + ks * 32);
 #pragma unroll
-                for (int fj = 0; fj < 8; ++fj) Traits<TS>::mma(acc[fi][fj], af, bf[fj]);
-            }
-            // keep one k-step of fragments live at a time (bounds register use)
+            for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+                for (int fj = 0; fj < 4; ++fj) Traits<TS>::mma(acc[fi][fj], fa[fi], fb[fj]);
+            // bounds the fragments live at once (left free, the scheduler
+            // hoists every fragment read of the tile)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // The last k-tile is peeled so that fetch/store are unconditional in the
-    // loop and the staging registers die at each store.
-    for (int kt = 0; kt + 1 < args.nkt; ++kt) {
+    // Prologue: tile 0 into stage 0, tile 1 fetched.  Iteration kt: fetch
+    // tile kt+2 (clamped to the last tile, so every load is in bounds), run
+    // the MFMAs of tile kt from stage kt % 2, store tile kt+1 into the other
+    // stage.  The loads are issued first and pinned there (left alone, the
+    // scheduler sinks them next to their use).
+    const int nkt = args.nkt;
+    A.fetch(args, 0);
+    B.fetch(args, 0);
+    A.rotate();
+    B.rotate();
+    A.store(args, lds, 0);
+    B.store(args, lds + TILE_BYTES, 0);
+    A.fetch(args, min(1, nkt - 1));
+    B.fetch(args, min(1, nkt - 1));
+    A.rotate();
+    B.rotate();
+    __syncthreads();
+    for (int kt = 0; kt + 1 < nkt; ++kt) {
         const int cur = kt & 1;
-        A.fetch(args, kt + 1);
-        B.fetch(args, kt + 1);
-        const char* As = lds + cur * STAGE_BYTES;
-        compute(As, As + TILE_BYTES);
+        A.fetch(args, min(kt + 2, nkt - 1));
+        B.fetch(args, min(kt + 2, nkt - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        const char* Sc = lds + cur * STAGE_BYTES;
+        compute(Sc, Sc + TILE_BYTES);
         char* Sn = lds + (cur ^ 1) * STAGE_BYTES;
         A.store(args, Sn, kt + 1);
         B.store(args, Sn + TILE_BYTES, kt + 1);
+        A.rotate();
+        B.rotate();
         __syncthreads();
     }
     {
-        const char* As = lds + ((args.nkt - 1) & 1) * STAGE_BYTES;
-        compute(As, As + TILE_BYTES);
-        __syncthreads();
+        const char* Sc = lds + ((nkt - 1) & 1) * STAGE_BYTES;
+        compute(Sc, Sc + TILE_BYTES);
     }
+    __syncthreads();
     Epi::template run<TS>(args, acc, tm, tn, lds);
 }
 
@@ -525,18 +561,13 @@ __global__ void prep_dy_kernel(const float* __restrict__ dy, TS* __restrict__ dy
     }
 }
 
-template <typename K>
-hipError_t set_lds(K kernel, int bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 template <typename TS, class AOp, class BOp, class Epi>
 hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
     auto kern = gemm_kernel<TS, AOp, BOp, Epi>;
-    hipError_t e = set_lds(kern, LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(NTHR), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -599,6 +630,37 @@ hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, 
     return hipGetLastError();
 }
 
+// Inputs that can meet one k-tile of the forward: ceil((BK - 1) / Kb) + 1.
+static int fwd_nin(const Plan& p) { return (p.BK - 1 + p.Kb - 1) / p.Kb + 1; }
+
+template <typename TS>
+static hipError_t fwd_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    const int n = fwd_nin(p);
+    if (n <= 2) return run_gemm<TS, GenA<TS, 2>, LoadB, EpiY>(a, s);
+    if (n <= 3) return run_gemm<TS, GenA<TS, 3>, LoadB, EpiY>(a, s);
+    if (n <= 4) return run_gemm<TS, GenA<TS, 4>, LoadB, EpiY>(a, s);
+    if (n <= 6) return run_gemm<TS, GenA<TS, 6>, LoadB, EpiY>(a, s);
+    if (n <= 9) return run_gemm<TS, GenA<TS, 9>, LoadB, EpiY>(a, s);
+    return run_gemm<TS, GenA<TS, 18>, LoadB, EpiY>(a, s);
+}
+
+// (inputs per lane NQ, zero-fill instructions per input ZR) of the dC
+// generator, from Kb: the 256-row tile meets ceil(255 / Kb) + 1 inputs, dealt
+// to 8 waves.
+static int dc_nq(const Plan& p) { return ((255 + p.Kb - 1) / p.Kb + 1 + 7) / 8; }
+
+template <typename TS>
+static hipError_t dc_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    constexpr int LPW = 64 / Traits<TS>::BK;
+    const int zr = (p.Kb + 7) / 8;
+    const int nq = (dc_nq(p) + LPW - 1) / LPW;       // inputs per lane
+    if (zr <= 1 && nq <= 9) return run_gemm<TS, LoadA, GenB<TS, 9, 1>, EpiDC>(a, s);
+    if (zr <= 2 && nq <= 4) return run_gemm<TS, LoadA, GenB<TS, 4, 2>, EpiDC>(a, s);
+    if (zr <= 3 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 3>, EpiDC>(a, s);
+    if (zr <= 7 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 7>, EpiDC>(a, s);
+    return run_gemm<TS, LoadA, GenB<TS, 1, 32>, EpiDC>(a, s);
+}
+
 hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s) {
     GemmArgs a = base_args(p, x);
     a.tiles_m = (int)(p.Npad / 256);
@@ -607,8 +669,8 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.ldb = p.Kf * p.esize;
     a.nkt = (int)(p.Kf / p.BK);
     a.out0 = y;
-    if (p.dtype == KAN_F32) return run_gemm<float, GenA<float>, LoadB, EpiY>(a, s);
-    return run_gemm<uint16_t, GenA<uint16_t>, LoadB, EpiY>(a, s);
+    if (p.dtype == KAN_F32) return fwd_dispatch<float>(p, a, s);
+    return fwd_dispatch<uint16_t>(p, a, s);
 }
 
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
@@ -637,8 +699,8 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.out0 = dC;
     a.out1 = dW;
     a.group_m = 2;
-    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, GenB<float>, EpiDC>(a, s);
-    return run_gemm<uint16_t, LoadA, GenB<uint16_t>, EpiDC>(a, s);
+    if (p.dtype == KAN_F32) return dc_dispatch<float>(p, a, s);
+    return dc_dispatch<uint16_t>(p, a, s);
 }
 
 }  // namespace kan
