@@ -156,52 +156,69 @@ struct LoadBdx : LoadOp {              // rows n0 = tn * Qn * Kb: whole inputs p
         : LoadOp(a.b, (int64_t)tn * a.Qn * a.Kb, a.ldb) {}
 };
 
-// Forward A operand Phi'[b, (i, m)]: thread t (< 256) owns row b = m0 + t of
-// the tile and writes that row only (zero fill, then the <= 4 spline values
-// and the silu value of every input that meets the k-tile), so no barrier is
-// needed between the two; threads 256 .. 511 (one wave per SIMD) do not
-// generate.  NIN (inputs meeting one k-tile) is a compile-time bound, x loads
-// are clamped in bounds, and writes that fall outside the tile go to the row's
-// 16 pad bytes, which no fragment read touches: no divergent branches.
+// Forward A operand Phi'[b, (i, m)].  The (row, input) pairs of a k-tile are
+// dealt to all 512 threads with the NIN inputs of one row in NIN adjacent
+// lanes (NIN a power of two dividing the wave), so one load instruction
+// touches 64 / NIN rows of x rather than 64.  The lanes of a row zero-fill it
+// and then scatter its <= 4 spline values and silu value per input; they are
+// in one wave, whose LDS writes land in program order, so no barrier is
+// needed between the two.  x loads are clamped in bounds and writes that fall
+// outside the tile go to the row's 16 pad bytes, which no fragment read
+// touches: the generator has no divergent branches.
 template <typename TS, int NIN>
 struct GenA {
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
+    static constexpr int PPT = 256 * NIN / NTHR;       // pairs per thread
+    static constexpr int RSTEP = NTHR / NIN;           // rows between a thread's pairs
+    static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
     const TS* x;
-    int64_t xrow;
-    bool row_ok, active;
-    int i_cur, i_nxt;
-    float xr[NIN], xn[NIN];
+    int q, row0, i_cur, i_nxt;
+    int64_t xrow[PPT];
+    bool row_ok[PPT];
+    float xr[PPT], xn[PPT];
     __device__ GenA(const GemmArgs& a, int tm, int) {
         x = static_cast<const TS*>(a.x);
-        active = threadIdx.x < 256;
-        const int b = tm * 256 + (threadIdx.x & 255);
-        row_ok = b < a.N;
-        xrow = (int64_t)min(b, a.N - 1) * a.I;
+        q = threadIdx.x % NIN;
+        row0 = threadIdx.x / NIN;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int b = tm * 256 + row0 + RSTEP * j;
+            row_ok[j] = b < a.N;
+            xrow[j] = (int64_t)min(b, a.N - 1) * a.I;
+        }
     }
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
         i_nxt = (unsigned)(kt * BK) / (unsigned)a.Kb;
-        if (!active) return;
+        const int i = min(i_nxt + q, a.I - 1);
 #pragma unroll
-        for (int q = 0; q < NIN; ++q) xn[q] = load_f(x, xrow + min(i_nxt + q, a.I - 1));
+        for (int j = 0; j < PPT; ++j) xn[j] = load_f(x, xrow[j] + i);
     }
     __device__ __forceinline__ void rotate() {
         i_cur = i_nxt;
 #pragma unroll
-        for (int q = 0; q < NIN; ++q) xr[q] = xn[q];
+        for (int j = 0; j < PPT; ++j) xr[j] = xn[j];
     }
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
-        if (!active) return;
-        char* row = S + threadIdx.x * PITCH;
+        // zero fill: the NIN lanes of a row clear its 8 chunks of 16 bytes
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < PPT; ++j) {
+            char* row = S + (row0 + RSTEP * j) * PITCH;
+#pragma unroll
+            for (int c = 0; c < (8 + NIN - 1) / NIN; ++c) {
+                const int chunk = q * ((8 + NIN - 1) / NIN) + c;
+                *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
+            }
+        }
         const int k0 = kt * BK;
+        const int i = i_cur + q;
+        const int cb = i * a.Kb - k0;                 // tile column of (i, m = 0)
+        const int cs = cb + a.K;                      // silu column
 #pragma unroll
-        for (int q = 0; q < NIN; ++q) {
-            const int i = i_cur + q;
-            const bool ok = row_ok & (i < a.I);
-            const int cb = i * a.Kb - k0;             // tile column of (i, m = 0)
-            const float xv = xr[q];
+        for (int j = 0; j < PPT; ++j) {
+            char* row = S + (row0 + RSTEP * j) * PITCH;
+            const bool ok = row_ok[j] & (i < a.I);
+            const float xv = xr[j];
             float u;
             const int s = span_u(xv, a.g, u);
             float bb[4];
@@ -213,53 +230,59 @@ struct GenA {
                 const bool v = ok & (m >= 0) & (m < a.K) & (col >= 0) & (col < BK);
                 Traits<TS>::put(row + (v ? col : BK) * ES, bb[r]);
             }
-            const int cs = cb + a.K;                  // silu column, uniform
-            if (a.base && cs >= 0 && cs < BK)
-                Traits<TS>::put(row + (ok ? cs : BK) * ES, silu(xv));
+            const bool v = ok & (a.base != 0) & (cs >= 0) & (cs < BK);
+            Traits<TS>::put(row + (v ? cs : BK) * ES, silu(xv));
         }
     }
 };
 
 // dC B operand Phi'^T[(i, m), b]: tile rows are the 256 packed columns
-// n0 .. n0+255 of Phi', k runs over the batch.  Lane l of wave w handles row
-// b = k0 + (l % BK) of the k-tile and the tile inputs w + 8 j (the fp32 tile,
-// 32 rows deep, puts two inputs in one wave instruction).  Wave w also zero
-// fills the tile rows of exactly those inputs before scattering into them,
-// so the zero fill and the scatter of a row come from one wave, in order,
-// and need no barrier.  ZR = ceil(Kb / 8) zero-fill instructions per input;
-// writes outside the tile go to the pad bytes of row 0.
-template <typename TS, int NQ, int ZR>
+// n0 .. n0+255 of Phi', k runs over the batch.  Wave w owns the NQW tile
+// inputs w NQW .. w NQW + NQW - 1: it zero-fills their tile rows and then
+// scatters their non-zeros, in program order, so no barrier is needed.  The
+// wave's (row b, input) pairs run input-fastest over its lanes, so one x load
+// instruction touches 64 / NQW rows of x.  ZR = ceil(Kb / 8) zero-fill
+// instructions per input; writes outside the tile go to the pad bytes of
+// row 0.
+template <typename TS, int NQW, int ZR>
 struct GenB {
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
-    static constexpr int LPW = 64 / BK;                  // inputs per wave instruction
+    static constexpr int PPL = BK * NQW / 64;            // pairs per lane
+    static_assert(BK * NQW % 64 == 0, "whole pairs per lane");
     const TS* x;
-    int n0, i_first, bl, islot, wave, lane;
-    float xr[NQ], xn[NQ];
+    int n0, i0, wave, lane;
+    int bl[PPL], il[PPL];
+    float xr[PPL], xn[PPL];
     __device__ GenB(const GemmArgs& a, int, int tn) {
         x = static_cast<const TS*>(a.x);
         n0 = tn * 256;
-        i_first = (unsigned)n0 / (unsigned)a.Kb;
         lane = threadIdx.x & 63;
         wave = threadIdx.x >> 6;
-        bl = lane % BK;
-        islot = wave + 8 * (lane / BK);                  // first tile input of this lane
+        i0 = (unsigned)n0 / (unsigned)a.Kb + wave * NQW;  // first input of this wave
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const int pp = lane + 64 * j;
+            bl[j] = pp / NQW;
+            il[j] = pp % NQW;
+        }
     }
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
-        const int64_t brow = (int64_t)min(kt * BK + bl, a.N - 1) * a.I;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            xn[q] = load_f(x, brow + min(i_first + islot + 8 * LPW * q, a.I - 1));
+        for (int j = 0; j < PPL; ++j) {
+            const int64_t brow = (int64_t)min(kt * BK + bl[j], a.N - 1) * a.I;
+            xn[j] = load_f(x, brow + min(i0 + il[j], a.I - 1));
+        }
     }
     __device__ __forceinline__ void rotate() {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) xr[q] = xn[q];
+        for (int j = 0; j < PPL; ++j) xr[j] = xn[j];
     }
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
         // zero the rows of this wave's inputs: 8 rows of 128 bytes per instruction
 #pragma unroll
-        for (int j = 0; j < NQ * LPW; ++j) {
-            const int rb = (i_first + wave + 8 * j) * a.Kb - n0;
+        for (int e = 0; e < NQW; ++e) {
+            const int rb = (i0 + e) * a.Kb - n0;
 #pragma unroll
             for (int z = 0; z < ZR; ++z) {
                 const int rr = 8 * z + (lane >> 3);
@@ -269,14 +292,13 @@ struct GenB {
                     make_uint4(0, 0, 0, 0);
             }
         }
-        const bool b_ok = kt * BK + bl < a.N;
-        char* colp = S + bl * ES;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = i_first + islot + 8 * LPW * q;
-            const bool ok = b_ok & (i < a.I);
+        for (int j = 0; j < PPL; ++j) {
+            const int i = i0 + il[j];
+            const bool ok = (kt * BK + bl[j] < a.N) & (i < a.I);
             const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
-            const float xv = xr[q];
+            char* colp = S + bl[j] * ES;
+            const float xv = xr[j];
             float u;
             const int s = span_u(xv, a.g, u);
             float bb[4];
@@ -288,11 +310,9 @@ struct GenB {
                 const bool v = ok & (m >= 0) & (m < a.K) & (row >= 0) & (row < 256);
                 Traits<TS>::put(v ? colp + row * PITCH : S + 128, bb[r]);
             }
-            if (a.base) {
-                const int row = rb + a.K;
-                const bool v = ok & (row >= 0) & (row < 256);
-                Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
-            }
+            const int row = rb + a.K;
+            const bool v = ok & (a.base != 0) & (row >= 0) & (row < 256);
+            Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
         }
     }
 };
@@ -635,30 +655,29 @@ static int fwd_nin(const Plan& p) { return (p.BK - 1 + p.Kb - 1) / p.Kb + 1; }
 
 template <typename TS>
 static hipError_t fwd_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
-    const int n = fwd_nin(p);
+    const int n = fwd_nin(p);           // rounded up to a power of two
     if (n <= 2) return run_gemm<TS, GenA<TS, 2>, LoadB, EpiY>(a, s);
-    if (n <= 3) return run_gemm<TS, GenA<TS, 3>, LoadB, EpiY>(a, s);
     if (n <= 4) return run_gemm<TS, GenA<TS, 4>, LoadB, EpiY>(a, s);
-    if (n <= 6) return run_gemm<TS, GenA<TS, 6>, LoadB, EpiY>(a, s);
-    if (n <= 9) return run_gemm<TS, GenA<TS, 9>, LoadB, EpiY>(a, s);
-    return run_gemm<TS, GenA<TS, 18>, LoadB, EpiY>(a, s);
+    if (n <= 8) return run_gemm<TS, GenA<TS, 8>, LoadB, EpiY>(a, s);
+    if (n <= 16) return run_gemm<TS, GenA<TS, 16>, LoadB, EpiY>(a, s);
+    return run_gemm<TS, GenA<TS, 32>, LoadB, EpiY>(a, s);
 }
 
-// (inputs per lane NQ, zero-fill instructions per input ZR) of the dC
+// (inputs per wave NQW, zero-fill instructions per input ZR) of the dC
 // generator, from Kb: the 256-row tile meets ceil(255 / Kb) + 1 inputs, dealt
-// to 8 waves.
-static int dc_nq(const Plan& p) { return ((255 + p.Kb - 1) / p.Kb + 1 + 7) / 8; }
+// to 8 waves: Kb 4..8 needs up to 9 inputs per wave, 9..16 up to 4, larger Kb
+// up to 2.
+static int dc_nqw(const Plan& p) { return ((255 + p.Kb - 1) / p.Kb + 1 + 7) / 8; }
 
 template <typename TS>
 static hipError_t dc_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
-    constexpr int LPW = 64 / Traits<TS>::BK;
     const int zr = (p.Kb + 7) / 8;
-    const int nq = (dc_nq(p) + LPW - 1) / LPW;       // inputs per lane
-    if (zr <= 1 && nq <= 9) return run_gemm<TS, LoadA, GenB<TS, 9, 1>, EpiDC>(a, s);
+    const int nq = dc_nqw(p);
+    if (zr <= 1 && nq <= 10) return run_gemm<TS, LoadA, GenB<TS, 10, 1>, EpiDC>(a, s);
     if (zr <= 2 && nq <= 4) return run_gemm<TS, LoadA, GenB<TS, 4, 2>, EpiDC>(a, s);
-    if (zr <= 3 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 3>, EpiDC>(a, s);
+    if (zr <= 4 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 4>, EpiDC>(a, s);
     if (zr <= 7 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 7>, EpiDC>(a, s);
-    return run_gemm<TS, LoadA, GenB<TS, 1, 32>, EpiDC>(a, s);
+    return run_gemm<TS, LoadA, GenB<TS, 2, 32>, EpiDC>(a, s);
 }
 
 hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s) {
@@ -684,6 +703,9 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     a.ldb = p.Opad * p.esize;
     a.nkt = (int)(p.Opad / p.BK);
     a.out0 = dx;
+    // both operands are copied and equally large per tile: 8 x 4 tiles per
+    // 32 resident workgroups of an XCD share each dy and each C'^T tile
+    a.group_m = 8;
     if (p.dtype == KAN_F32) return run_gemm<float, LoadA, LoadBdx, EpiDX>(a, s);
     return run_gemm<uint16_t, LoadA, LoadBdx, EpiDX>(a, s);
 }
