@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None)
+    ap.add_argument("--code-digest", action="store_true",
+                    help="print the digest that ties a counter summary to the kernel source")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (HBM counter calibration)")
     return ap.parse_args()
@@ -71,6 +73,9 @@ def stage_names(nl):
 
 def main():
     args = parse()
+    if args.code_digest:
+        print(kernel_code_digest())
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -241,6 +246,16 @@ def main():
     print(json.dumps(out))
 
 
+def kernel_code_digest():
+    """sha256 of the contraction kernels' source with // comments and blank
+    lines removed: a counter summary stays valid across comment edits and goes
+    stale with any change to the code."""
+    import re
+    src = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc", "kan_mfma.hip")
+    lines = [re.sub(r"//.*", "", l).rstrip() for l in open(src).read().splitlines()]
+    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()
+
+
 def read_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -252,8 +267,7 @@ def read_traffic(workload, kernel):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc", "kan_mfma.hip")
-    if kv.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if kv.get("code_sha256") != kernel_code_digest():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

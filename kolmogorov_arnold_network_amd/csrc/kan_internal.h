@@ -13,12 +13,11 @@
 namespace kan {
 
 // MFMA tile geometry (both dtypes): 256 x 256 output tile per workgroup of
-// 4 waves (2 x 2, 128 x 128 each), k-tiles of 128 bytes per row (64 bf16 or
+// 8 waves (4 x 2, 64 x 128 each), k-tiles of 128 bytes per row (64 bf16 or
 // 32 float) staged in LDS with a 144-byte row pitch, two stages.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 constexpr int kTileKBytes = 128;
-constexpr int kThreads = 256;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 

@@ -17,9 +17,10 @@
 // in a fixed order without atomics (FlashKAT abstract: atomic gradient
 // accumulation and memory stalls are what slow the backward pass).
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2 waves of
-// 128 x 128 = 4 x 4 MFMA blocks of 32 x 32), k-tiles of 128 bytes per row
-// (64 bf16 / 32 float), two LDS stages of A and B with a 144-byte row pitch.
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (4 x 2 waves of
+// 64 x 128 = 2 x 4 MFMA blocks of 32 x 32, two waves per SIMD), k-tiles of
+// 128 bytes per row (64 bf16 / 32 float), two LDS stages of A and B with a
+// 144-byte row pitch; global loads run two k-tiles ahead of the MFMAs.
 // bf16 uses v_mfma_f32_32x32x16_bf16, float uses v_mfma_f32_32x32x2_f32;
 // both accumulate in float32.  The 32 x 32 blocks keep each accumulator in
 // one 16-register tuple, which the register allocator leaves in place (16 x
@@ -108,14 +109,15 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& a, int& tm, int& tn)
 }
 
 // ---- operands ----
-// Every operand has three hooks, called by the k-loop:
-//   fetch(kt)     start the global loads of k-tile kt into the `next` slot
-//                 (a copied operand: the tile itself; a generated one: the x
-//                 values it needs)
-//   store(S, kt)  write k-tile kt into LDS tile S from the `current` slot
-//   rotate()      next -> current
-// A tile is fetched two k-tiles ahead of its store, so its loads have two
-// k-tiles of MFMA work to arrive.  The workgroup has 8 waves (2 per SIMD, so
+// Every operand holds two register slots and has two hooks, called by the
+// k-loop with a compile-time slot index SL:
+//   fetch<SL>(kt)     start the global loads of k-tile kt into slot SL (a
+//                     copied operand: the tile itself; a generated one: the x
+//                     values it needs)
+//   store<SL>(S, kt)  write k-tile kt into LDS tile S from slot SL
+// The loop alternates the slots, so a tile's loads have two k-tiles of MFMA
+// work to arrive and no slot is ever copied (a register copy out of a slot
+// whose loads are in flight would wait for them).  The workgroup has 8 waves (2 per SIMD, so
 // one wave's vector work runs while the other's MFMAs execute), arranged
 // 4 x 2 over the 256 x 256 tile; wave w owns rows 64 (w / 2) .. +64 and
 // columns 128 (w % 2) .. +128.
@@ -127,22 +129,20 @@ constexpr int NTHR = 512;
 struct LoadOp {
     const char* base;    // this thread's row and 16-byte column in the tile
     int64_t ld;
-    uint4 cur[4], nxt[4];
+    uint4 v[2][4];
     __device__ LoadOp(const char* p, int64_t r0, int64_t ld_)
         : base(p + (r0 + (threadIdx.x >> 3)) * ld_ + (threadIdx.x & 7) * 16), ld(ld_) {}
+    template <int SL>
     __device__ __forceinline__ void fetch(const GemmArgs&, int kt) {
         const char* p = base + (int64_t)kt * 128;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const uint4*>(p + (int64_t)(64 * q) * ld);
+        for (int q = 0; q < 4; ++q) v[SL][q] = *reinterpret_cast<const uint4*>(p + (int64_t)(64 * q) * ld);
     }
+    template <int SL>
     __device__ __forceinline__ void store(const GemmArgs&, char* S, int) {
         const int t = threadIdx.x, c = t & 7, r = t >> 3;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(S + (r + 64 * q) * PITCH + c * 16) = cur[q];
-    }
-    __device__ __forceinline__ void rotate() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(S + (r + 64 * q) * PITCH + c * 16) = v[SL][q];
     }
 };
 struct LoadA : LoadOp {                // rows m0 = tm * 256
@@ -173,10 +173,11 @@ struct GenA {
     static constexpr int RSTEP = NTHR / NIN;           // rows between a thread's pairs
     static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
     const TS* x;
-    int q, row0, i_cur, i_nxt;
+    int q, row0;
     int64_t xrow[PPT];
     bool row_ok[PPT];
-    float xr[PPT], xn[PPT];
+    float xs[2][PPT];    // slots: x values of this lane's pairs
+    int is[2];           // slots: this lane's input
     __device__ GenA(const GemmArgs& a, int tm, int) {
         x = static_cast<const TS*>(a.x);
         q = threadIdx.x % NIN;
@@ -188,17 +189,14 @@ struct GenA {
             xrow[j] = (int64_t)min(b, a.N - 1) * a.I;
         }
     }
+    template <int SL>
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
-        i_nxt = (unsigned)(kt * BK) / (unsigned)a.Kb;
-        const int i = min(i_nxt + q, a.I - 1);
+        is[SL] = (unsigned)(kt * BK) / (unsigned)a.Kb + q;
+        const int i = min(is[SL], a.I - 1);
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) xn[j] = load_f(x, xrow[j] + i);
+        for (int j = 0; j < PPT; ++j) xs[SL][j] = load_f(x, xrow[j] + i);
     }
-    __device__ __forceinline__ void rotate() {
-        i_cur = i_nxt;
-#pragma unroll
-        for (int j = 0; j < PPT; ++j) xr[j] = xn[j];
-    }
+    template <int SL>
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
         // zero fill: the NIN lanes of a row clear its 8 chunks of 16 bytes
 #pragma unroll
@@ -211,14 +209,14 @@ struct GenA {
             }
         }
         const int k0 = kt * BK;
-        const int i = i_cur + q;
+        const int i = is[SL];
         const int cb = i * a.Kb - k0;                 // tile column of (i, m = 0)
         const int cs = cb + a.K;                      // silu column
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
             char* row = S + (row0 + RSTEP * j) * PITCH;
             const bool ok = row_ok[j] & (i < a.I);
-            const float xv = xr[j];
+            const float xv = xs[SL][j];
             float u;
             const int s = span_u(xv, a.g, u);
             float bb[4];
@@ -253,7 +251,7 @@ struct GenB {
     const TS* x;
     int n0, i0, wave, lane;
     int bl[PPL], il[PPL];
-    float xr[PPL], xn[PPL];
+    float xs[2][PPL];    // slots: x values of this lane's pairs
     __device__ GenB(const GemmArgs& a, int, int tn) {
         x = static_cast<const TS*>(a.x);
         n0 = tn * 256;
@@ -267,17 +265,15 @@ struct GenB {
             il[j] = pp % NQW;
         }
     }
+    template <int SL>
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
 #pragma unroll
         for (int j = 0; j < PPL; ++j) {
             const int64_t brow = (int64_t)min(kt * BK + bl[j], a.N - 1) * a.I;
-            xn[j] = load_f(x, brow + min(i0 + il[j], a.I - 1));
+            xs[SL][j] = load_f(x, brow + min(i0 + il[j], a.I - 1));
         }
     }
-    __device__ __forceinline__ void rotate() {
-#pragma unroll
-        for (int j = 0; j < PPL; ++j) xr[j] = xn[j];
-    }
+    template <int SL>
     __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
         // zero the rows of this wave's inputs: 8 rows of 128 bytes per instruction
 #pragma unroll
@@ -298,7 +294,7 @@ struct GenB {
             const bool ok = (kt * BK + bl[j] < a.N) & (i < a.I);
             const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
             char* colp = S + bl[j] * ES;
-            const float xv = xr[j];
+            const float xv = xs[SL][j];
             float u;
             const int s = span_u(xv, a.g, u);
             float bb[4];
@@ -460,40 +456,47 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Prologue: tile 0 into stage 0, tile 1 fetched.  Iteration kt: fetch
-    // tile kt+2 (clamped to the last tile, so every load is in bounds), run
-    // the MFMAs of tile kt from stage kt % 2, store tile kt+1 into the other
-    // stage.  The loads are issued first and pinned there (left alone, the
-    // scheduler sinks them next to their use).
+    // Two LDS stages S0, S1 and two register slots per operand.  Invariant at
+    // the top of each pass of the loop (kt even): S0 holds tile kt, slot 1 is
+    // loading tile kt+1 and slot 0 tile kt+2.  A slot is refilled right after
+    // its tile is stored, so each tile's loads have two k-tiles of MFMAs to
+    // arrive.  Fetch indexes are clamped to the last tile, so every load is in
+    // bounds; the extra loads at the end are never stored.
     const int nkt = args.nkt;
-    A.fetch(args, 0);
-    B.fetch(args, 0);
-    A.rotate();
-    B.rotate();
-    A.store(args, lds, 0);
-    B.store(args, lds + TILE_BYTES, 0);
-    A.fetch(args, min(1, nkt - 1));
-    B.fetch(args, min(1, nkt - 1));
-    A.rotate();
-    B.rotate();
+    char* S0 = lds;
+    char* S1 = lds + STAGE_BYTES;
+    A.template fetch<0>(args, 0);
+    B.template fetch<0>(args, 0);
+    A.template fetch<1>(args, min(1, nkt - 1));
+    B.template fetch<1>(args, min(1, nkt - 1));
+    A.template store<0>(args, S0, 0);
+    B.template store<0>(args, S0 + TILE_BYTES, 0);
+    A.template fetch<0>(args, min(2, nkt - 1));
+    B.template fetch<0>(args, min(2, nkt - 1));
     __syncthreads();
-    for (int kt = 0; kt + 1 < nkt; ++kt) {
-        const int cur = kt & 1;
-        A.fetch(args, min(kt + 2, nkt - 1));
-        B.fetch(args, min(kt + 2, nkt - 1));
+    int kt = 0;
+    for (; kt + 2 < nkt; kt += 2) {
+        compute(S0, S0 + TILE_BYTES);
+        A.template store<1>(args, S1, kt + 1);
+        B.template store<1>(args, S1 + TILE_BYTES, kt + 1);
+        A.template fetch<1>(args, min(kt + 3, nkt - 1));
+        B.template fetch<1>(args, min(kt + 3, nkt - 1));
         __builtin_amdgcn_sched_barrier(0);
-        const char* Sc = lds + cur * STAGE_BYTES;
-        compute(Sc, Sc + TILE_BYTES);
-        char* Sn = lds + (cur ^ 1) * STAGE_BYTES;
-        A.store(args, Sn, kt + 1);
-        B.store(args, Sn + TILE_BYTES, kt + 1);
-        A.rotate();
-        B.rotate();
+        __syncthreads();
+        compute(S1, S1 + TILE_BYTES);
+        A.template store<0>(args, S0, kt + 2);
+        B.template store<0>(args, S0 + TILE_BYTES, kt + 2);
+        A.template fetch<0>(args, min(kt + 4, nkt - 1));
+        B.template fetch<0>(args, min(kt + 4, nkt - 1));
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     }
-    {
-        const char* Sc = lds + ((nkt - 1) & 1) * STAGE_BYTES;
-        compute(Sc, Sc + TILE_BYTES);
+    compute(S0, S0 + TILE_BYTES);
+    if (kt + 1 < nkt) {
+        A.template store<1>(args, S1, kt + 1);
+        B.template store<1>(args, S1 + TILE_BYTES, kt + 1);
+        __syncthreads();
+        compute(S1, S1 + TILE_BYTES);
     }
     __syncthreads();
     Epi::template run<TS>(args, acc, tm, tn, lds);
