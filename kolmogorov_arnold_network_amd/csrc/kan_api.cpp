@@ -80,7 +80,6 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.Kf = round_up(q.IKb, q.BK);
         q.Qn = kTileN / q.Kb;
         q.tiles_dx = (q.I + q.Qn - 1) / q.Qn;
-        q.rowsT = round_up((q.tiles_dx - 1) * q.Qn * q.Kb + kTileN, q.BK);
         size_t off = 0;
         auto take = [&](size_t bytes, size_t* o, size_t* sz) {
             *o = off;
@@ -90,7 +89,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         take((size_t)(q.Opad * q.Kf) * q.esize, &q.off_cp, &q.sz_cp);
         q.ws_fwd = off;
         off = 0;
-        take((size_t)(q.rowsT * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
+        take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
         take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
         take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
         q.ws_bwd = off;

@@ -38,13 +38,14 @@ struct Plan {
     int64_t Kf;          // forward contraction length: IKb rounded up to BK
     int Qn;              // inputs per n-tile of the dx contraction (floor(256 / Kb))
     int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I / Qn)
-    int64_t rowsT;       // rows of the transposed packed C' (covers the last dx tile)
 
-    // workspace layout (bytes); forward uses [off_cp, +sz_cp)
-    size_t off_cp, sz_cp;      // C' packed [Opad][Kf]
-    size_t off_cpt, sz_cpt;    // C'^T packed [rowsT][Opad]
-    size_t off_dyp, sz_dyp;    // dy in storage dtype [Npad][Opad]
-    size_t off_dyt, sz_dyt;    // dy^T in storage dtype [Opad][Npad]
+    // workspace layout (bytes); forward uses [off_cp, +sz_cp).  Every array is
+    // blocked: 256-row tiles, each cut into k-tiles of 256 x BK contiguous
+    // elements.
+    size_t off_cp, sz_cp;      // C': rows j < Opad, k = (i, m) < Kf
+    size_t off_cpt, sz_cpt;    // C'^T: tiles_dx tiles of whole inputs, k = j < Opad
+    size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
+    size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t ws_fwd, ws_bwd;
 };
 

@@ -31,6 +31,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kan_internal.h"
 
@@ -40,12 +41,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes in 4 registers
 
 constexpr int PITCH = 144;                     // bytes per LDS tile row (128 data + 16 pad)
 constexpr int TILE_BYTES = 256 * PITCH;        // one 256-row operand tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // A + B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;     // two stages: 147456 bytes
 constexpr int DX_PITCH = 260;                  // floats per row of the dx epilogue staging
+constexpr int BLOCK_BYTES = 256 * 128;         // one packed k-tile of one 256-row tile
 
 template <typename TS> struct Traits;
 template <> struct Traits<uint16_t> {          // bf16 storage
@@ -75,12 +78,22 @@ template <> struct Traits<float> {
     __device__ static void put(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
 };
 
+// Calls f(std::integral_constant<int, I>()) for I = B .. E-1, so that the
+// index is a constant expression inside f.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
+}
+
 struct GemmArgs {
     int tiles_m, tiles_n, nkt, group_m;
-    const char* a;       // loaded A operand (row-major [rows][k]), or null
-    int64_t lda;         // bytes per row
+    const char* a;       // loaded A operand (blocked, see LoadOp), or null
+    int64_t a_tstride;   // bytes per 256-row tile: k-tiles * BLOCK_BYTES
     const char* b;       // loaded B operand, or null
-    int64_t ldb;
+    int64_t b_tstride;
     const void* x;       // generator input x [N, I]
     GridK g;
     int N, I, O, K, Kb, base, Qn;
@@ -109,51 +122,60 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& a, int& tm, int& tn)
 }
 
 // ---- operands ----
-// Every operand holds two register slots and has two hooks, called by the
-// k-loop with a compile-time slot index SL:
-//   fetch<SL>(kt)     start the global loads of k-tile kt into slot SL (a
-//                     copied operand: the tile itself; a generated one: the x
-//                     values it needs)
-//   store<SL>(S, kt)  write k-tile kt into LDS tile S from slot SL
-// The loop alternates the slots, so a tile's loads have two k-tiles of MFMA
-// work to arrive and no slot is ever copied (a register copy out of a slot
-// whose loads are in flight would wait for them).  The workgroup has 8 waves (2 per SIMD, so
-// one wave's vector work runs while the other's MFMAs execute), arranged
-// 4 x 2 over the 256 x 256 tile; wave w owns rows 64 (w / 2) .. +64 and
-// columns 128 (w % 2) .. +128.
+// Every operand holds DEPTH = 2 register slots; the k-loop names a slot by a
+// compile-time index SL.  Hooks:
+//   fetch<SL>(kt)             start the global loads of k-tile kt into slot SL
+//                             (a copied operand: the tile itself; a generated
+//                             one: the x values it needs)
+//   part<SL, RF>(S, kt, ktn, p)  write part p (of NPART) of k-tile kt from
+//                             slot SL into LDS tile S, then (if RF) start
+//                             refilling what that part freed with k-tile
+//                             ktn = kt + DEPTH
+// The parts are spread over the MFMA k-steps of the tile being multiplied, so
+// LDS stores, generator arithmetic and load issue overlap the matrix cores
+// instead of forming a phase of their own before each barrier.  A part's
+// loads are issued two k-tiles before the part is stored, and no slot is
+// ever copied (a register copy out of a slot whose loads are in flight would
+// wait for them).  The workgroup has 8 waves (2 per SIMD), arranged 4 x 2
+// over the 256 x 256 tile; wave w owns rows 64 (w / 2) .. +64 and columns
+// 128 (w % 2) .. +128.
 constexpr int NTHR = 512;
 
-// Operand copied from a packed row-major array: rows [r0, r0+256), k-tile kt
-// = bytes [128 kt, 128 kt + 128) of each row.  8 threads read one row's 128
-// bytes (coalesced); the tile goes through registers into LDS.
+// Operand copied from a blocked packed array: k-tile kt of 256-row tile T is
+// one contiguous block of 256 rows x 128 bytes at T * tstride + kt *
+// BLOCK_BYTES.  (Row-major operands put the 256 rows of a k-tile kilobytes
+// apart, one page each, and loading them cost a quarter of the run time.)
+// Part q: thread t loads bytes 8192 q + 16 t of the block, i.e. row
+// 64 q + t / 8, 16-byte chunk t % 8, so one wave instruction reads 1 KB in
+// order; the part goes through registers into LDS.
 struct LoadOp {
-    const char* base;    // this thread's row and 16-byte column in the tile
-    int64_t ld;
-    uint4 v[2][4];
-    __device__ LoadOp(const char* p, int64_t r0, int64_t ld_)
-        : base(p + (r0 + (threadIdx.x >> 3)) * ld_ + (threadIdx.x & 7) * 16), ld(ld_) {}
+    static constexpr int NPART = 4;
+    static constexpr int DEPTH = 2;
+    const char* base;    // this thread's 16 bytes of k-tile 0 of the tile
+    u32x4 v[2][4];
+    __device__ LoadOp(const char* p, int64_t tile, int64_t tstride)
+        : base(p + tile * tstride + threadIdx.x * 16) {}
+    template <int SL>
+    __device__ __forceinline__ void load(int kt, int q) {
+        v[SL][q] = *reinterpret_cast<const u32x4*>(base + (int64_t)kt * BLOCK_BYTES + q * 8192);
+    }
     template <int SL>
     __device__ __forceinline__ void fetch(const GemmArgs&, int kt) {
-        const char* p = base + (int64_t)kt * 128;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[SL][q] = *reinterpret_cast<const uint4*>(p + (int64_t)(64 * q) * ld);
+        for (int q = 0; q < 4; ++q) load<SL>(kt, q);
     }
-    template <int SL>
-    __device__ __forceinline__ void store(const GemmArgs&, char* S, int) {
+    template <int SL, bool RF, int q>
+    __device__ __forceinline__ void part(const GemmArgs&, char* S, int, int ktn) {
         const int t = threadIdx.x, c = t & 7, r = t >> 3;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(S + (r + 64 * q) * PITCH + c * 16) = v[SL][q];
+        *reinterpret_cast<u32x4*>(S + (r + 64 * q) * PITCH + c * 16) = v[SL][q];
+        if (RF) load<SL>(ktn, q);
     }
 };
-struct LoadA : LoadOp {                // rows m0 = tm * 256
-    __device__ LoadA(const GemmArgs& a, int tm, int) : LoadOp(a.a, (int64_t)tm * 256, a.lda) {}
+struct LoadA : LoadOp {                // tile tm of A
+    __device__ LoadA(const GemmArgs& a, int tm, int) : LoadOp(a.a, tm, a.a_tstride) {}
 };
-struct LoadB : LoadOp {                // rows n0 = tn * 256
-    __device__ LoadB(const GemmArgs& a, int, int tn) : LoadOp(a.b, (int64_t)tn * 256, a.ldb) {}
-};
-struct LoadBdx : LoadOp {              // rows n0 = tn * Qn * Kb: whole inputs per tile
-    __device__ LoadBdx(const GemmArgs& a, int, int tn)
-        : LoadOp(a.b, (int64_t)tn * a.Qn * a.Kb, a.ldb) {}
+struct LoadB : LoadOp {                // tile tn of B
+    __device__ LoadB(const GemmArgs& a, int, int tn) : LoadOp(a.b, tn, a.b_tstride) {}
 };
 
 // Forward A operand Phi'[b, (i, m)].  The (row, input) pairs of a k-tile are
@@ -170,6 +192,8 @@ struct GenA {
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
     static constexpr int PPT = 256 * NIN / NTHR;       // pairs per thread
+    static constexpr int NPART = PPT;                  // part j: pair j (its row)
+    static constexpr int DEPTH = 2;                    // two slots of x values
     static constexpr int RSTEP = NTHR / NIN;           // rows between a thread's pairs
     static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
     const TS* x;
@@ -196,41 +220,35 @@ struct GenA {
 #pragma unroll
         for (int j = 0; j < PPT; ++j) xs[SL][j] = load_f(x, xrow[j] + i);
     }
-    template <int SL>
-    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
-        // zero fill: the NIN lanes of a row clear its 8 chunks of 16 bytes
+    // Pair j: the NIN lanes of its row clear the row's 8 chunks of 16 bytes,
+    // then each scatters its input's <= 4 spline values and silu value.
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* row = S + (row0 + RSTEP * j) * PITCH;
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            char* row = S + (row0 + RSTEP * j) * PITCH;
-#pragma unroll
-            for (int c = 0; c < (8 + NIN - 1) / NIN; ++c) {
-                const int chunk = q * ((8 + NIN - 1) / NIN) + c;
-                *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
-            }
+        for (int c = 0; c < (8 + NIN - 1) / NIN; ++c) {
+            const int chunk = q * ((8 + NIN - 1) / NIN) + c;
+            *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
         }
-        const int k0 = kt * BK;
         const int i = is[SL];
-        const int cb = i * a.Kb - k0;                 // tile column of (i, m = 0)
+        const int cb = i * a.Kb - kt * BK;            // tile column of (i, m = 0)
         const int cs = cb + a.K;                      // silu column
+        const bool ok = row_ok[j] & (i < a.I);
+        const float xv = xs[SL][j];
+        float u;
+        const int s = span_u(xv, a.g, u);
+        float bb[4];
+        pieces(u, bb[0], bb[1], bb[2], bb[3]);
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            char* row = S + (row0 + RSTEP * j) * PITCH;
-            const bool ok = row_ok[j] & (i < a.I);
-            const float xv = xs[SL][j];
-            float u;
-            const int s = span_u(xv, a.g, u);
-            float bb[4];
-            pieces(u, bb[0], bb[1], bb[2], bb[3]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = s - 3 + r;
-                const int col = cb + m;
-                const bool v = ok & (m >= 0) & (m < a.K) & (col >= 0) & (col < BK);
-                Traits<TS>::put(row + (v ? col : BK) * ES, bb[r]);
-            }
-            const bool v = ok & (a.base != 0) & (cs >= 0) & (cs < BK);
-            Traits<TS>::put(row + (v ? cs : BK) * ES, silu(xv));
+        for (int r = 0; r < 4; ++r) {
+            const int m = s - 3 + r;
+            const int col = cb + m;
+            const bool v = ok & (m >= 0) & (m < a.K) & (col >= 0) & (col < BK);
+            Traits<TS>::put(row + (v ? col : BK) * ES, bb[r]);
         }
+        const bool v = ok & (a.base != 0) & (cs >= 0) & (cs < BK);
+        Traits<TS>::put(row + (v ? cs : BK) * ES, silu(xv));
+        if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
 
@@ -247,6 +265,8 @@ struct GenB {
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
     static constexpr int PPL = BK * NQW / 64;            // pairs per lane
+    static constexpr int NPART = 1 + PPL;                // zero fill, then pair by pair
+    static constexpr int DEPTH = 2;                      // two slots of x values
     static_assert(BK * NQW % 64 == 0, "whole pairs per lane");
     const TS* x;
     int n0, i0, wave, lane;
@@ -273,42 +293,45 @@ struct GenB {
             xs[SL][j] = load_f(x, brow + min(i0 + il[j], a.I - 1));
         }
     }
-    template <int SL>
-    __device__ __forceinline__ void store(const GemmArgs& a, char* S, int kt) {
-        // zero the rows of this wave's inputs: 8 rows of 128 bytes per instruction
+    template <int SL, bool RF, int p>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        if constexpr (p == 0) {
+            // zero the rows of this wave's inputs: 8 rows of 128 bytes per instruction
 #pragma unroll
-        for (int e = 0; e < NQW; ++e) {
-            const int rb = (i0 + e) * a.Kb - n0;
+            for (int e = 0; e < NQW; ++e) {
+                const int rb = (i0 + e) * a.Kb - n0;
 #pragma unroll
-            for (int z = 0; z < ZR; ++z) {
-                const int rr = 8 * z + (lane >> 3);
-                const int row = rb + rr;
-                const bool v = (rr < a.Kb) & (row >= 0) & (row < 256);
-                *reinterpret_cast<uint4*>(v ? S + row * PITCH + (lane & 7) * 16 : S + 128) =
-                    make_uint4(0, 0, 0, 0);
+                for (int z = 0; z < ZR; ++z) {
+                    const int rr = 8 * z + (lane >> 3);
+                    const int row = rb + rr;
+                    const bool v = (rr < a.Kb) & (row >= 0) & (row < 256);
+                    *reinterpret_cast<uint4*>(v ? S + row * PITCH + (lane & 7) * 16 : S + 128) =
+                        make_uint4(0, 0, 0, 0);
+                }
             }
+            return;
+        } else {
+        constexpr int j = p - 1;
+        const int i = i0 + il[j];
+        const bool ok = (kt * BK + bl[j] < a.N) & (i < a.I);
+        const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
+        char* colp = S + bl[j] * ES;
+        const float xv = xs[SL][j];
+        float u;
+        const int s = span_u(xv, a.g, u);
+        float bb[4];
+        pieces(u, bb[0], bb[1], bb[2], bb[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = s - 3 + r;
+            const int row = rb + m;
+            const bool v = ok & (m >= 0) & (m < a.K) & (row >= 0) & (row < 256);
+            Traits<TS>::put(v ? colp + row * PITCH : S + 128, bb[r]);
         }
-#pragma unroll
-        for (int j = 0; j < PPL; ++j) {
-            const int i = i0 + il[j];
-            const bool ok = (kt * BK + bl[j] < a.N) & (i < a.I);
-            const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
-            char* colp = S + bl[j] * ES;
-            const float xv = xs[SL][j];
-            float u;
-            const int s = span_u(xv, a.g, u);
-            float bb[4];
-            pieces(u, bb[0], bb[1], bb[2], bb[3]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = s - 3 + r;
-                const int row = rb + m;
-                const bool v = ok & (m >= 0) & (m < a.K) & (row >= 0) & (row < 256);
-                Traits<TS>::put(v ? colp + row * PITCH : S + 128, bb[r]);
-            }
-            const int row = rb + a.K;
-            const bool v = ok & (a.base != 0) & (row >= 0) & (row < 256);
-            Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
+        const int row = rb + a.K;
+        const bool v = ok & (a.base != 0) & (row >= 0) & (row < 256);
+        Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
+        if constexpr (RF && p == NPART - 1) fetch<SL>(a, ktn);
         }
     }
 };
@@ -436,10 +459,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
 
     const int arow = (wm + (lane & 31)) * PITCH + (lane >> 5) * 16;
     const int brow = (wn + (lane & 31)) * PITCH + (lane >> 5) * 16;
-    // MFMAs over one staged k-tile: 4 k-steps of 32 bytes per row.
-    auto compute = [&](const char* As, const char* Bs) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+    // MFMAs over one staged k-tile: 4 k-steps of 32 bytes per row; after(ks)
+    // issues the work placed behind k-step ks.
+    auto compute = [&](const char* As, const char* Bs, auto&& after) {
+        static_for<0, 4>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
             uint4 fa[2], fb[4];
 #pragma unroll
             for (int f = 0; f < 4; ++f)
@@ -451,99 +475,123 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
             for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) Traits<TS>::mma(acc[fi][fj], fa[fi], fb[fj]);
-            // bounds the fragments live at once (left free, the scheduler
-            // hoists every fragment read of the tile)
+            after(ksc);
+            // pins the k-step's work in place (left free, the scheduler hoists
+            // every fragment read of the tile and sinks the stores)
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
-    // Two LDS stages S0, S1 and two register slots per operand.  Invariant at
-    // the top of each pass of the loop (kt even): S0 holds tile kt, slot 1 is
-    // loading tile kt+1 and slot 0 tile kt+2.  A slot is refilled right after
-    // its tile is stored, so each tile's loads have two k-tiles of MFMAs to
-    // arrive.  Fetch indexes are clamped to the last tile, so every load is in
-    // bounds; the extra loads at the end are never stored.
+    // Store k-tile kts from slot SL into stage S, part by part behind the
+    // k-steps of the tile being multiplied, and (if RF) refill each operand's
+    // slot with tile kts + DEPTH (clamped to the last tile, so every load is
+    // in bounds; the extra loads at the end are never stored).
     const int nkt = args.nkt;
+    auto stage = [&](auto slot, auto refill, char* S, int kts, auto ksc) {
+        constexpr int SL = decltype(slot)::value;
+        constexpr bool RF = decltype(refill)::value;
+        constexpr int ks = decltype(ksc)::value;
+        const int ka = min(kts + AOp::DEPTH, nkt - 1), kb = min(kts + BOp::DEPTH, nkt - 1);
+        static_for<0, AOp::NPART>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            if constexpr (p * 4 / AOp::NPART == ks) A.template part<SL, RF, p>(args, S, kts, ka);
+        });
+        static_for<0, BOp::NPART>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            if constexpr (p * 4 / BOp::NPART == ks)
+                B.template part<SL, RF, p>(args, S + TILE_BYTES, kts, kb);
+        });
+    };
+    const std::integral_constant<int, 0> slot0;
+    const std::integral_constant<int, 1> slot1;
+    const std::true_type refill;
+    const std::false_type last;
+    auto nothing = [](auto) {};
+    // Two LDS stages S0, S1.  Invariant at the top of each pass of the loop
+    // (kt even): S0 holds tile kt; an operand of DEPTH 2 has slot 1 loading
+    // tile kt+1 and slot 0 tile kt+2, one of DEPTH 1 has its slot loading tile
+    // kt+1.  While tile kt is multiplied from S0, tile kt+1 goes into S1 and
+    // the slots refill; then the same with the stages swapped.
     char* S0 = lds;
     char* S1 = lds + STAGE_BYTES;
     A.template fetch<0>(args, 0);
     B.template fetch<0>(args, 0);
-    A.template fetch<1>(args, min(1, nkt - 1));
-    B.template fetch<1>(args, min(1, nkt - 1));
-    A.template store<0>(args, S0, 0);
-    B.template store<0>(args, S0 + TILE_BYTES, 0);
-    A.template fetch<0>(args, min(2, nkt - 1));
-    B.template fetch<0>(args, min(2, nkt - 1));
+    if (AOp::DEPTH == 2) A.template fetch<1>(args, min(1, nkt - 1));
+    if (BOp::DEPTH == 2) B.template fetch<1>(args, min(1, nkt - 1));
+    static_for<0, 4>([&](auto ksc) { stage(slot0, refill, S0, 0, ksc); });
     __syncthreads();
     int kt = 0;
     for (; kt + 2 < nkt; kt += 2) {
-        compute(S0, S0 + TILE_BYTES);
-        A.template store<1>(args, S1, kt + 1);
-        B.template store<1>(args, S1 + TILE_BYTES, kt + 1);
-        A.template fetch<1>(args, min(kt + 3, nkt - 1));
-        B.template fetch<1>(args, min(kt + 3, nkt - 1));
-        __builtin_amdgcn_sched_barrier(0);
+        compute(S0, S0 + TILE_BYTES, [&](auto ks) { stage(slot1, refill, S1, kt + 1, ks); });
         __syncthreads();
-        compute(S1, S1 + TILE_BYTES);
-        A.template store<0>(args, S0, kt + 2);
-        B.template store<0>(args, S0 + TILE_BYTES, kt + 2);
-        A.template fetch<0>(args, min(kt + 4, nkt - 1));
-        B.template fetch<0>(args, min(kt + 4, nkt - 1));
-        __builtin_amdgcn_sched_barrier(0);
+        compute(S1, S1 + TILE_BYTES, [&](auto ks) { stage(slot0, refill, S0, kt + 2, ks); });
         __syncthreads();
     }
-    compute(S0, S0 + TILE_BYTES);
-    if (kt + 1 < nkt) {
-        A.template store<1>(args, S1, kt + 1);
-        B.template store<1>(args, S1 + TILE_BYTES, kt + 1);
-        __syncthreads();
-        compute(S1, S1 + TILE_BYTES);
-    }
+    // Last one or two tiles.  Tile kt+1 may not exist: its store then only
+    // writes the free stage S1 (every load behind it is clamped in bounds).
+    compute(S0, S0 + TILE_BYTES, [&](auto ks) { stage(slot1, last, S1, kt + 1, ks); });
+    __syncthreads();
+    if (kt + 1 < nkt) compute(S1, S1 + TILE_BYTES, nothing);
     __syncthreads();
     Epi::template run<TS>(args, acc, tm, tn, lds);
 }
 
 // ---- packing ----
+// The loaded operands are stored blocked: element (row r, k) of an operand
+// with nk = K / BK k-tiles sits at ((r / 256) * nk + k / BK) * 256 * BK +
+// (r % 256) * BK + k % BK (elements), so each k-tile of each 256-row tile is
+// one contiguous block.
+template <typename TS>
+__device__ __forceinline__ int64_t blk(int64_t r, int64_t k, int64_t nk) {
+    constexpr int BK = Traits<TS>::BK;
+    return ((r >> 8) * nk + k / BK) * (256 * BK) + (r & 255) * BK + k % BK;
+}
+
 // C'[j][k], k = i * Kb + m: C[j, i, m] for m < K, W_base[j, i] for m = K; zero
-// outside [0, O) x [0, I*Kb).  One block row per j, 4 consecutive k per thread.
+// outside [0, O) x [0, I*Kb).  Rows j < Opad, k < nk * BK.  One block row
+// per j, 4 consecutive k per thread.
 template <typename TS>
 __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
-                                TS* __restrict__ cp, int O, int I, int K, int Kb, int64_t Kf,
+                                TS* __restrict__ cp, int O, int I, int K, int Kb, int64_t nk,
                                 int64_t Opad) {
     const int64_t IKb = (int64_t)I * Kb;
+    const int64_t Kf = nk * Traits<TS>::BK;
     for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
-    TS* dst = cp + j * Kf;
-    for (int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k0 < Kf;
-         k0 += (int64_t)gridDim.x * blockDim.x * 4) {
-        int i = (int)(k0 / Kb), m = (int)(k0 - (int64_t)i * Kb);
+        for (int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k0 < Kf;
+             k0 += (int64_t)gridDim.x * blockDim.x * 4) {
+            int i = (int)(k0 / Kb), m = (int)(k0 - (int64_t)i * Kb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t k = k0 + e;
-            TS v = TS(0);
-            if (j < O && k < IKb)
-                v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
-            if (k < Kf) dst[k] = v;
-            if (++m == Kb) { m = 0; ++i; }
+            for (int e = 0; e < 4; ++e) {
+                const int64_t k = k0 + e;
+                TS v = TS(0);
+                if (j < O && k < IKb)
+                    v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
+                if (k < Kf) cp[blk<TS>(j, k, nk)] = v;
+                if (++m == Kb) { m = 0; ++i; }
+            }
         }
-    }
     }
 }
 
-// Transposed C'^T[k][j] for k < rowsT, j < Opad, through a 64 x 64 LDS tile.
+// dx B operand: tile tn holds rows rr < Qn * Kb = C'^T[tn * Qn * Kb + rr][j]
+// (the whole inputs tn * Qn ..) and zero rows above; k runs over j < nk * BK.
+// 64 rows x 64 j per block through an LDS tile.
 template <typename TS>
 __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
-                                TS* __restrict__ cpt, int O, int I, int K, int Kb,
-                                int64_t rowsT, int64_t Opad) {
+                                TS* __restrict__ cpt, int O, int I, int K, int Kb, int Qn,
+                                int64_t nk) {
     __shared__ TS tile[64][65];
-    const int64_t k0 = (int64_t)blockIdx.x * 64;
+    const int64_t R0 = (int64_t)blockIdx.x * 64;       // tile row tn * 256 + rr
     const int j0 = blockIdx.y * 64;
     const int64_t IKb = (int64_t)I * Kb;
     const int t = threadIdx.x;
     for (int e = t; e < 64 * 64; e += 256) {
         const int jj = e / 64, kk = e % 64;
         const int j = j0 + jj;
-        const int64_t k = k0 + kk;
+        const int64_t R = R0 + kk;
+        const int rr = (int)(R & 255);
+        const int64_t k = (R >> 8) * Qn * Kb + rr;
         TS v = TS(0);
-        if (j < O && k < IKb) {
+        if (j < O && rr < Qn * Kb && k < IKb) {
             const int i = (int)(k / Kb), m = (int)(k - (int64_t)i * Kb);
             v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
         }
@@ -552,8 +600,7 @@ __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__
     __syncthreads();
     for (int e = t; e < 64 * 64; e += 256) {
         const int kk = e / 64, jj = e % 64;
-        const int64_t k = k0 + kk;
-        if (k < rowsT) cpt[k * Opad + j0 + jj] = tile[jj][kk];
+        cpt[blk<TS>(R0 + kk, j0 + jj, nk)] = tile[jj][kk];
     }
 }
 
@@ -561,12 +608,14 @@ template <typename TS> __device__ __forceinline__ TS to_store(float v);
 template <> __device__ __forceinline__ float to_store<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { return f2bf(v); }
 
-// dy (float32 [N, O]) -> dyp [Npad][Opad] and dyT [Opad][Npad] in the storage
-// dtype, zero-padded; 64 x 64 tiles through LDS.
+// dy (float32 [N, O]) -> dx A operand dyp (rows b < Npad, k = j < Opad) and dC
+// A operand dyT (rows j < Opad, k = b < Npad) in the storage dtype,
+// zero-padded; 64 x 64 tiles through LDS.
 template <typename TS>
 __global__ void prep_dy_kernel(const float* __restrict__ dy, TS* __restrict__ dyp,
                                TS* __restrict__ dyt, int N, int O, int64_t Npad, int64_t Opad) {
     __shared__ TS tile[64][65];
+    constexpr int BK = Traits<TS>::BK;
     const int64_t b0 = (int64_t)blockIdx.x * 64;
     const int64_t j0 = (int64_t)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -574,13 +623,13 @@ __global__ void prep_dy_kernel(const float* __restrict__ dy, TS* __restrict__ dy
         const int bb = e / 64, jj = e % 64;
         const int64_t b = b0 + bb, j = j0 + jj;
         const TS v = (b < N && j < O) ? to_store<TS>(dy[b * O + j]) : TS(0);
-        dyp[b * Opad + j] = v;
+        dyp[blk<TS>(b, j, Opad / BK)] = v;
         tile[bb][jj] = v;
     }
     __syncthreads();
     for (int e = t; e < 64 * 64; e += 256) {
         const int jj = e / 64, bb = e % 64;
-        dyt[(j0 + jj) * Npad + b0 + bb] = tile[bb][jj];
+        dyt[blk<TS>(j0 + jj, b0 + bb, Npad / BK)] = tile[bb][jj];
     }
 }
 
@@ -615,29 +664,31 @@ GemmArgs base_args(const Plan& p, const void* x) {
 
 hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s) {
     const int64_t per_block = 256 * 4;
+    const int64_t nk = p.Kf / p.BK;
     dim3 grid((unsigned)std::min<int64_t>((p.Kf + per_block - 1) / per_block, 65535),
               (unsigned)std::min<int64_t>(p.Opad, 65535));
     if (p.dtype == KAN_F32)
         hipLaunchKernelGGL(pack_fwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
                            static_cast<const float*>(W), static_cast<float*>(cp), (int)p.O, (int)p.I,
-                           p.K, p.Kb, p.Kf, p.Opad);
+                           p.K, p.Kb, nk, p.Opad);
     else
         hipLaunchKernelGGL(pack_fwd_kernel<uint16_t>, grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(W),
-                           static_cast<uint16_t*>(cp), (int)p.O, (int)p.I, p.K, p.Kb, p.Kf, p.Opad);
+                           static_cast<uint16_t*>(cp), (int)p.O, (int)p.I, p.K, p.Kb, nk, p.Opad);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s) {
-    dim3 grid((unsigned)((p.rowsT + 63) / 64), (unsigned)(p.Opad / 64));
+    dim3 grid((unsigned)(p.tiles_dx * 256 / 64), (unsigned)(p.Opad / 64));
+    const int64_t nk = p.Opad / p.BK;
     if (p.dtype == KAN_F32)
         hipLaunchKernelGGL(pack_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
                            static_cast<const float*>(W), static_cast<float*>(cpt), (int)p.O, (int)p.I,
-                           p.K, p.Kb, p.rowsT, p.Opad);
+                           p.K, p.Kb, p.Qn, nk);
     else
         hipLaunchKernelGGL(pack_bwd_kernel<uint16_t>, grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(W),
-                           static_cast<uint16_t*>(cpt), (int)p.O, (int)p.I, p.K, p.Kb, p.rowsT, p.Opad);
+                           static_cast<uint16_t*>(cpt), (int)p.O, (int)p.I, p.K, p.Kb, p.Qn, nk);
     return hipGetLastError();
 }
 
@@ -688,8 +739,8 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.tiles_m = (int)(p.Npad / 256);
     a.tiles_n = (int)(p.Opad / 256);
     a.b = static_cast<const char*>(cp);
-    a.ldb = p.Kf * p.esize;
     a.nkt = (int)(p.Kf / p.BK);
+    a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
     a.out0 = y;
     if (p.dtype == KAN_F32) return fwd_dispatch<float>(p, a, s);
     return fwd_dispatch<uint16_t>(p, a, s);
@@ -701,16 +752,16 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     a.tiles_m = (int)(p.Npad / 256);
     a.tiles_n = (int)p.tiles_dx;
     a.a = static_cast<const char*>(dyp);
-    a.lda = p.Opad * p.esize;
+    a.a_tstride = p.Opad / p.BK * BLOCK_BYTES;
     a.b = static_cast<const char*>(cpt);
-    a.ldb = p.Opad * p.esize;
+    a.b_tstride = p.Opad / p.BK * BLOCK_BYTES;
     a.nkt = (int)(p.Opad / p.BK);
     a.out0 = dx;
     // both operands are copied and equally large per tile: 8 x 4 tiles per
     // 32 resident workgroups of an XCD share each dy and each C'^T tile
     a.group_m = 8;
-    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, LoadBdx, EpiDX>(a, s);
-    return run_gemm<uint16_t, LoadA, LoadBdx, EpiDX>(a, s);
+    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, LoadB, EpiDX>(a, s);
+    return run_gemm<uint16_t, LoadA, LoadB, EpiDX>(a, s);
 }
 
 hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
@@ -719,7 +770,7 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.tiles_m = (int)(p.Opad / 256);
     a.tiles_n = (int)((p.IKb + 255) / 256);
     a.a = static_cast<const char*>(dyt);
-    a.lda = p.Npad * p.esize;
+    a.a_tstride = p.Npad / p.BK * BLOCK_BYTES;
     a.nkt = (int)(p.Npad / p.BK);
     a.out0 = dC;
     a.out1 = dW;

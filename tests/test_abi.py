@@ -150,9 +150,8 @@ def test_workspace_sizes(L):
             assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == r(r(O, 256) * r(I * Kb, bk) * es, 256)
             Qn = 256 // Kb
             tiles = (I + Qn - 1) // Qn
-            rowsT = r((tiles - 1) * Qn * Kb + 256, bk)
             Op, Np = r(O, 256), r(N, 256)
-            want = r(rowsT * Op * es, 256) + 2 * r(Np * Op * es, 256)
+            want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256)
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores, float32 on the gather kernels, and the gather
     # kernels whenever an input's columns exceed one tile
