@@ -287,7 +287,7 @@ def cpu_baseline(d, rows=None):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     N = d["N"]
-    default_rows = {"c1": 32, "c2": 1024, "c3": 1024, "c4": 1024, "c5": 512}
+    default_rows = {"c1": 32, "c2": 1024, "c3": 1024, "c4": 1024, "c5": 2048}
     n = min(N, rows or default_rows[d["name"]])
     R = wl.sample_indices(N, n, 99)
     lo, hi, G = d["lo"], d["hi"], d["G"]
