@@ -186,7 +186,8 @@ struct LoadB : LoadOp {                // tile tn of B
 // in one wave, whose LDS writes land in program order, so no barrier is
 // needed between the two.  x loads are clamped in bounds and writes that fall
 // outside the tile go to the row's 16 pad bytes, which no fragment read
-// touches: the generator has no divergent branches.
+// touches: the generator has no divergent branches.  Rows past N are
+// generated from a clamped row and never stored by the epilogue.
 template <typename TS, int NIN>
 struct GenA {
     static constexpr int BK = Traits<TS>::BK;
@@ -199,7 +200,6 @@ struct GenA {
     const TS* x;
     int q, row0;
     int64_t xrow[PPT];
-    bool row_ok[PPT];
     float xs[2][PPT];    // slots: x values of this lane's pairs
     int is[2];           // slots: this lane's input
     __device__ GenA(const GemmArgs& a, int tm, int) {
@@ -207,11 +207,8 @@ struct GenA {
         q = threadIdx.x % NIN;
         row0 = threadIdx.x / NIN;
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            const int b = tm * 256 + row0 + RSTEP * j;
-            row_ok[j] = b < a.N;
-            xrow[j] = (int64_t)min(b, a.N - 1) * a.I;
-        }
+        for (int j = 0; j < PPT; ++j)
+            xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
     }
     template <int SL>
     __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
@@ -230,24 +227,29 @@ struct GenA {
             const int chunk = q * ((8 + NIN - 1) / NIN) + c;
             *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
         }
+        // This lane's input i covers tile columns cb .. cb + Kb - 1; spline
+        // index m is written when lo <= m < lo + n (inside [0, K) and inside
+        // the tile), the silu column when vs.  Both hold for the whole k-tile.
         const int i = is[SL];
-        const int cb = i * a.Kb - kt * BK;            // tile column of (i, m = 0)
-        const int cs = cb + a.K;                      // silu column
-        const bool ok = row_ok[j] & (i < a.I);
+        const int cb = i * a.Kb - kt * BK;
+        const int lo = max(0, -cb);
+        const int n = i < a.I ? max(0, min(a.K, BK - cb) - lo) : 0;
+        const int cs = cb + a.K;
+        const bool vs = (a.base != 0) & (i < a.I) & ((unsigned)cs < (unsigned)BK);
         const float xv = xs[SL][j];
         float u;
         const int s = span_u(xv, a.g, u);
         float bb[4];
         pieces(u, bb[0], bb[1], bb[2], bb[3]);
+        // value r goes to column cb + s - 3 + r; a rejected one to the pad
+        char* first = row + (cb + s - 3) * ES;
+        char* pad = row + BK * ES;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = s - 3 + r;
-            const int col = cb + m;
-            const bool v = ok & (m >= 0) & (m < a.K) & (col >= 0) & (col < BK);
-            Traits<TS>::put(row + (v ? col : BK) * ES, bb[r]);
+            const bool v = (unsigned)(s - 3 - lo + r) < (unsigned)n;
+            Traits<TS>::put((v ? first : pad) + r * ES, bb[r]);
         }
-        const bool v = ok & (a.base != 0) & (cs >= 0) & (cs < BK);
-        Traits<TS>::put(row + (v ? cs : BK) * ES, silu(xv));
+        Traits<TS>::put(vs ? row + cs * ES : pad, silu(xv));
         if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
@@ -271,6 +273,10 @@ struct GenB {
     const TS* x;
     int n0, i0, wave, lane;
     int bl[PPL], il[PPL];
+    // per pair: byte offset of (row of (i, m = 0), column b) in the tile (row
+    // may be negative), valid spline index range [lo, lo + n), and the silu
+    // value's offset (the pad of row 0 when it has no place in the tile)
+    int off[PPL], lo[PPL], cnt[PPL], soff[PPL];
     float xs[2][PPL];    // slots: x values of this lane's pairs
     __device__ GenB(const GemmArgs& a, int, int tn) {
         x = static_cast<const TS*>(a.x);
@@ -283,6 +289,13 @@ struct GenB {
             const int pp = lane + 64 * j;
             bl[j] = pp / NQW;
             il[j] = pp % NQW;
+            const int i = i0 + il[j];
+            const int rb = i * a.Kb - n0;                 // tile row of (i, m = 0)
+            off[j] = rb * PITCH + bl[j] * ES;
+            lo[j] = max(0, -rb);
+            cnt[j] = i < a.I ? max(0, min(a.K, 256 - rb) - lo[j]) : 0;
+            const int rs = rb + a.K;
+            soff[j] = (a.base != 0) & (i < a.I) & ((unsigned)rs < 256u) ? rs * PITCH + bl[j] * ES : 128;
         }
     }
     template <int SL>
@@ -312,25 +325,22 @@ struct GenB {
             return;
         } else {
         constexpr int j = p - 1;
-        const int i = i0 + il[j];
-        const bool ok = (kt * BK + bl[j] < a.N) & (i < a.I);
-        const int rb = i * a.Kb - n0;                // tile row of (i, m = 0)
-        char* colp = S + bl[j] * ES;
+        // Batch rows past N are generated from a clamped row: dy^T is zero
+        // there, so they add nothing.
         const float xv = xs[SL][j];
         float u;
-        const int s = span_u(xv, a.g, u);
+        const int s = min(span_u(xv, a.g, u), a.K + 3);   // larger spans hold no index < K
         float bb[4];
         pieces(u, bb[0], bb[1], bb[2], bb[3]);
+        // value r goes to tile row rb + s - 3 + r; a rejected one to the pad
+        // of row r
+        const int first = off[j] + (s - 3) * PITCH;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = s - 3 + r;
-            const int row = rb + m;
-            const bool v = ok & (m >= 0) & (m < a.K) & (row >= 0) & (row < 256);
-            Traits<TS>::put(v ? colp + row * PITCH : S + 128, bb[r]);
+            const bool v = (unsigned)(s - 3 - lo[j] + r) < (unsigned)cnt[j];
+            Traits<TS>::put(S + (v ? first : 128) + r * PITCH, bb[r]);
         }
-        const int row = rb + a.K;
-        const bool v = ok & (a.base != 0) & (row >= 0) & (row < 256);
-        Traits<TS>::put(v ? colp + row * PITCH : S + 128, silu(xv));
+        Traits<TS>::put(S + soff[j], silu(xv));
         if constexpr (RF && p == NPART - 1) fetch<SL>(a, ktn);
         }
     }
@@ -729,6 +739,7 @@ static hipError_t dc_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
     const int nq = dc_nqw(p);
     if (zr <= 1 && nq <= 10) return run_gemm<TS, LoadA, GenB<TS, 10, 1>, EpiDC>(a, s);
     if (zr <= 2 && nq <= 4) return run_gemm<TS, LoadA, GenB<TS, 4, 2>, EpiDC>(a, s);
+    if (zr <= 3 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 3>, EpiDC>(a, s);
     if (zr <= 4 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 4>, EpiDC>(a, s);
     if (zr <= 7 && nq <= 2) return run_gemm<TS, LoadA, GenB<TS, 2, 7>, EpiDC>(a, s);
     return run_gemm<TS, LoadA, GenB<TS, 2, 32>, EpiDC>(a, s);
