@@ -108,6 +108,17 @@ typedef struct {
  * not have changed those inputs since. */
 #define KAN_FLAG_PREPARED 1
 
+/* The MFMA forward of a bf16 layer with 11 <= G+3+has_base <= 32 runs by
+ * default on the structured-sparse matrix instructions: every input's
+ * G+3+has_base basis columns are permuted so that any 4 consecutive basis
+ * functions (the non-zero ones of a knot span; InKAN page, "Why InKAN?") and
+ * the silu column fall at most 2 to a group of 4, and the 2:4-sparse basis
+ * tile is multiplied at twice the dense rate.  The result is the same sum in
+ * a different order.  This flag asks for the dense basis instead.  It may be
+ * combined with KAN_FLAG_PREPARED; both passes of a prepared pair must agree
+ * on it. */
+#define KAN_FLAG_DENSE_FORWARD 2
+
 /* KAN_ABI_VERSION of the loaded library. */
 int kan_abi_version(void);
 

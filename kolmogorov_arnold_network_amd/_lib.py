@@ -31,6 +31,7 @@ KAN_PASS_FORWARD = 0
 KAN_PASS_BACKWARD = 1
 
 KAN_FLAG_PREPARED = 1
+KAN_FLAG_DENSE_FORWARD = 2
 
 ABI_VERSION = 1
 

@@ -42,7 +42,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
     if (d->has_base != 0 && d->has_base != 1) return KAN_ERR_UNSUPPORTED;
     if (d->variant < KAN_VARIANT_AUTO || d->variant > KAN_VARIANT_GATHER) return KAN_ERR_UNSUPPORTED;
-    if (d->flags != 0 && d->flags != KAN_FLAG_PREPARED) return KAN_ERR_UNSUPPORTED;
+    if (d->flags & ~(KAN_FLAG_PREPARED | KAN_FLAG_DENSE_FORWARD)) return KAN_ERR_UNSUPPORTED;
 
     Plan q;
     memset(&q, 0, sizeof(q));
@@ -86,7 +86,18 @@ int make_plan(const kan_desc_t* d, Plan* p) {
             *sz = bytes;
             off += (size_t)round_up((int64_t)bytes, 256);
         };
-        take((size_t)(q.Opad * q.Kf) * q.esize, &q.off_cp, &q.sz_cp);
+        // Sparse forward: NG = ceil(Kb / 4) groups, at least 4 (so that 4
+        // consecutive columns land in 4 groups) and even (so that an input's
+        // index nibbles fill whole bytes); taken when its padded width costs
+        // at most 3/4 of the dense contraction.
+        int ng = std::max(4, (q.Kb + 3) / 4);
+        ng += ng & 1;
+        q.sparse = q.dtype == KAN_BF16 && !(d->flags & KAN_FLAG_DENSE_FORWARD) && ng <= 8 &&
+                   q.Kb >= 11 && 8 * ng <= 3 * q.Kb && q.I * 4 * ng <= kIndexLimit;
+        q.NG = ng;
+        q.Kb8 = 4 * ng;
+        q.Kfs = round_up(q.I * q.Kb8, 64);
+        take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
         q.ws_fwd = off;
         off = 0;
         take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
@@ -146,7 +157,8 @@ static int prepare_impl(const Plan& p, int pass, const void* C, const void* W, c
     if (p.variant != KAN_VARIANT_MFMA) return KAN_OK;
     hipError_t e = hipSuccess;
     if (pass == KAN_PASS_FORWARD) {
-        e = launch_pack_fwd(p, C, W, ws_at(ws, p.off_cp), s);
+        e = p.sparse ? launch_pack_fwd_sparse(p, C, W, ws_at(ws, p.off_cp), s)
+                     : launch_pack_fwd(p, C, W, ws_at(ws, p.off_cp), s);
     } else {
         e = launch_pack_bwd(p, C, W, ws_at(ws, p.off_cpt), s);
         if (e == hipSuccess && p.N > 0)

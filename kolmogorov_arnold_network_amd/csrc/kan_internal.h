@@ -39,10 +39,17 @@ struct Plan {
     int Qn;              // inputs per n-tile of the dx contraction (floor(256 / Kb))
     int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I / Qn)
 
+    // structured-sparse forward (bf16): each input's Kb columns become NG
+    // groups of 4 (Kb8 = 4 NG columns); column c goes to group c % NG,
+    // position c / NG
+    int sparse;          // 1: the forward uses the sparse layout
+    int NG, Kb8;
+    int64_t Kfs;         // sparse forward contraction length: I * Kb8 rounded up to 64
+
     // workspace layout (bytes); forward uses [off_cp, +sz_cp).  Every array is
     // blocked: 256-row tiles, each cut into k-tiles of 256 x BK contiguous
     // elements.
-    size_t off_cp, sz_cp;      // C': rows j < Opad, k = (i, m) < Kf
+    size_t off_cp, sz_cp;      // C': rows j < Opad, k = (i, m) < Kf (sparse: < Kfs, permuted)
     size_t off_cpt, sz_cpt;    // C'^T: tiles_dx tiles of whole inputs, k = j < Opad
     size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
@@ -66,6 +73,7 @@ hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float
                             hipStream_t s);
 
 hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
+hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
 hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s);
 hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s);
 hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s);

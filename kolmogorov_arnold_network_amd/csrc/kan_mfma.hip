@@ -42,6 +42,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes in 4 registers
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ u32x8 make_u32x8(const uint4& lo, const uint4& hi) {
+    u32x8 v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+}
 
 constexpr int PITCH = 144;                     // bytes per LDS tile row (128 data + 16 pad)
 constexpr int TILE_BYTES = 256 * PITCH;        // one 256-row operand tile
@@ -77,6 +85,14 @@ template <> struct Traits<float> {
     }
     __device__ static void put(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
 };
+
+// x as loaded into a generator slot: the stored bits in a 32-bit register
+// (bf16 zero-extended), turned into a float where it is used.
+__device__ __forceinline__ uint32_t raw_bits(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+__device__ __forceinline__ uint32_t raw_bits(const uint16_t* p, int64_t i) { return p[i]; }
+template <typename TS> __device__ __forceinline__ float raw_to_float(uint32_t w);
+template <> __device__ __forceinline__ float raw_to_float<float>(uint32_t w) { return __uint_as_float(w); }
+template <> __device__ __forceinline__ float raw_to_float<uint16_t>(uint32_t w) { return __uint_as_float(w << 16); }
 
 // Calls f(std::integral_constant<int, I>()) for I = B .. E-1, so that the
 // index is a constant expression inside f.
@@ -149,6 +165,8 @@ constexpr int NTHR = 512;
 // 64 q + t / 8, 16-byte chunk t % 8, so one wave instruction reads 1 KB in
 // order; the part goes through registers into LDS.
 struct LoadOp {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
     static constexpr int NPART = 4;
     static constexpr int DEPTH = 2;
     const char* base;    // this thread's 16 bytes of k-tile 0 of the tile
@@ -190,6 +208,8 @@ struct LoadB : LoadOp {                // tile tn of B
 // generated from a clamped row and never stored by the epilogue.
 template <typename TS, int NIN>
 struct GenA {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
     static constexpr int PPT = 256 * NIN / NTHR;       // pairs per thread
@@ -264,6 +284,8 @@ struct GenA {
 // row 0.
 template <typename TS, int NQW, int ZR>
 struct GenB {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
     static constexpr int BK = Traits<TS>::BK;
     static constexpr int ES = Traits<TS>::ES;
     static constexpr int PPL = BK * NQW / 64;            // pairs per lane
@@ -343,6 +365,128 @@ struct GenB {
         Traits<TS>::put(S + soff[j], silu(xv));
         if constexpr (RF && p == NPART - 1) fetch<SL>(a, ktn);
         }
+    }
+};
+
+// Forward A operand in 2:4 structured-sparse form (bf16 only).  An input's
+// Kb columns are spread over NG groups of 4: basis column c (the silu column
+// being c = K) goes to group c % NG, position c / NG.  With NG >= 4 the 4
+// consecutive basis functions of a knot span land in 4 different groups, so
+// every group holds at most 2 non-zeros (one basis value, and the silu value
+// in its group): exactly what v_smfmac_f32_32x32x32_bf16 multiplies at twice
+// the dense rate.  The coefficient operand is packed with the same column
+// order (pack_fwd_sparse).
+//
+// A k-tile is 64 logical columns = 16 groups.  LDS row (PITCH bytes): group G
+// in [-8, 24) keeps its two values at byte 4 (G + 8); the tile's groups 0..15
+// are bytes 32..95, the rest is margin that inputs straddling the tile write
+// and no fragment reads.  The index nibbles of groups G, G + 1 (G even) are
+// byte 128 + ((G + 16) / 2) % 16, so groups 0..15 are bytes 136..143.  A
+// nibble holds the positions of the group's two stored values: first in bits
+// 1:0, second in bits 3:2, first < second.
+//
+// Everything a pair needs besides its 4 basis values and silu depends only on
+// the first non-zero basis index sigma = span - 3, so a table in LDS (built
+// once per workgroup) holds, per sigma: the input's NG nibbles, and the byte
+// offset inside the input's group block of each of the 4 values and of the
+// silu value (0xFF: not stored).
+template <int NG>
+struct GenS {
+    static constexpr bool SPARSE = true;
+    static constexpr bool SWZ = false;
+    static constexpr int DEPTH = 2;
+    static constexpr int NIN = NG == 8 ? 2 : 4;                 // inputs meeting one k-tile
+    static constexpr int PPT = 256 * NIN / NTHR;                // pairs per thread
+    static constexpr int NPART = PPT;
+    static constexpr int RSTEP = NTHR / NIN;
+    static_assert(NG == 4 || NG == 6 || NG == 8, "groups per input");
+    const uint16_t* x;
+    const uint4* tab;
+    int q, row0;
+    int64_t xrow[PPT];
+    uint32_t xs[2][PPT];
+    int is[2];
+    __device__ GenS(const GemmArgs& a, int tm, int) {
+        x = static_cast<const uint16_t*>(a.x);
+        q = threadIdx.x % NIN;
+        row0 = threadIdx.x / NIN;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+            xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
+    }
+    // Table entry e: e = sigma + 3 for sigma in [-3, K - 1]; e = K + 3: no
+    // basis value stored (x off the grid); e = K + 4: the input does not exist.
+    __device__ static uint4 entry(int e, int K, int base) {
+        uint32_t nib = NG == 8 ? 0x44444444u : (0x44444444u & ((1u << (4 * NG)) - 1));
+        uint32_t offs = 0xFFFFFFFFu, offs_silu = 0xFFu;
+        auto setnib = [&](int g, uint32_t v) { nib = (nib & ~(0xFu << (4 * g))) | (v << (4 * g)); };
+        auto setoff = [&](int r, uint32_t o) { offs = (offs & ~(0xFFu << (8 * r))) | (o << (8 * r)); };
+        const int gs = K % NG, ps = K / NG;                     // the silu column's group, position
+        int sr = -1, sp = 0;
+        if (e <= K + 2) {
+            for (int r = 0; r < 4; ++r) {
+                const int m = e - 3 + r;
+                if (m < 0 || m >= K) continue;
+                const int g = m % NG, p = m / NG;
+                if (base && g == gs) {
+                    sr = r;
+                    sp = p;
+                } else {
+                    setnib(g, p == 0 ? 4u : (uint32_t)(p << 2));
+                    setoff(r, 4 * g + (p == 0 ? 0 : 2));
+                }
+            }
+        }
+        if (base && e <= K + 3) {
+            if (sr >= 0) {
+                setnib(gs, (uint32_t)((max(sp, ps) << 2) | min(sp, ps)));
+                setoff(sr, 4 * gs + (sp < ps ? 0 : 2));
+                offs_silu = 4 * gs + (ps < sp ? 0 : 2);
+            } else {
+                setnib(gs, ps == 0 ? 4u : (uint32_t)(ps << 2));
+                offs_silu = 4 * gs + (ps == 0 ? 0 : 2);
+            }
+        }
+        return make_uint4(nib, offs, offs_silu, 0);
+    }
+    __device__ __forceinline__ void init(const GemmArgs& a, uint4* aux) {
+        for (int e = threadIdx.x; e < a.K + 5; e += NTHR) aux[e] = entry(e, a.K, a.base);
+        tab = aux;
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        is[SL] = (16 * kt) / NG + q;
+        const int i = min(is[SL], a.I - 1);
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) xs[SL][j] = raw_bits(x, xrow[j] + i);
+    }
+    // Pair j: the input's group block (zeros), its index bytes, then its
+    // stored values.
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* row = S + (row0 + RSTEP * j) * PITCH;
+        const int i = is[SL];
+        const int gofs = i * NG - 16 * kt;                      // tile group of the input's group 0
+        char* blk = row + 4 * (gofs + 8);
+#pragma unroll
+        for (int c = 0; c < NG / 2; ++c) *reinterpret_cast<uint2*>(blk + 8 * c) = make_uint2(0, 0);
+        const float xv = raw_to_float<uint16_t>(xs[SL][j]);
+        float u;
+        const int sig = span_u(xv, a.g, u) - 3;
+        const int e = i >= a.I ? a.K + 4 : ((unsigned)(sig + 3) <= (unsigned)(a.K + 2) ? sig + 3 : a.K + 3);
+        const uint4 ent = tab[e];
+        const int nb0 = (gofs + 16) >> 1;
+#pragma unroll
+        for (int c = 0; c < NG / 2; ++c) row[128 + ((nb0 + c) & 15)] = (char)(ent.x >> (8 * c));
+        float bb[4];
+        pieces(u, bb[0], bb[1], bb[2], bb[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t o = (ent.y >> (8 * r)) & 0xFFu;
+            Traits<uint16_t>::put(o == 0xFFu ? row : blk + o, bb[r]);    // row + 0: unused margin
+        }
+        Traits<uint16_t>::put(ent.z == 0xFFu ? row : blk + ent.z, silu(xv));
+        if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
 
@@ -459,6 +603,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     AOp A(args, tm, tn);
     BOp B(args, tm, tn);
+    __shared__ uint4 lds_aux[64];        // per-workgroup tables of the sparse generator
+    A.init(args, lds_aux);
+    B.init(args, lds_aux);
+    if (AOp::SPARSE) __syncthreads();
     Acc acc;
 #pragma unroll
     for (int fi = 0; fi < 2; ++fi)
@@ -472,6 +620,46 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     // MFMAs over one staged k-tile: 4 k-steps of 32 bytes per row; after(ks)
     // issues the work placed behind k-step ks.
     auto compute = [&](const char* As, const char* Bs, auto&& after) {
+      if constexpr (AOp::SPARSE) {
+        // 2 sparse steps of 32 logical k; sub-step ks runs step ks / 2 for B
+        // blocks 2 (ks % 2), +1.  Lane half h holds logical k 16 h .. +15 of a
+        // step in A (8 stored values + 4 index nibbles) and, in B, k 8 h .. +7
+        // and 16 + 8 h .. +7 of its column.
+        const int h = lane >> 5;
+        uint4 sa[2];
+        uint2 sidx[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+            sidx[f] = *reinterpret_cast<const uint2*>(As + arow - h * 16 + f * 32 * PITCH + 136);
+        static_for<0, 4>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value, t = ks >> 1, hb = ks & 1;
+            if constexpr (hb == 0) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    sa[f] = *reinterpret_cast<const uint4*>(As + arow + f * 32 * PITCH + 32 + 32 * t);
+            }
+            uint4 fb[2][2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    fb[f][e] = *reinterpret_cast<const uint4*>(Bs + brow + (2 * hb + f) * 32 * PITCH +
+                                                               64 * t + 32 * e);
+#pragma unroll
+            for (int fi = 0; fi < 2; ++fi) {
+                const uint32_t w = t == 0 ? sidx[fi].x : sidx[fi].y;
+                const int idx = (int)((w >> (16 * h)) & 0xFFFFu);
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const bf16x16 bv = __builtin_bit_cast(bf16x16, make_u32x8(fb[f][0], fb[f][1]));
+                    acc[fi][2 * hb + f] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                        __builtin_bit_cast(bf16x8, sa[fi]), bv, acc[fi][2 * hb + f], idx, 0, 0);
+                }
+            }
+            after(ksc);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
         static_for<0, 4>([&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
             uint4 fa[2], fb[4];
@@ -490,6 +678,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
             // every fragment read of the tile and sinks the stores)
             __builtin_amdgcn_sched_barrier(0);
         });
+      }
     };
     // Store k-tile kts from slot SL into stage S, part by part behind the
     // k-steps of the tile being multiplied, and (if RF) refill each operand's
@@ -578,6 +767,31 @@ __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__
                 if (k < Kf) cp[blk<TS>(j, k, nk)] = v;
                 if (++m == Kb) { m = 0; ++i; }
             }
+        }
+    }
+}
+
+// C' for the sparse forward (bf16): input i owns the Kb8 = 4 NG columns
+// i Kb8 + 4 g + p, holding its basis column c = p NG + g (C for c < K,
+// W_base for c = K when there is a base branch, zero otherwise); zero
+// outside [0, O) x [0, I Kb8).  Rows j < Opad, k < nk * 64.
+__global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uint16_t* __restrict__ W,
+                                       uint16_t* __restrict__ cp, int O, int I, int K, int base,
+                                       int NG, int64_t nk, int64_t Opad) {
+    const int Kb8 = 4 * NG;
+    const int64_t Kf = nk * 64;
+    for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
+        for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < Kf;
+             k += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t i = k / Kb8;
+            const int qq = (int)(k - i * Kb8);
+            const int c = (qq & 3) * NG + (qq >> 2);
+            uint16_t v = 0;
+            if (j < O && i < I) {
+                if (c < K) v = C[((int64_t)j * I + i) * K + c];
+                else if (c == K && base) v = W[(int64_t)j * I + i];
+            }
+            cp[blk<uint16_t>(j, k, nk)] = v;
         }
     }
 }
@@ -688,6 +902,16 @@ hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp
     return hipGetLastError();
 }
 
+hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s) {
+    const int64_t nk = p.Kfs / 64;
+    dim3 grid((unsigned)std::min<int64_t>((p.Kfs + 255) / 256, 65535),
+              (unsigned)std::min<int64_t>(p.Opad, 65535));
+    hipLaunchKernelGGL(pack_fwd_sparse_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(C),
+                       static_cast<const uint16_t*>(W), static_cast<uint16_t*>(cp), (int)p.O, (int)p.I,
+                       p.K, p.base, p.NG, nk, p.Opad);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s) {
     dim3 grid((unsigned)(p.tiles_dx * 256 / 64), (unsigned)(p.Opad / 64));
     const int64_t nk = p.Opad / p.BK;
@@ -750,9 +974,16 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.tiles_m = (int)(p.Npad / 256);
     a.tiles_n = (int)(p.Opad / 256);
     a.b = static_cast<const char*>(cp);
+    a.out0 = y;
+    if (p.sparse) {
+        a.nkt = (int)(p.Kfs / 64);
+        a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
+        if (p.NG == 4) return run_gemm<uint16_t, GenS<4>, LoadB, EpiY>(a, s);
+        if (p.NG == 6) return run_gemm<uint16_t, GenS<6>, LoadB, EpiY>(a, s);
+        return run_gemm<uint16_t, GenS<8>, LoadB, EpiY>(a, s);
+    }
     a.nkt = (int)(p.Kf / p.BK);
     a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
-    a.out0 = y;
     if (p.dtype == KAN_F32) return fwd_dispatch<float>(p, a, s);
     return fwd_dispatch<uint16_t>(p, a, s);
 }

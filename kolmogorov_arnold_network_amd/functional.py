@@ -67,9 +67,9 @@ def workspace(desc, pass_, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
-def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None):
+def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None, dense_forward=False):
     """Packs the pass's operands into a workspace; returns ``(ws, ws_bytes)``."""
-    desc = layer_desc(x, C, W, grid, variant)
+    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
     if ws is None:
         ws = workspace(desc, pass_, C.device)
     buf, n = ws
@@ -78,12 +78,15 @@ def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None):
     return ws
 
 
-def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None):
-    """``y [N, O]`` float32 of one KAN layer."""
+def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None,
+                dense_forward=False):
+    """``y [N, O]`` float32 of one KAN layer.  ``dense_forward`` turns off the
+    structured-sparse forward of bf16 layers (``KAN_FLAG_DENSE_FORWARD``)."""
     _check_tensor(x, "x", _DTYPES)
     _check_tensor(C, "C", _DTYPES, x.device)
     _check_tensor(W, "W_base", _DTYPES, x.device)
-    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_PREPARED if prepared else 0)
+    flags = (L.KAN_FLAG_PREPARED if prepared else 0) | (L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
+    desc = layer_desc(x, C, W, grid, variant, flags)
     if ws is None:
         ws = workspace(desc, L.KAN_PASS_FORWARD, x.device)
     buf, n = ws

@@ -147,7 +147,17 @@ def test_workspace_sizes(L):
     for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
         for (N, I, O, G, base) in [(64, 16, 8, 8, 1), (1000, 777, 300, 20, 0), (5, 3, 2, 1, 1)]:
             Kb = G + 3 + base
-            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == r(r(O, 256) * r(I * Kb, bk) * es, 256)
+            # bf16 forwards with 11 <= Kb <= 32 whose 2:4 layout (NG groups of 4
+            # columns per input) costs <= 3/4 of the dense one pack I * 4 NG columns
+            ng = max(4, (Kb + 3) // 4)
+            ng += ng & 1
+            sparse = dt == L.KAN_BF16 and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
+            kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
+            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == r(r(O, 256) * kf * es, 256)
+            if sparse:
+                assert L.lib().kan_workspace_size(ctypes.byref(desc(
+                    L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)), 0) == \
+                    r(r(O, 256) * r(I * Kb, bk) * es, 256)
             Qn = 256 // Kb
             tiles = (I + Qn - 1) // Qn
             Op, Np = r(O, 256), r(N, 256)

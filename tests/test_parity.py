@@ -119,6 +119,39 @@ def test_small_layer(F, shape, dtype, variant):
         assert e <= tol, "%s error %.3e > %.0e" % (name, e, tol)
 
 
+# bf16 layers whose forward runs on the 2:4-sparse matrix instructions:
+# N, I, O, G, base (columns per input Kb -> groups NG)
+SPARSE = [
+    (300, 37, 70, 7, True),     # Kb 11 -> NG 4
+    (129, 50, 33, 12, False),   # Kb 15 -> NG 4
+    (77, 23, 260, 17, True),    # Kb 21 -> NG 6
+    (256, 66, 40, 20, True),    # Kb 24 -> NG 6, inputs straddle k-tiles
+    (45, 9, 19, 21, False),     # Kb 24 -> NG 6, no base branch
+    (300, 31, 50, 28, True),    # Kb 32 -> NG 8
+    (70, 17, 24, 26, False),    # Kb 29 -> NG 8
+]
+
+
+@pytest.mark.parametrize("shape", SPARSE, ids=["x".join(map(str, s)) for s in SPARSE])
+def test_sparse_forward(F, shape):
+    """The structured-sparse forward against the oracle, and against the
+    dense forward on the same stored bits (the same bf16 products summed in
+    float32 in another order)."""
+    N, I, O, G, base = shape
+    say("sparse forward %s" % (shape,))
+    d = wl.random_layer(N, I, O, G, dtype="bf16", base=base, seed=3 * N + I + O + G)
+    (C, W), x = d["layers"][0], d["x"]
+    grid = (d["lo"], d["hi"], G)
+    xt, Ct, Wt = to_dev(x, "bf16"), to_dev(C, "bf16"), to_dev(W, "bf16")
+    y_s = F.kan_forward(xt, Ct, Wt, grid, "mfma")
+    y_d = F.kan_forward(xt, Ct, Wt, grid, "mfma", dense_forward=True)
+    _sync()
+    y_s, y_d = _np(y_s), _np(y_d)
+    ref = oracle.layer_forward(x, C, W, *grid)
+    assert rel_fro(y_s, ref) <= TOL_BF16
+    assert rel_inf(y_s, y_d) <= 1e-5
+
+
 def test_deterministic_and_prepared(F):
     import torch
     d = wl.random_layer(700, 48, 300, 8, dtype="bf16", base=True, seed=5)
