@@ -71,6 +71,26 @@ template <> struct Traits<uint16_t> {          // bf16 storage
     __device__ static void put(char* p, float v) {
         *reinterpret_cast<uint16_t*>(p) = __builtin_bit_cast(uint16_t, (__bf16)v);
     }
+    // A pair's 4 basis values and silu value in storage form: two values per
+    // conversion; store<r> writes value r (4: silu) from its half.
+    struct Vals { uint32_t p01, p23, ps; };
+    // v_cvt_pk_bf16_f32 of two values (left to itself the compiler converts
+    // each value on its own and stores both halves from separate registers)
+    __device__ static uint32_t pk(float a, float b) {
+        uint32_t r;
+        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    }
+    __device__ static Vals vals(float u, float silu_x) {
+        float b0, b1, b2, b3;
+        pieces_fast(u, b0, b1, b2, b3);
+        return Vals{pk(b0, b1), pk(b2, b3), pk(silu_x, 0.0f)};
+    }
+    template <int r>
+    __device__ static void store(char* p, const Vals& v) {
+        const uint32_t w = r < 2 ? v.p01 : r < 4 ? v.p23 : v.ps;
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)((r & 1) ? (w >> 16) : w);
+    }
 };
 template <> struct Traits<float> {
     static constexpr int ES = 4;
@@ -84,6 +104,15 @@ template <> struct Traits<float> {
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
     }
     __device__ static void put(char* p, float v) { *reinterpret_cast<float*>(p) = v; }
+    struct Vals { float v[5]; };
+    __device__ static Vals vals(float u, float silu_x) {
+        Vals r;
+        pieces(u, r.v[0], r.v[1], r.v[2], r.v[3]);
+        r.v[4] = silu_x;
+        return r;
+    }
+    template <int r>
+    __device__ static void store(char* p, const Vals& v) { *reinterpret_cast<float*>(p) = v.v[r]; }
 };
 
 // x as loaded into a generator slot: the stored bits in a 32-bit register
@@ -259,17 +288,16 @@ struct GenA {
         const float xv = xs[SL][j];
         float u;
         const int s = span_u(xv, a.g, u);
-        float bb[4];
-        pieces(u, bb[0], bb[1], bb[2], bb[3]);
+        const typename Traits<TS>::Vals val = Traits<TS>::vals(u, silu(xv));
         // value r goes to column cb + s - 3 + r; a rejected one to the pad
         char* first = row + (cb + s - 3) * ES;
         char* pad = row + BK * ES;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const bool v = (unsigned)(s - 3 - lo + r) < (unsigned)n;
-            Traits<TS>::put((v ? first : pad) + r * ES, bb[r]);
-        }
-        Traits<TS>::put(vs ? row + cs * ES : pad, silu(xv));
+            Traits<TS>::template store<r>((v ? first : pad) + r * ES, val);
+        });
+        Traits<TS>::template store<4>(vs ? row + cs * ES : pad, val);
         if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
@@ -352,17 +380,16 @@ struct GenB {
         const float xv = xs[SL][j];
         float u;
         const int s = min(span_u(xv, a.g, u), a.K + 3);   // larger spans hold no index < K
-        float bb[4];
-        pieces(u, bb[0], bb[1], bb[2], bb[3]);
+        const typename Traits<TS>::Vals val = Traits<TS>::vals(u, silu(xv));
         // value r goes to tile row rb + s - 3 + r; a rejected one to the pad
         // of row r
         const int first = off[j] + (s - 3) * PITCH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const bool v = (unsigned)(s - 3 - lo[j] + r) < (unsigned)cnt[j];
-            Traits<TS>::put(S + (v ? first : 128) + r * PITCH, bb[r]);
-        }
-        Traits<TS>::put(S + soff[j], silu(xv));
+            Traits<TS>::template store<r>(S + (v ? first : 128) + r * PITCH, val);
+        });
+        Traits<TS>::template store<4>(S + soff[j], val);
         if constexpr (RF && p == NPART - 1) fetch<SL>(a, ktn);
         }
     }
@@ -478,14 +505,13 @@ struct GenS {
         const int nb0 = (gofs + 16) >> 1;
 #pragma unroll
         for (int c = 0; c < NG / 2; ++c) row[128 + ((nb0 + c) & 15)] = (char)(ent.x >> (8 * c));
-        float bb[4];
-        pieces(u, bb[0], bb[1], bb[2], bb[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        const Traits<uint16_t>::Vals val = Traits<uint16_t>::vals(u, silu(xv));
+        static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const uint32_t o = (ent.y >> (8 * r)) & 0xFFu;
-            Traits<uint16_t>::put(o == 0xFFu ? row : blk + o, bb[r]);    // row + 0: unused margin
-        }
-        Traits<uint16_t>::put(ent.z == 0xFFu ? row : blk + ent.z, silu(xv));
+            Traits<uint16_t>::store<r>(o == 0xFFu ? row : blk + o, val);   // row + 0: unused margin
+        });
+        Traits<uint16_t>::store<4>(ent.z == 0xFFu ? row : blk + ent.z, val);
         if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
