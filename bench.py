@@ -189,19 +189,25 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
 
     # work counts: algorithmic = the 4 non-zero basis functions (+ silu) per input
-    # in each of the three contractions; executed = the dense I*(G+3+base) basis
+    # in each of the three contractions; executed = the dense I*(G+3+base) basis,
+    # except a structured-sparse forward, whose matrix instructions run half of
+    # its 4 NG columns per input (the rule of KAN_FLAG_DENSE_FORWARD in kan.h)
     Kb = G + 3 + (1 if base else 0)
+    ng = max(4, (Kb + 3) // 4)
+    ng += ng & 1
+    sparse = dt == "bf16" and args.variant in ("auto", "mfma") and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
+    fwd_cols = 2 * ng if sparse else Kb
     alg = exe = 0.0
     for l in range(nl):
         I, O = widths[l], widths[l + 1]
         alg += 6.0 * N * I * O * (4 + (1 if base else 0))
-        exe += 6.0 * N * I * O * Kb
+        exe += 2.0 * N * I * O * (fwd_cols + 2 * Kb)
     gemm_stages = [nm for nm in names if nm.split(".")[1] in ("fwd", "dx", "dC")]
     dom = max(gemm_stages, key=lambda nm: stage_ms[nm])
     dl = int(dom[1])
     I, O = widths[dl], widths[dl + 1]
     alg_dom = 2.0 * N * I * O * (4 + (1 if base else 0))
-    exe_dom = 2.0 * N * I * O * Kb
+    exe_dom = 2.0 * N * I * O * (fwd_cols if dom.endswith(".fwd") else Kb)
     mfma_path = args.variant == "mfma" or (args.variant == "auto" and dt == "bf16")
     peak = PEAK_TFLOPS[dt]
     t_dom = stage_ms[dom] * 1e-3
@@ -238,6 +244,7 @@ def main():
                    "base_branch": base, "variant": args.variant},
         "gflops_algorithmic": alg / (ms_per_step * 1e-3) / 1e9,
         "gflops_executed": exe / (ms_per_step * 1e-3) / 1e9,
+        "sparse_forward": sparse,
         "stage_ms": stage_ms,
         "roofline": roof,
     }

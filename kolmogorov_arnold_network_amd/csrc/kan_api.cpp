@@ -78,8 +78,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.Opad = round_up(q.O, kTileN);
         q.Npad = round_up(std::max<int64_t>(q.N, 1), kTileM);
         q.Kf = round_up(q.IKb, q.BK);
-        q.Qn = kTileN / q.Kb;
-        q.tiles_dx = (q.I + q.Qn - 1) / q.Qn;
+        q.tiles_dx = (q.IKb + kTileN - 1) / kTileN;
         size_t off = 0;
         auto take = [&](size_t bytes, size_t* o, size_t* sz) {
             *o = off;
@@ -103,6 +102,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
         take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
         take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
+        take((size_t)(q.Npad * q.tiles_dx * 2) * 4, &q.off_part, &q.sz_part);
         q.ws_bwd = off;
     }
     *p = q;
@@ -268,7 +268,9 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
         if (st != KAN_OK) return st;
     }
     hipError_t e = hipSuccess;
-    if (dx) e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt), dx, s);
+    if (dx)
+        e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),
+                           reinterpret_cast<float*>(ws_at(ws, p.off_part)), dx, s);
     if (e == hipSuccess && (dC || dW)) e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), dC, dW, s);
     return status_of(e);
 }

@@ -36,8 +36,7 @@ struct Plan {
     int64_t Opad;        // O rounded up to the tile (rows of the packed C')
     int64_t Npad;        // N rounded up to the tile
     int64_t Kf;          // forward contraction length: IKb rounded up to BK
-    int Qn;              // inputs per n-tile of the dx contraction (floor(256 / Kb))
-    int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I / Qn)
+    int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I * Kb / 256)
 
     // structured-sparse forward (bf16): each input's Kb columns become NG
     // groups of 4 (Kb8 = 4 NG columns); column c goes to group c % NG,
@@ -53,6 +52,7 @@ struct Plan {
     size_t off_cpt, sz_cpt;    // C'^T: tiles_dx tiles of whole inputs, k = j < Opad
     size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
+    size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
     size_t ws_fwd, ws_bwd;
 };
 
@@ -78,7 +78,7 @@ hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cp
 hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s);
 hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s);
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
-                          float* dx, hipStream_t s);
+                          float* part, float* dx, hipStream_t s);
 hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
                           hipStream_t s);
 

@@ -141,10 +141,10 @@ struct GemmArgs {
     int64_t b_tstride;
     const void* x;       // generator input x [N, I]
     GridK g;
-    int N, I, O, K, Kb, base, Qn;
+    int N, I, O, K, Kb, base;
     int64_t IKb;
     float* out0;         // y, dx or dC
-    float* out1;         // dW_base
+    float* out1;         // dW_base, or the dx partial sums
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
@@ -575,13 +575,19 @@ struct EpiDC {
 // (row, input) pair of those rows contracts its <= 4 spline columns with B'
 // and its silu column with silu'.
 struct EpiDX {
+    // Tile tn holds P columns 256 tn .. +255 of the inputs i_lo .. i_hi.  An
+    // input inside the tile gets its dx written here; one cut by a tile edge
+    // gets the partial sum over its columns in this tile written to
+    // part[b][tn][0] (the input's tail, cut by the left edge) or [1] (its
+    // head), and dx_fixup adds the two.
     template <typename TS>
     __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char* lds) {
         float* P = reinterpret_cast<float*>(lds);
         const TS* x = static_cast<const TS*>(a.x);
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-        const int i0 = tn * a.Qn;
-        const int nin = min(a.Qn, a.I - i0);
+        const int c0 = tn * 256;
+        const int i_lo = c0 / a.Kb;
+        const int nin = min((c0 + 255) / a.Kb, a.I - 1) - i_lo + 1;
         const int cw = (wave & 1) * 128 + (lane & 31);
         const int rw = (wave >> 1) * 32 + 4 * (lane >> 5);
 #pragma unroll
@@ -596,27 +602,45 @@ struct EpiDX {
             for (int e = t; e < 128 * nin; e += NTHR) {
                 const int rl = e / nin, il = e - rl * nin;
                 const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
-                const int i = i0 + il;
+                const int i = i_lo + il;
+                const int cb = i * a.Kb - c0;            // tile column of (i, m = 0)
                 if (b < a.N) {
                     const float xv = load_f(x, (int64_t)b * a.I + i);
                     float u;
                     const int s = span_u(xv, a.g, u);
                     float d[4];
                     dpieces(u, a.g.scale, d[0], d[1], d[2], d[3]);
-                    const float* prow = P + rl * DX_PITCH + il * a.Kb;
-                    float v = a.base ? prow[a.K] * silu_prime(xv) : 0.0f;
+                    const float* prow = P + rl * DX_PITCH;
+                    const int cs = cb + a.K;
+                    float v = (a.base && cs >= 0 && cs < 256) ? prow[cs] * silu_prime(xv) : 0.0f;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int m = s - 3 + r;
-                        if (m >= 0 && m < a.K) v = __builtin_fmaf(prow[m], d[r], v);
+                        const int m = s - 3 + r, c = cb + m;
+                        if (m >= 0 && m < a.K && c >= 0 && c < 256) v = __builtin_fmaf(prow[c], d[r], v);
                     }
-                    a.out0[(int64_t)b * a.I + i] = v;
+                    if (cb >= 0 && cb + a.Kb <= 256) a.out0[(int64_t)b * a.I + i] = v;
+                    else a.out1[((int64_t)b * a.tiles_n + tn) * 2 + (cb < 0 ? 0 : 1)] = v;
                 }
             }
             __syncthreads();
         }
     }
 };
+
+// dx of the inputs cut by a tile edge: input i = 256 (t + 1) / Kb spans
+// tiles t and t + 1 when 256 (t + 1) is not a multiple of Kb; its dx is the
+// head partial of tile t plus the tail partial of tile t + 1 (a fixed order).
+__global__ void dx_fixup_kernel(const float* __restrict__ part, float* __restrict__ dx, int N, int I,
+                                int Kb, int tiles) {
+    for (int t = blockIdx.y; t + 1 < tiles; t += gridDim.y) {       // edge between tiles t, t + 1
+        const int64_t c = 256 * (int64_t)(t + 1);
+        if (c % Kb == 0 || c / Kb >= I) continue;
+        const int i = (int)(c / Kb);
+        for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < N; b += gridDim.x * blockDim.x)
+            dx[(int64_t)b * I + i] =
+                part[((int64_t)b * tiles + t) * 2 + 1] + part[((int64_t)b * tiles + t + 1) * 2];
+    }
+}
 
 // ---- the contraction kernel ----
 template <typename TS, class AOp, class BOp, class Epi>
@@ -804,44 +828,47 @@ __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__
 __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uint16_t* __restrict__ W,
                                        uint16_t* __restrict__ cp, int O, int I, int K, int base,
                                        int NG, int64_t nk, int64_t Opad) {
+    // one group (4 consecutive k: columns g, NG + g, 2 NG + g, 3 NG + g of
+    // one input) per thread, stored as one 8-byte word
     const int Kb8 = 4 * NG;
-    const int64_t Kf = nk * 64;
+    const int ngroups = (int)(nk * 16);
     for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
-        for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < Kf;
-             k += (int64_t)gridDim.x * blockDim.x) {
-            const int64_t i = k / Kb8;
-            const int qq = (int)(k - i * Kb8);
-            const int c = (qq & 3) * NG + (qq >> 2);
-            uint16_t v = 0;
+        for (int gg = blockIdx.x * blockDim.x + threadIdx.x; gg < ngroups; gg += gridDim.x * blockDim.x) {
+            const int k0 = 4 * gg;
+            const int i = k0 / Kb8;
+            const int g = (k0 - i * Kb8) >> 2;
+            uint16_t v[4] = {0, 0, 0, 0};
             if (j < O && i < I) {
-                if (c < K) v = C[((int64_t)j * I + i) * K + c];
-                else if (c == K && base) v = W[(int64_t)j * I + i];
+                const uint16_t* crow = C + ((int64_t)j * I + i) * K;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int c = p * NG + g;
+                    if (c < K) v[p] = crow[c];
+                    else if (c == K && base) v[p] = W[(int64_t)j * I + i];
+                }
             }
-            cp[blk<uint16_t>(j, k, nk)] = v;
+            *reinterpret_cast<uint2*>(cp + blk<uint16_t>(j, k0, nk)) =
+                make_uint2(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16));
         }
     }
 }
 
-// dx B operand: tile tn holds rows rr < Qn * Kb = C'^T[tn * Qn * Kb + rr][j]
-// (the whole inputs tn * Qn ..) and zero rows above; k runs over j < nk * BK.
-// 64 rows x 64 j per block through an LDS tile.
+// dx B operand: row R < tiles_dx * 256 is column R of C' (zero for R >= I Kb);
+// k runs over j < nk * BK.  64 rows x 64 j per block through an LDS tile.
 template <typename TS>
 __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
-                                TS* __restrict__ cpt, int O, int I, int K, int Kb, int Qn,
-                                int64_t nk) {
+                                TS* __restrict__ cpt, int O, int I, int K, int Kb, int64_t nk) {
     __shared__ TS tile[64][65];
-    const int64_t R0 = (int64_t)blockIdx.x * 64;       // tile row tn * 256 + rr
+    const int64_t R0 = (int64_t)blockIdx.x * 64;
     const int j0 = blockIdx.y * 64;
     const int64_t IKb = (int64_t)I * Kb;
     const int t = threadIdx.x;
     for (int e = t; e < 64 * 64; e += 256) {
         const int jj = e / 64, kk = e % 64;
         const int j = j0 + jj;
-        const int64_t R = R0 + kk;
-        const int rr = (int)(R & 255);
-        const int64_t k = (R >> 8) * Qn * Kb + rr;
+        const int64_t k = R0 + kk;
         TS v = TS(0);
-        if (j < O && rr < Qn * Kb && k < IKb) {
+        if (j < O && k < IKb) {
             const int i = (int)(k / Kb), m = (int)(k - (int64_t)i * Kb);
             v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
         }
@@ -904,7 +931,6 @@ GemmArgs base_args(const Plan& p, const void* x) {
     a.K = p.K;
     a.Kb = p.Kb;
     a.base = p.base;
-    a.Qn = p.Qn;
     a.IKb = p.IKb;
     a.group_m = 16;
     return a;
@@ -930,7 +956,7 @@ hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp
 
 hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s) {
     const int64_t nk = p.Kfs / 64;
-    dim3 grid((unsigned)std::min<int64_t>((p.Kfs + 255) / 256, 65535),
+    dim3 grid((unsigned)std::min<int64_t>((p.Kfs / 4 + 255) / 256, 65535),
               (unsigned)std::min<int64_t>(p.Opad, 65535));
     hipLaunchKernelGGL(pack_fwd_sparse_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(C),
                        static_cast<const uint16_t*>(W), static_cast<uint16_t*>(cp), (int)p.O, (int)p.I,
@@ -944,11 +970,11 @@ hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cp
     if (p.dtype == KAN_F32)
         hipLaunchKernelGGL(pack_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(C),
                            static_cast<const float*>(W), static_cast<float*>(cpt), (int)p.O, (int)p.I,
-                           p.K, p.Kb, p.Qn, nk);
+                           p.K, p.Kb, nk);
     else
         hipLaunchKernelGGL(pack_bwd_kernel<uint16_t>, grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(W),
-                           static_cast<uint16_t*>(cpt), (int)p.O, (int)p.I, p.K, p.Kb, p.Qn, nk);
+                           static_cast<uint16_t*>(cpt), (int)p.O, (int)p.I, p.K, p.Kb, nk);
     return hipGetLastError();
 }
 
@@ -1015,7 +1041,7 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
 }
 
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
-                          float* dx, hipStream_t s) {
+                          float* part, float* dx, hipStream_t s) {
     GemmArgs a = base_args(p, x);
     a.tiles_m = (int)(p.Npad / 256);
     a.tiles_n = (int)p.tiles_dx;
@@ -1025,11 +1051,17 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     a.b_tstride = p.Opad / p.BK * BLOCK_BYTES;
     a.nkt = (int)(p.Opad / p.BK);
     a.out0 = dx;
+    a.out1 = part;
     // both operands are copied and equally large per tile: 8 x 4 tiles per
     // 32 resident workgroups of an XCD share each dy and each C'^T tile
     a.group_m = 8;
-    if (p.dtype == KAN_F32) return run_gemm<float, LoadA, LoadB, EpiDX>(a, s);
-    return run_gemm<uint16_t, LoadA, LoadB, EpiDX>(a, s);
+    hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDX>(a, s)
+                                      : run_gemm<uint16_t, LoadA, LoadB, EpiDX>(a, s);
+    if (e != hipSuccess || p.tiles_dx < 2) return e;
+    hipLaunchKernelGGL(dx_fixup_kernel, dim3((unsigned)std::min<int64_t>((p.N + 255) / 256, 1024),
+                                             (unsigned)std::min<int64_t>(p.tiles_dx - 1, 65535)),
+                       dim3(256), 0, s, part, dx, (int)p.N, (int)p.I, p.Kb, (int)p.tiles_dx);
+    return hipGetLastError();
 }
 
 hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,

@@ -158,10 +158,9 @@ def test_workspace_sizes(L):
                 assert L.lib().kan_workspace_size(ctypes.byref(desc(
                     L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)), 0) == \
                     r(r(O, 256) * r(I * Kb, bk) * es, 256)
-            Qn = 256 // Kb
-            tiles = (I + Qn - 1) // Qn
+            tiles = (I * Kb + 255) // 256           # dx tiles of 256 P columns
             Op, Np = r(O, 256), r(N, 256)
-            want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256)
+            want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores, float32 on the gather kernels, and the gather
     # kernels whenever an input's columns exceed one tile
