@@ -397,12 +397,14 @@ struct GenB {
 
 // Forward A operand in 2:4 structured-sparse form (bf16 only).  An input's
 // Kb columns are spread over NG groups of 4: basis column c (the silu column
-// being c = K) goes to group c % NG, position c / NG.  With NG >= 4 the 4
+// being c = K) goes to group (c + dl) % NG, position (c + dl) / NG, where the
+// shift dl = (NG - 1 - K) mod NG with a base branch (0 without) puts the
+// silu column at the top position of group NG - 1.  With NG >= 4 the 4
 // consecutive basis functions of a knot span land in 4 different groups, so
 // every group holds at most 2 non-zeros (one basis value, and the silu value
-// in its group): exactly what v_smfmac_f32_32x32x32_bf16 multiplies at twice
-// the dense rate.  The coefficient operand is packed with the same column
-// order (pack_fwd_sparse).
+// in group NG - 1): exactly what v_smfmac_f32_32x32x32_bf16 multiplies at
+// twice the dense rate.  The coefficient operand is packed with the same
+// column order (pack_fwd_sparse).
 //
 // A k-tile is 64 logical columns = 16 groups.  LDS row (PITCH bytes): group G
 // in [-8, 24) keeps its two values at byte 4 (G + 8); the tile's groups 0..15
@@ -412,11 +414,19 @@ struct GenB {
 // nibble holds the positions of the group's two stored values: first in bits
 // 1:0, second in bits 3:2, first < second.
 //
-// Everything a pair needs besides its 4 basis values and silu depends only on
-// the first non-zero basis index sigma = span - 3, so a table in LDS (built
-// once per workgroup) holds, per sigma: the input's NG nibbles, and the byte
-// offset inside the input's group block of each of the 4 values and of the
-// silu value (0xFF: not stored).
+// Each pair builds its input's whole block of NG dwords in registers and
+// writes it with NG / 2 8-byte stores (zeros included).  What a dword holds
+// depends only on the first non-zero basis index sigma = span - 3, so a table
+// in LDS (built once per workgroup) holds per sigma: for each group, the
+// v_perm_b32 selector that moves its basis value out of the packed pairs
+// (b0 b1 : b2 b3) into its half (selector byte 0x0C gives zero); the NG
+// nibbles; and a mask that keeps or drops the silu half of dword NG - 1.
+// Group shift dl of the sparse column order: the silu column K lands in
+// group NG - 1.
+__host__ __device__ inline int sparse_group_shift(int NG, int K, int base) {
+    return base ? (NG - 1 - K % NG + NG) % NG : 0;
+}
+
 template <int NG>
 struct GenS {
     static constexpr bool SPARSE = true;
@@ -426,6 +436,7 @@ struct GenS {
     static constexpr int PPT = 256 * NIN / NTHR;                // pairs per thread
     static constexpr int NPART = PPT;
     static constexpr int RSTEP = NTHR / NIN;
+    static constexpr int EQ = (NG + 5) / 4;                     // uint4 per table entry
     static_assert(NG == 4 || NG == 6 || NG == 8, "groups per input");
     const uint16_t* x;
     const uint4* tab;
@@ -441,43 +452,49 @@ struct GenS {
         for (int j = 0; j < PPT; ++j)
             xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
     }
-    // Table entry e: e = sigma + 3 for sigma in [-3, K - 1]; e = K + 3: no
-    // basis value stored (x off the grid); e = K + 4: the input does not exist.
-    __device__ static uint4 entry(int e, int K, int base) {
+    // Table entry e, dwords w[0 .. NG + 1]: e = sigma + 3 for sigma in
+    // [-3, K - 1]; e = K + 3: no basis value (x off the grid); e = K + 4: the
+    // input does not exist (all zero).
+    __host__ __device__ static void entry(int e, int K, int base, uint32_t* w) {
+        const int dl = sparse_group_shift(NG, K, base);
+        const int ps = (K + dl) / NG;                           // the silu column's position
         uint32_t nib = NG == 8 ? 0x44444444u : (0x44444444u & ((1u << (4 * NG)) - 1));
-        uint32_t offs = 0xFFFFFFFFu, offs_silu = 0xFFu;
         auto setnib = [&](int g, uint32_t v) { nib = (nib & ~(0xFu << (4 * g))) | (v << (4 * g)); };
-        auto setoff = [&](int r, uint32_t o) { offs = (offs & ~(0xFFu << (8 * r))) | (o << (8 * r)); };
-        const int gs = K % NG, ps = K / NG;                     // the silu column's group, position
-        int sr = -1, sp = 0;
+        for (int g = 0; g < NG; ++g) w[g] = 0x0C0C0C0Cu;
+        bool silu_group_taken = false;
         if (e <= K + 2) {
             for (int r = 0; r < 4; ++r) {
                 const int m = e - 3 + r;
                 if (m < 0 || m >= K) continue;
-                const int g = m % NG, p = m / NG;
-                if (base && g == gs) {
-                    sr = r;
-                    sp = p;
+                const int g = (m + dl) % NG, p = (m + dl) / NG;
+                const uint32_t lo = 0x0C0C0000u | ((2u * r + 1) << 8) | (2u * r);
+                const uint32_t hi = 0x00000C0Cu | ((2u * r + 1) << 24) | ((2u * r) << 16);
+                if (base && g == NG - 1) {                      // below the silu value
+                    w[g] = lo;
+                    setnib(g, (uint32_t)((ps << 2) | p));
+                    silu_group_taken = true;
+                } else if (p == 0) {
+                    w[g] = lo;
+                    setnib(g, 4u);
                 } else {
-                    setnib(g, p == 0 ? 4u : (uint32_t)(p << 2));
-                    setoff(r, 4 * g + (p == 0 ? 0 : 2));
+                    w[g] = hi;
+                    setnib(g, (uint32_t)(p << 2));
                 }
             }
         }
-        if (base && e <= K + 3) {
-            if (sr >= 0) {
-                setnib(gs, (uint32_t)((max(sp, ps) << 2) | min(sp, ps)));
-                setoff(sr, 4 * gs + (sp < ps ? 0 : 2));
-                offs_silu = 4 * gs + (ps < sp ? 0 : 2);
-            } else {
-                setnib(gs, ps == 0 ? 4u : (uint32_t)(ps << 2));
-                offs_silu = 4 * gs + (ps == 0 ? 0 : 2);
-            }
-        }
-        return make_uint4(nib, offs, offs_silu, 0);
+        const bool silu = base && e <= K + 3;
+        if (silu && !silu_group_taken) setnib(NG - 1, (uint32_t)(ps << 2));
+        w[NG] = nib;
+        w[NG + 1] = silu ? 0xFFFF0000u : 0u;
+        for (int k = NG + 2; k < 4 * EQ; ++k) w[k] = 0;
     }
     __device__ __forceinline__ void init(const GemmArgs& a, uint4* aux) {
-        for (int e = threadIdx.x; e < a.K + 5; e += NTHR) aux[e] = entry(e, a.K, a.base);
+        for (int e = threadIdx.x; e < a.K + 5; e += NTHR) {
+            uint32_t w[4 * EQ];
+            entry(e, a.K, a.base, w);
+#pragma unroll
+            for (int k = 0; k < EQ; ++k) aux[EQ * e + k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+        }
         tab = aux;
     }
     template <int SL>
@@ -487,31 +504,35 @@ struct GenS {
 #pragma unroll
         for (int j = 0; j < PPT; ++j) xs[SL][j] = raw_bits(x, xrow[j] + i);
     }
-    // Pair j: the input's group block (zeros), its index bytes, then its
-    // stored values.
+    // Pair j: the input's index bytes, then its block.
     template <int SL, bool RF, int j>
     __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
         char* row = S + (row0 + RSTEP * j) * PITCH;
         const int i = is[SL];
-        const int gofs = i * NG - 16 * kt;                      // tile group of the input's group 0
-        char* blk = row + 4 * (gofs + 8);
-#pragma unroll
-        for (int c = 0; c < NG / 2; ++c) *reinterpret_cast<uint2*>(blk + 8 * c) = make_uint2(0, 0);
+        const int gofs = i * NG - 16 * kt;                      // tile group of the input's group 0 (even)
         const float xv = raw_to_float<uint16_t>(xs[SL][j]);
         float u;
         const int sig = span_u(xv, a.g, u) - 3;
         const int e = i >= a.I ? a.K + 4 : ((unsigned)(sig + 3) <= (unsigned)(a.K + 2) ? sig + 3 : a.K + 3);
-        const uint4 ent = tab[e];
+        uint32_t w[4 * EQ];
+#pragma unroll
+        for (int k = 0; k < EQ; ++k) {
+            const uint4 t = tab[EQ * e + k];
+            w[4 * k] = t.x, w[4 * k + 1] = t.y, w[4 * k + 2] = t.z, w[4 * k + 3] = t.w;
+        }
         const int nb0 = (gofs + 16) >> 1;
 #pragma unroll
-        for (int c = 0; c < NG / 2; ++c) row[128 + ((nb0 + c) & 15)] = (char)(ent.x >> (8 * c));
-        const Traits<uint16_t>::Vals val = Traits<uint16_t>::vals(u, silu(xv));
-        static_for<0, 4>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const uint32_t o = (ent.y >> (8 * r)) & 0xFFu;
-            Traits<uint16_t>::store<r>(o == 0xFFu ? row : blk + o, val);   // row + 0: unused margin
-        });
-        Traits<uint16_t>::store<4>(ent.z == 0xFFu ? row : blk + ent.z, val);
+        for (int c = 0; c < NG / 2; ++c) row[128 + ((nb0 + c) & 15)] = (char)(w[NG] >> (8 * c));
+        float b0, b1, b2, b3;
+        pieces_fast(u, b0, b1, b2, b3);
+        const uint32_t p01 = Traits<uint16_t>::pk(b0, b1), p23 = Traits<uint16_t>::pk(b2, b3);
+        uint32_t d[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) d[g] = __builtin_amdgcn_perm(p23, p01, w[g]);
+        d[NG - 1] |= Traits<uint16_t>::pk(0.0f, silu(xv)) & w[NG + 1];
+        char* blk = row + 4 * (gofs + 8);
+#pragma unroll
+        for (int c = 0; c < NG / 2; ++c) *reinterpret_cast<uint2*>(blk + 8 * c) = make_uint2(d[2 * c], d[2 * c + 1]);
         if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
     }
 };
@@ -653,7 +674,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     AOp A(args, tm, tn);
     BOp B(args, tm, tn);
-    __shared__ uint4 lds_aux[64];        // per-workgroup tables of the sparse generator
+    __shared__ uint4 lds_aux[128];       // per-workgroup table of the sparse generator
     A.init(args, lds_aux);
     B.init(args, lds_aux);
     if (AOp::SPARSE) __syncthreads();
@@ -822,14 +843,15 @@ __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__
 }
 
 // C' for the sparse forward (bf16): input i owns the Kb8 = 4 NG columns
-// i Kb8 + 4 g + p, holding its basis column c = p NG + g (C for c < K,
-// W_base for c = K when there is a base branch, zero otherwise); zero
-// outside [0, O) x [0, I Kb8).  Rows j < Opad, k < nk * 64.
+// i Kb8 + 4 g + p, holding its basis column c = p NG + g - dl (C for
+// 0 <= c < K, W_base for c = K when there is a base branch, zero otherwise;
+// dl as in GenS); zero outside [0, O) x [0, I Kb8).  Rows j < Opad,
+// k < nk * 64.
 __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uint16_t* __restrict__ W,
                                        uint16_t* __restrict__ cp, int O, int I, int K, int base,
-                                       int NG, int64_t nk, int64_t Opad) {
-    // one group (4 consecutive k: columns g, NG + g, 2 NG + g, 3 NG + g of
-    // one input) per thread, stored as one 8-byte word
+                                       int NG, int dl, int64_t nk, int64_t Opad) {
+    // one group (4 consecutive k: columns g - dl, NG + g - dl, ... of one
+    // input) per thread, stored as one 8-byte word
     const int Kb8 = 4 * NG;
     const int ngroups = (int)(nk * 16);
     for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
@@ -842,7 +864,8 @@ __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uin
                 const uint16_t* crow = C + ((int64_t)j * I + i) * K;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const int c = p * NG + g;
+                    const int c = p * NG + g - dl;
+                    if (c < 0) continue;
                     if (c < K) v[p] = crow[c];
                     else if (c == K && base) v[p] = W[(int64_t)j * I + i];
                 }
@@ -960,7 +983,7 @@ hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, v
               (unsigned)std::min<int64_t>(p.Opad, 65535));
     hipLaunchKernelGGL(pack_fwd_sparse_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(C),
                        static_cast<const uint16_t*>(W), static_cast<uint16_t*>(cp), (int)p.O, (int)p.I,
-                       p.K, p.base, p.NG, nk, p.Opad);
+                       p.K, p.base, p.NG, sparse_group_shift(p.NG, p.K, p.base), nk, p.Opad);
     return hipGetLastError();
 }
 
