@@ -689,7 +689,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     const int arow = (wm + (lane & 31)) * PITCH + (lane >> 5) * 16;
     const int brow = (wn + (lane & 31)) * PITCH + (lane >> 5) * 16;
     // MFMAs over one staged k-tile: 4 k-steps of 32 bytes per row; after(ks)
-    // issues the work placed behind k-step ks.
+    // issues the work placed behind k-step ks.  It runs between the fragment
+    // reads and the MFMAs of k-step ks + 1, where it covers the latency of
+    // those reads (the last one runs at the end of the tile).
     auto compute = [&](const char* As, const char* Bs, auto&& after) {
       if constexpr (AOp::SPARSE) {
         // 2 sparse steps of 32 logical k; sub-step ks runs step ks / 2 for B
@@ -716,6 +718,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
                 for (int e = 0; e < 2; ++e)
                     fb[f][e] = *reinterpret_cast<const uint4*>(Bs + brow + (2 * hb + f) * 32 * PITCH +
                                                                64 * t + 32 * e);
+            if constexpr (ks > 0) after(std::integral_constant<int, ks - 1>());
 #pragma unroll
             for (int fi = 0; fi < 2; ++fi) {
                 const uint32_t w = t == 0 ? sidx[fi].x : sidx[fi].y;
@@ -727,7 +730,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
                         __builtin_bit_cast(bf16x8, sa[fi]), bv, acc[fi][2 * hb + f], idx, 0, 0);
                 }
             }
-            after(ksc);
+            if constexpr (ks == 3) {
+                __builtin_amdgcn_sched_barrier(0);
+                after(ksc);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
       } else {
@@ -740,11 +746,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
 #pragma unroll
             for (int f = 0; f < 2; ++f)
                 fa[f] = *reinterpret_cast<const uint4*>(As + arow + f * 32 * PITCH + ks * 32);
+            if constexpr (ks > 0) after(std::integral_constant<int, ks - 1>());
 #pragma unroll
             for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) Traits<TS>::mma(acc[fi][fj], fa[fi], fb[fj]);
-            after(ksc);
+            if constexpr (ks == 3) {
+                __builtin_amdgcn_sched_barrier(0);
+                after(ksc);
+            }
             // pins the k-step's work in place (left free, the scheduler hoists
             // every fragment read of the tile and sinks the stores)
             __builtin_amdgcn_sched_barrier(0);
