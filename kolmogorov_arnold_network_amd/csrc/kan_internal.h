@@ -49,7 +49,7 @@ struct Plan {
     // blocked: 256-row tiles, each cut into k-tiles of 256 x BK contiguous
     // elements.
     size_t off_cp, sz_cp;      // C': rows j < Opad, k = (i, m) < Kf (sparse: < Kfs, permuted)
-    size_t off_cpt, sz_cpt;    // C'^T: tiles_dx tiles of whole inputs, k = j < Opad
+    size_t off_cpt, sz_cpt;    // C'^T: tiles_dx tiles of 256 consecutive columns of C', k = j < Opad
     size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float

@@ -651,15 +651,19 @@ struct EpiDX {
 // dx of the inputs cut by a tile edge: input i = 256 (t + 1) / Kb spans
 // tiles t and t + 1 when 256 (t + 1) is not a multiple of Kb; its dx is the
 // head partial of tile t plus the tail partial of tile t + 1 (a fixed order).
-__global__ void dx_fixup_kernel(const float* __restrict__ part, float* __restrict__ dx, int N, int I,
+__global__ void dx_fixup_kernel(const float* __restrict__ part, float* __restrict__ dx, int64_t N, int I,
                                 int Kb, int tiles) {
-    for (int t = blockIdx.y; t + 1 < tiles; t += gridDim.y) {       // edge between tiles t, t + 1
+    // one (row b, edge t) per thread, edges fastest: the partials of a row
+    // are read in order
+    const int edges = tiles - 1;
+    const int64_t total = N * edges;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = k / edges;
+        const int t = (int)(k - b * edges);
         const int64_t c = 256 * (int64_t)(t + 1);
         if (c % Kb == 0 || c / Kb >= I) continue;
-        const int i = (int)(c / Kb);
-        for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < N; b += gridDim.x * blockDim.x)
-            dx[(int64_t)b * I + i] =
-                part[((int64_t)b * tiles + t) * 2 + 1] + part[((int64_t)b * tiles + t + 1) * 2];
+        dx[b * I + c / Kb] = part[(b * tiles + t) * 2 + 1] + part[(b * tiles + t + 1) * 2];
     }
 }
 
@@ -1091,9 +1095,9 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDX>(a, s)
                                       : run_gemm<uint16_t, LoadA, LoadB, EpiDX>(a, s);
     if (e != hipSuccess || p.tiles_dx < 2) return e;
-    hipLaunchKernelGGL(dx_fixup_kernel, dim3((unsigned)std::min<int64_t>((p.N + 255) / 256, 1024),
-                                             (unsigned)std::min<int64_t>(p.tiles_dx - 1, 65535)),
-                       dim3(256), 0, s, part, dx, (int)p.N, (int)p.I, p.Kb, (int)p.tiles_dx);
+    hipLaunchKernelGGL(dx_fixup_kernel,
+                       dim3((unsigned)std::min<int64_t>((p.N * (p.tiles_dx - 1) + 255) / 256, 16384)),
+                       dim3(256), 0, s, part, dx, (int64_t)p.N, (int)p.I, p.Kb, (int)p.tiles_dx);
     return hipGetLastError();
 }
 
