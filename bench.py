@@ -254,12 +254,15 @@ def main():
 
 
 def kernel_code_digest():
-    """sha256 of the contraction kernels' source with // comments and blank
-    lines removed: a counter summary stays valid across comment edits and goes
-    stale with any change to the code."""
+    """sha256 of the contraction kernels' source (the kernel file, the headers
+    it includes and the launch planner) with // comments and blank lines
+    removed: a counter summary stays valid across comment edits and goes stale
+    with any change to the code."""
     import re
-    src = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc", "kan_mfma.hip")
-    lines = [re.sub(r"//.*", "", l).rstrip() for l in open(src).read().splitlines()]
+    csrc = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc")
+    lines = []
+    for name in ("kan_mfma.hip", "kan_device.h", "kan_sparse.h", "kan_internal.h", "kan_api.cpp"):
+        lines += [re.sub(r"//.*", "", l).rstrip() for l in open(os.path.join(csrc, name)).read().splitlines()]
     return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()
 
 

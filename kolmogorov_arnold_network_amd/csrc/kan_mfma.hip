@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "kan_internal.h"
+#include "kan_sparse.h"
 
 namespace kan {
 
@@ -395,38 +396,22 @@ struct GenB {
     }
 };
 
-// Forward A operand in 2:4 structured-sparse form (bf16 only).  An input's
-// Kb columns are spread over NG groups of 4: basis column c (the silu column
-// being c = K) goes to group (c + dl) % NG, position (c + dl) / NG, where the
-// shift dl = (NG - 1 - K) mod NG with a base branch (0 without) puts the
-// silu column at the top position of group NG - 1.  With NG >= 4 the 4
-// consecutive basis functions of a knot span land in 4 different groups, so
-// every group holds at most 2 non-zeros (one basis value, and the silu value
-// in group NG - 1): exactly what v_smfmac_f32_32x32x32_bf16 multiplies at
-// twice the dense rate.  The coefficient operand is packed with the same
-// column order (pack_fwd_sparse).
+// Forward A operand in 2:4 structured-sparse form (bf16 only), in the column
+// order of kan_sparse.h; the coefficient operand is packed in the same order
+// (pack_fwd_sparse).
 //
 // A k-tile is 64 logical columns = 16 groups.  LDS row (PITCH bytes): group G
 // in [-8, 24) keeps its two values at byte 4 (G + 8); the tile's groups 0..15
 // are bytes 32..95, the rest is margin that inputs straddling the tile write
 // and no fragment reads.  The index nibbles of groups G, G + 1 (G even) are
-// byte 128 + ((G + 16) / 2) % 16, so groups 0..15 are bytes 136..143.  A
-// nibble holds the positions of the group's two stored values: first in bits
-// 1:0, second in bits 3:2, first < second.
+// byte 128 + ((G + 16) / 2) % 16, so groups 0..15 are bytes 136..143.
 //
 // Each pair builds its input's whole block of NG dwords in registers and
 // writes it with NG / 2 8-byte stores (zeros included).  What a dword holds
-// depends only on the first non-zero basis index sigma = span - 3, so a table
-// in LDS (built once per workgroup) holds per sigma: for each group, the
-// v_perm_b32 selector that moves its basis value out of the packed pairs
-// (b0 b1 : b2 b3) into its half (selector byte 0x0C gives zero); the NG
-// nibbles; and a mask that keeps or drops the silu half of dword NG - 1.
-// Group shift dl of the sparse column order: the silu column K lands in
-// group NG - 1.
-__host__ __device__ inline int sparse_group_shift(int NG, int K, int base) {
-    return base ? (NG - 1 - K % NG + NG) % NG : 0;
-}
-
+// depends only on the first non-zero basis index sigma = span - 3, so the
+// per-sigma table of kan_sparse.h sits in LDS (built once per workgroup):
+// one v_perm_b32 per dword moves the basis value into place, and the silu
+// value is or-ed into dword NG - 1 under the entry's mask.
 template <int NG>
 struct GenS {
     static constexpr bool SPARSE = true;
@@ -436,7 +421,7 @@ struct GenS {
     static constexpr int PPT = 256 * NIN / NTHR;                // pairs per thread
     static constexpr int NPART = PPT;
     static constexpr int RSTEP = NTHR / NIN;
-    static constexpr int EQ = (NG + 5) / 4;                     // uint4 per table entry
+    static constexpr int EQ = sparse_entry_quads<NG>();         // uint4 per table entry
     static_assert(NG == 4 || NG == 6 || NG == 8, "groups per input");
     const uint16_t* x;
     const uint4* tab;
@@ -452,46 +437,10 @@ struct GenS {
         for (int j = 0; j < PPT; ++j)
             xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
     }
-    // Table entry e, dwords w[0 .. NG + 1]: e = sigma + 3 for sigma in
-    // [-3, K - 1]; e = K + 3: no basis value (x off the grid); e = K + 4: the
-    // input does not exist (all zero).
-    __host__ __device__ static void entry(int e, int K, int base, uint32_t* w) {
-        const int dl = sparse_group_shift(NG, K, base);
-        const int ps = (K + dl) / NG;                           // the silu column's position
-        uint32_t nib = NG == 8 ? 0x44444444u : (0x44444444u & ((1u << (4 * NG)) - 1));
-        auto setnib = [&](int g, uint32_t v) { nib = (nib & ~(0xFu << (4 * g))) | (v << (4 * g)); };
-        for (int g = 0; g < NG; ++g) w[g] = 0x0C0C0C0Cu;
-        bool silu_group_taken = false;
-        if (e <= K + 2) {
-            for (int r = 0; r < 4; ++r) {
-                const int m = e - 3 + r;
-                if (m < 0 || m >= K) continue;
-                const int g = (m + dl) % NG, p = (m + dl) / NG;
-                const uint32_t lo = 0x0C0C0000u | ((2u * r + 1) << 8) | (2u * r);
-                const uint32_t hi = 0x00000C0Cu | ((2u * r + 1) << 24) | ((2u * r) << 16);
-                if (base && g == NG - 1) {                      // below the silu value
-                    w[g] = lo;
-                    setnib(g, (uint32_t)((ps << 2) | p));
-                    silu_group_taken = true;
-                } else if (p == 0) {
-                    w[g] = lo;
-                    setnib(g, 4u);
-                } else {
-                    w[g] = hi;
-                    setnib(g, (uint32_t)(p << 2));
-                }
-            }
-        }
-        const bool silu = base && e <= K + 3;
-        if (silu && !silu_group_taken) setnib(NG - 1, (uint32_t)(ps << 2));
-        w[NG] = nib;
-        w[NG + 1] = silu ? 0xFFFF0000u : 0u;
-        for (int k = NG + 2; k < 4 * EQ; ++k) w[k] = 0;
-    }
     __device__ __forceinline__ void init(const GemmArgs& a, uint4* aux) {
         for (int e = threadIdx.x; e < a.K + 5; e += NTHR) {
             uint32_t w[4 * EQ];
-            entry(e, a.K, a.base, w);
+            sparse_table_entry<NG>(e, a.K, a.base, w);
 #pragma unroll
             for (int k = 0; k < EQ; ++k) aux[EQ * e + k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
         }
@@ -859,7 +808,7 @@ __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__
 // C' for the sparse forward (bf16): input i owns the Kb8 = 4 NG columns
 // i Kb8 + 4 g + p, holding its basis column c = p NG + g - dl (C for
 // 0 <= c < K, W_base for c = K when there is a base branch, zero otherwise;
-// dl as in GenS); zero outside [0, O) x [0, I Kb8).  Rows j < Opad,
+// dl = sparse_group_shift); zero outside [0, O) x [0, I Kb8).  Rows j < Opad,
 // k < nk * 64.
 __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uint16_t* __restrict__ W,
                                        uint16_t* __restrict__ cp, int O, int I, int K, int base,
