@@ -840,30 +840,36 @@ __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uin
 }
 
 // dx B operand: row R < tiles_dx * 256 is column R of C' (zero for R >= I Kb);
-// k runs over j < nk * BK.  64 rows x 64 j per block through an LDS tile.
+// k runs over j < nk * BK.  64 rows x 64 j per block through an LDS tile,
+// written back 16 bytes (consecutive j of one row) per thread.  I Kb is
+// below the planner's index limit, so column indices fit in 32 bits.
 template <typename TS>
 __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__ W,
                                 TS* __restrict__ cpt, int O, int I, int K, int Kb, int64_t nk) {
-    __shared__ TS tile[64][65];
-    const int64_t R0 = (int64_t)blockIdx.x * 64;
+    constexpr int V = 16 / (int)sizeof(TS);               // elements per 16-byte store
+    __shared__ TS tile[64][66];
+    const uint32_t R0 = blockIdx.x * 64u;
     const int j0 = blockIdx.y * 64;
-    const int64_t IKb = (int64_t)I * Kb;
+    const uint32_t IKb = (uint32_t)I * (uint32_t)Kb;
     const int t = threadIdx.x;
     for (int e = t; e < 64 * 64; e += 256) {
-        const int jj = e / 64, kk = e % 64;
+        const int jj = e >> 6, kk = e & 63;
         const int j = j0 + jj;
-        const int64_t k = R0 + kk;
+        const uint32_t k = R0 + kk;
         TS v = TS(0);
         if (j < O && k < IKb) {
-            const int i = (int)(k / Kb), m = (int)(k - (int64_t)i * Kb);
-            v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
+            const uint32_t i = k / (uint32_t)Kb, m = k - i * (uint32_t)Kb;
+            v = (int)m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
         }
         tile[jj][kk] = v;
     }
     __syncthreads();
-    for (int e = t; e < 64 * 64; e += 256) {
-        const int kk = e / 64, jj = e % 64;
-        cpt[blk<TS>(R0 + kk, j0 + jj, nk)] = tile[jj][kk];
+    for (int e = t; e < 64 * 64 / V; e += 256) {
+        const int kk = e / (64 / V), jq = (e % (64 / V)) * V;
+        union { TS v[V]; uint4 q; } w;
+#pragma unroll
+        for (int q = 0; q < V; ++q) w.v[q] = tile[jq + q][kk];
+        *reinterpret_cast<uint4*>(cpt + blk<TS>(R0 + kk, j0 + jq, nk)) = w.q;
     }
 }
 
