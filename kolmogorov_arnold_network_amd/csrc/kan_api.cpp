@@ -30,6 +30,29 @@ bool overlap(const Range& a, const Range& b) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 
+// Slices of the k range for a contraction of `tiles` output tiles over `nkt`
+// k-tiles with `out_bytes` of fp32 output.  The contraction kernel runs one
+// workgroup per CU, so its time is estimated as the rounds of kCUs
+// workgroups times the k-tiles each runs; a split adds its partial outputs,
+// written and then summed (2 P + 1 passes over out_bytes).  The split with
+// the least estimate is taken if it saves at least 1/16; each slice keeps
+// at least 8 k-tiles.  Returns the slice count; *nks = k-tiles per slice.
+int k_slices(int64_t tiles, int64_t nkt, int64_t out_bytes, int esize, int64_t* nks) {
+    constexpr int64_t kCUs = 256;                         // MI355X compute units
+    const int64_t kt_ns = esize == 2 ? 2000 : 8000;       // one k-tile of one workgroup
+    constexpr int64_t kBytesPerNs = 4000;                 // streaming rate of the partials
+    auto est = [&](int64_t P) {
+        const int64_t per = (nkt + P - 1) / P, rounds = (tiles * P + kCUs - 1) / kCUs;
+        return rounds * per * kt_ns + (P > 1 ? (2 * P + 1) * out_bytes / kBytesPerNs : 0);
+    };
+    int64_t best = 1, tb = est(1);
+    for (int64_t P = 2; P <= 8 && (nkt + P - 1) / P >= 8; ++P)
+        if (est(P) < tb) best = P, tb = est(P);
+    if (tb > est(1) - est(1) / 16) best = 1;
+    *nks = (nkt + best - 1) / best;
+    return (int)((nkt + *nks - 1) / *nks);
+}
+
 }  // namespace
 
 int make_plan(const kan_desc_t* d, Plan* p) {
@@ -97,12 +120,19 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.Kb8 = 4 * ng;
         q.Kfs = round_up(q.I * q.Kb8, 64);
         take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
+        const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
+        q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
+                               &q.nks_fwd);
+        if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
         q.ws_fwd = off;
         off = 0;
         take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
         take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
         take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
         take((size_t)(q.Npad * q.tiles_dx * 2) * 4, &q.off_part, &q.sz_part);
+        q.split_dc = k_slices((q.Opad / kTileM) * ((q.IKb + kTileN - 1) / kTileN), q.Npad / q.BK,
+                              q.O * q.I * q.Kb * 4, q.esize, &q.nks_dc);
+        if (q.split_dc > 1) take((size_t)(q.split_dc * q.O * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
         q.ws_bwd = off;
     }
     *p = q;
@@ -218,7 +248,8 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
         st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
         if (st != KAN_OK) return st;
     }
-    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp), y, s));
+    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
+                                     reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
 }
 
 int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
@@ -271,7 +302,9 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
     if (dx)
         e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),
                            reinterpret_cast<float*>(ws_at(ws, p.off_part)), dx, s);
-    if (e == hipSuccess && (dC || dW)) e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), dC, dW, s);
+    if (e == hipSuccess && (dC || dW))
+        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), reinterpret_cast<float*>(ws_at(ws, p.off_dcp)),
+                           dC, dW, s);
     return status_of(e);
 }
 

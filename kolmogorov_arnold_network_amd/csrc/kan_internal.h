@@ -39,11 +39,16 @@ struct Plan {
     int64_t tiles_dx;    // n-tiles of the dx contraction: ceil(I * Kb / 256)
 
     // structured-sparse forward (bf16): each input's Kb columns become NG
-    // groups of 4 (Kb8 = 4 NG columns); column c goes to group c % NG,
-    // position c / NG
+    // groups of 4 (Kb8 = 4 NG columns) in the column order of kan_sparse.h
     int sparse;          // 1: the forward uses the sparse layout
     int NG, Kb8;
     int64_t Kfs;         // sparse forward contraction length: I * Kb8 rounded up to 64
+
+    // k-split of launches with too few output tiles: the forward (over its
+    // k-tiles) and dC (over the batch) run as split_* slices of nks_* k-tiles
+    // that write fp32 partial outputs, summed afterwards in slice order
+    int split_fwd, split_dc;
+    int64_t nks_fwd, nks_dc;
 
     // workspace layout (bytes); forward uses [off_cp, +sz_cp).  Every array is
     // blocked: 256-row tiles, each cut into k-tiles of 256 x BK contiguous
@@ -53,6 +58,8 @@ struct Plan {
     size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
+    size_t off_yp, sz_yp;      // forward slices' partial y: [split_fwd][N][O] float (split_fwd > 1)
+    size_t off_dcp, sz_dcp;    // dC slices' partials: [split_dc][O][I][K] then [split_dc][O][I] float
     size_t ws_fwd, ws_bwd;
 };
 
@@ -76,10 +83,11 @@ hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp
 hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
 hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s);
 hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s);
-hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s);
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y,
+                           hipStream_t s);
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
                           float* part, float* dx, hipStream_t s);
-hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
-                          hipStream_t s);
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float* dC,
+                          float* dW, hipStream_t s);
 
 }  // namespace kan

@@ -146,6 +146,10 @@ struct GemmArgs {
     int64_t IKb;
     float* out0;         // y, dx or dC
     float* out1;         // dW_base, or the dx partial sums
+    // k-split: slice blockIdx.y runs k-tiles [nks * slice, min(nkt, nks * (slice + 1)))
+    // and writes its epilogue output at out0 + slice * ostride0 (out1 likewise)
+    int nks;
+    int64_t ostride0, ostride1;
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
@@ -623,6 +627,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     char* lds = reinterpret_cast<char*>(lds4);
     int tm, tn;
     tile_coords(args, tm, tn);
+    // this workgroup's slice of the k range (the whole range unless split)
+    const int slice = blockIdx.y;
+    const int kb = slice * args.nks, ke = min(args.nkt, kb + args.nks);
+    if (args.out0) args.out0 += slice * args.ostride0;
+    if (args.out1) args.out1 += slice * args.ostride1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     AOp A(args, tm, tn);
@@ -716,22 +725,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     };
     // Store k-tile kts from slot SL into stage S, part by part behind the
     // k-steps of the tile being multiplied, and (if RF) refill each operand's
-    // slot with tile kts + DEPTH (clamped to the last tile, so every load is
-    // in bounds; the extra loads at the end are never stored).
-    const int nkt = args.nkt;
+    // slot with tile kts + DEPTH (clamped to the slice's last tile, so every
+    // load is in bounds; the extra loads at the end are never stored).
     auto stage = [&](auto slot, auto refill, char* S, int kts, auto ksc) {
         constexpr int SL = decltype(slot)::value;
         constexpr bool RF = decltype(refill)::value;
         constexpr int ks = decltype(ksc)::value;
-        const int ka = min(kts + AOp::DEPTH, nkt - 1), kb = min(kts + BOp::DEPTH, nkt - 1);
+        const int kna = min(kts + AOp::DEPTH, ke - 1), knb = min(kts + BOp::DEPTH, ke - 1);
         static_for<0, AOp::NPART>([&](auto pc) {
             constexpr int p = decltype(pc)::value;
-            if constexpr (p * 4 / AOp::NPART == ks) A.template part<SL, RF, p>(args, S, kts, ka);
+            if constexpr (p * 4 / AOp::NPART == ks) A.template part<SL, RF, p>(args, S, kts, kna);
         });
         static_for<0, BOp::NPART>([&](auto pc) {
             constexpr int p = decltype(pc)::value;
             if constexpr (p * 4 / BOp::NPART == ks)
-                B.template part<SL, RF, p>(args, S + TILE_BYTES, kts, kb);
+                B.template part<SL, RF, p>(args, S + TILE_BYTES, kts, knb);
         });
     };
     const std::integral_constant<int, 0> slot0;
@@ -740,20 +748,20 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     const std::false_type last;
     auto nothing = [](auto) {};
     // Two LDS stages S0, S1.  Invariant at the top of each pass of the loop
-    // (kt even): S0 holds tile kt; an operand of DEPTH 2 has slot 1 loading
-    // tile kt+1 and slot 0 tile kt+2, one of DEPTH 1 has its slot loading tile
-    // kt+1.  While tile kt is multiplied from S0, tile kt+1 goes into S1 and
-    // the slots refill; then the same with the stages swapped.
+    // (kt - kb even): S0 holds tile kt; an operand of DEPTH 2 has slot 1
+    // loading tile kt+1 and slot 0 tile kt+2, one of DEPTH 1 has its slot
+    // loading tile kt+1.  While tile kt is multiplied from S0, tile kt+1 goes
+    // into S1 and the slots refill; then the same with the stages swapped.
     char* S0 = lds;
     char* S1 = lds + STAGE_BYTES;
-    A.template fetch<0>(args, 0);
-    B.template fetch<0>(args, 0);
-    if (AOp::DEPTH == 2) A.template fetch<1>(args, min(1, nkt - 1));
-    if (BOp::DEPTH == 2) B.template fetch<1>(args, min(1, nkt - 1));
-    static_for<0, 4>([&](auto ksc) { stage(slot0, refill, S0, 0, ksc); });
+    A.template fetch<0>(args, kb);
+    B.template fetch<0>(args, kb);
+    if (AOp::DEPTH == 2) A.template fetch<1>(args, min(kb + 1, ke - 1));
+    if (BOp::DEPTH == 2) B.template fetch<1>(args, min(kb + 1, ke - 1));
+    static_for<0, 4>([&](auto ksc) { stage(slot0, refill, S0, kb, ksc); });
     __syncthreads();
-    int kt = 0;
-    for (; kt + 2 < nkt; kt += 2) {
+    int kt = kb;
+    for (; kt + 2 < ke; kt += 2) {
         compute(S0, S0 + TILE_BYTES, [&](auto ks) { stage(slot1, refill, S1, kt + 1, ks); });
         __syncthreads();
         compute(S1, S1 + TILE_BYTES, [&](auto ks) { stage(slot0, refill, S0, kt + 2, ks); });
@@ -763,7 +771,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     // writes the free stage S1 (every load behind it is clamped in bounds).
     compute(S0, S0 + TILE_BYTES, [&](auto ks) { stage(slot1, last, S1, kt + 1, ks); });
     __syncthreads();
-    if (kt + 1 < nkt) compute(S1, S1 + TILE_BYTES, nothing);
+    if (kt + 1 < ke) compute(S1, S1 + TILE_BYTES, nothing);
     __syncthreads();
     Epi::template run<TS>(args, acc, tm, tn, lds);
 }
@@ -908,7 +916,26 @@ hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(NTHR), LDS_BYTES, s, a);
+    const unsigned slices = (unsigned)((a.nkt + a.nks - 1) / a.nks);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n), slices), dim3(NTHR), LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+// out[e] = sum over slices s = 0 .. P-1, in that order, of part[s n + e]
+__global__ void sum_slices_kernel(const float* __restrict__ part, float* __restrict__ out, int64_t n,
+                                  int P) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        float v = part[e];
+        for (int q = 1; q < P; ++q) v += part[q * n + e];
+        out[e] = v;
+    }
+}
+
+hipError_t sum_slices(const float* part, float* out, int64_t n, int P, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 16384)),
+                       dim3(256), 0, s, part, out, n, P);
     return hipGetLastError();
 }
 
@@ -925,6 +952,7 @@ GemmArgs base_args(const Plan& p, const void* x) {
     a.base = p.base;
     a.IKb = p.IKb;
     a.group_m = 16;
+    a.nks = 1 << 30;     // one slice unless a launcher splits the k range
     return a;
 }
 
@@ -1013,23 +1041,31 @@ static hipError_t dc_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
     return run_gemm<TS, LoadA, GenB<TS, 2, 32>, EpiDC>(a, s);
 }
 
-hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* y, hipStream_t s) {
-    GemmArgs a = base_args(p, x);
-    a.tiles_m = (int)(p.Npad / 256);
-    a.tiles_n = (int)(p.Opad / 256);
-    a.b = static_cast<const char*>(cp);
-    a.out0 = y;
+static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
     if (p.sparse) {
-        a.nkt = (int)(p.Kfs / 64);
-        a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
         if (p.NG == 4) return run_gemm<uint16_t, GenS<4>, LoadB, EpiY>(a, s);
         if (p.NG == 6) return run_gemm<uint16_t, GenS<6>, LoadB, EpiY>(a, s);
         return run_gemm<uint16_t, GenS<8>, LoadB, EpiY>(a, s);
     }
-    a.nkt = (int)(p.Kf / p.BK);
-    a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
     if (p.dtype == KAN_F32) return fwd_dispatch<float>(p, a, s);
     return fwd_dispatch<uint16_t>(p, a, s);
+}
+
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y,
+                           hipStream_t s) {
+    GemmArgs a = base_args(p, x);
+    a.tiles_m = (int)(p.Npad / 256);
+    a.tiles_n = (int)(p.Opad / 256);
+    a.b = static_cast<const char*>(cp);
+    a.nkt = (int)(p.sparse ? p.Kfs / 64 : p.Kf / p.BK);
+    a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
+    a.out0 = y;
+    if (p.split_fwd <= 1) return fwd_run(p, a, s);
+    a.out0 = ypart;
+    a.nks = (int)p.nks_fwd;
+    a.ostride0 = p.N * p.O;
+    hipError_t e = fwd_run(p, a, s);
+    return e != hipSuccess ? e : sum_slices(ypart, y, p.N * p.O, p.split_fwd, s);
 }
 
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
@@ -1056,8 +1092,8 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* dC, float* dW,
-                          hipStream_t s) {
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float* dC,
+                          float* dW, hipStream_t s) {
     GemmArgs a = base_args(p, x);
     a.tiles_m = (int)(p.Opad / 256);
     a.tiles_n = (int)((p.IKb + 255) / 256);
@@ -1067,8 +1103,20 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.out0 = dC;
     a.out1 = dW;
     a.group_m = 2;
-    if (p.dtype == KAN_F32) return dc_dispatch<float>(p, a, s);
-    return dc_dispatch<uint16_t>(p, a, s);
+    if (p.split_dc <= 1)
+        return p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
+    // the batch in split_dc fixed slices: partials, then a sum in slice order
+    const int64_t nc = p.O * p.I * p.K, nw = p.O * p.I;
+    float* wpart = cpart + p.split_dc * nc;
+    a.out0 = dC ? cpart : nullptr;
+    a.out1 = dW ? wpart : nullptr;
+    a.nks = (int)p.nks_dc;
+    a.ostride0 = nc;
+    a.ostride1 = nw;
+    hipError_t e = p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
+    if (e == hipSuccess && dC) e = sum_slices(cpart, dC, nc, p.split_dc, s);
+    if (e == hipSuccess && dW) e = sum_slices(wpart, dW, nw, p.split_dc, s);
+    return e;
 }
 
 }  // namespace kan

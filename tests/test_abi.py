@@ -138,6 +138,30 @@ def test_empty_batch_forward_returns_ok_without_launch(L):
     assert fwd(L, desc(L, N=0)) == L.KAN_OK
 
 
+def k_slices(tiles, nkt, out_bytes, esize):
+    """The planner's k-split rule, restated: slices of the k range for a
+    contraction of `tiles` output tiles over `nkt` k-tiles with `out_bytes`
+    of fp32 output (estimate: rounds of 256 one-per-CU workgroups x k-tiles
+    per workgroup at 2 us (bf16) or 8 us (fp32), plus 2P + 1 passes over
+    the partials at 4 bytes/ns; taken when it saves >= 1/16, >= 8 k-tiles a
+    slice).  Returns (slices, k-tiles per slice)."""
+    kt_ns = 2000 if esize == 2 else 8000
+
+    def est(P):
+        per, rounds = (nkt + P - 1) // P, (tiles * P + 255) // 256
+        return rounds * per * kt_ns + ((2 * P + 1) * out_bytes // 4000 if P > 1 else 0)
+    best, tb = 1, est(1)
+    P = 2
+    while P <= 8 and (nkt + P - 1) // P >= 8:
+        if est(P) < tb:
+            best, tb = P, est(P)
+        P += 1
+    if tb > est(1) - est(1) // 16:
+        best = 1
+    nks = (nkt + best - 1) // best
+    return (nkt + nks - 1) // nks, nks
+
+
 def test_workspace_sizes(L):
     ws = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 0)
     wb = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 1)
@@ -145,22 +169,30 @@ def test_workspace_sizes(L):
     # MFMA forward: packed C' [O padded to 256][I*Kb padded to the k-tile]
     r = lambda a, b: (a + b - 1) // b * b
     for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
-        for (N, I, O, G, base) in [(64, 16, 8, 8, 1), (1000, 777, 300, 20, 0), (5, 3, 2, 1, 1)]:
+        for (N, I, O, G, base) in [(64, 16, 8, 8, 1), (1000, 777, 300, 20, 0), (5, 3, 2, 1, 1),
+                                   (12608, 768, 3072, 5, 1), (12608, 3072, 768, 5, 1), (8192, 1024, 1024, 50, 0)]:
             Kb = G + 3 + base
             # bf16 forwards with 11 <= Kb <= 32 whose 2:4 layout (NG groups of 4
             # columns per input) costs <= 3/4 of the dense one pack I * 4 NG columns
             ng = max(4, (Kb + 3) // 4)
             ng += ng & 1
             sparse = dt == L.KAN_BF16 and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
+            Op, Np = r(O, 256), r(N, 256)
+
+            def fwd_bytes(kf, nkt):
+                # packed C', then the partial y of a split forward
+                P, _ = k_slices((Np // 256) * (Op // 256), nkt, N * O * 4, es)
+                return r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
             kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
-            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == r(r(O, 256) * kf * es, 256)
+            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == fwd_bytes(kf, kf // (64 if sparse else bk))
             if sparse:
                 assert L.lib().kan_workspace_size(ctypes.byref(desc(
                     L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)), 0) == \
-                    r(r(O, 256) * r(I * Kb, bk) * es, 256)
+                    fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk)
             tiles = (I * Kb + 255) // 256           # dx tiles of 256 P columns
-            Op, Np = r(O, 256), r(N, 256)
             want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
+            P, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)   # dC over batch slices
+            want += r(P * O * I * Kb * 4, 256) if P > 1 else 0
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores, float32 on the gather kernels, and the gather
     # kernels whenever an input's columns exceed one tile
