@@ -179,6 +179,36 @@ def test_deterministic_and_prepared(F):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_batch_dc(F, dtype):
+    """2048 rows against 2 output tiles: dC runs in 4 (bf16) or 8 (float32)
+    fixed batch slices that are summed in slice order (no atomics).  dC
+    alone, dW_base alone and both together give the oracle's values and the
+    same bits, every time.  The G = 20 bf16 layer also takes the 2:4 sparse
+    forward (the SPARSE shapes above cover its k-split)."""
+    import torch
+    for (N, I, O, G) in [(2048, 40, 100, 8), (2048, 21, 23, 20)]:
+        d = wl.random_layer(N, I, O, G, dtype=dtype, base=True, seed=9)
+        (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+        grid = (d["lo"], d["hi"], d["G"])
+        xt, Ct, Wt, dyt = to_dev(x, dtype), to_dev(C, dtype), to_dev(W, dtype), to_dev(dy, "f32")
+        say("split %s %dx%dx%d G=%d" % (dtype, N, I, O, G))
+        both = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+        only_c = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, need_dW=False, variant="mfma")
+        only_w = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, need_dC=False, variant="mfma")
+        again = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+        y = F.kan_forward(xt, Ct, Wt, grid, "mfma")
+        y2 = F.kan_forward(xt, Ct, Wt, grid, "mfma")
+        _sync()
+        assert only_c[2] is None and only_w[1] is None
+        assert torch.equal(both[1], only_c[1]) and torch.equal(both[2], only_w[2])
+        assert torch.equal(both[1], again[1]) and torch.equal(both[2], again[2]) and torch.equal(y, y2)
+        err, tol = metric(dtype)
+        _, rdC, rdW = oracle.layer_backward(x, C, W, dy, *grid, need=("dC", "dW"))
+        assert err(_np(both[1]), rdC) <= tol and err(_np(both[2]), rdW) <= tol
+        assert err(_np(y), oracle.layer_forward(x, C, W, *grid)) <= tol
+
+
 @pytest.mark.parametrize("variant", ["mfma", "gather"])
 def test_empty_batch(F, variant):
     import torch
