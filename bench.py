@@ -38,8 +38,8 @@ WORKLOAD_TEXT = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 10 for c5, else 20)")
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--G", type=int, default=None, help="grid size (c3 only: 8, 20 or 50)")
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "gather"])
@@ -49,7 +49,10 @@ def parse():
                     help="print the digest that ties a counter summary to the kernel source")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (HBM counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10 if args.workload == "c5" else 20
+    return args
 
 
 def copy_probe(nbytes):
@@ -81,7 +84,8 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the KAN layer path here has no multi-GPU "
-              "mode (data-parallel sharding over rows is described in DESIGN.md); run with "
+              "mode (it would shard the rows, one process per GPU, and all-reduce dC and "
+              "dW_base); run with "
               "--gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -187,7 +191,9 @@ def main():
         for k, nm in enumerate(names):
             stage_ms[nm] += evs[k].elapsed_time(evs[k + 1]) / args.steps
     ms_per_step = 1e3 * elapsed / args.steps
-
+    step_ms = sorted(evs[0].elapsed_time(evs[-1]) for evs in per_step_events)
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     # work counts: algorithmic = the 4 non-zero basis functions (+ silu) per input
     # in each of the three contractions; executed = the dense I*(G+3+base) basis,
     # except a structured-sparse forward, whose matrix instructions run half of
@@ -234,6 +240,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "median_ms_per_step": median_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
