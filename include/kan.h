@@ -71,11 +71,14 @@ typedef enum {
 
 typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
 
-/* Kernel family.  AUTO picks per shape and dtype.  MFMA runs the contraction
- * over the dense basis (I*(G+3+has_base) wide) on the matrix cores, with the
- * basis generated in LDS and never written to memory.  GATHER touches only the
- * 4 non-zero basis functions per input (InKAN page, "Why InKAN?": local
- * 4-basis lookup) on the vector ALUs. */
+/* Kernel family.  MFMA runs the contraction over the dense basis
+ * (I*(G+3+has_base) wide) on the matrix cores, with the basis generated in LDS
+ * and never written to memory; it needs G+3+has_base <= 256.  GATHER touches
+ * only the 4 non-zero basis functions per input (InKAN page, "Why InKAN?":
+ * local 4-basis lookup) on the vector ALUs.  AUTO picks per pass: bf16 runs
+ * both passes on MFMA; float32 runs the forward on GATHER (float64 addition
+ * across inputs) and the backward on MFMA once N*I*O >= 2^16 (GATHER below);
+ * GATHER wherever MFMA does not fit. */
 typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 2 } kan_variant_t;
 
 typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;

@@ -84,18 +84,28 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     q.gk.shift = (float)(3.0 - lo * (double)q.G / (hi - lo));
     q.gk.G = q.G;
 
-    // The dx epilogue keeps whole inputs inside one 256-wide tile.  AUTO: bf16
-    // runs on the matrix cores; float32 takes the local gather kernels (the
-    // dense contraction would execute (G+3+base)/(4+base) times the useful
-    // work at the float32 matrix rate, which equals the vector rate, and the
-    // gather forward accumulates in float64).
+    // An input's Kb columns must fit one 256-wide tile on the matrix cores.
+    // AUTO: bf16 runs both passes on the matrix cores.  float32 runs the
+    // forward on the local gather kernel, which adds the per-input partials in
+    // float64: in a chain of layers the next layer's B' amplifies forward
+    // rounding about tenfold, beyond what the float32 matrix instruction's
+    // rounding leaves room for.  Its backward (dx, dC) feeds no B', so it runs
+    // on the matrix cores, several times faster than the gather backward once
+    // the layer has at least 2^16 edge-rows (N I O); below that the packing
+    // and launches of the matrix-core path cost more than the work.
     const bool mfma_ok = q.Kb <= kTileN;
     if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
-    if (d->variant == KAN_VARIANT_GATHER) q.variant = KAN_VARIANT_GATHER;
-    else if (d->variant == KAN_VARIANT_MFMA) q.variant = KAN_VARIANT_MFMA;
-    else q.variant = (mfma_ok && q.dtype == KAN_BF16) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
+    if (d->variant == KAN_VARIANT_GATHER) {
+        q.variant_fwd = q.variant_bwd = KAN_VARIANT_GATHER;
+    } else if (d->variant == KAN_VARIANT_MFMA) {
+        q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
+    } else {
+        q.variant_fwd = (mfma_ok && q.dtype == KAN_BF16) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
+        const bool big = q.N * q.I * q.O >= (int64_t(1) << 16);
+        q.variant_bwd = mfma_ok && (q.dtype == KAN_BF16 || big) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
+    }
 
-    if (q.variant == KAN_VARIANT_MFMA) {
+    if (q.variant_fwd == KAN_VARIANT_MFMA || q.variant_bwd == KAN_VARIANT_MFMA) {
         q.BK = kTileKBytes / q.esize;
         q.IKb = q.I * q.Kb;
         q.Opad = round_up(q.O, kTileN);
@@ -124,7 +134,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
                                &q.nks_fwd);
         if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
-        q.ws_fwd = off;
+        q.ws_fwd = q.variant_fwd == KAN_VARIANT_MFMA ? off : 0;
         off = 0;
         take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
         take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
@@ -133,7 +143,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.split_dc = k_slices((q.Opad / kTileM) * ((q.IKb + kTileN - 1) / kTileN), q.Npad / q.BK,
                               q.O * q.I * q.Kb * 4, q.esize, &q.nks_dc);
         if (q.split_dc > 1) take((size_t)(q.split_dc * q.O * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
-        q.ws_bwd = off;
+        q.ws_bwd = q.variant_bwd == KAN_VARIANT_MFMA ? off : 0;
     }
     *p = q;
     return KAN_OK;
@@ -167,12 +177,15 @@ size_t kan_workspace_size(const kan_desc_t* desc, int pass) {
     Plan p;
     if (make_plan(desc, &p) != KAN_OK) return SIZE_MAX;
     if (pass != KAN_PASS_FORWARD && pass != KAN_PASS_BACKWARD) return SIZE_MAX;
-    if (p.variant != KAN_VARIANT_MFMA) return 0;
     return pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
 }
 
+static int pass_variant(const Plan& p, int pass) {
+    return pass == KAN_PASS_FORWARD ? p.variant_fwd : p.variant_bwd;
+}
+
 static int check_ws(const Plan& p, int pass, const void* ws, size_t ws_bytes) {
-    if (p.variant != KAN_VARIANT_MFMA) return KAN_OK;
+    if (pass_variant(p, pass) != KAN_VARIANT_MFMA) return KAN_OK;
     const size_t need = pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
     if (ws_bytes < need) return KAN_ERR_WORKSPACE;
     if (need > 0 && !ws) return KAN_ERR_NULL;
@@ -184,7 +197,7 @@ static char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; 
 
 static int prepare_impl(const Plan& p, int pass, const void* C, const void* W, const float* dy,
                         void* ws, hipStream_t s) {
-    if (p.variant != KAN_VARIANT_MFMA) return KAN_OK;
+    if (pass_variant(p, pass) != KAN_VARIANT_MFMA) return KAN_OK;
     hipError_t e = hipSuccess;
     if (pass == KAN_PASS_FORWARD) {
         e = p.sparse ? launch_pack_fwd_sparse(p, C, W, ws_at(ws, p.off_cp), s)
@@ -210,7 +223,7 @@ int kan_prepare(const kan_desc_t* desc, int pass, const void* C, const void* W_b
         return KAN_ERR_ALIGN;
     if ((st = check_ws(p, pass, ws, ws_bytes)) != KAN_OK) return st;
     const size_t wsn = pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
-    const Range wr{ws, p.variant == KAN_VARIANT_MFMA ? wsn : 0};
+    const Range wr{ws, wsn};
     const Range in[] = {{C, (size_t)(p.O * p.I * p.K) * p.esize},
                         {W_base, (size_t)(p.O * p.I) * p.esize},
                         {dy, pass == KAN_PASS_BACKWARD ? (size_t)(p.N * p.O) * 4 : 0}};
@@ -232,7 +245,7 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
         if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
     if ((st = check_ws(p, KAN_PASS_FORWARD, ws, ws_bytes)) != KAN_OK) return st;
     const Range out{y, (size_t)(p.N * p.O) * 4};
-    const Range wr{ws, p.variant == KAN_VARIANT_MFMA ? p.ws_fwd : 0};
+    const Range wr{ws, p.ws_fwd};
     const Range in[] = {{x, (size_t)(p.N * p.I) * p.esize},
                         {C, (size_t)(p.O * p.I * p.K) * p.esize},
                         {W_base, (size_t)(p.O * p.I) * p.esize}};
@@ -243,7 +256,7 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (p.variant == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, s));
+    if (p.variant_fwd == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, s));
     if (!(desc->flags & KAN_FLAG_PREPARED)) {
         st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
         if (st != KAN_OK) return st;
@@ -268,7 +281,7 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
     const Range outs[] = {{dx, (size_t)(p.N * p.I) * 4},
                           {dC, (size_t)(p.O * p.I * p.K) * 4},
                           {dW, (size_t)(p.O * p.I) * 4},
-                          {ws, p.variant == KAN_VARIANT_MFMA ? p.ws_bwd : 0}};
+                          {ws, p.ws_bwd}};
     const Range ins[] = {{x, (size_t)(p.N * p.I) * p.esize},
                          {C, (size_t)(p.O * p.I * p.K) * p.esize},
                          {W_base, (size_t)(p.O * p.I) * p.esize},
@@ -288,7 +301,7 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
         if (e == hipSuccess && dW) e = launch_fill_zero(dW, p.O * p.I, s);
         return status_of(e);
     }
-    if (p.variant == KAN_VARIANT_GATHER) {
+    if (p.variant_bwd == KAN_VARIANT_GATHER) {
         hipError_t e = hipSuccess;
         if (dx) e = launch_gather_dx(p, x, C, W_base, dy, dx, s);
         if (e == hipSuccess && (dC || dW)) e = launch_gather_dc(p, x, dy, dC, dW, s);

@@ -26,7 +26,8 @@ struct Plan {
     int G, K, Kb;        // K = G+3 spline functions; Kb = K + has_base columns per input
     int base;
     int dtype;           // KAN_F32 / KAN_BF16
-    int variant;         // resolved: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
+    int variant_fwd;     // resolved per pass: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
+    int variant_bwd;
     int esize;           // bytes per stored element (4 or 2)
     GridK gk;
 

@@ -194,10 +194,16 @@ def test_workspace_sizes(L):
             P, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)   # dC over batch slices
             want += r(P * O * I * Kb * 4, 256) if P > 1 else 0
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
-    # auto: bf16 on the matrix cores, float32 on the gather kernels, and the gather
-    # kernels whenever an input's columns exceed one tile
+    # auto: bf16 on the matrix cores; float32 forward on the gather kernel and
+    # backward on the matrix cores; the gather kernels whenever an input's
+    # columns exceed one tile
     assert ws(G=254, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == 0
+    assert wb(G=254, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
+    # float32 AUTO: gather forward (no workspace), matrix-core backward
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
+    assert wb(N=64, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == wb(
+        N=64, I=32, O=32, variant=L.KAN_VARIANT_MFMA, dtype=L.KAN_F32) > 0          # 2^16 edge-rows
+    assert wb(N=63, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0  # below: gather
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ws(variant=L.KAN_VARIANT_MFMA,
                                                                    dtype=L.KAN_BF16) > 0
 
