@@ -60,7 +60,7 @@ typedef enum {
     KAN_OK = 0,
     KAN_ERR_NULL = -1,        /* a required pointer is NULL, or a forbidden one is not */
     KAN_ERR_SHAPE = -2,       /* N < 0, I < 1, O < 1, or a size beyond the index range */
-    KAN_ERR_GRID = -3,        /* G < 1, lo >= hi, or lo / hi not finite */
+    KAN_ERR_GRID = -3,        /* G < 1 or G > 125, lo >= hi, or lo / hi not finite */
     KAN_ERR_DTYPE = -4,       /* dtype not KAN_F32 / KAN_BF16 */
     KAN_ERR_ALIGN = -5,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
     KAN_ERR_WORKSPACE = -6,   /* workspace smaller than kan_workspace_size() */
@@ -83,7 +83,9 @@ typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 
 
 typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;
 
-/* Grid: G intervals on [lo, hi]; degree must be 3 (cubic, InKAN page). */
+/* Grid: G intervals on [lo, hi], 1 <= G <= 125 (the G+3 coefficients of an
+ * input for a tile of outputs are staged in LDS); degree must be 3 (cubic,
+ * InKAN page). */
 typedef struct {
     float lo;
     float hi;

@@ -14,6 +14,7 @@ namespace kan {
 namespace {
 
 constexpr int64_t kIndexLimit = (int64_t(1) << 31) - 4096;  // keeps 32-bit tile math safe
+constexpr int kMaxG = 125;                                      // K = G + 3 <= 128
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -59,7 +60,9 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     if (!d || !p) return KAN_ERR_NULL;
     if (d->N < 0 || d->I < 1 || d->O < 1) return KAN_ERR_SHAPE;
     if (d->grid.degree != 3) return KAN_ERR_UNSUPPORTED;
-    if (d->grid.G < 1 || d->grid.G > 4096) return KAN_ERR_GRID;
+    // G <= kMaxG: the gather kernels stage an input's K = G+3 coefficients
+    // for a tile of outputs in LDS, which holds 128 of them
+    if (d->grid.G < 1 || d->grid.G > kMaxG) return KAN_ERR_GRID;
     if (!isfinite(d->grid.lo) || !isfinite(d->grid.hi) || !(d->grid.lo < d->grid.hi))
         return KAN_ERR_GRID;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
@@ -162,7 +165,7 @@ const char* kan_status_string(int status) {
         case KAN_OK: return "ok";
         case KAN_ERR_NULL: return "required pointer is NULL (or a forbidden one is not)";
         case KAN_ERR_SHAPE: return "invalid shape";
-        case KAN_ERR_GRID: return "invalid grid (G < 1 or > 4096, lo >= hi, or non-finite)";
+        case KAN_ERR_GRID: return "invalid grid (G < 1 or > 125, lo >= hi, or non-finite)";
         case KAN_ERR_DTYPE: return "unsupported dtype";
         case KAN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, workspace 256)";
         case KAN_ERR_WORKSPACE: return "workspace too small";

@@ -82,11 +82,10 @@ def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(N=-1), "SHAPE"), (dict(I=0), "SHAPE"), (dict(O=0), "SHAPE"), (dict(N=1 << 40), "SHAPE"),
-    (dict(G=0), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
+    (dict(G=0), "GRID"), (dict(G=126), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
     (dict(lo=2.0, hi=1.0), "GRID"), (dict(lo=float("nan")), "GRID"), (dict(hi=float("inf")), "GRID"),
     (dict(degree=2), "UNSUPPORTED"), (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
     (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
-    (dict(G=254, variant=2 - 1), "UNSUPPORTED"),     # Kb = 258 > 256: no MFMA tile
 ])
 def test_bad_descriptors(L, kw, code):
     d = desc(L, **kw)
@@ -195,10 +194,9 @@ def test_workspace_sizes(L):
             want += r(P * O * I * Kb * 4, 256) if P > 1 else 0
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores; float32 forward on the gather kernel and
-    # backward on the matrix cores; the gather kernels whenever an input's
-    # columns exceed one tile
-    assert ws(G=254, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == 0
-    assert wb(G=254, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
+    # backward on the matrix cores
+    assert ws(G=125, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) > 0      # largest grid: MFMA fits
+    assert ws(G=126, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ctypes.c_size_t(-1).value
     # float32 AUTO: gather forward (no workspace), matrix-core backward
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
     assert wb(N=64, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == wb(
