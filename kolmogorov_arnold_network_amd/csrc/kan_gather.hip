@@ -79,15 +79,56 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 
 // ---------------------------------------------------------------------------
 // Forward.  Block: 64 rows x 64 outputs; thread: 4 rows x 4 consecutive outputs.
-// Inputs advance in chunks of 4; the chunk's coefficients sit in LDS as
-// Cs[i][m][j] so that C[j..j+3, i, m] is one 16-byte read.  Each input's
-// five-term partial phi_ji(x_i) is formed in float32 and added into a float64
+// Inputs advance in chunks of IC inputs, as many (up to 7) as keep both chunk
+// buffers within 40 KB of LDS, so that 4 blocks share a CU; a chunk's
+// coefficients for the 64 outputs are then at most 20 values per thread (32
+// for K > 80, with one input per chunk).  They sit
+// in LDS as Cs[i][m][j], so that C[j..j+3, i, m] is one 16-byte read.  LDS
+// holds two chunk buffers: while one chunk is multiplied, the next chunk's
+// coefficients, W_base and x are loaded into registers, and are then written
+// (x as its span record) to the other buffer.  Global latency overlaps the
+// arithmetic, and each chunk costs one barrier.  Each input's five-term
+// partial phi_ji(x_i) is formed in float32 and added into a float64
 // accumulator: a chain of KAN layers feeds y through B' of the next layer,
 // which amplifies forward rounding error about tenfold, and float64 adds cost
 // the same as float32 FMAs on the vector ALU.
-constexpr int GF_TB = 64, GF_TJ = 64, GF_IC = 4;
+constexpr int GF_TB = 64, GF_TJ = 64;
 
-template <typename TS>
+// A (row, input) pair of the forward chunk: the LDS index of its first
+// coefficient row Cs[ii][mb][0], with mb = s - 3 clamped to [0, K - 4] so that
+// rows mb .. mb + 3 all exist, and the four weights of those rows (the spline
+// pieces shifted by the clamp, zero where a basis index is out of range).
+struct RecF {
+    int cb;
+    float w[4];
+    float base;
+};
+
+__device__ __forceinline__ RecF make_recf(float xv, const GridK& g, int ii, int base) {
+    const Rec r = make_rec<false>(xv, g);
+    const int K = g.G + 3;
+    const int mb = clampi(r.m0, 0, K - 4);
+    RecF f;
+    f.cb = (ii * K + mb) * GF_TJ;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = mb + q - r.m0;                 // which piece multiplies row mb + q
+        f.w[q] = k == 0 ? r.w[0] : k == 1 ? r.w[1] : k == 2 ? r.w[2] : k == 3 ? r.w[3] : 0.0f;
+    }
+    f.base = base ? r.base : 0.0f;
+    return f;
+}
+
+__host__ __device__ inline int gather_fwd_ic(int K) {
+    const int ic = 5120 / (GF_TJ * K + GF_TJ + GF_TB * (int)(sizeof(RecF) / 4));
+    return ic < 1 ? 1 : (ic > 7 ? 7 : ic);
+}
+__host__ __device__ inline int gather_fwd_buf_floats(int K) {
+    const int ic = gather_fwd_ic(K);
+    return ic * K * GF_TJ + ic * GF_TJ + ic * GF_TB * (int)(sizeof(RecF) / 4);
+}
+
+template <typename TS, int MAXQ>
 __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, int O, int base,
                                                          const TS* __restrict__ x,
                                                          const TS* __restrict__ C,
@@ -96,60 +137,111 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
     const int K = g.G + 3;
-    float* Cs = smem;                                  // [IC][K][TJ]
-    float* Ws = Cs + GF_IC * K * GF_TJ;                // [IC][TJ]
-    Rec* Rs = reinterpret_cast<Rec*>(Ws + GF_IC * GF_TJ);  // [IC][TB]
-
+    const int IC = gather_fwd_ic(K);
+    const int ICK = IC * K;                          // coefficients of one output in a chunk
+    const int csz = ICK * GF_TJ, wsz = IC * GF_TJ;
+    const int bufsz = gather_fwd_buf_floats(K);      // floats per buffer: Cs, Ws, Rs
     const int t = threadIdx.x;
     const int jq = t % 16, rq = t / 16;
     const int b0 = blockIdx.x * GF_TB, j0 = blockIdx.y * GF_TJ;
-    double acc[4][4] = {};
+    const int nch = (I + IC - 1) / IC;
 
-    for (int i0 = 0; i0 < I; i0 += GF_IC) {
-        const int nic = min(GF_IC, I - i0);
-        __syncthreads();
-        // coefficients: C[j0 + jj, i0 + ii, m] -> Cs[ii][m][jj]
-        for (int e = t; e < GF_TJ * GF_IC * K; e += 256) {
-            const int jj = e / (GF_IC * K), rem = e % (GF_IC * K);
-            const int ii = rem / K, m = rem % K;
-            const int j = j0 + jj, i = i0 + ii;
-            Cs[(ii * K + m) * GF_TJ + jj] =
-                (j < O && ii < nic) ? load_f(C, ((int64_t)j * I + i) * K + m) : 0.0f;
+    // this thread's coefficient loads: elements e = t + 256 q of the chunk,
+    // e = jj * ICK + rem (rem = ii * K + m, contiguous in C for one output)
+    const int jC0 = t / ICK, rC0 = t % ICK, dj = 256 / ICK, dr = 256 % ICK;
+    const int nq = (csz + 255) / 256;                // <= MAXQ
+    // W_base and x: the 64 IC (output or row, input) pairs of a chunk, pair
+    // u = t + 256 v (v < 2, as IC <= 7) at pair index pj = u / IC, pi = u % IC
+    int pj[2], pi[2];
+    bool has_pair[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int u = t + 256 * v;
+        has_pair[v] = u < IC * 64;
+        pj[v] = u / IC;
+        pi[v] = u % IC;
+    }
+
+    float cp[MAXQ];
+    float wp[2] = {0.0f, 0.0f}, xp[2] = {0.0f, 0.0f};
+    auto load = [&](int c) {
+        const int i0 = c * IC, nic = min(IC, I - i0);
+        int jj = jC0, rem = rC0;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            if (q < nq) {
+                const int j = j0 + jj;
+                cp[q] = (jj < GF_TJ && j < O && rem < nic * K)
+                            ? load_f(C, ((int64_t)j * I + i0) * K + rem) : 0.0f;
+                jj += dj;
+                rem += dr;
+                if (rem >= ICK) rem -= ICK, ++jj;
+            }
         }
-        for (int e = t; e < GF_TJ * GF_IC; e += 256) {
-            const int jj = e / GF_IC, ii = e % GF_IC;
-            const int j = j0 + jj, i = i0 + ii;
-            Ws[ii * GF_TJ + jj] = (base && j < O && ii < nic) ? load_f(W, (int64_t)j * I + i) : 0.0f;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            wp[v] = (has_pair[v] && base && j0 + pj[v] < O && pi[v] < nic)
+                        ? load_f(W, (int64_t)(j0 + pj[v]) * I + i0 + pi[v]) : 0.0f;
+            xp[v] = (has_pair[v] && b0 + pj[v] < N && pi[v] < nic)
+                        ? load_f(x, (int64_t)(b0 + pj[v]) * I + i0 + pi[v]) : 0.0f;
         }
-        for (int e = t; e < GF_TB * GF_IC; e += 256) {
-            const int bb = e / GF_IC, ii = e % GF_IC;
-            const int b = b0 + bb, i = i0 + ii;
-            Rec r;
-            if (b < N && ii < nic) {
-                r = make_rec<false>(load_f(x, (int64_t)b * I + i), g);
-                if (!base) r.base = 0.0f;
+    };
+    auto store = [&](int c, int buf) {
+        float* Cs = smem + buf * bufsz;
+        float* Ws = Cs + csz;
+        RecF* Rs = reinterpret_cast<RecF*>(Ws + wsz);
+        const int i0 = c * IC, nic = min(IC, I - i0);
+        int jj = jC0, rem = rC0;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            if (q < nq) {
+                if (jj < GF_TJ) Cs[rem * GF_TJ + jj] = cp[q];
+                jj += dj;
+                rem += dr;
+                if (rem >= ICK) rem -= ICK, ++jj;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            if (!has_pair[v]) continue;
+            Ws[pi[v] * GF_TJ + pj[v]] = wp[v];
+            RecF r;
+            if (b0 + pj[v] < N && pi[v] < nic) {
+                r = make_recf(xp[v], g, pi[v], base);
             } else {
-                r.m0 = 0;
+                r.cb = pi[v] * K * GF_TJ;
                 r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0.0f;
                 r.base = 0.0f;
             }
-            Rs[ii * GF_TB + bb] = r;
+            Rs[pi[v] * GF_TB + pj[v]] = r;
         }
-        __syncthreads();
+    };
+
+    double acc[4][4] = {};
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const bool more = c + 1 < nch;
+        if (more) load(c + 1);
+        const float* Cs = smem + (c & 1) * bufsz;
+        const float* Ws = Cs + csz;
+        const RecF* Rs = reinterpret_cast<const RecF*>(Ws + wsz);
+        const int nic = min(IC, I - c * IC);
         for (int ii = 0; ii < nic; ++ii) {
             const float4 wv = *reinterpret_cast<const float4*>(&Ws[ii * GF_TJ + 4 * jq]);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const Rec r = Rs[ii * GF_TB + rq + 16 * p];
+                const RecF r = Rs[ii * GF_TB + rq + 16 * p];
                 float a0 = r.base * wv.x, a1 = r.base * wv.y, a2 = r.base * wv.z, a3 = r.base * wv.w;
+                const float* crow = Cs + r.cb + 4 * jq;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int m = clampi(r.m0 + q, 0, K - 1);
-                    const float4 c = *reinterpret_cast<const float4*>(&Cs[(ii * K + m) * GF_TJ + 4 * jq]);
-                    a0 = __builtin_fmaf(r.w[q], c.x, a0);
-                    a1 = __builtin_fmaf(r.w[q], c.y, a1);
-                    a2 = __builtin_fmaf(r.w[q], c.z, a2);
-                    a3 = __builtin_fmaf(r.w[q], c.w, a3);
+                    const float4 cv = *reinterpret_cast<const float4*>(crow + q * GF_TJ);
+                    a0 = __builtin_fmaf(r.w[q], cv.x, a0);
+                    a1 = __builtin_fmaf(r.w[q], cv.y, a1);
+                    a2 = __builtin_fmaf(r.w[q], cv.z, a2);
+                    a3 = __builtin_fmaf(r.w[q], cv.w, a3);
                 }
                 acc[p][0] += (double)a0;
                 acc[p][1] += (double)a1;
@@ -157,6 +249,8 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
                 acc[p][3] += (double)a3;
             }
         }
+        if (more) store(c + 1, (c + 1) & 1);
+        __syncthreads();
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -362,17 +456,26 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TS>
-static hipError_t gather_fwd_t(const Plan& p, const void* x, const void* C, const void* W,
-                               float* y, hipStream_t s) {
-    const size_t lds = (size_t)(GF_IC * p.K * GF_TJ + GF_IC * GF_TJ) * 4 + GF_IC * GF_TB * sizeof(Rec);
+template <typename TS, int MAXQ>
+static hipError_t gather_fwd_run(const Plan& p, const void* x, const void* C, const void* W, float* y,
+                                 hipStream_t s) {
+    const size_t lds = (size_t)2 * gather_fwd_buf_floats(p.K) * 4;   // two chunk buffers
     dim3 grid((unsigned)((p.N + GF_TB - 1) / GF_TB), (unsigned)((p.O + GF_TJ - 1) / GF_TJ));
-    hipError_t e = allow_lds(gather_fwd_kernel<TS>, lds);
+    hipError_t e = allow_lds(gather_fwd_kernel<TS, MAXQ>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_fwd_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+    hipLaunchKernelGGL((gather_fwd_kernel<TS, MAXQ>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
                        (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
                        static_cast<const TS*>(W), y);
     return hipGetLastError();
+}
+
+// prefetch registers per thread: ceil(64 IC K / 256) coefficients
+template <typename TS>
+static hipError_t gather_fwd_t(const Plan& p, const void* x, const void* C, const void* W,
+                               float* y, hipStream_t s) {
+    const int nq = (gather_fwd_ic(p.K) * p.K * GF_TJ + 255) / 256;
+    if (nq <= 20) return gather_fwd_run<TS, 20>(p, x, C, W, y, s);
+    return gather_fwd_run<TS, 32>(p, x, C, W, y, s);
 }
 
 template <typename TS>
