@@ -146,10 +146,11 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
     const int b0 = blockIdx.x * GF_TB, j0 = blockIdx.y * GF_TJ;
     const int nch = (I + IC - 1) / IC;
 
-    // this thread's coefficient loads: elements e = t + 256 q of the chunk,
-    // e = jj * ICK + rem (rem = ii * K + m, contiguous in C for one output)
-    const int jC0 = t / ICK, rC0 = t % ICK, dj = 256 / ICK, dr = 256 % ICK;
-    const int nq = (csz + 255) / 256;                // <= MAXQ
+    // this thread's coefficient loads: output jc = t / 4 of the tile, and of
+    // that output's ICK chunk coefficients (rem = ii * K + m, contiguous in
+    // C) those with rem = t % 4 + 4 q
+    const int jc = t >> 2, rc = t & 3;
+    const int nq = (ICK + 3) / 4;                    // <= MAXQ
     // W_base and x: the 64 IC (output or row, input) pairs of a chunk, pair
     // u = t + 256 v (v < 2, as IC <= 7) at pair index pj = u / IC, pi = u % IC
     int pj[2], pi[2];
@@ -162,28 +163,28 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         pi[v] = u % IC;
     }
 
+    // Loads are issued unconditionally from addresses clamped in bounds (a
+    // guarded load into a register that was zeroed first makes the compiler
+    // wait for every earlier load); invalid values are zeroed when stored.
     float cp[MAXQ];
-    float wp[2] = {0.0f, 0.0f}, xp[2] = {0.0f, 0.0f};
+    float wp[2], xp[2];
+    const bool jc_ok = j0 + jc < O;
     auto load = [&](int c) {
         const int i0 = c * IC, nic = min(IC, I - i0);
-        int jj = jC0, rem = rC0;
+        // row of output j0 + jc from input i0 on (output 0 when the output
+        // does not exist); indices past the chunk's last input are clamped
+        const TS* row = C + (jc_ok ? ((int64_t)(j0 + jc) * I + i0) * K : 0);
+        const int last = jc_ok ? nic * K - 1 : 0;
 #pragma unroll
-        for (int q = 0; q < MAXQ; ++q) {
-            if (q < nq) {
-                const int j = j0 + jj;
-                cp[q] = (jj < GF_TJ && j < O && rem < nic * K)
-                            ? load_f(C, ((int64_t)j * I + i0) * K + rem) : 0.0f;
-                jj += dj;
-                rem += dr;
-                if (rem >= ICK) rem -= ICK, ++jj;
-            }
-        }
+        for (int q = 0; q < MAXQ; ++q)
+            if (q < nq) cp[q] = load_f(row, min(rc + 4 * q, last));
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-            wp[v] = (has_pair[v] && base && j0 + pj[v] < O && pi[v] < nic)
-                        ? load_f(W, (int64_t)(j0 + pj[v]) * I + i0 + pi[v]) : 0.0f;
-            xp[v] = (has_pair[v] && b0 + pj[v] < N && pi[v] < nic)
-                        ? load_f(x, (int64_t)(b0 + pj[v]) * I + i0 + pi[v]) : 0.0f;
+            const bool okw = has_pair[v] && base && j0 + pj[v] < O && pi[v] < nic;
+            const bool okx = has_pair[v] && b0 + pj[v] < N && pi[v] < nic;
+            wp[v] = load_f(W ? W : x, okw ? (int64_t)(j0 + pj[v]) * I + i0 + pi[v] : 0);
+            xp[v] = load_f(x, okx ? (int64_t)(b0 + pj[v]) * I + i0 + pi[v] : 0);
+            wp[v] = okw ? wp[v] : 0.0f;
         }
     };
     auto store = [&](int c, int buf) {
@@ -191,15 +192,11 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         float* Ws = Cs + csz;
         RecF* Rs = reinterpret_cast<RecF*>(Ws + wsz);
         const int i0 = c * IC, nic = min(IC, I - i0);
-        int jj = jC0, rem = rC0;
+        const int lim = jc_ok ? nic * K : 0;         // valid coefficients of this output
 #pragma unroll
         for (int q = 0; q < MAXQ; ++q) {
-            if (q < nq) {
-                if (jj < GF_TJ) Cs[rem * GF_TJ + jj] = cp[q];
-                jj += dj;
-                rem += dr;
-                if (rem >= ICK) rem -= ICK, ++jj;
-            }
+            const int rem = rc + 4 * q;
+            if (q < nq && rem < ICK) Cs[rem * GF_TJ + jc] = rem < lim ? cp[q] : 0.0f;
         }
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
