@@ -230,15 +230,19 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const RecF r = Rs[ii * GF_TB + rq + 16 * p];
-                float a0 = r.base * wv.x, a1 = r.base * wv.y, a2 = r.base * wv.z, a3 = r.base * wv.w;
                 const float* crow = Cs + r.cb + 4 * jq;
+                // the row's four coefficient reads go out together, ahead of
+                // the FMAs that use them
+                float4 cv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cv[q] = *reinterpret_cast<const float4*>(crow + q * GF_TJ);
+                float a0 = r.base * wv.x, a1 = r.base * wv.y, a2 = r.base * wv.z, a3 = r.base * wv.w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 cv = *reinterpret_cast<const float4*>(crow + q * GF_TJ);
-                    a0 = __builtin_fmaf(r.w[q], cv.x, a0);
-                    a1 = __builtin_fmaf(r.w[q], cv.y, a1);
-                    a2 = __builtin_fmaf(r.w[q], cv.z, a2);
-                    a3 = __builtin_fmaf(r.w[q], cv.w, a3);
+                    a0 = __builtin_fmaf(r.w[q], cv[q].x, a0);
+                    a1 = __builtin_fmaf(r.w[q], cv[q].y, a1);
+                    a2 = __builtin_fmaf(r.w[q], cv[q].z, a2);
+                    a3 = __builtin_fmaf(r.w[q], cv[q].w, a3);
                 }
                 acc[p][0] += (double)a0;
                 acc[p][1] += (double)a1;
