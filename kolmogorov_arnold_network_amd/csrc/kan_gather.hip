@@ -227,9 +227,12 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         const int nic = min(IC, I - c * IC);
         for (int ii = 0; ii < nic; ++ii) {
             const float4 wv = *reinterpret_cast<const float4*>(&Ws[ii * GF_TJ + 4 * jq]);
+            RecF rr[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) rr[p] = Rs[ii * GF_TB + rq + 16 * p];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const RecF r = Rs[ii * GF_TB + rq + 16 * p];
+                const RecF& r = rr[p];
                 const float* crow = Cs + r.cb + 4 * jq;
                 // the row's four coefficient reads go out together, ahead of
                 // the FMAs that use them
