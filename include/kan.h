@@ -27,7 +27,8 @@
  *   fastest; W_base [O, I]; y, dy [N, O]; dx [N, I]; dC [O, I, G+3];
  *   dW_base [O, I].
  * - x, C and W_base share one storage dtype (KAN_F32 or KAN_BF16); y, dy, dx,
- *   dC and dW_base are always float32.  Arithmetic accumulates in float32.
+ *   dC and dW_base are always float32.  Arithmetic accumulates in float32 (the
+ *   float32 gather forward adds its per-input partials in float64).
  * - Tensor pointers are DEVICE pointers, 16-byte aligned.  `desc` and `grid`
  *   are HOST pointers, read during the call only.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
@@ -103,7 +104,7 @@ typedef struct {
     int32_t dtype;     /* kan_dtype_t: storage of x, C, W_base */
     int32_t has_base;  /* 0 or 1 */
     int32_t variant;   /* kan_variant_t */
-    int32_t flags;     /* 0 or KAN_FLAG_PREPARED */
+    int32_t flags;     /* 0, or KAN_FLAG_PREPARED and/or KAN_FLAG_DENSE_FORWARD */
 } kan_desc_t;
 
 /* The workspace already holds this pass's packed operands, written by
@@ -130,15 +131,20 @@ int kan_abi_version(void);
 /* Static description of a status code (never NULL). */
 const char* kan_status_string(int status);
 
-/* Bytes of workspace a pass needs (0 if none; SIZE_MAX if `desc` is invalid).
- * `pass` is kan_pass_t. */
+/* Bytes of workspace a pass needs (0 when the pass runs on GATHER; SIZE_MAX
+ * if `desc` is invalid).  `pass` is kan_pass_t.  Besides the packed operands
+ * of kan_prepare it holds, for a contraction with too few output tiles to fill
+ * the GPU, the float32 partial outputs of its k-range slices (the forward's
+ * y, dC and dW_base over batch slices), which are added in slice order. */
 size_t kan_workspace_size(const kan_desc_t* desc, int pass);
 
-/* Packs what a pass reads into the workspace: for the MFMA variant the
+/* Packs what a pass reads into the workspace: for a pass on MFMA the
  * coefficient operand C' = [C | W_base] per input, zero-padded to the tile
- * grid (forward: [O][I*(G+3+has_base)]; backward: its transpose), and for the
- * backward pass also dy rounded to the storage dtype in both orientations.
- * dy may be NULL for the forward pass.  A no-op for the GATHER variant. */
+ * grid (forward: [O][I*(G+3+has_base)], or the structured-sparse column order
+ * described at KAN_FLAG_DENSE_FORWARD; backward: the transpose of the dense
+ * form), and for the backward pass also dy rounded to the storage dtype in
+ * both orientations.  dy may be NULL for the forward pass.  A no-op for a
+ * pass on GATHER. */
 int kan_prepare(const kan_desc_t* desc, int pass, const void* C, const void* W_base,
                 const float* dy, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -151,7 +157,9 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
  * [O, I] are float32 outputs; each may be NULL to skip it (dW_base must be
  * NULL when has_base == 0).  dC and dW_base are sums over all N rows, reduced
  * in a fixed order without atomics (FlashKAT abstract: atomic gradient
- * accumulation is what slows the backward pass). */
+ * accumulation is what slows the backward pass); when there are too few
+ * output tiles, over fixed batch slices whose partial sums are then added in
+ * slice order. */
 int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
                  const float* dy, float* dx, float* dC, float* dW_base,
                  void* workspace, size_t workspace_bytes, void* stream);
