@@ -172,6 +172,20 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
 int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
                    float* B, float* dB, void* stream);
 
+/* The same dense B and dB from the truncated-power form instead (FlashKAN
+ * project page: each cubic B-spline is a combination of five shifted
+ * (x)_+^3 terms, with the normalised coordinate clamped to [0, k+1]):
+ * u = (x[k] - t_m) / h clamped to [0, 4],
+ *     B_m = (u^3 - 4 (u-1)_+^3 + 6 (u-2)_+^3 - 4 (u-3)_+^3) / 6,
+ *     dB_m/dx = (u^2 - 4 (u-1)_+^2 + 6 (u-2)_+^2 - 4 (u-3)_+^2) / (2 h).
+ * Every (k, m) is evaluated on its own, with no span lookup.  The alternating
+ * sum cancels near u = 4, so in float32 it is less accurate than
+ * kan_basis_eval (absolute error up to ~1e-5, and values may round slightly
+ * below 0, where the local form cannot; InKAN page, "Why InKAN?").  Arguments,
+ * validation and errors as for kan_basis_eval. */
+int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
+                      float* B, float* dB, void* stream);
+
 /* float32 -> bfloat16, round to nearest even (NaN stays NaN).  n elements;
  * `out` receives the 16-bit patterns.  Used between bf16 layers, where a
  * float32 layer output becomes the next layer's bf16 input. */

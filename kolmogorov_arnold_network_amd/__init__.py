@@ -9,9 +9,10 @@ package binds that ABI (``functional``) and wraps it as torch modules
 """
 
 from . import _lib
-from .functional import (kan_forward, kan_backward, kan_prepare, kan_basis_eval,
+from .functional import (kan_forward, kan_backward, kan_prepare, kan_basis_eval, kan_basis_eval_tp,
                          kan_cast_f32_to_bf16, kan_workspace_size, layer_desc, workspace)
 from .modules import KANLayer, KANNetwork, KANFunction
 
-__all__ = ["kan_forward", "kan_backward", "kan_prepare", "kan_basis_eval", "kan_cast_f32_to_bf16",
+__all__ = ["kan_forward", "kan_backward", "kan_prepare", "kan_basis_eval", "kan_basis_eval_tp",
+           "kan_cast_f32_to_bf16",
            "kan_workspace_size", "layer_desc", "workspace", "KANLayer", "KANNetwork", "KANFunction"]

@@ -37,7 +37,7 @@ ABI_VERSION = 1
 
 # every symbol include/kan.h declares
 EXPORTS = ("kan_abi_version", "kan_status_string", "kan_workspace_size", "kan_prepare",
-           "kan_forward", "kan_backward", "kan_basis_eval", "kan_cast_f32_to_bf16")
+           "kan_forward", "kan_backward", "kan_basis_eval", "kan_basis_eval_tp", "kan_cast_f32_to_bf16")
 
 
 class kan_grid_t(ctypes.Structure):
@@ -86,8 +86,9 @@ def lib():
     L.kan_forward.argtypes = [P(kan_desc_t), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     L.kan_backward.restype = ctypes.c_int
     L.kan_backward.argtypes = [P(kan_desc_t), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-    L.kan_basis_eval.restype = ctypes.c_int
-    L.kan_basis_eval.argtypes = [P(kan_grid_t), _i64, ctypes.c_int, _vp, _vp, _vp, _vp]
+    for f in (L.kan_basis_eval, L.kan_basis_eval_tp):
+        f.restype = ctypes.c_int
+        f.argtypes = [P(kan_grid_t), _i64, ctypes.c_int, _vp, _vp, _vp, _vp]
     L.kan_cast_f32_to_bf16.restype = ctypes.c_int
     L.kan_cast_f32_to_bf16.argtypes = [_vp, _vp, _i64, _vp]
     if L.kan_abi_version() != ABI_VERSION:

@@ -324,8 +324,8 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
     return status_of(e);
 }
 
-int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
-                   float* dB, void* stream) {
+static int basis_eval_impl(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
+                           float* dB, bool truncated_power, void* stream) {
     if (!grid) return KAN_ERR_NULL;
     kan_desc_t d;
     memset(&d, 0, sizeof(d));
@@ -345,7 +345,17 @@ int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, 
     const Range rx{x, (size_t)n * p.esize}, rb{B, ob}, rd{dB, ob};
     if (overlap(rx, rb) || overlap(rx, rd) || overlap(rb, rd)) return KAN_ERR_ALIAS;
     (void)hipGetLastError();
-    return status_of(launch_basis_eval(p.gk, n, dtype, x, B, dB, (hipStream_t)stream));
+    return status_of(launch_basis_eval(p.gk, n, dtype, x, B, dB, truncated_power, (hipStream_t)stream));
+}
+
+int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
+                   float* dB, void* stream) {
+    return basis_eval_impl(grid, n, dtype, x, B, dB, false, stream);
+}
+
+int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
+                      float* dB, void* stream) {
+    return basis_eval_impl(grid, n, dtype, x, B, dB, true, stream);
 }
 
 int kan_cast_f32_to_bf16(const float* in, void* out, int64_t n, void* stream) {

@@ -65,6 +65,23 @@ __device__ __forceinline__ void pieces_fast(float u, float& b0, float& b1, float
     b2 = __builtin_fmaf(w2, __builtin_fmaf(0.5f, w, -1.0f), t3);
 }
 
+// Truncated-power form of one basis function (FlashKAN project page: five
+// shifted (x)_+^3 terms with the normalised coordinate clamped to [0, k+1]):
+// u = (x - t_m) / h clamped to [0, 4], and
+//   B_m = (u^3 - 4 (u-1)_+^3 + 6 (u-2)_+^3 - 4 (u-3)_+^3) / 6
+//   B'_m = (u^2 - 4 (u-1)_+^2 + 6 (u-2)_+^2 - 4 (u-3)_+^2) / 2 * (1/h),
+// the fifth term (u-4)_+ being 0 under the clamp.  Needs no span, but the
+// alternating sum cancels: near u = 4 terms of size 64 leave a result near 0,
+// so float32 loses up to ~1e-5 and may round below 0.
+__device__ __forceinline__ void tp_basis(float u, float scale, float& b, float& d) {
+    u = __builtin_fminf(__builtin_fmaxf(u, 0.0f), 4.0f);
+    const float p1 = __builtin_fmaxf(u - 1.0f, 0.0f), p2 = __builtin_fmaxf(u - 2.0f, 0.0f),
+                p3 = __builtin_fmaxf(u - 3.0f, 0.0f);
+    const float q0 = u * u, q1 = p1 * p1, q2 = p2 * p2, q3 = p3 * p3;
+    b = (q0 * u - 4.0f * (q1 * p1) + 6.0f * (q2 * p2) - 4.0f * (q3 * p3)) * (1.0f / 6.0f);
+    d = (q0 - 4.0f * q1 + 6.0f * q2 - 4.0f * q3) * (0.5f * scale);
+}
+
 // d/dx of the same pieces: (db/du) * (du/dx), du/dx = 1/h = scale.
 __device__ __forceinline__ void dpieces(float u, float scale, float& d0, float& d1, float& d2,
                                         float& d3) {

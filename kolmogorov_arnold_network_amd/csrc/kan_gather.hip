@@ -42,26 +42,33 @@ __device__ __forceinline__ Rec make_rec(float xv, const GridK& g) {
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // ---------------------------------------------------------------------------
-// Standalone basis: dense B[k, m] and dB[k, m] from the local pieces.
-template <typename TS>
+// Standalone basis: dense B[k, m] and dB[k, m], one element per thread (m
+// fastest, so the stores are contiguous; n K < 2^31 is checked by the
+// caller).  Local form (TP false): the span and the 4 pieces of x[k], element
+// m taking piece m - (s - 3) or 0.  Truncated-power form (TP true): every
+// element on its own from u = (x[k] - t_m) / h, with no span.
+template <typename TS, bool TP>
 __global__ void basis_eval_kernel(GridK g, int64_t n, const TS* __restrict__ x,
                                   float* __restrict__ B, float* __restrict__ dB) {
     const int K = g.G + 3;
-    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
-         k += (int64_t)gridDim.x * blockDim.x) {
+    const int total = (int)(n * K);
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
+        const int k = e / K, m = e - k * K;
         const float xv = load_f(x, k);
-        float u;
-        const int s = span_u(xv, g, u);
-        float b[4], d[4];
-        pieces(u, b[0], b[1], b[2], b[3]);
-        dpieces(u, g.scale, d[0], d[1], d[2], d[3]);
-        for (int m = 0; m < K; ++m) {
-            const int r = m - (s - 3);
-            const bool in = r >= 0 && r < 4;
-            const int rr = clampi(r, 0, 3);
-            if (B) B[k * K + m] = in ? b[rr] : 0.0f;
-            if (dB) dB[k * K + m] = in ? d[rr] : 0.0f;
+        float b, d;
+        if constexpr (TP) {
+            tp_basis(__builtin_fmaf(xv, g.scale, g.shift - (float)m), g.scale, b, d);
+        } else {
+            float u;
+            const int r = m - (span_u(xv, g, u) - 3);
+            float p[4], q[4];
+            pieces(u, p[0], p[1], p[2], p[3]);
+            dpieces(u, g.scale, q[0], q[1], q[2], q[3]);
+            b = r == 0 ? p[0] : r == 1 ? p[1] : r == 2 ? p[2] : r == 3 ? p[3] : 0.0f;
+            d = r == 0 ? q[0] : r == 1 ? q[1] : r == 2 ? q[2] : r == 3 ? q[3] : 0.0f;
         }
+        if (B) B[e] = b;
+        if (dB) dB[e] = d;
     }
 }
 
@@ -439,13 +446,15 @@ hipError_t allow_lds(Kern k, size_t bytes) {
 }  // namespace
 
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
-                             float* dB, hipStream_t s) {
-    if (dtype == KAN_F32)
-        hipLaunchKernelGGL(basis_eval_kernel<float>, dim3(grid1d(n)), dim3(256), 0, s, g, n,
-                           static_cast<const float*>(x), B, dB);
-    else
-        hipLaunchKernelGGL(basis_eval_kernel<uint16_t>, dim3(grid1d(n)), dim3(256), 0, s, g, n,
-                           static_cast<const uint16_t*>(x), B, dB);
+                             float* dB, bool truncated_power, hipStream_t s) {
+    const dim3 grid(grid1d(n * (g.G + 3))), block(256);
+    if (dtype == KAN_F32) {
+        auto k = truncated_power ? basis_eval_kernel<float, true> : basis_eval_kernel<float, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, s, g, n, static_cast<const float*>(x), B, dB);
+    } else {
+        auto k = truncated_power ? basis_eval_kernel<uint16_t, true> : basis_eval_kernel<uint16_t, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, s, g, n, static_cast<const uint16_t*>(x), B, dB);
+    }
     return hipGetLastError();
 }
 

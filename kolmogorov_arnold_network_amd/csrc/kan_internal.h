@@ -69,7 +69,7 @@ int make_plan(const kan_desc_t* desc, Plan* p);
 
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
-                             float* dB, hipStream_t s);
+                             float* dB, bool truncated_power, hipStream_t s);
 hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

@@ -215,18 +215,24 @@ def test_prepare_checks(L):
     assert lib.kan_prepare(ctypes.byref(d), 0, C, W, None, C, 1 << 30, None) == L.KAN_ERR_ALIAS
 
 
-def test_basis_and_cast_checks(L):
-    lib = L.lib()
+@pytest.mark.parametrize("fn", ["kan_basis_eval", "kan_basis_eval_tp"])
+def test_basis_checks(L, fn):
+    f = getattr(L.lib(), fn)
     g = L.kan_grid_t(-1.0, 1.0, 8, 3)
-    assert lib.kan_basis_eval(None, 4, 0, X, Y, DY, None) == L.KAN_ERR_NULL
-    assert lib.kan_basis_eval(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 0, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
-    assert lib.kan_basis_eval(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 1)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
-    assert lib.kan_basis_eval(ctypes.byref(g), -1, 0, X, Y, None, None) == L.KAN_ERR_SHAPE
-    assert lib.kan_basis_eval(ctypes.byref(g), 0, 0, X, Y, None, None) == L.KAN_OK
-    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X, None, None, None) == L.KAN_ERR_NULL
-    assert lib.kan_basis_eval(ctypes.byref(g), 4, 3, X, Y, None, None) == L.KAN_ERR_DTYPE
-    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X + 4, Y, None, None) == L.KAN_ERR_ALIGN
-    assert lib.kan_basis_eval(ctypes.byref(g), 4, 0, X, X, None, None) == L.KAN_ERR_ALIAS
+    assert f(None, 4, 0, X, Y, DY, None) == L.KAN_ERR_NULL
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 0, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 126, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 1)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(g), -1, 0, X, Y, None, None) == L.KAN_ERR_SHAPE
+    assert f(ctypes.byref(g), 0, 0, X, Y, None, None) == L.KAN_OK
+    assert f(ctypes.byref(g), 4, 0, X, None, None, None) == L.KAN_ERR_NULL
+    assert f(ctypes.byref(g), 4, 3, X, Y, None, None) == L.KAN_ERR_DTYPE
+    assert f(ctypes.byref(g), 4, 0, X + 4, Y, None, None) == L.KAN_ERR_ALIGN
+    assert f(ctypes.byref(g), 4, 0, X, X, None, None) == L.KAN_ERR_ALIAS
+
+
+def test_cast_checks(L):
+    lib = L.lib()
     assert lib.kan_cast_f32_to_bf16(X, Y, -1, None) == L.KAN_ERR_SHAPE
     assert lib.kan_cast_f32_to_bf16(X, Y, 0, None) == L.KAN_OK
     assert lib.kan_cast_f32_to_bf16(None, Y, 4, None) == L.KAN_ERR_NULL

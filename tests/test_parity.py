@@ -74,6 +74,46 @@ def test_basis_kernel(F, G, dtype):
     assert np.max(np.abs(dB - dref)) <= tol * 4 * (G / (hi - lo))
 
 
+# Truncated-power form (FlashKAN page): (u^3 - 4 (u-1)_+^3 + 6 (u-2)_+^3 -
+# 4 (u-3)_+^3) / 6 with u clamped to [0, 4].  Error bound in float32: the
+# four terms' magnitudes sum to at most (64 + 4*27 + 6*8 + 4) / 6 = 37.3,
+# each carrying ~2 roundings, and the three partial sums (<= 64) one each:
+# ~107 ulp of 1, 6.4e-6 -> tolerance 1e-5.  The derivative in units of 1/h:
+# (16 + 4*9 + 6*4 + 4) / 2 = 40 and partial sums <= 16: ~64 ulp, 3.8e-6.
+TP_TOL = 1e-5
+
+
+@pytest.mark.parametrize("G", [1, 5, 8, 20, 50])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_basis_truncated_power(F, G, dtype):
+    lo, hi = -1.0, 1.0
+    h = (hi - lo) / G
+    rng = np.random.default_rng(100 + G)
+    x = np.concatenate([rng.uniform(lo - 4 * h, hi + 4 * h, 200000),
+                        lo + (np.arange(G + 7) - 3) * h, [lo, hi, 0.0, lo - 1e-7, hi + 1e-7, -50.0, 50.0]])
+    x = x.astype(np.float32)
+    if dtype == "bf16":
+        x = wl.to_bf16_values(x)
+    say("truncated-power basis G=%d dtype=%s n=%d" % (G, dtype, x.size))
+    xt = to_dev(x, dtype)
+    B, dB = F.kan_basis_eval_tp(xt, (lo, hi, G))
+    Bl, _ = F.kan_basis_eval(xt, (lo, hi, G), need_dB=False)
+    _sync()
+    B, dB, Bl = _np(B), _np(dB), _np(Bl)
+    ref = oracle.basis(x.astype(np.float64), lo, hi, G)
+    dref = oracle.basis_derivative(x.astype(np.float64), lo, hi, G)
+    e, el = np.max(np.abs(B - ref)), np.max(np.abs(Bl - ref))
+    ed = np.max(np.abs(dB - dref)) * h
+    say("  max |B - B_exact|: truncated power %.2e, local span %.2e; min B %.2e; "
+        "max |dB - dB_exact| h %.2e" % (e, el, B.min(), ed))
+    assert e <= TP_TOL and ed <= TP_TOL
+    # exactly zero beyond the extended grid and far outside it (the test in
+    # float64: the float32 knot t_{G+6} may lie just inside the grid)
+    xd = x.astype(np.float64)
+    far = (xd < lo - 3 * h) | (xd >= hi + 3 * h)
+    assert np.all(B[far] == 0.0) and np.all(dB[far] == 0.0)
+
+
 # ---------------------------------------------------------------------------
 # small ragged layers, every variant, in full
 SMALL = [  # N, I, O, G, base
