@@ -12,6 +12,7 @@ Contents
 ``layer``    single KAN layer forward / backward, two-layer networks,
              sampled gradients for large shapes.
 ``bf16``     round-to-nearest-even cast of float32 to bfloat16.
+``grouped``  per-channel (grouped) spline activation forward / backward.
 
 Every function cites the passage of the pages it follows.  Pinned by the
 ``-m "not gpu"`` tests in ``tests/test_oracle.py``; there is no function here
@@ -23,10 +24,12 @@ from .layer import (silu, silu_prime, layer_forward, layer_backward,
                     layer_forward_rows, layer_backward_rows,
                     coef_grad_pairs, network_forward, network_backward)
 from .bf16 import round_bf16
+from .grouped import group_of, grouped_forward, grouped_backward
 
 __all__ = [
     "knots", "cox_de_boor", "basis", "basis_derivative", "n_basis",
     "silu", "silu_prime", "layer_forward", "layer_backward",
     "layer_forward_rows", "layer_backward_rows", "coef_grad_pairs",
     "network_forward", "network_backward", "round_bf16",
+    "group_of", "grouped_forward", "grouped_backward",
 ]
