@@ -8,7 +8,10 @@ before timing starts.  Prints one JSON line.
 
 Default workload: one layer 4096 -> 4096, 65536 rows, G = 20 cubic, bf16 x /
 C / W_base, float32 accumulation, silu base branch.  Other workloads:
-``--workload c1 .. c5`` (c2 and c4 are two-layer chains).
+``--workload c1 .. c5`` (c2 and c4 are two-layer chains), and ``g1`` / ``g2``,
+the grouped spline activation (one spline per group of channels): a step is
+its forward and its backward (dx, and dC reduced over every row), and the
+line reports elements/s against the HBM roofline.
 """
 
 import argparse
@@ -32,7 +35,14 @@ WORKLOAD_TEXT = {
           "x/C/W_base, fp32 accumulate, silu base branch",
     "c5": "KAN layer 4096->4096, 65536 rows, G=20 cubic on [-1,1], bf16 x/C/W_base, fp32 "
           "accumulate, silu base branch",
+    "g1": "grouped spline activation, 25216 rows (128 x 197 tokens) x 3072 channels, 8 groups, "
+          "G=5 cubic on [-1,1], bf16 x/C, fp32 y/dx/dC",
+    "g2": "per-channel spline activation, 32768 rows (8 x 4096 tokens) x 2048 channels, 2048 "
+          "groups, G=8 cubic on [-1,1], bf16 x/C, fp32 y/dx/dC",
 }
+GROUPED_METRIC = "grouped spline activation fwd+bwd elements/sec; % of HBM roofline, 1 GPU"
+MFMA_FILES = ("kan_mfma.hip", "kan_device.h", "kan_sparse.h", "kan_internal.h", "kan_api.cpp")
+GROUPED_FILES = ("kan_grouped.hip", "kan_device.h", "kan_internal.h", "kan_api.cpp")
 
 
 def parse():
@@ -45,7 +55,7 @@ def parse():
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None)
-    ap.add_argument("--code-digest", action="store_true",
+    ap.add_argument("--code-digest", nargs="?", const="mfma", default=None, choices=["mfma", "grouped"],
                     help="print the digest that ties a counter summary to the kernel source")
     ap.add_argument("--basis-forms", type=int, default=0, metavar="POINTS",
                     help="time the local-span and truncated-power basis evaluations on POINTS inputs")
@@ -113,7 +123,7 @@ def stage_names(nl):
 def main():
     args = parse()
     if args.code_digest:
-        print(kernel_code_digest())
+        print(kernel_code_digest(GROUPED_FILES if args.code_digest == "grouped" else MFMA_FILES))
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -127,6 +137,9 @@ def main():
               "dW_base); run with "
               "--gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("g"):
+        grouped_bench(args)
+        return
 
     import numpy as np
     import torch
@@ -299,20 +312,155 @@ def main():
     print(json.dumps(out))
 
 
-def kernel_code_digest():
-    """sha256 of the contraction kernels' source (the kernel file, the headers
-    it includes and the launch planner) with // comments and blank lines
+def grouped_bench(args):
+    """Forward and backward of the grouped spline activation, timed per stage
+    with HIP events on the launch stream."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from kolmogorov_arnold_network_amd import _lib as L
+    from kolmogorov_arnold_network_amd import functional as F
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.make_grouped(args.workload)
+    N, I, groups, G = d["N"], d["I"], d["groups"], d["G"]
+    K = G + 3
+    tdt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+    es = 2 if d["dtype"] == "bf16" else 4
+    x = torch.from_numpy(d["x"]).to(dev).to(tdt)
+    C = torch.from_numpy(d["C"]).to(dev).to(tdt)
+    dy = torch.from_numpy(d["dy"]).to(dev)
+    y = torch.empty((N, I), dtype=torch.float32, device=dev)
+    dx = torch.empty((N, I), dtype=torch.float32, device=dev)
+    dC = torch.empty((groups, K), dtype=torch.float32, device=dev)
+    desc = F.group_desc(x, C, (d["lo"], d["hi"], G))
+    nws = F.kan_group_workspace_size(desc)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    lib = L.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    S = ctypes.c_void_p(stream.cuda_stream)
+    names = ["group.fwd", "group.bwd"]
+    events = None
+
+    def rec(k):
+        if events is not None:
+            events[k].record(stream)
+
+    def step():
+        rec(0)
+        L.check(lib.kan_group_forward(ctypes.byref(desc), P(x), P(C), P(y), S), "group forward")
+        rec(1)
+        L.check(lib.kan_group_backward(ctypes.byref(desc), P(x), P(C), P(dy), P(dx), P(dC), P(ws), nws, S),
+                "group backward")
+        rec(2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_step = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        per_step.append(events)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {nm: sum(ev[k].elapsed_time(ev[k + 1]) for ev in per_step) / args.steps
+                for k, nm in enumerate(names)}
+    ms_per_step = 1e3 * elapsed / args.steps
+    step_ms = sorted(ev[0].elapsed_time(ev[2]) for ev in per_step)
+    median_ms = step_ms[len(step_ms) // 2]
+    # algorithmic HBM bytes: every element of x read once and y written once
+    # (forward); x and dy read and dx written once (backward); C once, dC once
+    alg = {"group.fwd": N * I * (es + 4) + groups * K * es,
+           "group.bwd": N * I * (es + 4 + 4) + groups * K * (es + 4)}
+    dom = max(names, key=lambda nm: stage_ms[nm])
+    achieved = alg[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(args.workload, dom.replace(".", "_"),
+                                                                     GROUPED_FILES),
+            "algorithmic_bytes": alg[dom], "dominant_ms": stage_ms[dom],
+            "stage_GBps": {nm: alg[nm] / (stage_ms[nm] * 1e-3) / 1e9 for nm in names}}
+    out = {
+        "metric": GROUPED_METRIC,
+        "value": N * I * 1e3 / ms_per_step,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "median_ms_per_step": median_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": d["dtype"],
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "rows": N,
+                   "channels": I, "groups": groups, "G": G},
+        "stage_ms": stage_ms,
+        "workspace_bytes": nws,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = grouped_cpu_baseline(d, args.cpu_rows)
+    print(json.dumps(out))
+
+
+def grouped_cpu_baseline(d, rows=None):
+    """The float64 NumPy oracle of the grouped activation on a bounded sample
+    of rows: y, dx and the rows' own dC contributions, timed on the host."""
+    import oracle
+    import workloads as wl
+    N, I = d["N"], d["I"]
+    n = min(N, rows or 2048)
+    R = wl.sample_indices(N, n, 98)
+    x, dy = d["x"][R].astype("float64"), d["dy"][R].astype("float64")
+    t0 = time.perf_counter()
+    oracle.grouped_forward(x, d["C"], d["lo"], d["hi"], d["G"])
+    oracle.grouped_backward(x, d["C"], dy, d["lo"], d["hi"], d["G"])
+    dt = time.perf_counter() - t0
+    return {"value": n * I / dt, "unit": "elements/s", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": "%d of %d rows (%d elements): forward, dx and the rows' own dC contributions "
+                      "in float64 NumPy, %.1f s; CPU %s" % (n, N, n * I, dt, _cpu_model())}
+
+
+def _cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def kernel_code_digest(files=MFMA_FILES):
+    """sha256 of a kernel family's source (the kernel file, the headers it
+    includes and the launch planner) with // comments and blank lines
     removed: a counter summary stays valid across comment edits and goes stale
     with any change to the code."""
     import re
     csrc = os.path.join(ROOT, "kolmogorov_arnold_network_amd", "csrc")
     lines = []
-    for name in ("kan_mfma.hip", "kan_device.h", "kan_sparse.h", "kan_internal.h", "kan_api.cpp"):
+    for name in files:
         lines += [re.sub(r"//.*", "", l).rstrip() for l in open(os.path.join(csrc, name)).read().splitlines()]
     return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()
 
 
-def read_traffic(workload, kernel):
+def read_traffic(workload, kernel, files=MFMA_FILES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
@@ -323,7 +471,7 @@ def read_traffic(workload, kernel):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("code_sha256") != kernel_code_digest():
+    if kv.get("code_sha256") != kernel_code_digest(files):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -337,11 +485,7 @@ def cpu_baseline(d, rows=None):
     import numpy as np
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_threads()
     N = d["N"]
     default_rows = {"c1": 32, "c2": 1024, "c3": 1024, "c4": 1024, "c5": 2048}
     n = min(N, rows or default_rows[d["name"]])
@@ -352,14 +496,7 @@ def cpu_baseline(d, rows=None):
     acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf)
     oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G)
     dt = time.perf_counter() - t0
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    model = _cpu_model()
     return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d rows: forward and backward (dx, and the rows' own dC/dW_base "
                       "contributions) in float64 NumPy, %.1f s; CPU %s" % (n, N, dt, model)}

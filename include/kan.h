@@ -186,6 +186,45 @@ int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
 int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
                       float* B, float* dB, void* stream);
 
+/* ---- Grouped spline activation ------------------------------------------
+ * The element-wise form of the edge function: every channel of a row passes
+ * through one learned cubic B-spline, shared by a group of consecutive
+ * channels (InKAN project page: per-coordinate spline curves; FlashKAT
+ * abstract: grouped KAN activations, whose training is held back by the
+ * atomic accumulation of the coefficient gradient),
+ *
+ *     y[b, i]  = sum_m C[g(i), m] * B_m(x[b, i]),    g(i) = floor(i * groups / I),
+ *     dx[b, i] = dy[b, i] * sum_m C[g(i), m] * B'_m(x[b, i]),
+ *     dC[g, m] = sum_b sum_{i : g(i) = g} dy[b, i] * B_m(x[b, i]),
+ *
+ * with B_m the basis of the layer (grid as for kan_desc_t).  Layouts: x, y,
+ * dy, dx [N, I]; C, dC [groups, G+3], m fastest.  x and C in `dtype`; y, dy,
+ * dx and dC float32.  The conventions of the layer entry points hold
+ * (device pointers 16-byte aligned, outputs overwritten, no overlap,
+ * validation before any work, deterministic results). */
+typedef struct {
+    int64_t N;          /* rows, >= 0 */
+    int64_t I;          /* channels, >= 1 */
+    int32_t groups;     /* 1 <= groups <= I; groups == I: one spline per channel */
+    int32_t dtype;      /* kan_dtype_t: storage of x and C */
+    kan_grid_t grid;
+} kan_group_desc_t;
+
+/* Bytes of workspace kan_group_backward needs for dC (SIZE_MAX if `desc` is
+ * invalid): the per-channel sums of fixed chunks of rows, then their sum over
+ * the chunks, which the groups' channels are added from (no atomics). */
+size_t kan_group_workspace_size(const kan_group_desc_t* desc);
+
+/* Forward: y [N, I] float32. */
+int kan_group_forward(const kan_group_desc_t* desc, const void* x, const void* C, float* y,
+                      void* stream);
+
+/* Backward: dy [N, I] in; dx [N, I] and dC [groups, G+3] out, either may be
+ * NULL to skip it.  The workspace (256-byte aligned) is needed only with dC.
+ * N = 0 fills dC with zeros. */
+int kan_group_backward(const kan_group_desc_t* desc, const void* x, const void* C, const float* dy,
+                       float* dx, float* dC, void* workspace, size_t workspace_bytes, void* stream);
+
 /* float32 -> bfloat16, round to nearest even (NaN stays NaN).  n elements;
  * `out` receives the 16-bit patterns.  Used between bf16 layers, where a
  * float32 layer output becomes the next layer's bf16 input. */

@@ -11,7 +11,7 @@ INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libkan_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["kan_api.cpp", "kan_gather.hip", "kan_mfma.hip"]
+SOURCES = ["kan_api.cpp", "kan_gather.hip", "kan_grouped.hip", "kan_mfma.hip"]
 
 # -packed-fp32-ops off: the compiler must not form packed float32 ALU ops.
 HIPCC_FLAGS = [

@@ -358,6 +358,88 @@ int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* 
     return basis_eval_impl(grid, n, dtype, x, B, dB, true, stream);
 }
 
+// Validates a grouped activation; on success *gk and *K describe the grid.
+static int group_check(const kan_group_desc_t* d, GridK* gk, int* K, int* esize) {
+    if (!d) return KAN_ERR_NULL;
+    kan_desc_t ld;
+    memset(&ld, 0, sizeof(ld));
+    ld.N = 1;
+    ld.I = 1;
+    ld.O = 1;
+    ld.grid = d->grid;
+    ld.dtype = d->dtype;
+    Plan p;
+    int st = make_plan(&ld, &p);
+    if (st != KAN_OK) return st;
+    if (d->N < 0 || d->I < 1 || d->groups < 1 || d->groups > d->I) return KAN_ERR_SHAPE;
+    if (d->N > kIndexLimit || d->I > kIndexLimit) return KAN_ERR_SHAPE;
+    *gk = p.gk;
+    *K = p.K;
+    *esize = p.esize;
+    return KAN_OK;
+}
+
+size_t kan_group_workspace_size(const kan_group_desc_t* desc) {
+    GridK gk;
+    int K, es;
+    if (group_check(desc, &gk, &K, &es) != KAN_OK) return SIZE_MAX;
+    if (desc->N == 0) return 0;
+    const GroupPlan gp = grouped_plan(desc->N, desc->I, K);
+    return (size_t)round_up((gp.part_floats + gp.red_floats) * 4, 256);
+}
+
+int kan_group_forward(const kan_group_desc_t* desc, const void* x, const void* C, float* y,
+                      void* stream) {
+    GridK gk;
+    int K, es;
+    int st = group_check(desc, &gk, &K, &es);
+    if (st != KAN_OK) return st;
+    const int64_t NI = desc->N * desc->I;
+    if (!C || (NI > 0 && (!x || !y))) return KAN_ERR_NULL;
+    const void* ptrs[] = {x, C, y};
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    const Range out{y, (size_t)NI * 4};
+    if (overlap(out, Range{x, (size_t)NI * es}) || overlap(out, Range{C, (size_t)desc->groups * K * es}))
+        return KAN_ERR_ALIAS;
+    if (NI == 0) return KAN_OK;
+    (void)hipGetLastError();
+    return status_of(launch_grouped_fwd(gk, desc->N, desc->I, desc->groups, desc->dtype, x, C, y,
+                                        (hipStream_t)stream));
+}
+
+int kan_group_backward(const kan_group_desc_t* desc, const void* x, const void* C, const float* dy,
+                       float* dx, float* dC, void* ws, size_t ws_bytes, void* stream) {
+    GridK gk;
+    int K, es;
+    int st = group_check(desc, &gk, &K, &es);
+    if (st != KAN_OK) return st;
+    const int64_t N = desc->N, I = desc->I, NI = N * I;
+    if (!C || (N > 0 && (!x || !dy))) return KAN_ERR_NULL;
+    const void* ptrs[] = {x, C, dy, dx, dC};
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    const size_t need = dC ? kan_group_workspace_size(desc) : 0;
+    if (ws_bytes < need) return KAN_ERR_WORKSPACE;
+    if (need > 0 && !ws) return KAN_ERR_NULL;
+    if (need > 0 && !aligned(ws, 256)) return KAN_ERR_ALIGN;
+    const Range outs[] = {{dx, (size_t)NI * 4}, {dC, (size_t)desc->groups * K * 4}, {ws, need}};
+    const Range ins[] = {{x, (size_t)NI * es}, {C, (size_t)desc->groups * K * es}, {dy, (size_t)NI * 4}};
+    for (int a = 0; a < 3; ++a) {
+        for (const Range& r : ins)
+            if (overlap(outs[a], r)) return KAN_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlap(outs[a], outs[b])) return KAN_ERR_ALIAS;
+    }
+    if (!dx && !dC) return KAN_OK;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    float* part = static_cast<float*>(ws);
+    float* red = part ? part + grouped_plan(N > 0 ? N : 1, I, K).part_floats : nullptr;
+    return status_of(launch_grouped_bwd(gk, N, I, desc->groups, desc->dtype, x, C, dy, dx, dC, part,
+                                        red, s));
+}
+
 int kan_cast_f32_to_bf16(const float* in, void* out, int64_t n, void* stream) {
     if (n < 0) return KAN_ERR_SHAPE;
     if (n == 0) return KAN_OK;

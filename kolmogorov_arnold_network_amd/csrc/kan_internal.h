@@ -91,4 +91,19 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
 hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float* dC,
                           float* dW, hipStream_t s);
 
+// Grouped spline activation: blocks of 256 channels by chunks of rows.
+struct GroupPlan {
+    int64_t xb;                  // channel blocks: ceil(I / 256)
+    int64_t rows_fwd, gy_fwd;    // forward: rows per chunk, chunks
+    int64_t rows_bwd, gy_bwd;    // backward: rows per chunk, chunks (= partial sets of dC)
+    int64_t part_floats;         // gy_bwd * K * I: per-chunk partials of the per-channel dC
+    int64_t red_floats;          // K * I: partials summed over the chunks
+};
+GroupPlan grouped_plan(int64_t N, int64_t I, int K);
+hipError_t launch_grouped_fwd(const GridK& g, int64_t N, int64_t I, int groups, int dtype,
+                              const void* x, const void* C, float* y, hipStream_t s);
+hipError_t launch_grouped_bwd(const GridK& g, int64_t N, int64_t I, int groups, int dtype,
+                              const void* x, const void* C, const float* dy, float* dx, float* dC,
+                              float* part, float* red, hipStream_t s);
+
 }  // namespace kan

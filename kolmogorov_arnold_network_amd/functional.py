@@ -141,6 +141,56 @@ def kan_basis_eval_tp(x, grid, need_B=True, need_dB=True):
     return _basis(L.lib().kan_basis_eval_tp, "kan_basis_eval_tp", x, grid, need_B, need_dB)
 
 
+def group_desc(x, C, grid):
+    """``kan_group_desc_t`` for ``x [N, I]`` and ``C [groups, G+3]``."""
+    lo, hi, G = grid
+    if x.dim() != 2 or C.dim() != 2 or C.shape[1] != G + 3:
+        raise ValueError("x must be [N, I] and C [groups, G+3]")
+    if x.dtype != C.dtype:
+        raise ValueError("x and C must share one dtype")
+    return L.make_group_desc(x.shape[0], x.shape[1], C.shape[0], lo, hi, G, _DTYPES[x.dtype])
+
+
+def kan_group_workspace_size(desc):
+    n = L.lib().kan_group_workspace_size(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid grouped activation description")
+    return int(n)
+
+
+def kan_group_forward(x, C, grid, out=None):
+    """``y [N, I]`` float32 of the grouped spline activation
+    ``y[b, i] = sum_m C[g(i), m] B_m(x[b, i])``, ``g(i) = i * groups // I``."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    desc = group_desc(x, C, grid)
+    y = out if out is not None else torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check_tensor(y, "y", (torch.float32,), x.device)
+    L.check(L.lib().kan_group_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(y), _stream(x)),
+            "kan_group_forward")
+    return y
+
+
+def kan_group_backward(x, C, dy, grid, need_dx=True, need_dC=True, ws=None):
+    """``(dx [N, I], dC [groups, G+3])`` float32; unrequested ones are None."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    _check_tensor(dy, "dy", (torch.float32,), x.device)
+    desc = group_desc(x, C, grid)
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must be [N, I]")
+    if ws is None:
+        n = kan_group_workspace_size(desc) if need_dC else 0
+        ws = (torch.empty(max(n, 1), dtype=torch.uint8, device=x.device), n)
+    buf, n = ws
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty(x.shape, **f32) if need_dx else None
+    dC = torch.empty(C.shape, **f32) if need_dC else None
+    L.check(L.lib().kan_group_backward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(dy), _ptr(dx),
+                                       _ptr(dC), _ptr(buf), n, _stream(x)), "kan_group_backward")
+    return dx, dC
+
+
 def kan_cast_f32_to_bf16(t, out=None):
     """Round-to-nearest-even float32 -> bfloat16 on the device."""
     _check_tensor(t, "input", (torch.float32,))

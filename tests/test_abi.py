@@ -240,6 +240,78 @@ def test_cast_checks(L):
     assert lib.kan_cast_f32_to_bf16(X, X + 16, 8, None) == L.KAN_ERR_ALIAS
 
 
+def gdesc(L, N=100, I=300, groups=5, G=8, dtype=0, lo=-1.0, hi=1.0, degree=3):
+    return L.make_group_desc(N, I, groups, lo, hi, G, dtype, degree)
+
+
+def group_workspace(N, I, K):
+    """The grouped backward's workspace, restated: channel blocks of 256, row
+    chunks aimed at 1024 blocks with at least max(64, 24 K) rows (a multiple
+    of 4), K floats per channel per chunk, then K per channel summed."""
+    if N == 0:
+        return 0
+    xb = (I + 255) // 256
+    gy = max(1, (1024 + xb - 1) // xb)
+    R = max(max(64, 24 * K), (N + gy - 1) // gy)
+    R = (R + 3) // 4 * 4
+    chunks = (N + R - 1) // R
+    return ((chunks * K * I + K * I) * 4 + 255) // 256 * 256
+
+
+def test_group_struct_layout(L):
+    assert ctypes.sizeof(L.kan_group_desc_t) == 2 * 8 + 2 * 4 + 16
+
+
+def test_group_workspace_sizes(L):
+    f = lambda d: L.lib().kan_group_workspace_size(ctypes.byref(d))
+    for (N, I, groups, G) in [(100, 300, 5, 8), (25216, 3072, 8, 5), (32768, 2048, 2048, 8),
+                              (1, 1, 1, 1), (1000000, 17, 17, 125), (0, 5, 5, 3)]:
+        assert f(gdesc(L, N=N, I=I, groups=groups, G=G)) == group_workspace(N, I, G + 3)
+        assert f(gdesc(L, N=N, I=I, groups=groups, G=G, dtype=1)) == group_workspace(N, I, G + 3)
+    bad = ctypes.c_size_t(-1).value
+    assert L.lib().kan_group_workspace_size(None) == bad
+    assert f(gdesc(L, groups=301)) == bad
+    assert f(gdesc(L, G=126)) == bad
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), -2), (dict(I=0), -2), (dict(groups=0), -2), (dict(groups=301), -2),
+    (dict(N=1 << 40), -2), (dict(G=0), -3), (dict(G=126), -3), (dict(lo=1.0, hi=1.0), -3),
+    (dict(lo=float("nan")), -3), (dict(dtype=2), -4), (dict(degree=2), -8)])
+def test_group_bad_descriptors(L, kw, code):
+    d = gdesc(L, **kw)
+    lib = L.lib()
+    assert lib.kan_group_forward(ctypes.byref(d), X, C, Y, None) == code
+    assert lib.kan_group_backward(ctypes.byref(d), X, C, DY, DX, DC, WS, 1 << 30, None) == code
+
+
+def test_group_pointer_checks(L):
+    d = gdesc(L)
+    lib = L.lib()
+    n = lib.kan_group_workspace_size(ctypes.byref(d))
+    fwd = lambda *a: lib.kan_group_forward(ctypes.byref(d), *a, None)
+    bwd = lambda *a: lib.kan_group_backward(ctypes.byref(d), *a, None)
+    assert lib.kan_group_forward(None, X, C, Y, None) == L.KAN_ERR_NULL
+    assert fwd(None, C, Y) == L.KAN_ERR_NULL
+    assert fwd(X, None, Y) == L.KAN_ERR_NULL
+    assert fwd(X, C, None) == L.KAN_ERR_NULL
+    assert fwd(X + 8, C, Y) == L.KAN_ERR_ALIGN
+    assert fwd(X, C, X + 16) == L.KAN_ERR_ALIAS                 # y over x
+    assert fwd(X, C, C) == L.KAN_ERR_ALIAS                      # y over C
+    assert bwd(None, C, DY, DX, DC, WS, n) == L.KAN_ERR_NULL
+    assert bwd(X, C, None, DX, DC, WS, n) == L.KAN_ERR_NULL
+    assert bwd(X, C, DY, DX, DC, WS, n - 1) == L.KAN_ERR_WORKSPACE
+    assert bwd(X, C, DY, DX, DC, None, n) == L.KAN_ERR_NULL
+    assert bwd(X, C, DY, DX, DC, WS + 16, n) == L.KAN_ERR_ALIGN
+    assert bwd(X, C, DY, DX + 4, DC, WS, n) == L.KAN_ERR_ALIGN
+    assert bwd(X, C, DY, DY, DC, WS, n) == L.KAN_ERR_ALIAS      # dx over dy
+    assert bwd(X, C, DY, DX, DX, WS, n) == L.KAN_ERR_ALIAS      # dC over dx
+    assert bwd(X, C, DY, DX, DC, DC, n) == L.KAN_ERR_ALIAS      # workspace over dC
+    assert bwd(X, C, DY, None, None, None, 0) == L.KAN_OK       # nothing asked: no work
+    e = gdesc(L, N=0)
+    assert lib.kan_group_forward(ctypes.byref(e), None, C, None, None) == L.KAN_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     from kolmogorov_arnold_network_amd import _lib
     monkeypatch.setattr(_lib, "_lib", None)

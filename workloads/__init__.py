@@ -25,6 +25,17 @@ Workloads (shapes follow the pages' own examples):
   base branch; x ~ U(-1, 1); C ~ N(0, 0.02); W_base ~ N(0, 1/64);
   dy ~ N(0, 1).
 
+Grouped spline activation workloads (``make_grouped``):
+
+* ``g1``  25216 rows (128 images x 197 tokens) by 3072 channels (the hidden
+  width of a ViT-B channel mixer), 8 groups of 384 channels, G = 5, bf16 x
+  and C: the shape of the grouped KAN activations of the Kolmogorov-Arnold
+  Transformer that FlashKAT studies; x ~ U(-1, 1); C ~ N(0, 0.3);
+  dy ~ N(0, 1).
+* ``g2``  32768 rows (8 sequences x 4096 tokens) by 2048 channels, one
+  spline per channel (2048 groups), G = 8, bf16 x and C: per-coordinate
+  spline curves over a 2048-wide projection; same draws.
+
 ``N(0, s)`` means standard deviation ``s``.  Draws are float32 from NumPy's
 ``default_rng`` seeded by ``SeedSequence([1000 + id, G])``, with child
 streams spawned in the order x, then per layer C and W_base, then dy.  bf16
@@ -48,6 +59,12 @@ CONFIGS = {
                base=True, x=("normal", 0.3), clamp=True, c_std=0.02),
     "c5": dict(id=5, N=65536, widths=[4096, 4096], G=20, lo=-1.0, hi=1.0, dtype="bf16",
                base=True, x=("uniform", 1.0), clamp=False, c_std=0.02),
+}
+
+
+GROUPED = {
+    "g1": dict(id=11, N=25216, I=3072, groups=8, G=5, lo=-1.0, hi=1.0, dtype="bf16"),
+    "g2": dict(id=12, N=32768, I=2048, groups=2048, G=8, lo=-1.0, hi=1.0, dtype="bf16"),
 }
 
 
@@ -157,3 +174,46 @@ def sample_pairs(O, I, count, seed):
     js = rng.integers(0, O, size=count)
     is_ = rng.integers(0, I, size=count)
     return np.stack([js, is_], axis=1)
+
+
+def make_grouped(name, N=None):
+    """Inputs of one grouped activation workload: dict with ``name, N, I,
+    groups, G, lo, hi, dtype, x [N, I], C [groups, G+3], dy [N, I]`` (float32
+    arrays; bf16 workloads hold bf16-exact values).  ``N`` may shrink the
+    batch (the first rows of the same streams)."""
+    spec = dict(GROUPED[name])
+    Nfull, I, groups, G = spec["N"], spec["I"], spec["groups"], spec["G"]
+    N = Nfull if N is None else N
+    kids = np.random.SeedSequence([1000 + spec["id"], G]).spawn(3)
+    x = _draw_x(np.random.default_rng(kids[0]), (N, I), ("uniform", 1.0), False)
+    C = np.random.default_rng(kids[1]).standard_normal((groups, G + 3), dtype=np.float32) * np.float32(0.3)
+    dy = np.random.default_rng(kids[2]).standard_normal((N, I), dtype=np.float32)
+    if spec["dtype"] == "bf16":
+        x = to_bf16_values(x)
+        C = to_bf16_values(C)
+    spec.update(name=name, N=N, x=x, C=C, dy=dy)
+    return spec
+
+
+def random_grouped(N, I, groups, G, dtype="f32", seed=0, lo=-1.0, hi=1.0, special=True):
+    """A small random grouped activation for parity tests; ``special`` mixes in
+    the knots and the points around and far outside the grid, as
+    ``random_layer`` does."""
+    rng = np.random.default_rng(np.random.SeedSequence([9, seed, N, I, groups, G]))
+    mid, half = 0.5 * (lo + hi), 0.5 * (hi - lo)
+    x = (mid + half * 1.3 * (2 * rng.random((N, I)) - 1)).astype(np.float32)
+    if special and N * I > 0:
+        h = (hi - lo) / G
+        pts = [lo + (r - 3) * h for r in range(G + 7)]
+        pts += [lo, hi, np.nextafter(np.float32(hi), np.float32(-np.inf)),
+                np.nextafter(np.float32(lo), np.float32(-np.inf)),
+                lo - 3 * h - 1e-3, hi + 3 * h + 1e-3, lo - 10.0, hi + 10.0, 0.0]
+        pts = np.asarray(pts, dtype=np.float32)
+        mask = rng.random((N, I)) < 0.25
+        x[mask] = pts[rng.integers(0, len(pts), size=int(mask.sum()))]
+    C = (rng.standard_normal((groups, G + 3)) * 0.3).astype(np.float32)
+    dy = rng.standard_normal((N, I)).astype(np.float32)
+    if dtype == "bf16":
+        x = to_bf16_values(x)
+        C = to_bf16_values(C)
+    return dict(N=N, I=I, groups=groups, G=G, lo=lo, hi=hi, dtype=dtype, x=x, C=C, dy=dy)
