@@ -372,7 +372,7 @@ static int group_check(const kan_group_desc_t* d, GridK* gk, int* K, int* esize)
     int st = make_plan(&ld, &p);
     if (st != KAN_OK) return st;
     if (d->N < 0 || d->I < 1 || d->groups < 1 || d->groups > d->I) return KAN_ERR_SHAPE;
-    if (d->N > kIndexLimit || d->I > kIndexLimit) return KAN_ERR_SHAPE;
+    if (d->N > kIndexLimit || d->I * p.K > kIndexLimit) return KAN_ERR_SHAPE;
     *gk = p.gk;
     *K = p.K;
     *esize = p.esize;

@@ -245,15 +245,16 @@ def gdesc(L, N=100, I=300, groups=5, G=8, dtype=0, lo=-1.0, hi=1.0, degree=3):
 
 
 def group_workspace(N, I, K):
-    """The grouped backward's workspace, restated: channel blocks of 256, row
-    chunks aimed at 1024 blocks with at least max(64, 24 K) rows (a multiple
-    of 4), K floats per channel per chunk, then K per channel summed."""
+    """The grouped backward's workspace, restated: channel blocks of 64, row
+    chunks aimed at no more than 1024 blocks, with at least max(64, 24 K) rows
+    (a multiple of 32: 4 row waves of 8 rows), K floats per channel per chunk,
+    then K per channel summed."""
     if N == 0:
         return 0
-    xb = (I + 255) // 256
-    gy = max(1, (1024 + xb - 1) // xb)
+    xb = (I + 63) // 64
+    gy = max(1, 1024 // xb)
     R = max(max(64, 24 * K), (N + gy - 1) // gy)
-    R = (R + 3) // 4 * 4
+    R = (R + 31) // 32 * 32
     chunks = (N + R - 1) // R
     return ((chunks * K * I + K * I) * 4 + 255) // 256 * 256
 
@@ -272,6 +273,7 @@ def test_group_workspace_sizes(L):
     assert L.lib().kan_group_workspace_size(None) == bad
     assert f(gdesc(L, groups=301)) == bad
     assert f(gdesc(L, G=126)) == bad
+    assert f(gdesc(L, N=10, I=(1 << 31) // 11, groups=1, G=8)) == bad     # I * (G+3) beyond the index range
 
 
 @pytest.mark.parametrize("kw,code", [
