@@ -417,7 +417,7 @@ def grouped_cpu_baseline(d, rows=None):
     import oracle
     import workloads as wl
     N, I = d["N"], d["I"]
-    n = min(N, rows or 2048)
+    n = min(N, rows or 4096)
     R = wl.sample_indices(N, n, 98)
     x, dy = d["x"][R].astype("float64"), d["dy"][R].astype("float64")
     t0 = time.perf_counter()

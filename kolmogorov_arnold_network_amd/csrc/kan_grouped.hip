@@ -39,8 +39,9 @@ constexpr int GP_UF = 16;               // rows whose loads a forward thread iss
 constexpr int GP_UB = 8;                // the same, backward
 constexpr size_t kTabLimit = 32 * 1024; // LDS bytes for the per-span table
 
-// p[i] for a wave-uniform row base p and a lane's channel i: a 32-bit
-// unsigned byte offset lets the load take the scalar-base address form
+// p[i] for a wave-uniform row base p and a lane's channel i, as a 32-bit
+// unsigned byte offset from p (the backward's global loads and stores; the
+// buffer form below saves address arithmetic but measured slower there)
 template <typename T>
 __device__ __forceinline__ T& at(T* p, int i) {
     using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
@@ -49,6 +50,24 @@ __device__ __forceinline__ T& at(T* p, int i) {
 __device__ __forceinline__ float load_at(const float* p, int i) { return at(p, i); }
 __device__ __forceinline__ float load_at(const uint16_t* p, int i) {
     return __uint_as_float(((uint32_t)at(p, i)) << 16);
+}
+
+// Raw buffer access to one row of `bytes` bytes at a wave-uniform base: the
+// resource is built in scalar registers, a lane supplies only its 32-bit
+// byte offset, and offsets past the row read 0 / write nothing.  The third
+// resource word is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float row_load(const float* row, int I, int i) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(row, I * 4), i * 4, 0, 0));
+}
+__device__ __forceinline__ float row_load(const uint16_t* row, int I, int i) {
+    return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(row_rsrc(row, I * 2), i * 2, 0, 0))
+                           << 16);
+}
+__device__ __forceinline__ void row_store(float* row, int I, int i, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), row_rsrc(row, I * 4), i * 4, 0, 0);
 }
 
 __device__ __forceinline__ int group_of(int i, int I, int groups) {
@@ -122,7 +141,7 @@ __global__ void __launch_bounds__(GP_T, 8) grouped_fwd_kernel(GridK g, int N, in
     for (int b = r0 + w; b < r1; b += GP_W * GP_UF) {
         float xv[GP_UF];
 #pragma unroll
-        for (int q = 0; q < GP_UF; ++q) xv[q] = load_at(x + (int64_t)min(b + q * GP_W, r1 - 1) * I, i);
+        for (int q = 0; q < GP_UF; ++q) xv[q] = row_load(x + (int64_t)min(b + q * GP_W, r1 - 1) * I, I, i);
         // every row of the batch is computed (rows past the chunk repeat its
         // last row) and only the stores are predicated, so that the loads are
         // all issued before the first use
@@ -147,7 +166,7 @@ __global__ void __launch_bounds__(GP_T, 8) grouped_fwd_kernel(GridK g, int N, in
                     if (m >= 0 && m < K) v = __builtin_fmaf(load_f(c, m), p[r], v);
                 }
             }
-            if (row < r1) at(y + (int64_t)row * I, i) = v;
+            if (row < r1) row_store(y + (int64_t)row * I, I, i, v);
         }
     }
 }
