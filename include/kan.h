@@ -61,7 +61,7 @@ typedef enum {
     KAN_OK = 0,
     KAN_ERR_NULL = -1,        /* a required pointer is NULL, or a forbidden one is not */
     KAN_ERR_SHAPE = -2,       /* N < 0, I < 1, O < 1, or a size beyond the index range */
-    KAN_ERR_GRID = -3,        /* G < 1 or G > 125, lo >= hi, or lo / hi not finite */
+    KAN_ERR_GRID = -3,        /* G < 1 or G > 125 (2-D layer: 13), lo >= hi, or lo / hi not finite */
     KAN_ERR_DTYPE = -4,       /* dtype not KAN_F32 / KAN_BF16 */
     KAN_ERR_ALIGN = -5,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
     KAN_ERR_WORKSPACE = -6,   /* workspace smaller than kan_workspace_size() */
@@ -224,6 +224,55 @@ int kan_group_forward(const kan_group_desc_t* desc, const void* x, const void* C
  * N = 0 fills dC with zeros. */
 int kan_group_backward(const kan_group_desc_t* desc, const void* x, const void* C, const float* dy,
                        float* dx, float* dC, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- 2-D tensor-product spline layer ---------------------------------------
+ * Beside univariate spline layers, the InKAN project page ("1D and 2D
+ * Splines") offers tensor-product B-spline surfaces for approximating a
+ * function of two inputs jointly.  Here the inputs of a row are taken in
+ * consecutive pairs (x[b, 2p], x[b, 2p+1]), p = 0 .. P-1, every (output j,
+ * pair p) edge carries one bicubic surface over the layer's 1-D basis, and
+ * output j sums its edges:
+ *
+ *     y[b, j] = sum_p sum_{m,n} C[j, p, m, n] * B_m(x[b, 2p]) * B_n(x[b, 2p+1]),
+ *
+ * at most 16 non-zero products per (row, pair).  Backward with dy [N, O]:
+ *
+ *     dx[b, 2p]      = sum_j dy[b, j] sum_{m,n} C[j, p, m, n] B'_m(x[b, 2p]) B_n(x[b, 2p+1])
+ *     dx[b, 2p+1]    = sum_j dy[b, j] sum_{m,n} C[j, p, m, n] B_m(x[b, 2p]) B'_n(x[b, 2p+1])
+ *     dC[j, p, m, n] = sum_b dy[b, j] B_m(x[b, 2p]) B_n(x[b, 2p+1])
+ *
+ * Layouts: x, dx [N, 2P]; C, dC [O, P, G+3, G+3] with n fastest; y, dy
+ * [N, O].  x and C in `dtype`, the rest float32.  Both passes run on the
+ * matrix cores over the (G+3)^2 products per pair, generated in LDS; a pair's
+ * columns must fit one 256-wide tile, so 1 <= G <= 13.  The conventions of
+ * the layer entry points hold (device pointers 16-byte aligned, workspace
+ * 256-byte aligned and caller-owned, outputs overwritten, no overlap,
+ * validation before any work, deterministic results; N = 0 fills dC with
+ * zeros). */
+typedef struct {
+    int64_t N;          /* rows, >= 0 */
+    int64_t P;          /* input pairs, >= 1 (x has 2P columns) */
+    int64_t O;          /* outputs, >= 1 */
+    kan_grid_t grid;    /* 1 <= G <= 13, degree 3 */
+    int32_t dtype;      /* kan_dtype_t: storage of x and C */
+    int32_t flags;      /* must be 0 */
+} kan_surface_desc_t;
+
+/* Bytes of workspace a pass of the 2-D layer needs (SIZE_MAX if `desc` is
+ * invalid): the packed coefficient operand, and for the backward dy in both
+ * orientations and the dx partial sums of pairs cut by a tile edge, plus the
+ * float32 partial outputs of k-range slices, as for kan_workspace_size. */
+size_t kan_surface_workspace_size(const kan_surface_desc_t* desc, int pass);
+
+/* Forward: y [N, O] float32. */
+int kan_surface_forward(const kan_surface_desc_t* desc, const void* x, const void* C, float* y,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: dx [N, 2P] and dC [O, P, G+3, G+3], float32; either may be NULL
+ * to skip it.  dC is reduced over all rows in a fixed order without atomics. */
+int kan_surface_backward(const kan_surface_desc_t* desc, const void* x, const void* C,
+                         const float* dy, float* dx, float* dC, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* float32 -> bfloat16, round to nearest even (NaN stays NaN).  n elements;
  * `out` receives the 16-bit patterns.  Used between bf16 layers, where a

@@ -38,7 +38,8 @@ ABI_VERSION = 1
 # every symbol include/kan.h declares
 EXPORTS = ("kan_abi_version", "kan_status_string", "kan_workspace_size", "kan_prepare",
            "kan_forward", "kan_backward", "kan_basis_eval", "kan_basis_eval_tp", "kan_cast_f32_to_bf16",
-           "kan_group_workspace_size", "kan_group_forward", "kan_group_backward")
+           "kan_group_workspace_size", "kan_group_forward", "kan_group_backward",
+           "kan_surface_workspace_size", "kan_surface_forward", "kan_surface_backward")
 
 
 class kan_grid_t(ctypes.Structure):
@@ -55,6 +56,11 @@ class kan_desc_t(ctypes.Structure):
 class kan_group_desc_t(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("I", ctypes.c_int64), ("groups", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("grid", kan_grid_t)]
+
+
+class kan_surface_desc_t(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("P", ctypes.c_int64), ("O", ctypes.c_int64),
+                ("grid", kan_grid_t), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class KanError(RuntimeError):
@@ -101,6 +107,12 @@ def lib():
     L.kan_group_forward.argtypes = [P(kan_group_desc_t), _vp, _vp, _vp, _vp]
     L.kan_group_backward.restype = ctypes.c_int
     L.kan_group_backward.argtypes = [P(kan_group_desc_t), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.kan_surface_workspace_size.restype = _sz
+    L.kan_surface_workspace_size.argtypes = [P(kan_surface_desc_t), ctypes.c_int]
+    L.kan_surface_forward.restype = ctypes.c_int
+    L.kan_surface_forward.argtypes = [P(kan_surface_desc_t), _vp, _vp, _vp, _vp, _sz, _vp]
+    L.kan_surface_backward.restype = ctypes.c_int
+    L.kan_surface_backward.argtypes = [P(kan_surface_desc_t), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     L.kan_cast_f32_to_bf16.restype = ctypes.c_int
     L.kan_cast_f32_to_bf16.argtypes = [_vp, _vp, _i64, _vp]
     if L.kan_abi_version() != ABI_VERSION:
@@ -131,5 +143,12 @@ def make_desc(N, I, O, lo, hi, G, dtype, has_base, variant=KAN_VARIANT_AUTO, fla
 def make_group_desc(N, I, groups, lo, hi, G, dtype, degree=3):
     d = kan_group_desc_t()
     d.N, d.I, d.groups, d.dtype = int(N), int(I), int(groups), int(dtype)
+    d.grid.lo, d.grid.hi, d.grid.G, d.grid.degree = float(lo), float(hi), int(G), int(degree)
+    return d
+
+
+def make_surface_desc(N, P, O, lo, hi, G, dtype, degree=3, flags=0):
+    d = kan_surface_desc_t()
+    d.N, d.P, d.O, d.dtype, d.flags = int(N), int(P), int(O), int(dtype), int(flags)
     d.grid.lo, d.grid.hi, d.grid.G, d.grid.degree = float(lo), float(hi), int(G), int(degree)
     return d

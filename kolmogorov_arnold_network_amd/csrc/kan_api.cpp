@@ -54,17 +54,103 @@ int k_slices(int64_t tiles, int64_t nkt, int64_t out_bytes, int esize, int64_t* 
     return (int)((nkt + *nks - 1) / *nks);
 }
 
+// Matrix-core geometry and workspace layout of a plan whose shape, K, Kb,
+// base, dtype and per-pass variants are set.
+void plan_layout(Plan& q, bool dense_forward) {
+    if (q.variant_fwd != KAN_VARIANT_MFMA && q.variant_bwd != KAN_VARIANT_MFMA) return;
+    q.BK = kTileKBytes / q.esize;
+    q.IKb = q.I * q.Kb;
+    q.Opad = round_up(q.O, kTileN);
+    q.Npad = round_up(std::max<int64_t>(q.N, 1), kTileM);
+    q.Kf = round_up(q.IKb, q.BK);
+    q.tiles_dx = (q.IKb + kTileN - 1) / kTileN;
+    size_t off = 0;
+    auto take = [&](size_t bytes, size_t* o, size_t* sz) {
+        *o = off;
+        *sz = bytes;
+        off += (size_t)round_up((int64_t)bytes, 256);
+    };
+    // Sparse forward: NG = ceil(Kb / 4) groups, at least 4 (so that 4
+    // consecutive columns land in 4 groups) and even (so that an input's
+    // index nibbles fill whole bytes); taken when its padded width costs
+    // at most 3/4 of the dense contraction.
+    int ng = std::max(4, (q.Kb + 3) / 4);
+    ng += ng & 1;
+    q.sparse = q.dtype == KAN_BF16 && !dense_forward && !q.pair && ng <= 8 && q.Kb >= 11 &&
+               8 * ng <= 3 * q.Kb && q.I * 4 * ng <= kIndexLimit;
+    q.NG = ng;
+    q.Kb8 = 4 * ng;
+    q.Kfs = round_up(q.I * q.Kb8, 64);
+    take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
+    const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
+    q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
+                           &q.nks_fwd);
+    if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
+    q.ws_fwd = q.variant_fwd == KAN_VARIANT_MFMA ? off : 0;
+    off = 0;
+    take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
+    take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
+    take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
+    take((size_t)(q.Npad * q.tiles_dx * 2 * (q.pair ? 2 : 1)) * 4, &q.off_part, &q.sz_part);
+    q.split_dc = k_slices((q.Opad / kTileM) * ((q.IKb + kTileN - 1) / kTileN), q.Npad / q.BK,
+                          q.O * q.I * q.Kb * 4, q.esize, &q.nks_dc);
+    if (q.split_dc > 1) take((size_t)(q.split_dc * q.O * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
+    q.ws_bwd = q.variant_bwd == KAN_VARIANT_MFMA ? off : 0;
+}
+
+int grid_check(const kan_grid_t& g, int max_G) {
+    if (g.degree != 3) return KAN_ERR_UNSUPPORTED;
+    if (g.G < 1 || g.G > max_G) return KAN_ERR_GRID;
+    if (!isfinite(g.lo) || !isfinite(g.hi) || !(g.lo < g.hi)) return KAN_ERR_GRID;
+    return KAN_OK;
+}
+
+void grid_constants(Plan& q, const kan_grid_t& g) {
+    const double lo = g.lo, hi = g.hi;
+    q.G = g.G;
+    q.gk.scale = (float)((double)q.G / (hi - lo));
+    q.gk.shift = (float)(3.0 - lo * (double)q.G / (hi - lo));
+    q.gk.G = q.G;
+}
+
 }  // namespace
+
+int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
+    if (!d || !p) return KAN_ERR_NULL;
+    if (d->N < 0 || d->P < 1 || d->O < 1) return KAN_ERR_SHAPE;
+    // a pair's (G+3)^2 columns must fit one 256-wide tile
+    int st = grid_check(d->grid, 13);
+    if (st != KAN_OK) return st;
+    if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
+    if (d->flags != 0) return KAN_ERR_UNSUPPORTED;
+    Plan q;
+    memset(&q, 0, sizeof(q));
+    q.pair = 1;
+    q.N = d->N;
+    q.I = d->P;
+    q.xI = 2 * d->P;
+    q.O = d->O;
+    grid_constants(q, d->grid);
+    q.K = (q.G + 3) * (q.G + 3);
+    q.base = 0;
+    q.Kb = q.K;
+    q.dtype = d->dtype;
+    q.esize = d->dtype == KAN_F32 ? 4 : 2;
+    if (q.N > kIndexLimit || q.O > kIndexLimit || q.xI > kIndexLimit || q.I * q.Kb > kIndexLimit)
+        return KAN_ERR_SHAPE;
+    q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
+    plan_layout(q, true);
+    *p = q;
+    return KAN_OK;
+}
 
 int make_plan(const kan_desc_t* d, Plan* p) {
     if (!d || !p) return KAN_ERR_NULL;
     if (d->N < 0 || d->I < 1 || d->O < 1) return KAN_ERR_SHAPE;
-    if (d->grid.degree != 3) return KAN_ERR_UNSUPPORTED;
     // G <= kMaxG: the gather kernels stage an input's K = G+3 coefficients
     // for a tile of outputs in LDS, which holds 128 of them
-    if (d->grid.G < 1 || d->grid.G > kMaxG) return KAN_ERR_GRID;
-    if (!isfinite(d->grid.lo) || !isfinite(d->grid.hi) || !(d->grid.lo < d->grid.hi))
-        return KAN_ERR_GRID;
+    const int gst = grid_check(d->grid, kMaxG);
+    if (gst != KAN_OK) return gst;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
     if (d->has_base != 0 && d->has_base != 1) return KAN_ERR_UNSUPPORTED;
     if (d->variant < KAN_VARIANT_AUTO || d->variant > KAN_VARIANT_GATHER) return KAN_ERR_UNSUPPORTED;
@@ -74,18 +160,15 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     memset(&q, 0, sizeof(q));
     q.N = d->N;
     q.I = d->I;
+    q.xI = d->I;
     q.O = d->O;
-    q.G = d->grid.G;
+    grid_constants(q, d->grid);
     q.K = q.G + 3;
     q.base = d->has_base;
     q.Kb = q.K + q.base;
     q.dtype = d->dtype;
     q.esize = d->dtype == KAN_F32 ? 4 : 2;
     if (q.N > kIndexLimit || q.O > kIndexLimit || q.I * q.Kb > kIndexLimit) return KAN_ERR_SHAPE;
-    const double lo = d->grid.lo, hi = d->grid.hi;
-    q.gk.scale = (float)((double)q.G / (hi - lo));
-    q.gk.shift = (float)(3.0 - lo * (double)q.G / (hi - lo));
-    q.gk.G = q.G;
 
     // An input's Kb columns must fit one 256-wide tile on the matrix cores.
     // AUTO: bf16 runs both passes on the matrix cores.  float32 runs the
@@ -108,46 +191,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.variant_bwd = mfma_ok && (q.dtype == KAN_BF16 || big) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
     }
 
-    if (q.variant_fwd == KAN_VARIANT_MFMA || q.variant_bwd == KAN_VARIANT_MFMA) {
-        q.BK = kTileKBytes / q.esize;
-        q.IKb = q.I * q.Kb;
-        q.Opad = round_up(q.O, kTileN);
-        q.Npad = round_up(std::max<int64_t>(q.N, 1), kTileM);
-        q.Kf = round_up(q.IKb, q.BK);
-        q.tiles_dx = (q.IKb + kTileN - 1) / kTileN;
-        size_t off = 0;
-        auto take = [&](size_t bytes, size_t* o, size_t* sz) {
-            *o = off;
-            *sz = bytes;
-            off += (size_t)round_up((int64_t)bytes, 256);
-        };
-        // Sparse forward: NG = ceil(Kb / 4) groups, at least 4 (so that 4
-        // consecutive columns land in 4 groups) and even (so that an input's
-        // index nibbles fill whole bytes); taken when its padded width costs
-        // at most 3/4 of the dense contraction.
-        int ng = std::max(4, (q.Kb + 3) / 4);
-        ng += ng & 1;
-        q.sparse = q.dtype == KAN_BF16 && !(d->flags & KAN_FLAG_DENSE_FORWARD) && ng <= 8 &&
-                   q.Kb >= 11 && 8 * ng <= 3 * q.Kb && q.I * 4 * ng <= kIndexLimit;
-        q.NG = ng;
-        q.Kb8 = 4 * ng;
-        q.Kfs = round_up(q.I * q.Kb8, 64);
-        take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
-        const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
-        q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
-                               &q.nks_fwd);
-        if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
-        q.ws_fwd = q.variant_fwd == KAN_VARIANT_MFMA ? off : 0;
-        off = 0;
-        take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
-        take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
-        take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
-        take((size_t)(q.Npad * q.tiles_dx * 2) * 4, &q.off_part, &q.sz_part);
-        q.split_dc = k_slices((q.Opad / kTileM) * ((q.IKb + kTileN - 1) / kTileN), q.Npad / q.BK,
-                              q.O * q.I * q.Kb * 4, q.esize, &q.nks_dc);
-        if (q.split_dc > 1) take((size_t)(q.split_dc * q.O * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
-        q.ws_bwd = q.variant_bwd == KAN_VARIANT_MFMA ? off : 0;
-    }
+    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
     *p = q;
     return KAN_OK;
 }
@@ -165,7 +209,7 @@ const char* kan_status_string(int status) {
         case KAN_OK: return "ok";
         case KAN_ERR_NULL: return "required pointer is NULL (or a forbidden one is not)";
         case KAN_ERR_SHAPE: return "invalid shape";
-        case KAN_ERR_GRID: return "invalid grid (G < 1 or > 125, lo >= hi, or non-finite)";
+        case KAN_ERR_GRID: return "invalid grid (G < 1 or > 125 (2-D layer: 13), lo >= hi, or non-finite)";
         case KAN_ERR_DTYPE: return "unsupported dtype";
         case KAN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, workspace 256)";
         case KAN_ERR_WORKSPACE: return "workspace too small";
@@ -356,6 +400,74 @@ int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, 
 int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
                       float* dB, void* stream) {
     return basis_eval_impl(grid, n, dtype, x, B, dB, true, stream);
+}
+
+size_t kan_surface_workspace_size(const kan_surface_desc_t* desc, int pass) {
+    Plan p;
+    if (make_plan_surface(desc, &p) != KAN_OK) return SIZE_MAX;
+    if (pass != KAN_PASS_FORWARD && pass != KAN_PASS_BACKWARD) return SIZE_MAX;
+    return pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
+}
+
+int kan_surface_forward(const kan_surface_desc_t* desc, const void* x, const void* C, float* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+    Plan p;
+    int st = make_plan_surface(desc, &p);
+    if (st != KAN_OK) return st;
+    if (!C || (p.N > 0 && (!x || !y))) return KAN_ERR_NULL;
+    const void* ptrs[] = {x, C, y};
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    if ((st = check_ws(p, KAN_PASS_FORWARD, ws, ws_bytes)) != KAN_OK) return st;
+    const Range out{y, (size_t)(p.N * p.O) * 4};
+    const Range wr{ws, p.ws_fwd};
+    const Range in[] = {{x, (size_t)(p.N * p.xI) * p.esize}, {C, (size_t)(p.O * p.I * p.K) * p.esize}};
+    for (const Range& r : in)
+        if (overlap(out, r) || overlap(wr, r)) return KAN_ERR_ALIAS;
+    if (overlap(out, wr)) return KAN_ERR_ALIAS;
+    if (p.N == 0) return KAN_OK;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    st = prepare_impl(p, KAN_PASS_FORWARD, C, nullptr, nullptr, ws, s);
+    if (st != KAN_OK) return st;
+    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
+                                     reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
+}
+
+int kan_surface_backward(const kan_surface_desc_t* desc, const void* x, const void* C, const float* dy,
+                         float* dx, float* dC, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    int st = make_plan_surface(desc, &p);
+    if (st != KAN_OK) return st;
+    if (!C || (p.N > 0 && (!x || !dy))) return KAN_ERR_NULL;
+    const void* ptrs[] = {x, C, dy, dx, dC};
+    for (const void* q : ptrs)
+        if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
+    if ((st = check_ws(p, KAN_PASS_BACKWARD, ws, ws_bytes)) != KAN_OK) return st;
+    const Range outs[] = {{dx, (size_t)(p.N * p.xI) * 4}, {dC, (size_t)(p.O * p.I * p.K) * 4}, {ws, p.ws_bwd}};
+    const Range ins[] = {{x, (size_t)(p.N * p.xI) * p.esize},
+                         {C, (size_t)(p.O * p.I * p.K) * p.esize},
+                         {dy, (size_t)(p.N * p.O) * 4}};
+    for (int a = 0; a < 3; ++a) {
+        for (const Range& r : ins)
+            if (overlap(outs[a], r)) return KAN_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlap(outs[a], outs[b])) return KAN_ERR_ALIAS;
+    }
+    if (!dx && !dC) return KAN_OK;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (p.N == 0) return dC ? status_of(launch_fill_zero(dC, p.O * p.I * p.K, s)) : KAN_OK;
+    st = prepare_impl(p, KAN_PASS_BACKWARD, C, nullptr, dy, ws, s);
+    if (st != KAN_OK) return st;
+    hipError_t e = hipSuccess;
+    if (dx)
+        e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),
+                           reinterpret_cast<float*>(ws_at(ws, p.off_part)), dx, s);
+    if (e == hipSuccess && dC)
+        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), reinterpret_cast<float*>(ws_at(ws, p.off_dcp)),
+                           dC, nullptr, s);
+    return status_of(e);
 }
 
 // Validates a grouped activation; on success *gk and *K describe the grid.

@@ -26,6 +26,12 @@ struct Plan {
     int G, K, Kb;        // K = G+3 spline functions; Kb = K + has_base columns per input
     int base;
     int dtype;           // KAN_F32 / KAN_BF16
+    // 2-D tensor-product layer: "inputs" are the P pairs (x[b, 2p], x[b, 2p+1]),
+    // K = Kb = (G+3)^2 columns per pair (m for the first input, n for the
+    // second, n fastest); x rows are xI = 2P wide.  One-dimensional: pair = 0,
+    // xI = I.
+    int pair;
+    int64_t xI;
     int variant_fwd;     // resolved per pass: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
     int variant_bwd;
     int esize;           // bytes per stored element (4 or 2)
@@ -59,6 +65,7 @@ struct Plan {
     size_t off_dyp, sz_dyp;    // dy in storage dtype: rows b < Npad, k = j < Opad
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
+                               // (pairs: [Npad][tiles_dx][2][2], both inputs of the pair)
     size_t off_yp, sz_yp;      // forward slices' partial y: [split_fwd][N][O] float (split_fwd > 1)
     size_t off_dcp, sz_dcp;    // dC slices' partials: [split_dc][O][I][K] then [split_dc][O][I] float
     size_t ws_fwd, ws_bwd;
@@ -66,6 +73,8 @@ struct Plan {
 
 // Builds the plan; returns KAN_OK or the validation error for `desc` alone.
 int make_plan(const kan_desc_t* desc, Plan* p);
+// The plan of a 2-D tensor-product layer (always on the matrix cores).
+int make_plan_surface(const kan_surface_desc_t* desc, Plan* p);
 
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,

@@ -143,6 +143,7 @@ struct GemmArgs {
     const void* x;       // generator input x [N, I]
     GridK g;
     int N, I, O, K, Kb, base;
+    int xI;              // x row width: I, or 2P for the pairs of the 2-D layer
     int64_t IKb;
     float* out0;         // y, dx or dC
     float* out1;         // dW_base, or the dx partial sums
@@ -400,6 +401,176 @@ struct GenB {
     }
 };
 
+// ---- 2-D tensor-product layer: operands of the pairs ----
+// A pair p = (x[b, 2p], x[b, 2p+1]) owns Kb = K1^2 columns p Kb + m K1 + n
+// (K1 = G + 3); of them the 16 with m = s1-3+r, n = s2-3+q (r, q < 4, s1, s2
+// the spans of the two inputs) hold the products b_r(u1) b_q(u2), the rest
+// are zero.  Spans past K1 + 3 hold no index < K1 and are clamped there, so
+// the column arithmetic stays small.
+__device__ __forceinline__ void pair_pieces(float x1, float x2, const GridK& g, int& s1, int& s2, float w1[4],
+                                            float w2[4]) {
+    const int K1 = g.G + 3;
+    float u1, u2;
+    s1 = min(span_u(x1, g, u1), K1 + 3);
+    s2 = min(span_u(x2, g, u2), K1 + 3);
+    pieces(u1, w1[0], w1[1], w1[2], w1[3]);
+    pieces(u2, w2[0], w2[1], w2[2], w2[3]);
+}
+
+// Forward A operand of the 2-D layer: GenA with pairs for inputs.  The NIN
+// lanes of a row clear it and scatter their pair's <= 16 products (a column
+// outside the k-tile, or a product with m or n outside [0, K1), goes to the
+// row's pad bytes).
+template <typename TS, int NIN>
+struct GenA2 {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int ES = Traits<TS>::ES;
+    static constexpr int PPT = 256 * NIN / NTHR;       // (row, pair) items per thread
+    static constexpr int NPART = PPT;
+    static constexpr int DEPTH = 2;
+    static constexpr int RSTEP = NTHR / NIN;
+    static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
+    const TS* x;
+    int q, row0;
+    int64_t xrow[PPT];
+    float x1s[2][PPT], x2s[2][PPT];
+    int ps[2];
+    __device__ GenA2(const GemmArgs& a, int tm, int) {
+        x = static_cast<const TS*>(a.x);
+        q = threadIdx.x % NIN;
+        row0 = threadIdx.x / NIN;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+            xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.xI;
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        ps[SL] = (unsigned)(kt * BK) / (unsigned)a.Kb + q;
+        const int p = min(ps[SL], a.I - 1);
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            x1s[SL][j] = load_f(x, xrow[j] + 2 * p);
+            x2s[SL][j] = load_f(x, xrow[j] + 2 * p + 1);
+        }
+    }
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* row = S + (row0 + RSTEP * j) * PITCH;
+#pragma unroll
+        for (int c = 0; c < (8 + NIN - 1) / NIN; ++c) {
+            const int chunk = q * ((8 + NIN - 1) / NIN) + c;
+            *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
+        }
+        const int K1 = a.g.G + 3;
+        const int p = ps[SL];
+        const int cb = p * a.Kb - kt * BK;               // tile column of (p, 0, 0)
+        const bool live = p < a.I;
+        int s1, s2;
+        float w1[4], w2[4];
+        pair_pieces(x1s[SL][j], x2s[SL][j], a.g, s1, s2, w1, w2);
+        char* pad = row + BK * ES;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = s1 - 3 + r;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = s2 - 3 + qq, c = cb + m * K1 + n;
+                const bool v = live & ((unsigned)m < (unsigned)K1) & ((unsigned)n < (unsigned)K1) &
+                               ((unsigned)c < (unsigned)BK);
+                Traits<TS>::put(v ? row + c * ES : pad, w1[r] * w2[qq]);
+            }
+        }
+        if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
+    }
+};
+
+// dC B operand of the 2-D layer: GenB with pairs for inputs.  Tile rows are
+// the packed columns n0 .. n0+255 (pair, m, n); k runs over the batch.  Wave
+// w clears the rows of its NQW pairs, then each (row b, pair) scatters its
+// <= 16 products into column b (rejected ones to pad bytes).
+template <typename TS, int NQW, int ZR>
+struct GenB2 {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int ES = Traits<TS>::ES;
+    static constexpr int PPL = BK * NQW / 64;            // (row, pair) items per lane
+    static constexpr int NPART = 1 + PPL;
+    static constexpr int DEPTH = 2;
+    static_assert(BK * NQW % 64 == 0, "whole items per lane");
+    const TS* x;
+    int n0, i0, wave, lane;
+    int bl[PPL], il[PPL], rb[PPL];
+    float x1s[2][PPL], x2s[2][PPL];
+    __device__ GenB2(const GemmArgs& a, int, int tn) {
+        x = static_cast<const TS*>(a.x);
+        n0 = tn * 256;
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        i0 = (unsigned)n0 / (unsigned)a.Kb + wave * NQW;  // first pair of this wave
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const int pp = lane + 64 * j;
+            bl[j] = pp / NQW;
+            il[j] = pp % NQW;
+            const int p = i0 + il[j];
+            // tile row of (p, 0, 0); a pair past the last one gets a row that
+            // no product can reach
+            rb[j] = p < a.I ? p * a.Kb - n0 : 1 << 20;
+        }
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const int64_t brow = (int64_t)min(kt * BK + bl[j], a.N - 1) * a.xI;
+            const int p = min(i0 + il[j], a.I - 1);
+            x1s[SL][j] = load_f(x, brow + 2 * p);
+            x2s[SL][j] = load_f(x, brow + 2 * p + 1);
+        }
+    }
+    template <int SL, bool RF, int pi>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        if constexpr (pi == 0) {
+#pragma unroll
+            for (int e = 0; e < NQW; ++e) {
+                const int r0 = (i0 + e) * a.Kb - n0;
+#pragma unroll
+                for (int z = 0; z < ZR; ++z) {
+                    const int rr = 8 * z + (lane >> 3);
+                    const int row = r0 + rr;
+                    const bool v = (rr < a.Kb) & (row >= 0) & (row < 256);
+                    *reinterpret_cast<uint4*>(v ? S + row * PITCH + (lane & 7) * 16 : S + 128) =
+                        make_uint4(0, 0, 0, 0);
+                }
+            }
+            return;
+        } else {
+        constexpr int j = pi - 1;
+        // batch rows past N come from a clamped row; dy^T is zero there
+        const int K1 = a.g.G + 3;
+        int s1, s2;
+        float w1[4], w2[4];
+        pair_pieces(x1s[SL][j], x2s[SL][j], a.g, s1, s2, w1, w2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = s1 - 3 + r;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = s2 - 3 + qq, t = rb[j] + m * K1 + n;
+                const bool v = ((unsigned)m < (unsigned)K1) & ((unsigned)n < (unsigned)K1) &
+                               ((unsigned)t < 256u);
+                Traits<TS>::put(S + (v ? t * PITCH + bl[j] * ES : 128 + (4 * r + qq) * PITCH),
+                                w1[r] * w2[qq]);
+            }
+        }
+        if constexpr (RF && pi == NPART - 1) fetch<SL>(a, ktn);
+        }
+    }
+};
+
 // Forward A operand in 2:4 structured-sparse form (bf16 only), in the column
 // order of kan_sparse.h; the coefficient operand is packed in the same order
 // (pack_fwd_sparse).
@@ -617,6 +788,101 @@ __global__ void dx_fixup_kernel(const float* __restrict__ part, float* __restric
         const int64_t c = 256 * (int64_t)(t + 1);
         if (c % Kb == 0 || c / Kb >= I) continue;
         dx[b * I + c / Kb] = part[(b * tiles + t) * 2 + 1] + part[(b * tiles + t + 1) * 2];
+    }
+}
+
+// dx of the 2-D layer: EpiDX with pairs.  Each (row, pair) of the staged P
+// rows contracts its <= 16 columns with B'(x1) B(x2) for dx[b, 2p] and with
+// B(x1) B'(x2) for dx[b, 2p+1]: with a_r = sum_q P[m_r, n_q] b_q(u2) and
+// d_r = sum_q P[m_r, n_q] b'_q(u2), dx[b, 2p] = sum_r b'_r(u1) a_r and
+// dx[b, 2p+1] = sum_r b_r(u1) d_r.  A pair cut by a tile edge writes both
+// partial sums to part[b][tn][side][0..1].
+struct EpiDX2 {
+    template <typename TS>
+    __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char* lds) {
+        float* P = reinterpret_cast<float*>(lds);
+        const TS* x = static_cast<const TS*>(a.x);
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        const int K1 = a.g.G + 3;
+        const int c0 = tn * 256;
+        const int p_lo = c0 / a.Kb;
+        const int np = min((c0 + 255) / a.Kb, a.I - 1) - p_lo + 1;
+        const int cw = (wave & 1) * 128 + (lane & 31);
+        const int rw = (wave >> 1) * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    P[(rw + acc_row(0, r)) * DX_PITCH + cw + 32 * fj] = acc[h][fj][r];
+            __syncthreads();
+#pragma unroll 1
+            for (int e = t; e < 128 * np; e += NTHR) {
+                const int rl = e / np, pl = e - rl * np;
+                const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
+                const int p = p_lo + pl;
+                const int cb = p * a.Kb - c0;            // tile column of (p, 0, 0)
+                if (b < a.N) {
+                    const int64_t xo = (int64_t)b * a.xI + 2 * p;
+                    const float x1 = load_f(x, xo), x2 = load_f(x, xo + 1);
+                    float u1, u2;
+                    const int s1 = min(span_u(x1, a.g, u1), K1 + 3), s2 = min(span_u(x2, a.g, u2), K1 + 3);
+                    float w1[4], d1[4], w2[4], d2[4];
+                    pieces(u1, w1[0], w1[1], w1[2], w1[3]);
+                    pieces(u2, w2[0], w2[1], w2[2], w2[3]);
+                    dpieces(u1, a.g.scale, d1[0], d1[1], d1[2], d1[3]);
+                    dpieces(u2, a.g.scale, d2[0], d2[1], d2[2], d2[3]);
+                    const float* prow = P + rl * DX_PITCH;
+                    float v1 = 0.0f, v2 = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = s1 - 3 + r;
+                        float ar = 0.0f, dr = 0.0f;
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const int n = s2 - 3 + qq, c = cb + m * K1 + n;
+                            if ((unsigned)m < (unsigned)K1 && (unsigned)n < (unsigned)K1 && (unsigned)c < 256u) {
+                                ar = __builtin_fmaf(prow[c], w2[qq], ar);
+                                dr = __builtin_fmaf(prow[c], d2[qq], dr);
+                            }
+                        }
+                        v1 = __builtin_fmaf(d1[r], ar, v1);
+                        v2 = __builtin_fmaf(w1[r], dr, v2);
+                    }
+                    if (cb >= 0 && cb + a.Kb <= 256) {
+                        a.out0[xo] = v1;
+                        a.out0[xo + 1] = v2;
+                    } else {
+                        float* pp = a.out1 + (((int64_t)b * a.tiles_n + tn) * 2 + (cb < 0 ? 0 : 1)) * 2;
+                        pp[0] = v1;
+                        pp[1] = v2;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+};
+
+// dx of the pairs cut by a tile edge (the 2-D layer): pair p = 256 (t + 1) /
+// Kb spans tiles t and t + 1; each of its two inputs gets the head partial
+// of tile t plus the tail partial of tile t + 1.
+__global__ void dx_fixup2_kernel(const float* __restrict__ part, float* __restrict__ dx, int64_t N, int P,
+                                 int Kb, int tiles) {
+    const int edges = tiles - 1;
+    const int64_t total = N * edges;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = k / edges;
+        const int t = (int)(k - b * edges);
+        const int64_t c = 256 * (int64_t)(t + 1);
+        if (c % Kb == 0 || c / Kb >= P) continue;
+        const int64_t o = b * 2 * P + 2 * (c / Kb);
+        const float* head = part + ((b * tiles + t) * 2 + 1) * 2;
+        const float* tail = part + ((b * tiles + t + 1) * 2 + 0) * 2;
+        dx[o] = head[0] + tail[0];
+        dx[o + 1] = head[1] + tail[1];
     }
 }
 
@@ -946,6 +1212,7 @@ GemmArgs base_args(const Plan& p, const void* x) {
     a.g = p.gk;
     a.N = (int)p.N;
     a.I = (int)p.I;
+    a.xI = (int)p.xI;
     a.O = (int)p.O;
     a.K = p.K;
     a.Kb = p.Kb;
@@ -1041,7 +1308,32 @@ static hipError_t dc_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
     return run_gemm<TS, LoadA, GenB<TS, 2, 32>, EpiDC>(a, s);
 }
 
+template <typename TS>
+static hipError_t fwd_dispatch_pair(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    const int n = fwd_nin(p);           // pairs meeting a k-tile, rounded up to a power of two
+    if (n <= 2) return run_gemm<TS, GenA2<TS, 2>, LoadB, EpiY>(a, s);
+    if (n <= 4) return run_gemm<TS, GenA2<TS, 4>, LoadB, EpiY>(a, s);
+    return run_gemm<TS, GenA2<TS, 8>, LoadB, EpiY>(a, s);
+}
+
+// (pairs per wave, zero-fill instructions per pair) of the 2-D dC generator:
+// Kb = 16 meets up to 17 pairs per tile (3 per wave), Kb 25..49 up to 12 (2
+// per wave), Kb >= 64 up to 5 (1 per wave).  N1 pairs per wave give one
+// (row, pair) item per lane: 1 with bf16's 64-row k-tiles, 2 with float32's 32.
+template <typename TS>
+static hipError_t dc_dispatch_pair(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    constexpr int N1 = 64 / Traits<TS>::BK;
+    const int zr = (p.Kb + 7) / 8;
+    const int nq = dc_nqw(p);
+    if (zr <= 2 && nq <= 4) return run_gemm<TS, LoadA, GenB2<TS, 4, 2>, EpiDC>(a, s);
+    if (zr <= 7 && nq <= 2) return run_gemm<TS, LoadA, GenB2<TS, 2, 7>, EpiDC>(a, s);
+    if (zr <= 8 && nq <= N1) return run_gemm<TS, LoadA, GenB2<TS, N1, 8>, EpiDC>(a, s);
+    if (zr <= 16 && nq <= N1) return run_gemm<TS, LoadA, GenB2<TS, N1, 16>, EpiDC>(a, s);
+    return run_gemm<TS, LoadA, GenB2<TS, N1, 32>, EpiDC>(a, s);
+}
+
 static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
+    if (p.pair) return p.dtype == KAN_F32 ? fwd_dispatch_pair<float>(p, a, s) : fwd_dispatch_pair<uint16_t>(p, a, s);
     if (p.sparse) {
         if (p.NG == 4) return run_gemm<uint16_t, GenS<4>, LoadB, EpiY>(a, s);
         if (p.NG == 6) return run_gemm<uint16_t, GenS<6>, LoadB, EpiY>(a, s);
@@ -1083,6 +1375,15 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     // both operands are copied and equally large per tile: 8 x 4 tiles per
     // 32 resident workgroups of an XCD share each dy and each C'^T tile
     a.group_m = 8;
+    if (p.pair) {
+        hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDX2>(a, s)
+                                          : run_gemm<uint16_t, LoadA, LoadB, EpiDX2>(a, s);
+        if (e != hipSuccess || p.tiles_dx < 2) return e;
+        hipLaunchKernelGGL(dx_fixup2_kernel,
+                           dim3((unsigned)std::min<int64_t>((p.N * (p.tiles_dx - 1) + 255) / 256, 16384)),
+                           dim3(256), 0, s, part, dx, (int64_t)p.N, (int)p.I, p.Kb, (int)p.tiles_dx);
+        return hipGetLastError();
+    }
     hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDX>(a, s)
                                       : run_gemm<uint16_t, LoadA, LoadB, EpiDX>(a, s);
     if (e != hipSuccess || p.tiles_dx < 2) return e;
@@ -1103,8 +1404,11 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.out0 = dC;
     a.out1 = dW;
     a.group_m = 2;
-    if (p.split_dc <= 1)
+    auto dispatch = [&]() {
+        if (p.pair) return p.dtype == KAN_F32 ? dc_dispatch_pair<float>(p, a, s) : dc_dispatch_pair<uint16_t>(p, a, s);
         return p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
+    };
+    if (p.split_dc <= 1) return dispatch();
     // the batch in split_dc fixed slices: partials, then a sum in slice order
     const int64_t nc = p.O * p.I * p.K, nw = p.O * p.I;
     float* wpart = cpart + p.split_dc * nc;
@@ -1113,7 +1417,7 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.nks = (int)p.nks_dc;
     a.ostride0 = nc;
     a.ostride1 = nw;
-    hipError_t e = p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
+    hipError_t e = dispatch();
     if (e == hipSuccess && dC) e = sum_slices(cpart, dC, nc, p.split_dc, s);
     if (e == hipSuccess && dW) e = sum_slices(wpart, dW, nw, p.split_dc, s);
     return e;

@@ -191,6 +191,63 @@ def kan_group_backward(x, C, dy, grid, need_dx=True, need_dC=True, ws=None):
     return dx, dC
 
 
+def surface_desc(x, C, grid):
+    """``kan_surface_desc_t`` for ``x [N, 2P]`` and ``C [O, P, G+3, G+3]``."""
+    lo, hi, G = grid
+    if x.dim() != 2 or x.shape[1] % 2 or C.dim() != 4:
+        raise ValueError("x must be [N, 2P] and C [O, P, G+3, G+3]")
+    O, P, K1, K2 = C.shape
+    if 2 * P != x.shape[1] or K1 != G + 3 or K2 != G + 3:
+        raise ValueError("C must be [O, %d, %d, %d], got %s" % (x.shape[1] // 2, G + 3, G + 3, tuple(C.shape)))
+    if x.dtype != C.dtype:
+        raise ValueError("x and C must share one dtype")
+    return L.make_surface_desc(x.shape[0], P, O, lo, hi, G, _DTYPES[x.dtype])
+
+
+def kan_surface_workspace_size(desc, pass_):
+    n = L.lib().kan_surface_workspace_size(ctypes.byref(desc), int(pass_))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid 2-D layer description")
+    return int(n)
+
+
+def _surface_ws(desc, pass_, device):
+    n = kan_surface_workspace_size(desc, pass_)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def kan_surface_forward(x, C, grid, ws=None, out=None):
+    """``y [N, O]`` float32 of the 2-D tensor-product layer
+    ``y[b, j] = sum_p sum_{m,n} C[j, p, m, n] B_m(x[b, 2p]) B_n(x[b, 2p+1])``."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    desc = surface_desc(x, C, grid)
+    buf, n = ws if ws is not None else _surface_ws(desc, L.KAN_PASS_FORWARD, x.device)
+    y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
+                                                device=x.device)
+    _check_tensor(y, "y", (torch.float32,), x.device)
+    L.check(L.lib().kan_surface_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(y), _ptr(buf), n,
+                                        _stream(x)), "kan_surface_forward")
+    return y
+
+
+def kan_surface_backward(x, C, dy, grid, need_dx=True, need_dC=True, ws=None):
+    """``(dx [N, 2P], dC [O, P, G+3, G+3])`` float32; unrequested ones are None."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    _check_tensor(dy, "dy", (torch.float32,), x.device)
+    desc = surface_desc(x, C, grid)
+    if tuple(dy.shape) != (x.shape[0], C.shape[0]):
+        raise ValueError("dy must be [N, O]")
+    buf, n = ws if ws is not None else _surface_ws(desc, L.KAN_PASS_BACKWARD, x.device)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty(x.shape, **f32) if need_dx else None
+    dC = torch.empty(C.shape, **f32) if need_dC else None
+    L.check(L.lib().kan_surface_backward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(dy), _ptr(dx), _ptr(dC),
+                                         _ptr(buf), n, _stream(x)), "kan_surface_backward")
+    return dx, dC
+
+
 def kan_cast_f32_to_bf16(t, out=None):
     """Round-to-nearest-even float32 -> bfloat16 on the device."""
     _check_tensor(t, "input", (torch.float32,))

@@ -36,6 +36,13 @@ Grouped spline activation workloads (``make_grouped``):
   spline per channel (2048 groups), G = 8, bf16 x and C: per-coordinate
   spline curves over a 2048-wide projection; same draws.
 
+2-D tensor-product layer workload (``make_surface``):
+
+* ``s1``  8192 rows, 1024 inputs taken as 512 consecutive pairs -> 1024
+  outputs, G = 5, bf16 x and C (the 1024 -> 1024 layer of the InKAN
+  performance table, with bicubic surfaces over input pairs);
+  x ~ U(-1, 1); C ~ N(0, 0.02); dy ~ N(0, 1).
+
 ``N(0, s)`` means standard deviation ``s``.  Draws are float32 from NumPy's
 ``default_rng`` seeded by ``SeedSequence([1000 + id, G])``, with child
 streams spawned in the order x, then per layer C and W_base, then dy.  bf16
@@ -65,6 +72,11 @@ CONFIGS = {
 GROUPED = {
     "g1": dict(id=11, N=25216, I=3072, groups=8, G=5, lo=-1.0, hi=1.0, dtype="bf16"),
     "g2": dict(id=12, N=32768, I=2048, groups=2048, G=8, lo=-1.0, hi=1.0, dtype="bf16"),
+}
+
+
+SURFACE = {
+    "s1": dict(id=21, N=8192, P=512, O=1024, G=5, lo=-1.0, hi=1.0, dtype="bf16", c_std=0.02),
 }
 
 
@@ -217,3 +229,43 @@ def random_grouped(N, I, groups, G, dtype="f32", seed=0, lo=-1.0, hi=1.0, specia
         x = to_bf16_values(x)
         C = to_bf16_values(C)
     return dict(N=N, I=I, groups=groups, G=G, lo=lo, hi=hi, dtype=dtype, x=x, C=C, dy=dy)
+
+
+def make_surface(name, N=None):
+    """Inputs of a 2-D layer workload: dict with ``name, N, P, O, G, lo, hi,
+    dtype, x [N, 2P], C [O, P, G+3, G+3], dy [N, O]``."""
+    spec = dict(SURFACE[name])
+    P, O, G = spec["P"], spec["O"], spec["G"]
+    N = spec["N"] if N is None else N
+    kids = np.random.SeedSequence([1000 + spec["id"], G]).spawn(3)
+    x = _draw_x(np.random.default_rng(kids[0]), (N, 2 * P), ("uniform", 1.0), False)
+    C = np.random.default_rng(kids[1]).standard_normal((O, P, G + 3, G + 3), dtype=np.float32) \
+        * np.float32(spec["c_std"])
+    dy = np.random.default_rng(kids[2]).standard_normal((N, O), dtype=np.float32)
+    if spec["dtype"] == "bf16":
+        x = to_bf16_values(x)
+        C = to_bf16_values(C)
+    spec.update(name=name, N=N, x=x, C=C, dy=dy)
+    return spec
+
+
+def random_surface(N, P, O, G, dtype="f32", seed=0, lo=-1.0, hi=1.0, special=True):
+    """A small random 2-D layer for parity tests (x mixed with the knots and
+    points around and far outside the grid, as in ``random_layer``)."""
+    rng = np.random.default_rng(np.random.SeedSequence([11, seed, N, P, O, G]))
+    mid, half = 0.5 * (lo + hi), 0.5 * (hi - lo)
+    x = (mid + half * 1.2 * (2 * rng.random((N, 2 * P)) - 1)).astype(np.float32)
+    if special and N * P > 0:
+        h = (hi - lo) / G
+        pts = [lo + (r - 3) * h for r in range(G + 7)]
+        pts += [lo, hi, np.nextafter(np.float32(hi), np.float32(-np.inf)),
+                lo - 3 * h - 1e-3, hi + 3 * h + 1e-3, lo - 10.0, hi + 10.0, 0.0]
+        pts = np.asarray(pts, dtype=np.float32)
+        mask = rng.random((N, 2 * P)) < 0.2
+        x[mask] = pts[rng.integers(0, len(pts), size=int(mask.sum()))]
+    C = (rng.standard_normal((O, P, G + 3, G + 3)) * 0.1).astype(np.float32)
+    dy = rng.standard_normal((N, O)).astype(np.float32)
+    if dtype == "bf16":
+        x = to_bf16_values(x)
+        C = to_bf16_values(C)
+    return dict(N=N, P=P, O=O, G=G, lo=lo, hi=hi, dtype=dtype, x=x, C=C, dy=dy)
