@@ -39,7 +39,10 @@ WORKLOAD_TEXT = {
           "G=5 cubic on [-1,1], bf16 x/C, fp32 y/dx/dC",
     "g2": "per-channel spline activation, 32768 rows (8 x 4096 tokens) x 2048 channels, 2048 "
           "groups, G=8 cubic on [-1,1], bf16 x/C, fp32 y/dx/dC",
+    "s1": "2-D tensor-product spline layer, 8192 rows, 1024 inputs as 512 pairs -> 1024 outputs, "
+          "G=5 bicubic on [-1,1]^2, bf16 x/C, fp32 accumulate",
 }
+SURFACE_METRIC = "2-D tensor-product KAN layer fwd+bwd rows/sec; % of MFMA roofline, 1 GPU"
 GROUPED_METRIC = "grouped spline activation fwd+bwd elements/sec; % of HBM roofline, 1 GPU"
 MFMA_FILES = ("kan_mfma.hip", "kan_device.h", "kan_sparse.h", "kan_internal.h", "kan_api.cpp")
 GROUPED_FILES = ("kan_grouped.hip", "kan_device.h", "kan_internal.h", "kan_api.cpp")
@@ -139,6 +142,9 @@ def main():
         sys.exit(2)
     if args.workload.startswith("g"):
         grouped_bench(args)
+        return
+    if args.workload.startswith("s"):
+        surface_bench(args)
         return
 
     import numpy as np
@@ -409,6 +415,134 @@ def grouped_bench(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = grouped_cpu_baseline(d, args.cpu_rows)
     print(json.dumps(out))
+
+
+def surface_bench(args):
+    """One training step of the 2-D tensor-product layer: forward (packing
+    included), dx (packing of C^T and dy included) and dC, timed per stage
+    with HIP events on the launch stream."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from kolmogorov_arnold_network_amd import _lib as L
+    from kolmogorov_arnold_network_amd import functional as F
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.make_surface(args.workload)
+    N, P, O, G = d["N"], d["P"], d["O"], d["G"]
+    K1 = G + 3
+    tdt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+    x = torch.from_numpy(d["x"]).to(dev).to(tdt)
+    C = torch.from_numpy(d["C"]).to(dev).to(tdt)
+    dy = torch.from_numpy(d["dy"]).to(dev)
+    y = torch.empty((N, O), dtype=torch.float32, device=dev)
+    dx = torch.empty((N, 2 * P), dtype=torch.float32, device=dev)
+    dC = torch.empty(C.shape, dtype=torch.float32, device=dev)
+    grid = (d["lo"], d["hi"], G)
+    desc = F.surface_desc(x, C, grid)
+    dprep = F.surface_desc(x, C, grid)
+    dprep.flags = L.KAN_FLAG_PREPARED
+    nf = F.kan_surface_workspace_size(desc, L.KAN_PASS_FORWARD)
+    nb = F.kan_surface_workspace_size(desc, L.KAN_PASS_BACKWARD)
+    wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    lib = L.lib()
+    Pt = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    S = ctypes.c_void_p(stream.cuda_stream)
+    names = ["surface.fwd", "surface.dx", "surface.dC"]
+    events = None
+
+    def rec(k):
+        if events is not None:
+            events[k].record(stream)
+
+    def step():
+        rec(0)
+        L.check(lib.kan_surface_forward(ctypes.byref(desc), Pt(x), Pt(C), Pt(y), Pt(wsf), nf, S), "forward")
+        rec(1)
+        L.check(lib.kan_surface_backward(ctypes.byref(desc), Pt(x), Pt(C), Pt(dy), Pt(dx), None, Pt(wsb), nb, S),
+                "backward dx")
+        rec(2)
+        L.check(lib.kan_surface_backward(ctypes.byref(dprep), Pt(x), Pt(C), Pt(dy), None, Pt(dC), Pt(wsb), nb, S),
+                "backward dC")
+        rec(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_step = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        per_step.append(events)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {nm: sum(ev[k].elapsed_time(ev[k + 1]) for ev in per_step) / args.steps
+                for k, nm in enumerate(names)}
+    ms_per_step = 1e3 * elapsed / args.steps
+    step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in per_step)
+    median_ms = step_ms[len(step_ms) // 2]
+    # algorithmic: the 16 non-zero products per (row, pair) in each of the
+    # three contractions; executed: all (G+3)^2 columns of a pair
+    alg_one = 2.0 * N * O * P * 16
+    exe_one = 2.0 * N * O * P * K1 * K1
+    dom = max(names, key=lambda nm: stage_ms[nm])
+    peak = PEAK_TFLOPS[d["dtype"]]
+    t_dom = stage_ms[dom] * 1e-3
+    roof = {"bound": "mfma", "kernel": dom, "achieved": alg_one / t_dom / 1e12, "peak": peak,
+            "unit": "TFLOP/s", "frac": alg_one / t_dom / 1e12 / peak,
+            "traffic": read_traffic(args.workload, dom.split(".")[1]),
+            "executed_achieved": exe_one / t_dom / 1e12, "executed_frac": exe_one / t_dom / 1e12 / peak,
+            "dominant_ms": stage_ms[dom],
+            "stage_executed_TFLOPs": {nm: exe_one / (stage_ms[nm] * 1e-3) / 1e12 for nm in names}}
+    out = {
+        "metric": SURFACE_METRIC,
+        "value": N * 1e3 / ms_per_step,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "median_ms_per_step": median_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": d["dtype"],
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "rows": N, "pairs": P,
+                   "outputs": O, "G": G},
+        "gflops_algorithmic": 3 * alg_one / (ms_per_step * 1e-3) / 1e9,
+        "gflops_executed": 3 * exe_one / (ms_per_step * 1e-3) / 1e9,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = surface_cpu_baseline(d, args.cpu_rows)
+    print(json.dumps(out))
+
+
+def surface_cpu_baseline(d, rows=None):
+    """The float64 NumPy oracle of the 2-D layer on a bounded sample of rows:
+    y, dx and the rows' own dC contributions, timed on the host."""
+    import oracle
+    import workloads as wl
+    N = d["N"]
+    n = min(N, rows or 256)
+    R = wl.sample_indices(N, n, 97)
+    x, dy = d["x"][R].astype("float64"), d["dy"][R].astype("float64")
+    t0 = time.perf_counter()
+    oracle.surface_forward(x, d["C"], d["lo"], d["hi"], d["G"])
+    oracle.surface_backward(x, d["C"], dy, d["lo"], d["hi"], d["G"])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "rows/s", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": "%d of %d rows: forward, dx and the rows' own dC contributions in float64 "
+                      "NumPy, %.1f s; CPU %s" % (n, N, dt, _cpu_model())}
 
 
 def grouped_cpu_baseline(d, rows=None):

@@ -255,7 +255,9 @@ typedef struct {
     int64_t O;          /* outputs, >= 1 */
     kan_grid_t grid;    /* 1 <= G <= 13, degree 3 */
     int32_t dtype;      /* kan_dtype_t: storage of x and C */
-    int32_t flags;      /* must be 0 */
+    int32_t flags;      /* 0, or KAN_FLAG_PREPARED: the workspace holds this
+                           pass's packed operands from the last call without
+                           the flag (same desc, C, and dy for the backward) */
 } kan_surface_desc_t;
 
 /* Bytes of workspace a pass of the 2-D layer needs (SIZE_MAX if `desc` is

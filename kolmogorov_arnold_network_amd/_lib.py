@@ -150,5 +150,9 @@ def make_group_desc(N, I, groups, lo, hi, G, dtype, degree=3):
 def make_surface_desc(N, P, O, lo, hi, G, dtype, degree=3, flags=0):
     d = kan_surface_desc_t()
     d.N, d.P, d.O, d.dtype, d.flags = int(N), int(P), int(O), int(dtype), int(flags)
+    return _fill_grid(d, lo, hi, G, degree)
+
+
+def _fill_grid(d, lo, hi, G, degree):
     d.grid.lo, d.grid.hi, d.grid.G, d.grid.degree = float(lo), float(hi), int(G), int(degree)
     return d

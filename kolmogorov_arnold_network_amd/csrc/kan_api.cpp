@@ -122,7 +122,7 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     int st = grid_check(d->grid, 13);
     if (st != KAN_OK) return st;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
-    if (d->flags != 0) return KAN_ERR_UNSUPPORTED;
+    if (d->flags & ~KAN_FLAG_PREPARED) return KAN_ERR_UNSUPPORTED;
     Plan q;
     memset(&q, 0, sizeof(q));
     q.pair = 1;
@@ -428,8 +428,10 @@ int kan_surface_forward(const kan_surface_desc_t* desc, const void* x, const voi
     if (p.N == 0) return KAN_OK;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    st = prepare_impl(p, KAN_PASS_FORWARD, C, nullptr, nullptr, ws, s);
-    if (st != KAN_OK) return st;
+    if (!(desc->flags & KAN_FLAG_PREPARED)) {
+        st = prepare_impl(p, KAN_PASS_FORWARD, C, nullptr, nullptr, ws, s);
+        if (st != KAN_OK) return st;
+    }
     return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
                                      reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
 }
@@ -458,8 +460,10 @@ int kan_surface_backward(const kan_surface_desc_t* desc, const void* x, const vo
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (p.N == 0) return dC ? status_of(launch_fill_zero(dC, p.O * p.I * p.K, s)) : KAN_OK;
-    st = prepare_impl(p, KAN_PASS_BACKWARD, C, nullptr, dy, ws, s);
-    if (st != KAN_OK) return st;
+    if (!(desc->flags & KAN_FLAG_PREPARED)) {
+        st = prepare_impl(p, KAN_PASS_BACKWARD, C, nullptr, dy, ws, s);
+        if (st != KAN_OK) return st;
+    }
     hipError_t e = hipSuccess;
     if (dx)
         e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),

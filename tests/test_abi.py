@@ -314,6 +314,72 @@ def test_group_pointer_checks(L):
     assert lib.kan_group_forward(ctypes.byref(e), None, C, None, None) == L.KAN_OK
 
 
+def sdesc(L, N=100, P=8, O=20, G=5, dtype=1, lo=-1.0, hi=1.0, degree=3, flags=0):
+    return L.make_surface_desc(N, P, O, lo, hi, G, dtype, degree, flags)
+
+
+def test_surface_struct_layout(L):
+    assert ctypes.sizeof(L.kan_surface_desc_t) == 3 * 8 + 16 + 2 * 4
+
+
+def test_surface_workspace_sizes(L):
+    """The layer's layout restated for pairs: K = Kb = (G+3)^2 columns per
+    pair, no structured-sparse forward, and dx partials for both inputs of a
+    pair cut by a tile edge."""
+    r = lambda a, b: (a + b - 1) // b * b
+    for dt, es, bk in [(0, 4, 32), (1, 2, 64)]:
+        for (N, P, O, G) in [(100, 8, 20, 5), (8192, 512, 1024, 5), (300, 7, 33, 8), (5, 3, 2, 1),
+                             (77, 4, 300, 13)]:
+            Kb = (G + 3) ** 2
+            Op, Np = r(O, 256), r(N, 256)
+            kf = r(P * Kb, bk)
+            Pf, _ = k_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
+            want_f = r(Op * kf * es, 256) + (r(Pf * N * O * 4, 256) if Pf > 1 else 0)
+            tiles = (P * Kb + 255) // 256
+            want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 4 * 4, 256)
+            Pd, _ = k_slices((Op // 256) * tiles, Np // bk, O * P * Kb * 4, es)
+            want_b += r(Pd * O * P * Kb * 4, 256) if Pd > 1 else 0
+            d = sdesc(L, N=N, P=P, O=O, G=G, dtype=dt)
+            assert L.lib().kan_surface_workspace_size(ctypes.byref(d), 0) == want_f
+            assert L.lib().kan_surface_workspace_size(ctypes.byref(d), 1) == want_b
+    bad = ctypes.c_size_t(-1).value
+    assert L.lib().kan_surface_workspace_size(ctypes.byref(sdesc(L)), 2) == bad
+    assert L.lib().kan_surface_workspace_size(None, 0) == bad
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), -2), (dict(P=0), -2), (dict(O=0), -2), (dict(G=0), -3), (dict(G=14), -3),
+    (dict(lo=1.0, hi=0.5), -3), (dict(hi=float("inf")), -3), (dict(dtype=5), -4), (dict(degree=1), -8),
+    (dict(flags=2), -8), (dict(P=1 << 30), -2)])
+def test_surface_bad_descriptors(L, kw, code):
+    d = sdesc(L, **kw)
+    lib = L.lib()
+    assert lib.kan_surface_forward(ctypes.byref(d), X, C, Y, WS, 1 << 40, None) == code
+    assert lib.kan_surface_backward(ctypes.byref(d), X, C, DY, DX, DC, WS, 1 << 40, None) == code
+
+
+def test_surface_pointer_checks(L):
+    d = sdesc(L)
+    lib = L.lib()
+    nf = lib.kan_surface_workspace_size(ctypes.byref(d), 0)
+    nb = lib.kan_surface_workspace_size(ctypes.byref(d), 1)
+    fwd = lambda *a: lib.kan_surface_forward(ctypes.byref(d), *a, None)
+    bwd = lambda *a: lib.kan_surface_backward(ctypes.byref(d), *a, None)
+    assert fwd(None, C, Y, WS, nf) == L.KAN_ERR_NULL
+    assert fwd(X, None, Y, WS, nf) == L.KAN_ERR_NULL
+    assert fwd(X, C, None, WS, nf) == L.KAN_ERR_NULL
+    assert fwd(X + 2, C, Y, WS, nf) == L.KAN_ERR_ALIGN
+    assert fwd(X, C, Y, WS, nf - 1) == L.KAN_ERR_WORKSPACE
+    assert fwd(X, C, Y, WS + 64, nf) == L.KAN_ERR_ALIGN
+    assert fwd(X, C, X, WS, nf) == L.KAN_ERR_ALIAS
+    assert fwd(X, C, Y, C, nf) == L.KAN_ERR_ALIAS
+    assert bwd(X, C, None, DX, DC, WS, nb) == L.KAN_ERR_NULL
+    assert bwd(X, C, DY, DX, DC, WS, nb - 1) == L.KAN_ERR_WORKSPACE
+    assert bwd(X, C, DY, DY, DC, WS, nb) == L.KAN_ERR_ALIAS
+    assert bwd(X, C, DY, DX, DX, WS, nb) == L.KAN_ERR_ALIAS
+    assert bwd(X, C, DY, None, None, WS, nb) == L.KAN_OK        # nothing asked: no work
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     from kolmogorov_arnold_network_amd import _lib
     monkeypatch.setattr(_lib, "_lib", None)
