@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--code-digest", nargs="?", const="mfma", default=None, choices=["mfma", "grouped"],
                     help="print the digest that ties a counter summary to the kernel source")
+    ap.add_argument("--degree", type=int, default=3, help="spline degree of --basis-forms (1 .. 5)")
     ap.add_argument("--basis-forms", type=int, default=0, metavar="POINTS",
                     help="time the local-span and truncated-power basis evaluations on POINTS inputs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -70,10 +71,11 @@ def parse():
     return args
 
 
-def basis_forms(n, steps):
+def basis_forms(n, steps, degree=3):
     """Dense B and dB of n float32 inputs on [-1, 1] (+ one grid width each
     side) from the local span form (kan_basis_eval) and from the truncated-power
-    form (kan_basis_eval_tp), at G = 8, 20, 50: points/s and output GB/s."""
+    form (kan_basis_eval_tp), at G = 8, 20, 50 and the given degree: points/s
+    and output GB/s."""
     import ctypes
     import torch
     from kolmogorov_arnold_network_amd import _lib as L
@@ -81,10 +83,10 @@ def basis_forms(n, steps):
     x = torch.rand(n, device="cuda:0", generator=g) * 2.5 - 1.25
     res = {}
     for G in (8, 20, 50):
-        B = torch.empty(n, G + 3, device="cuda:0")
+        B = torch.empty(n, G + degree, device="cuda:0")
         dB = torch.empty_like(B)
         for name, fn in (("local_span", L.lib().kan_basis_eval), ("truncated_power", L.lib().kan_basis_eval_tp)):
-            grid = L.kan_grid_t(-1.0, 1.0, G, 3)
+            grid = L.kan_grid_t(-1.0, 1.0, G, degree)
             S = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             call = lambda: L.check(fn(ctypes.byref(grid), n, L.KAN_F32, ctypes.c_void_p(x.data_ptr()),
                                       ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(dB.data_ptr()), S), name)
@@ -97,11 +99,11 @@ def basis_forms(n, steps):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / steps
-            out_bytes = 2 * n * (G + 3) * 4
+            out_bytes = 2 * n * (G + degree) * 4
             res["G%d_%s" % (G, name)] = {"ms": ms, "points_per_s": n / (ms * 1e-3),
                                           "output_GB_per_s": out_bytes / (ms * 1e-3) / 1e9,
                                           "hbm_frac": out_bytes / (ms * 1e-3) / 8e12}
-    print(json.dumps({"basis_forms": res, "points": n, "steps": steps}))
+    print(json.dumps({"basis_forms": res, "points": n, "steps": steps, "degree": degree}))
 
 
 def copy_probe(nbytes):
@@ -132,7 +134,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.basis_forms:
-        basis_forms(args.basis_forms, args.steps)
+        basis_forms(args.basis_forms, args.steps, args.degree)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the KAN layer path here has no multi-GPU "

@@ -165,23 +165,31 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* The span / local-basis step on its own, for checking the device basis.
- * x [n] in `dtype`; B and dB [n, G+3] float32 outputs (either may be NULL):
- * B[k, m] = B_m(x[k]) and dB[k, m] = dB_m/dx(x[k]), computed from the 4
- * non-zero pieces of the knot span that holds x[k] (InKAN page, "Why InKAN?":
- * stable piecewise evaluation, local 4-basis lookup) and written densely. */
+ * x [n] in `dtype`; B and dB [n, G+D] float32 outputs (either may be NULL),
+ * D = grid->degree: B[k, m] = B_m(x[k]) and dB[k, m] = dB_m/dx(x[k]), computed
+ * from the D+1 non-zero pieces of the knot span that holds x[k] (InKAN page,
+ * "Why InKAN?": stable piecewise evaluation, local basis lookup) and written
+ * densely.  Here the degree may be 1 .. 5 (the layer entry points take 3):
+ * the grid is extended by D knots on each side (t_r = lo + (r - D) h), and
+ * for D != 3 the pieces come from the uniform-knot recurrence
+ * N^q_r = ((u + q - r) N^{q-1}_{r-1} + (r + 1 - u) N^{q-1}_r) / q, whose
+ * terms are non-negative. */
 int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
                    float* B, float* dB, void* stream);
 
 /* The same dense B and dB from the truncated-power form instead (FlashKAN
- * project page: each cubic B-spline is a combination of five shifted
- * (x)_+^3 terms, with the normalised coordinate clamped to [0, k+1]):
- * u = (x[k] - t_m) / h clamped to [0, 4],
- *     B_m = (u^3 - 4 (u-1)_+^3 + 6 (u-2)_+^3 - 4 (u-3)_+^3) / 6,
- *     dB_m/dx = (u^2 - 4 (u-1)_+^2 + 6 (u-2)_+^2 - 4 (u-3)_+^2) / (2 h).
+ * project page: a degree-k B-spline is a combination of k+2 shifted
+ * (x)_+^k terms, with the normalised coordinate clamped to [0, k+1]):
+ * u = (x[k] - t_m) / h clamped to [0, D+1],
+ *     B_m = sum_i (-1)^i C(D+1, i) (u-i)_+^D / D!,
+ *     dB_m/dx = sum_i (-1)^i C(D+1, i) (u-i)_+^(D-1) / ((D-1)! h),
+ * at D = 3: B_m = (u^3 - 4 (u-1)_+^3 + 6 (u-2)_+^3 - 4 (u-3)_+^3) / 6.  At D = 1
+ * the derivative's step terms take the unclamped u with (w)_+^0 = [w >= 0].
  * Every (k, m) is evaluated on its own, with no span lookup.  The alternating
  * sum cancels near u = 4, so in float32 it is less accurate than
- * kan_basis_eval (absolute error up to ~1e-5, and values may round slightly
- * below 0, where the local form cannot; InKAN page, "Why InKAN?").  Arguments,
+ * kan_basis_eval (absolute error up to ~1e-5 at D = 3, more at higher degree,
+ * and values may round slightly below 0, where the local form cannot; InKAN
+ * page, "Why InKAN?").  Arguments,
  * validation and errors as for kan_basis_eval. */
 int kan_basis_eval_tp(const kan_grid_t* grid, int64_t n, int dtype, const void* x,
                       float* B, float* dB, void* stream);

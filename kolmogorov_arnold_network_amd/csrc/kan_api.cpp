@@ -371,25 +371,31 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
 static int basis_eval_impl(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
                            float* dB, bool truncated_power, void* stream) {
     if (!grid) return KAN_ERR_NULL;
-    kan_desc_t d;
-    memset(&d, 0, sizeof(d));
-    d.N = n < 0 ? -1 : 1;
-    d.I = 1;
-    d.O = 1;
-    d.grid = *grid;
-    d.dtype = dtype;
-    Plan p;
-    int st = make_plan(&d, &p);
+    // the degree-3 checks of the layer, with any degree 1 .. 5 accepted
+    kan_grid_t g3 = *grid;
+    const int degree = grid->degree;
+    if (degree < 1 || degree > 5) return KAN_ERR_UNSUPPORTED;
+    g3.degree = 3;
+    int st = grid_check(g3, kMaxG);
     if (st != KAN_OK) return st;
-    if (n > kIndexLimit / (p.K > 0 ? p.K : 1)) return KAN_ERR_SHAPE;
+    if (n < 0) return KAN_ERR_SHAPE;
+    if (dtype != KAN_F32 && dtype != KAN_BF16) return KAN_ERR_DTYPE;
+    const int K = grid->G + degree;
+    if (n > kIndexLimit / K) return KAN_ERR_SHAPE;
     if (n == 0) return KAN_OK;
     if (!x || (!B && !dB)) return KAN_ERR_NULL;
     if (!aligned(x, 16) || (B && !aligned(B, 16)) || (dB && !aligned(dB, 16))) return KAN_ERR_ALIGN;
-    const size_t ob = (size_t)n * p.K * 4;
-    const Range rx{x, (size_t)n * p.esize}, rb{B, ob}, rd{dB, ob};
+    const size_t ob = (size_t)n * K * 4;
+    const Range rx{x, (size_t)n * (dtype == KAN_F32 ? 4 : 2)}, rb{B, ob}, rd{dB, ob};
     if (overlap(rx, rb) || overlap(rx, rd) || overlap(rb, rd)) return KAN_ERR_ALIAS;
+    // knot units from t_0 = lo - degree h
+    GridK gk;
+    const double lo = grid->lo, hi = grid->hi;
+    gk.G = grid->G;
+    gk.scale = (float)((double)gk.G / (hi - lo));
+    gk.shift = (float)((double)degree - lo * (double)gk.G / (hi - lo));
     (void)hipGetLastError();
-    return status_of(launch_basis_eval(p.gk, n, dtype, x, B, dB, truncated_power, (hipStream_t)stream));
+    return status_of(launch_basis_eval(gk, n, dtype, x, B, dB, truncated_power, degree, (hipStream_t)stream));
 }
 
 int kan_basis_eval(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,

@@ -72,6 +72,101 @@ __global__ void basis_eval_kernel(GridK g, int64_t n, const TS* __restrict__ x,
     }
 }
 
+// ---- basis functions of degree D != 3 (basis evaluation only) ----
+// The D + 1 non-zero uniform B-splines of degree D on a knot span, by local
+// coordinate u in [0, 1]: value r belongs to basis function s - D + r.  They
+// come from the degree-by-degree recurrence on uniform knots,
+//     N^q_r = ((u + q - r) N^{q-1}_{r-1} + (r + 1 - u) N^{q-1}_r) / q,
+// whose terms are all non-negative on [0, 1] (no alternating sum), and
+// the derivatives from one degree lower: dN^D_r/dx = (N^{D-1}_{r-1} -
+// N^{D-1}_r) / h.
+template <int D>
+__device__ __forceinline__ void local_basis(float u, float scale, float b[D + 1], float d[D + 1]) {
+    float N[D + 1];
+    N[0] = 1.0f;
+#pragma unroll
+    for (int q = 1; q <= D; ++q) {
+        if (q == D) {
+#pragma unroll
+            for (int r = 0; r <= D; ++r)
+                d[r] = ((r >= 1 ? N[r - 1] : 0.0f) - (r <= D - 1 ? N[r] : 0.0f)) * scale;
+        }
+        const float inv = 1.0f / (float)q;
+        // descending r: N[r - 1] still holds degree q - 1 when N[r] is replaced
+#pragma unroll
+        for (int r = q; r >= 0; --r) {
+            float v = r >= 1 ? (u + (float)(q - r)) * N[r - 1] : 0.0f;
+            if (r <= q - 1) v = __builtin_fmaf((float)(r + 1) - u, N[r], v);
+            N[r] = v * inv;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r <= D; ++r) b[r] = N[r];
+}
+
+// Truncated-power form of one degree-D basis function (FlashKAN project page:
+// D + 2 shifted (x)_+^D terms, coordinate clamped to [0, D + 1]):
+// u = (x - t_m) / h, B = sum_i (-1)^i C(D+1, i) (u - i)_+^D / D!, and
+// B' = sum_i (-1)^i C(D+1, i) (u - i)_+^{D-1} / (D-1)! / h, summed in i order
+// (the i = D + 1 term vanishes under the clamp).  At D = 1 the derivative's
+// terms are steps (w)_+^0 = [w >= 0], the right-hand derivative, as the
+// half-open knot spans have it; each step's sign is taken from its own
+// single-rounding FMA x/h + (shift - (m + i)), the test span_u uses for the
+// span, since u - i from a rounded u can land on the knot from below.
+template <int D>
+__device__ __forceinline__ void tp_basis_deg(float x, const GridK& g, int m, float& b, float& d) {
+    constexpr float fact[6] = {1.0f, 1.0f, 2.0f, 6.0f, 24.0f, 120.0f};
+    const float scale = g.scale;
+    const float u_raw = __builtin_fmaf(x, scale, g.shift - (float)m);
+    const float u = __builtin_fminf(__builtin_fmaxf(u_raw, 0.0f), (float)(D + 1));
+    float sb = 0.0f, sd = 0.0f;
+    int c = 1;                                   // C(D+1, i)
+#pragma unroll
+    for (int i = 0; i <= D + 1; ++i) {
+        const float sgn = (i & 1) ? -(float)c : (float)c;
+        const float w = __builtin_fmaxf(u - (float)i, 0.0f);
+        float wp = 1.0f;                         // w^(D-1)
+#pragma unroll
+        for (int e = 0; e < D - 1; ++e) wp *= w;
+        if (i <= D) sb = __builtin_fmaf(sgn, wp * w, sb);
+        if (D == 1) sd += __builtin_fmaf(x, scale, g.shift - (float)(m + i)) >= 0.0f ? sgn : 0.0f;
+        else if (i <= D) sd = __builtin_fmaf(sgn, wp, sd);
+        c = c * (D + 1 - i) / (i + 1);
+    }
+    b = sb * (1.0f / fact[D]);
+    d = sd * (scale / fact[D - 1]);
+}
+
+// Dense B, dB [n, G + D] for degree D != 3, one element per thread; g.shift
+// places t_0 = lo - D h.
+template <typename TS, bool TP, int D>
+__global__ void basis_eval_deg_kernel(GridK g, int64_t n, const TS* __restrict__ x,
+                                      float* __restrict__ B, float* __restrict__ dB) {
+    const int K = g.G + D;
+    const int total = (int)(n * K);
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
+        const int k = e / K, m = e - k * K;
+        const float xv = load_f(x, k);
+        float b = 0.0f, d = 0.0f;
+        if constexpr (TP) {
+            tp_basis_deg<D>(xv, g, m, b, d);
+        } else {
+            float u;
+            const int r = m - (span_u(xv, g, u) - D);
+            float bb[D + 1], dd[D + 1];
+            local_basis<D>(u, g.scale, bb, dd);
+#pragma unroll
+            for (int q = 0; q <= D; ++q)
+                if (r == q) {
+                    b = bb[q];
+                    d = dd[q];
+                }
+        }
+        if (B) B[e] = b;
+        if (dB) dB[e] = d;
+    }
+}
+
 __global__ void cast_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
     for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
          k += (int64_t)gridDim.x * blockDim.x)
@@ -445,8 +540,29 @@ hipError_t allow_lds(Kern k, size_t bytes) {
 
 }  // namespace
 
+template <int D>
+static hipError_t basis_deg_run(const GridK& g, int64_t n, int dtype, const void* x, float* B, float* dB,
+                                bool tp, hipStream_t s) {
+    const dim3 grid(grid1d(n * (g.G + D))), block(256);
+    if (dtype == KAN_F32) {
+        auto k = tp ? basis_eval_deg_kernel<float, true, D> : basis_eval_deg_kernel<float, false, D>;
+        hipLaunchKernelGGL(k, grid, block, 0, s, g, n, static_cast<const float*>(x), B, dB);
+    } else {
+        auto k = tp ? basis_eval_deg_kernel<uint16_t, true, D> : basis_eval_deg_kernel<uint16_t, false, D>;
+        hipLaunchKernelGGL(k, grid, block, 0, s, g, n, static_cast<const uint16_t*>(x), B, dB);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
-                             float* dB, bool truncated_power, hipStream_t s) {
+                             float* dB, bool truncated_power, int degree, hipStream_t s) {
+    switch (degree) {
+        case 1: return basis_deg_run<1>(g, n, dtype, x, B, dB, truncated_power, s);
+        case 2: return basis_deg_run<2>(g, n, dtype, x, B, dB, truncated_power, s);
+        case 4: return basis_deg_run<4>(g, n, dtype, x, B, dB, truncated_power, s);
+        case 5: return basis_deg_run<5>(g, n, dtype, x, B, dB, truncated_power, s);
+        default: break;
+    }
     const dim3 grid(grid1d(n * (g.G + 3))), block(256);
     if (dtype == KAN_F32) {
         auto k = truncated_power ? basis_eval_kernel<float, true> : basis_eval_kernel<float, false>;

@@ -77,8 +77,9 @@ int make_plan(const kan_desc_t* desc, Plan* p);
 int make_plan_surface(const kan_surface_desc_t* desc, Plan* p);
 
 // ---- launchers (return hipError_t of the launch) ----
+// degree 1 .. 5; g built for that degree (t_0 = lo - degree h)
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,
-                             float* dB, bool truncated_power, hipStream_t s);
+                             float* dB, bool truncated_power, int degree, hipStream_t s);
 hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

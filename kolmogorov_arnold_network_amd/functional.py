@@ -120,25 +120,25 @@ def kan_backward(x, C, W, dy, grid, need_dx=True, need_dC=True, need_dW=True, va
     return dx, dC, dW
 
 
-def _basis(fn, name, x, grid, need_B, need_dB):
+def _basis(fn, name, x, grid, need_B, need_dB, degree):
     _check_tensor(x, "x", _DTYPES)
     lo, hi, G = grid
-    g = L.kan_grid_t(float(lo), float(hi), int(G), 3)
+    g = L.kan_grid_t(float(lo), float(hi), int(G), int(degree))
     n = x.numel()
-    B = torch.empty((n, G + 3), dtype=torch.float32, device=x.device) if need_B else None
-    dB = torch.empty((n, G + 3), dtype=torch.float32, device=x.device) if need_dB else None
+    B = torch.empty((n, G + degree), dtype=torch.float32, device=x.device) if need_B else None
+    dB = torch.empty((n, G + degree), dtype=torch.float32, device=x.device) if need_dB else None
     L.check(fn(ctypes.byref(g), n, _DTYPES[x.dtype], _ptr(x), _ptr(B), _ptr(dB), _stream(x)), name)
     return B, dB
 
 
-def kan_basis_eval(x, grid, need_B=True, need_dB=True):
-    """Dense ``B [n, G+3]`` and ``dB [n, G+3]`` of a 1-D tensor of inputs (local span form)."""
-    return _basis(L.lib().kan_basis_eval, "kan_basis_eval", x, grid, need_B, need_dB)
+def kan_basis_eval(x, grid, need_B=True, need_dB=True, degree=3):
+    """Dense ``B [n, G+degree]`` and ``dB`` of a 1-D tensor of inputs (local span form)."""
+    return _basis(L.lib().kan_basis_eval, "kan_basis_eval", x, grid, need_B, need_dB, degree)
 
 
-def kan_basis_eval_tp(x, grid, need_B=True, need_dB=True):
+def kan_basis_eval_tp(x, grid, need_B=True, need_dB=True, degree=3):
     """The same, from the truncated-power form (every basis function on its own)."""
-    return _basis(L.lib().kan_basis_eval_tp, "kan_basis_eval_tp", x, grid, need_B, need_dB)
+    return _basis(L.lib().kan_basis_eval_tp, "kan_basis_eval_tp", x, grid, need_B, need_dB, degree)
 
 
 def group_desc(x, C, grid):

@@ -222,7 +222,11 @@ def test_basis_checks(L, fn):
     assert f(None, 4, 0, X, Y, DY, None) == L.KAN_ERR_NULL
     assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 0, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
     assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 126, 3)), 4, 0, X, Y, None, None) == L.KAN_ERR_GRID
-    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 1)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
+    # the basis step takes degrees 1 .. 5 (the layer only 3)
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 0)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 6)), 4, 0, X, Y, None, None) == L.KAN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 5)), 0, 0, X, Y, None, None) == L.KAN_OK
+    assert f(ctypes.byref(L.kan_grid_t(-1.0, 1.0, 8, 5)), 4, 0, X, X - 64, None, None) == L.KAN_ERR_ALIAS
     assert f(ctypes.byref(g), -1, 0, X, Y, None, None) == L.KAN_ERR_SHAPE
     assert f(ctypes.byref(g), 0, 0, X, Y, None, None) == L.KAN_OK
     assert f(ctypes.byref(g), 4, 0, X, None, None, None) == L.KAN_ERR_NULL

@@ -114,6 +114,45 @@ def test_basis_truncated_power(F, G, dtype):
     assert np.all(B[far] == 0.0) and np.all(dB[far] == 0.0)
 
 
+
+# Degrees 1, 2, 4, 5 (the basis step only; the layer is cubic).  Tolerances
+# from the arithmetic: the local recurrence adds non-negative terms, about
+# 2 D roundings of values <= 1, so 2e-6 (dB in units of 1/h likewise).  The
+# truncated-power sum has terms of total size S_D = sum_i C(D+1, i)
+# (D+1-i)^D / D! (4, 27, 37.3, 120, 394 for D = 1 .. 5), each carrying about
+# 2 roundings: 4 S_D ulp of 1.  Its derivative's terms, in units of 1/h, total
+# D S_{D-1}-like sums; the same bound with the degree-(D-1) powers is used.
+def _tp_scale(D, power):
+    import math
+    return sum(math.comb(D + 1, i) * (D + 1 - i) ** power for i in range(D + 2)) / math.factorial(power)
+
+
+@pytest.mark.parametrize("D", [1, 2, 4, 5])
+@pytest.mark.parametrize("G", [1, 5, 20])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_basis_general_degree(F, D, G, dtype):
+    lo, hi = -1.0, 1.0
+    h = (hi - lo) / G
+    rng = np.random.default_rng(100 * D + G)
+    x = np.concatenate([rng.uniform(lo - (D + 1) * h, hi + (D + 1) * h, 100000),
+                        lo + (np.arange(G + 2 * D + 1) - D) * h, [lo, hi, 0.0]]).astype(np.float32)
+    if dtype == "bf16":
+        x = wl.to_bf16_values(x)
+    say("basis degree %d G=%d %s n=%d" % (D, G, dtype, x.size))
+    ref = oracle.basis(x.astype(np.float64), lo, hi, G, D)
+    dref = oracle.basis_derivative(x.astype(np.float64), lo, hi, G, D) * h
+    B, dB = F.kan_basis_eval(to_dev(x, dtype), (lo, hi, G), degree=D)
+    B, dB = _np(B), _np(dB) * h
+    assert B.shape == ref.shape
+    assert np.max(np.abs(B - ref)) <= 2e-6 and np.max(np.abs(dB - dref)) <= 2e-6 * (D + 1)
+    assert B.min() >= 0.0
+    assert np.count_nonzero(B, axis=1).max() <= D + 1
+    Bt, dBt = F.kan_basis_eval_tp(to_dev(x, dtype), (lo, hi, G), degree=D)
+    Bt, dBt = _np(Bt), _np(dBt) * h
+    eps = 2.0 ** -24
+    assert np.max(np.abs(Bt - ref)) <= 4 * eps * _tp_scale(D, D) + 1e-7
+    assert np.max(np.abs(dBt - dref)) <= 4 * eps * (D + 1) * _tp_scale(D, max(D - 1, 0)) + 1e-7
+
 # ---------------------------------------------------------------------------
 # small ragged layers, every variant, in full
 SMALL = [  # N, I, O, G, base
