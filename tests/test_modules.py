@@ -143,3 +143,46 @@ def test_optimizer_step_changes_only_through_gradients(torch_mod):
     opt.step()
     for p, s in zip(layer.parameters(), snap):
         assert torch.equal(p.detach(), s)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_activation_autograd(torch_mod, dtype):
+    torch = torch_mod[0]
+    from kolmogorov_arnold_network_amd import KANGroupedActivation
+    d = wl.random_grouped(60, 90, 6, 8, dtype=dtype, seed=12)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    act = KANGroupedActivation(90, groups=6, grid_size=8, grid_range=(d["lo"], d["hi"]), dtype=tdt,
+                               device="cuda:0")
+    with torch.no_grad():
+        act.coef.copy_(torch.from_numpy(d["C"]).to(tdt))
+    xt = torch.from_numpy(d["x"]).reshape(3, 20, 90).to("cuda:0").requires_grad_(True)
+    y = act(xt)
+    assert y.shape == (3, 20, 90) and y.dtype == torch.float32
+    y.backward(torch.from_numpy(d["dy"]).reshape(3, 20, 90).to("cuda:0"))
+    torch.cuda.synchronize()
+    rdx, rdC = oracle.grouped_backward(d["x"], d["C"], d["dy"], d["lo"], d["hi"], 8)
+    _check("y", y.detach().reshape(60, 90).cpu().numpy(),
+           oracle.grouped_forward(d["x"], d["C"], d["lo"], d["hi"], 8), dtype)
+    _check("dx", xt.grad.reshape(60, 90).float().cpu().numpy(), rdx, dtype)
+    _check("dC", act.coef.grad.float().cpu().numpy(), rdC, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_surface_layer_autograd(torch_mod, dtype):
+    torch = torch_mod[0]
+    from kolmogorov_arnold_network_amd import KANSurfaceLayer
+    d = wl.random_surface(48, 7, 13, 5, dtype=dtype, seed=13)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    layer = KANSurfaceLayer(14, 13, grid_size=5, grid_range=(d["lo"], d["hi"]), dtype=tdt, device="cuda:0")
+    with torch.no_grad():
+        layer.coef.copy_(torch.from_numpy(d["C"]).to(tdt))
+    xt = torch.from_numpy(d["x"]).reshape(4, 12, 14).to("cuda:0").requires_grad_(True)
+    y = layer(xt)
+    assert y.shape == (4, 12, 13) and y.dtype == torch.float32
+    y.backward(torch.from_numpy(d["dy"]).reshape(4, 12, 13).to("cuda:0"))
+    torch.cuda.synchronize()
+    rdx, rdC = oracle.surface_backward(d["x"], d["C"], d["dy"], d["lo"], d["hi"], 5)
+    _check("y", y.detach().reshape(48, 13).cpu().numpy(),
+           oracle.surface_forward(d["x"], d["C"], d["lo"], d["hi"], 5), dtype)
+    _check("dx", xt.grad.reshape(48, 14).float().cpu().numpy(), rdx, dtype)
+    _check("dC", layer.coef.grad.float().cpu().numpy(), rdC, dtype)
