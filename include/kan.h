@@ -44,6 +44,9 @@
  *   on every call (no floating-point atomics anywhere).
  * - The library holds no mutable global state; concurrent calls on different
  *   streams with disjoint outputs are safe.
+ * - Every call only enqueues kernels on `stream` (zero fills are kernels, no
+ *   memset or copy nodes), so a call may be captured into a HIP graph, with
+ *   its workspace allocated beforehand, and the graph replayed.
  */
 #ifndef KAN_H
 #define KAN_H
