@@ -268,8 +268,16 @@ typedef struct {
     int32_t dtype;      /* kan_dtype_t: storage of x and C */
     int32_t flags;      /* 0, or KAN_FLAG_PREPARED: the workspace holds this
                            pass's packed operands from the last call without
-                           the flag (same desc, C, and dy for the backward) */
+                           the flag (same desc, C, and dy for the backward);
+                           and/or KAN_FLAG_DENSE_FORWARD (below) */
 } kan_surface_desc_t;
+
+/* With bf16 storage and G = 5 the forward of the 2-D layer runs on the
+ * structured-sparse matrix instructions: within each m-row of a pair's 8 x 8
+ * columns the n index is permuted into two groups of 4 by parity, so the 4
+ * consecutive n of a span put 2 values in each group, and the 2:4-sparse tile
+ * is multiplied at twice the dense rate.  KAN_FLAG_DENSE_FORWARD asks for the
+ * dense form; both passes of a prepared pair must agree on it. */
 
 /* Bytes of workspace a pass of the 2-D layer needs (SIZE_MAX if `desc` is
  * invalid): the packed coefficient operand, and for the backward dy in both

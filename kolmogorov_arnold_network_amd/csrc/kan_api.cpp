@@ -80,6 +80,13 @@ void plan_layout(Plan& q, bool dense_forward) {
                8 * ng <= 3 * q.Kb && q.I * 4 * ng <= kIndexLimit;
     q.NG = ng;
     q.Kb8 = 4 * ng;
+    if (q.pair) {
+        // 2-D layer: the sparse form exists for K1 = 8 (G = 5), a pair's 64
+        // columns in one k-tile, permuted but not widened
+        q.sparse = q.dtype == KAN_BF16 && !dense_forward && q.Kb == 64;
+        q.NG = 0;
+        q.Kb8 = 64;
+    }
     q.Kfs = round_up(q.I * q.Kb8, 64);
     take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
@@ -122,7 +129,7 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     int st = grid_check(d->grid, 13);
     if (st != KAN_OK) return st;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
-    if (d->flags & ~KAN_FLAG_PREPARED) return KAN_ERR_UNSUPPORTED;
+    if (d->flags & ~(KAN_FLAG_PREPARED | KAN_FLAG_DENSE_FORWARD)) return KAN_ERR_UNSUPPORTED;
     Plan q;
     memset(&q, 0, sizeof(q));
     q.pair = 1;
@@ -139,7 +146,7 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     if (q.N > kIndexLimit || q.O > kIndexLimit || q.xI > kIndexLimit || q.I * q.Kb > kIndexLimit)
         return KAN_ERR_SHAPE;
     q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
-    plan_layout(q, true);
+    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
     *p = q;
     return KAN_OK;
 }

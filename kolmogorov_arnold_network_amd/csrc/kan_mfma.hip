@@ -661,6 +661,73 @@ struct GenS {
     }
 };
 
+// Forward A operand of the 2-D layer in 2:4 structured-sparse form (bf16,
+// G = 5: K1 = 8, so a pair's 64 columns are exactly one k-tile).  Column
+// (m, n) of a pair is logical k = 8 m + 4 (n & 1) + (n >> 1): group 2 m +
+// (n & 1), position n >> 1, so the 4 consecutive n of a span put exactly 2
+// values into each of the two groups of row m (the coefficient operand is
+// packed in the same order).  A group's two stored values sit at positions
+// c, c + 1 with c = clamp(first position, 0, 2), zeros filling a position
+// that holds none (n outside [0, 8) at the grid's edge).  Two lanes build a
+// row: lane half h the 8 groups of m-rows 4 h .. 4 h + 3, stored with the
+// row's values at bytes 32 + 32 h (GenS's layout for a k-tile-aligned
+// input) and their nibbles at bytes 136 + 4 h.
+struct GenS2 {
+    static constexpr bool SPARSE = true;
+    static constexpr int DEPTH = 2;
+    static constexpr int NPART = 1;
+    const uint16_t* x;
+    int h, row;
+    int64_t xrow;
+    uint32_t x1s[2], x2s[2];
+    __device__ GenS2(const GemmArgs& a, int tm, int) {
+        x = static_cast<const uint16_t*>(a.x);
+        h = threadIdx.x & 1;
+        row = threadIdx.x >> 1;
+        xrow = (int64_t)min(tm * 256 + row, a.N - 1) * a.xI;
+    }
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs&, int kt) {
+        x1s[SL] = raw_bits(x, xrow + 2 * kt);            // pair kt
+        x2s[SL] = raw_bits(x, xrow + 2 * kt + 1);
+    }
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* r0 = S + row * PITCH;
+        float u1, u2;
+        const int s1 = min(span_u(raw_to_float<uint16_t>(x1s[SL]), a.g, u1), 11);
+        const int s2 = min(span_u(raw_to_float<uint16_t>(x2s[SL]), a.g, u2), 11);
+        float w1[4], w2[4];
+        pieces_fast(u1, w1[0], w1[1], w1[2], w1[3]);
+        pieces_fast(u2, w2[0], w2[1], w2[2], w2[3]);
+        const int n0 = s2 - 3;                          // first n of the span
+        uint32_t d[8], nib = 0;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            // the group's two n: n0 + ql and n0 + ql + 2, ql = 0 when g has n0's parity
+            const int ql = (g == (n0 & 1)) ? 0 : 1;
+            const int nl = n0 + ql, pl = nl >> 1;
+            const int c = min(max(pl, 0), 2);
+            const bool vl = (unsigned)nl < 8u, vh = (unsigned)(nl + 2) < 8u;
+            const float wl = ql ? w2[1] : w2[0], wh = ql ? w2[3] : w2[2];
+            const float v0 = (vl && pl == c) ? wl : (vh && pl + 1 == c) ? wh : 0.0f;
+            const float v1 = (vh && pl + 1 == c + 1) ? wh : (vl && pl == c + 1) ? wl : 0.0f;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+                const int r = 4 * h + mm - (s1 - 3);       // basis index of m = 4 h + mm
+                const float wr = r == 0 ? w1[0] : r == 1 ? w1[1] : r == 2 ? w1[2] : r == 3 ? w1[3] : 0.0f;
+                d[2 * mm + g] = Traits<uint16_t>::pk(wr * v0, wr * v1);
+                nib |= (uint32_t)(c | ((c + 1) << 2)) << (4 * (2 * mm + g));
+            }
+        }
+        *reinterpret_cast<uint4*>(r0 + 32 + 32 * h) = make_uint4(d[0], d[1], d[2], d[3]);
+        *reinterpret_cast<uint4*>(r0 + 48 + 32 * h) = make_uint4(d[4], d[5], d[6], d[7]);
+        *reinterpret_cast<uint32_t*>(r0 + 136 + 4 * h) = nib;
+        if constexpr (RF) fetch<SL>(a, ktn);
+    }
+};
+
 typedef f32x16 Acc[2][4];
 
 // ---- epilogues ----
@@ -1113,6 +1180,24 @@ __global__ void pack_fwd_sparse_kernel(const uint16_t* __restrict__ C, const uin
     }
 }
 
+// C' of the 2-D layer for its sparse forward (bf16, K1 = 8): pair p owns the
+// 64 logical columns p 64 + 8 m + 4 (n & 1) + (n >> 1) (GenS2's order); zero
+// outside [0, O) x [0, P).  Rows j < Opad, k < nk * 64.
+__global__ void pack_fwd_pair_sparse_kernel(const uint16_t* __restrict__ C, uint16_t* __restrict__ cp, int O,
+                                            int P, int64_t nk, int64_t Opad) {
+    const int64_t Kf = nk * 64;
+    for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
+        for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < Kf;
+             k += (int64_t)gridDim.x * blockDim.x) {
+            const int p = (int)(k >> 6), l = (int)(k & 63);
+            const int m = l >> 3, n = 2 * (l & 3) + ((l >> 2) & 1);
+            uint16_t v = 0;
+            if (j < O && p < P) v = C[(((int64_t)j * P + p) * 8 + m) * 8 + n];
+            cp[blk<uint16_t>(j, k, nk)] = v;
+        }
+    }
+}
+
 // dx B operand: row R < tiles_dx * 256 is column R of C' (zero for R >= I Kb);
 // k runs over j < nk * BK.  64 rows x 64 j per block through an LDS tile,
 // written back 16 bytes (consecutive j of one row) per thread.  I Kb is
@@ -1243,6 +1328,12 @@ hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp
 
 hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s) {
     const int64_t nk = p.Kfs / 64;
+    if (p.pair) {
+        dim3 grid((unsigned)std::min<int64_t>((p.Kfs + 255) / 256, 65535), (unsigned)std::min<int64_t>(p.Opad, 65535));
+        hipLaunchKernelGGL(pack_fwd_pair_sparse_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(C),
+                           static_cast<uint16_t*>(cp), (int)p.O, (int)p.I, nk, p.Opad);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)std::min<int64_t>((p.Kfs / 4 + 255) / 256, 65535),
               (unsigned)std::min<int64_t>(p.Opad, 65535));
     hipLaunchKernelGGL(pack_fwd_sparse_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(C),
@@ -1333,7 +1424,10 @@ static hipError_t dc_dispatch_pair(const Plan& p, const GemmArgs& a, hipStream_t
 }
 
 static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
-    if (p.pair) return p.dtype == KAN_F32 ? fwd_dispatch_pair<float>(p, a, s) : fwd_dispatch_pair<uint16_t>(p, a, s);
+    if (p.pair) {
+        if (p.sparse) return run_gemm<uint16_t, GenS2, LoadB, EpiY>(a, s);
+        return p.dtype == KAN_F32 ? fwd_dispatch_pair<float>(p, a, s) : fwd_dispatch_pair<uint16_t>(p, a, s);
+    }
     if (p.sparse) {
         if (p.NG == 4) return run_gemm<uint16_t, GenS<4>, LoadB, EpiY>(a, s);
         if (p.NG == 6) return run_gemm<uint16_t, GenS<6>, LoadB, EpiY>(a, s);

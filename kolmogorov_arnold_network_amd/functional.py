@@ -216,12 +216,15 @@ def _surface_ws(desc, pass_, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
-def kan_surface_forward(x, C, grid, ws=None, out=None):
+def kan_surface_forward(x, C, grid, ws=None, out=None, dense_forward=False):
     """``y [N, O]`` float32 of the 2-D tensor-product layer
-    ``y[b, j] = sum_p sum_{m,n} C[j, p, m, n] B_m(x[b, 2p]) B_n(x[b, 2p+1])``."""
+    ``y[b, j] = sum_p sum_{m,n} C[j, p, m, n] B_m(x[b, 2p]) B_n(x[b, 2p+1])``;
+    ``dense_forward`` turns off the structured-sparse forward (bf16, G = 5)."""
     _check_tensor(x, "x", _DTYPES)
     _check_tensor(C, "C", _DTYPES, x.device)
     desc = surface_desc(x, C, grid)
+    if dense_forward:
+        desc.flags = L.KAN_FLAG_DENSE_FORWARD
     buf, n = ws if ws is not None else _surface_ws(desc, L.KAN_PASS_FORWARD, x.device)
     y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
                                                 device=x.device)

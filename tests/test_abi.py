@@ -354,7 +354,7 @@ def test_surface_workspace_sizes(L):
 @pytest.mark.parametrize("kw,code", [
     (dict(N=-1), -2), (dict(P=0), -2), (dict(O=0), -2), (dict(G=0), -3), (dict(G=14), -3),
     (dict(lo=1.0, hi=0.5), -3), (dict(hi=float("inf")), -3), (dict(dtype=5), -4), (dict(degree=1), -8),
-    (dict(flags=2), -8), (dict(P=1 << 30), -2)])
+    (dict(flags=4), -8), (dict(P=1 << 30), -2)])
 def test_surface_bad_descriptors(L, kw, code):
     d = sdesc(L, **kw)
     lib = L.lib()

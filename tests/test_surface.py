@@ -114,3 +114,19 @@ def test_workload_s1(F):
     pairs = wl.sample_pairs(O, P, 24, seed=22)
     rdC = oracle.surface_coef_grad_pairs(d["x"], d["dy"], lo, hi, G, [tuple(q) for q in pairs])
     assert rel_fro(dCn[pairs[:, 0], pairs[:, 1]], rdC) <= 1e-2
+
+
+@pytest.mark.parametrize("N,P,O", [(300, 7, 40), (1000, 3, 300), (64, 1, 1)])
+def test_sparse_forward(F, N, P, O):
+    """bf16, G = 5: the 2:4 structured-sparse forward (the default) against the
+    dense form and the oracle; x includes knots and far-outside points."""
+    d = wl.random_surface(N, P, O, 5, "bf16", seed=N + 7)
+    grid = (d["lo"], d["hi"], 5)
+    x, C = to_dev(d["x"], "bf16"), to_dev(d["C"], "bf16")
+    ys = _np(F.kan_surface_forward(x, C, grid))
+    yd = _np(F.kan_surface_forward(x, C, grid, dense_forward=True))
+    ref = oracle.surface_forward(d["x"], d["C"], *grid)
+    assert rel_fro(ys, ref) <= 1e-2
+    assert rel_fro(yd, ref) <= 1e-2
+    # same bf16 products in a different summation order
+    assert rel_fro(ys, yd) <= 1e-5
