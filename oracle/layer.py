@@ -14,7 +14,10 @@ residual ``W_base * silu(x)`` branch is not on the pages; this library offers
 it as an option and the oracle states it here the same way.
 
 Shapes: ``x [N, I]``, ``C [O, I, K]`` with ``K = G + 3`` and ``m`` fastest,
-``W_base [O, I]`` (or ``None``), ``y``/``dy [N, O]``.
+``W_base [O, I]`` (or ``None``), ``y``/``dy [N, O]``.  The layer functions
+also take a spline degree ``k`` (default 3, the pages' cubic layer); for the
+degree-``k`` form the FlashKAN page states for its basis, ``K = G + k`` on a
+grid extended by ``k`` knots per side (``bspline``).
 
 Training backward ("same optimizer, same training loop", InKAN page, "Why
 InKAN?" and "Quick Start"): with upstream gradient ``dy``,
@@ -54,13 +57,13 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def layer_forward(x, C, W, lo, hi, G):
+def layer_forward(x, C, W, lo, hi, G, k=3):
     """``y [N, O]`` of one KAN layer (``W`` may be ``None``: no base branch)."""
     x, C, W = _f64(x), _f64(C), _f64(W)
     N, I = x.shape
     O, I2, K = C.shape
-    assert I2 == I and K == G + 3
-    B = basis(x, lo, hi, G)                      # [N, I, K]
+    assert I2 == I and K == G + k
+    B = basis(x, lo, hi, G, k)                   # [N, I, K]
     # sum over the pair (i, m), written as one product over the flattened index
     y = B.reshape(N, I * K) @ C.reshape(O, I * K).T
     if W is not None:
@@ -68,7 +71,7 @@ def layer_forward(x, C, W, lo, hi, G):
     return y
 
 
-def layer_backward(x, C, W, dy, lo, hi, G, need=("dx", "dC", "dW")):
+def layer_backward(x, C, W, dy, lo, hi, G, need=("dx", "dC", "dW"), k=3):
     """``(dx, dC, dW)`` of one KAN layer; entries not in ``need`` are ``None``.
 
     ``dW`` is ``None`` as well when ``W`` is ``None``.
@@ -78,14 +81,14 @@ def layer_backward(x, C, W, dy, lo, hi, G, need=("dx", "dC", "dW")):
     O, _, K = C.shape
     dx = dC = dW = None
     if "dx" in need:
-        dB = basis_derivative(x, lo, hi, G)      # [N, I, K]
+        dB = basis_derivative(x, lo, hi, G, k)   # [N, I, K]
         # P[b, i, m] = sum_j dy[b, j] C[j, i, m]
         P = (dy @ C.reshape(O, I * K)).reshape(N, I, K)
         dx = np.sum(P * dB, axis=2)
         if W is not None:
             dx = dx + (dy @ W) * silu_prime(x)
     if "dC" in need:
-        B = basis(x, lo, hi, G)
+        B = basis(x, lo, hi, G, k)
         dC = (dy.T @ B.reshape(N, I * K)).reshape(O, I, K)
     if "dW" in need and W is not None:
         dW = dy.T @ silu(x)

@@ -93,3 +93,34 @@ def test_planted_wrong_extension_is_caught():
     t = oracle.knots(lo, hi, G, k)
     want = BSpline.design_matrix(x, t, k).toarray()
     assert bad.shape != want.shape or np.max(np.abs(bad - want)) > 1e-3
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 5])
+def test_layer_at_degree_k_per_edge(k):
+    """The degree-k layer oracle against per-edge scipy splines: y[b, j] =
+    sum_i BSpline(t, C[j, i], k)(x[b, i]) + W silu, and dx from the splines'
+    derivatives, with x inside [lo, hi]."""
+    lo, hi, G, N, I, O = -1.0, 1.0, 6, 7, 5, 3
+    rng = np.random.default_rng(50 + k)
+    x = rng.uniform(lo, hi, (N, I))
+    C = rng.standard_normal((O, I, G + k))
+    W = rng.standard_normal((O, I))
+    dy = rng.standard_normal((N, O))
+    t = oracle.knots(lo, hi, G, k)
+    y = oracle.layer_forward(x, C, W, lo, hi, G, k=k)
+    dx, dC, dW = oracle.layer_backward(x, C, W, dy, lo, hi, G, k=k)
+    want = np.zeros((N, O))
+    wdx = np.zeros((N, I))
+    for j in range(O):
+        for i in range(I):
+            s = BSpline(t, C[j, i], k)
+            want[:, j] += s(x[:, i]) + W[j, i] * oracle.silu(x[:, i])
+            wdx[:, i] += dy[:, j] * (s.derivative()(x[:, i]) + W[j, i] * oracle.silu_prime(x[:, i]))
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dx, wdx, rtol=0, atol=1e-10)
+    # dC: the exact change of <dy, y> under a unit change of one coefficient
+    f = lambda CC: float(np.sum(dy * oracle.layer_forward(x, CC, W, lo, hi, G, k=k)))
+    for idx in [(0, 0, 0), (2, 4, G + k - 1), (1, 2, 3)]:
+        Cp = C.copy()
+        Cp[idx] += 1.0
+        assert abs(f(Cp) - f(C) - dC[idx]) < 1e-10
