@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--code-digest", nargs="?", const="mfma", default=None, choices=["mfma", "grouped"],
                     help="print the digest that ties a counter summary to the kernel source")
-    ap.add_argument("--degree", type=int, default=3, help="spline degree of --basis-forms (1 .. 5)")
+    ap.add_argument("--degree", type=int, default=3,
+                    help="spline degree (1 .. 5) of the layer workloads and of --basis-forms")
     ap.add_argument("--basis-forms", type=int, default=0, metavar="POINTS",
                     help="time the local-span and truncated-power basis evaluations on POINTS inputs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -158,7 +159,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = wl.make_workload(args.workload, G=args.G)
+    d = wl.make_workload(args.workload, G=args.G, degree=args.degree)
     G, lo, hi = d["G"], d["lo"], d["hi"]
     grid = (lo, hi, G)
     dt = d["dtype"]
@@ -254,27 +255,30 @@ def main():
     step_ms = sorted(evs[0].elapsed_time(evs[-1]) for evs in per_step_events)
     median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
         step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
-    # work counts: algorithmic = the 4 non-zero basis functions (+ silu) per input
-    # in each of the three contractions; executed = the dense I*(G+3+base) basis,
-    # except a structured-sparse forward, whose matrix instructions run half of
-    # its 4 NG columns per input (the rule of KAN_FLAG_DENSE_FORWARD in kan.h)
-    Kb = G + 3 + (1 if base else 0)
+    # work counts: algorithmic = the D + 1 non-zero basis functions (+ silu) per
+    # input in each of the three contractions (D = 3: 4); executed = the dense
+    # I*(G+D+base) basis, except a structured-sparse forward, whose matrix
+    # instructions run half of its 4 NG columns per input (the rule of
+    # KAN_FLAG_DENSE_FORWARD in kan.h; cubic layers only)
+    D = args.degree
+    Kb = G + D + (1 if base else 0)
     ng = max(4, (Kb + 3) // 4)
     ng += ng & 1
-    sparse = dt == "bf16" and args.variant in ("auto", "mfma") and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
+    sparse = (D == 3 and dt == "bf16" and args.variant in ("auto", "mfma") and ng <= 8 and Kb >= 11
+              and 8 * ng <= 3 * Kb)
     fwd_cols = 2 * ng if sparse else Kb
     alg = exe = 0.0
     for l in range(nl):
         I, O = widths[l], widths[l + 1]
-        alg += 6.0 * N * I * O * (4 + (1 if base else 0))
+        alg += 6.0 * N * I * O * (D + 1 + (1 if base else 0))
         exe += 2.0 * N * I * O * (fwd_cols + 2 * Kb)
     gemm_stages = [nm for nm in names if nm.split(".")[1] in ("fwd", "dx", "dC")]
     dom = max(gemm_stages, key=lambda nm: stage_ms[nm])
     dl = int(dom[1])
     I, O = widths[dl], widths[dl + 1]
-    alg_dom = 2.0 * N * I * O * (4 + (1 if base else 0))
+    alg_dom = 2.0 * N * I * O * (D + 1 + (1 if base else 0))
     exe_dom = 2.0 * N * I * O * (fwd_cols if dom.endswith(".fwd") else Kb)
-    mfma_path = args.variant == "mfma" or (args.variant == "auto" and dt == "bf16")
+    mfma_path = args.variant == "mfma" or (args.variant == "auto" and (dt == "bf16" or D != 3))
     peak = PEAK_TFLOPS[dt]
     t_dom = stage_ms[dom] * 1e-3
     roof = {
@@ -306,9 +310,10 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload] + (" (G=%d)" % G if args.workload == "c3" else ""),
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + (" (G=%d)" % G if args.workload == "c3" else "")
+                   + (" (spline degree %d)" % D if D != 3 else ""),
                    "name": args.workload, "rows": N, "widths": widths, "G": G,
-                   "base_branch": base, "variant": args.variant},
+                   "base_branch": base, "variant": args.variant, "degree": D},
         "gflops_algorithmic": alg / (ms_per_step * 1e-3) / 1e9,
         "gflops_executed": exe / (ms_per_step * 1e-3) / 1e9,
         "sparse_forward": sparse,
@@ -629,8 +634,9 @@ def cpu_baseline(d, rows=None):
     lo, hi, G = d["lo"], d["hi"], d["G"]
     bf = d["dtype"] == "bf16"
     t0 = time.perf_counter()
-    acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf)
-    oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G)
+    k = d["layers"][0][0].shape[2] - G                     # spline degree
+    acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf, k=k)
+    oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G, k=k)
     dt = time.perf_counter() - t0
     model = _cpu_model()
     return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",

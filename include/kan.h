@@ -69,7 +69,7 @@ typedef enum {
     KAN_ERR_ALIGN = -5,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
     KAN_ERR_WORKSPACE = -6,   /* workspace smaller than kan_workspace_size() */
     KAN_ERR_HIP = -7,         /* a HIP launch failed */
-    KAN_ERR_UNSUPPORTED = -8, /* degree != 3, bad variant / has_base / pass value */
+    KAN_ERR_UNSUPPORTED = -8, /* degree outside what the entry point takes, bad variant / has_base / pass / flags */
     KAN_ERR_ALIAS = -9        /* an output overlaps an input or another output */
 } kan_status_t;
 
@@ -88,8 +88,15 @@ typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 
 typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;
 
 /* Grid: G intervals on [lo, hi], 1 <= G <= 125 (the G+3 coefficients of an
- * input for a tile of outputs are staged in LDS); degree must be 3 (cubic,
- * InKAN page). */
+ * input for a tile of outputs are staged in LDS), and the spline degree.  The
+ * pages' layer is cubic (InKAN page) and 3 is the default everywhere; the
+ * layer also takes degree D = 1 .. 5 (FlashKAN page: the degree-k form of the
+ * basis), with the grid extended by D knots on each side (t_r = lo + (r - D) h)
+ * and K = G + D coefficients per edge, so C is [O, I, G+D] and the formulas
+ * at the top hold with B_m of degree D.  A layer of degree other than 3 runs
+ * both passes on the matrix cores (variant GATHER and the structured-sparse
+ * forward are cubic only) and needs G + D + has_base >= 4.  The grouped
+ * activation and the 2-D layer are cubic only. */
 typedef struct {
     float lo;
     float hi;

@@ -76,7 +76,7 @@ void plan_layout(Plan& q, bool dense_forward) {
     // at most 3/4 of the dense contraction.
     int ng = std::max(4, (q.Kb + 3) / 4);
     ng += ng & 1;
-    q.sparse = q.dtype == KAN_BF16 && !dense_forward && !q.pair && ng <= 8 && q.Kb >= 11 &&
+    q.sparse = q.dtype == KAN_BF16 && !dense_forward && !q.pair && q.degree == 3 && ng <= 8 && q.Kb >= 11 &&
                8 * ng <= 3 * q.Kb && q.I * 4 * ng <= kIndexLimit;
     q.NG = ng;
     q.Kb8 = 4 * ng;
@@ -105,18 +105,21 @@ void plan_layout(Plan& q, bool dense_forward) {
     q.ws_bwd = q.variant_bwd == KAN_VARIANT_MFMA ? off : 0;
 }
 
-int grid_check(const kan_grid_t& g, int max_G) {
-    if (g.degree != 3) return KAN_ERR_UNSUPPORTED;
+// degree 1 .. 5 when any_degree, else 3 only
+int grid_check(const kan_grid_t& g, int max_G, bool any_degree) {
+    if (any_degree ? (g.degree < 1 || g.degree > 5) : g.degree != 3) return KAN_ERR_UNSUPPORTED;
     if (g.G < 1 || g.G > max_G) return KAN_ERR_GRID;
     if (!isfinite(g.lo) || !isfinite(g.hi) || !(g.lo < g.hi)) return KAN_ERR_GRID;
     return KAN_OK;
 }
 
+// knot units measured from t_0 = lo - degree h
 void grid_constants(Plan& q, const kan_grid_t& g) {
     const double lo = g.lo, hi = g.hi;
     q.G = g.G;
+    q.degree = g.degree;
     q.gk.scale = (float)((double)q.G / (hi - lo));
-    q.gk.shift = (float)(3.0 - lo * (double)q.G / (hi - lo));
+    q.gk.shift = (float)((double)g.degree - lo * (double)q.G / (hi - lo));
     q.gk.G = q.G;
 }
 
@@ -126,7 +129,7 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     if (!d || !p) return KAN_ERR_NULL;
     if (d->N < 0 || d->P < 1 || d->O < 1) return KAN_ERR_SHAPE;
     // a pair's (G+3)^2 columns must fit one 256-wide tile
-    int st = grid_check(d->grid, 13);
+    int st = grid_check(d->grid, 13, false);
     if (st != KAN_OK) return st;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
     if (d->flags & ~(KAN_FLAG_PREPARED | KAN_FLAG_DENSE_FORWARD)) return KAN_ERR_UNSUPPORTED;
@@ -156,7 +159,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     if (d->N < 0 || d->I < 1 || d->O < 1) return KAN_ERR_SHAPE;
     // G <= kMaxG: the gather kernels stage an input's K = G+3 coefficients
     // for a tile of outputs in LDS, which holds 128 of them
-    const int gst = grid_check(d->grid, kMaxG);
+    const int gst = grid_check(d->grid, kMaxG, true);
     if (gst != KAN_OK) return gst;
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
     if (d->has_base != 0 && d->has_base != 1) return KAN_ERR_UNSUPPORTED;
@@ -170,7 +173,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     q.xI = d->I;
     q.O = d->O;
     grid_constants(q, d->grid);
-    q.K = q.G + 3;
+    q.K = q.G + q.degree;
     q.base = d->has_base;
     q.Kb = q.K + q.base;
     q.dtype = d->dtype;
@@ -186,9 +189,15 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     // on the matrix cores, several times faster than the gather backward once
     // the layer has at least 2^16 edge-rows (N I O); below that the packing
     // and launches of the matrix-core path cost more than the work.
-    const bool mfma_ok = q.Kb <= kTileN;
+    // Degrees other than 3 run on the matrix cores only (the gather kernels
+    // are cubic), with at least 4 columns per input (the operand generators'
+    // instances cover that many inputs per tile).
+    const bool mfma_ok = q.Kb <= kTileN && (q.degree == 3 || q.Kb >= 4);
     if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
-    if (d->variant == KAN_VARIANT_GATHER) {
+    if (q.degree != 3) {
+        if (d->variant == KAN_VARIANT_GATHER || !mfma_ok) return KAN_ERR_UNSUPPORTED;
+        q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
+    } else if (d->variant == KAN_VARIANT_GATHER) {
         q.variant_fwd = q.variant_bwd = KAN_VARIANT_GATHER;
     } else if (d->variant == KAN_VARIANT_MFMA) {
         q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
@@ -378,12 +387,8 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
 static int basis_eval_impl(const kan_grid_t* grid, int64_t n, int dtype, const void* x, float* B,
                            float* dB, bool truncated_power, void* stream) {
     if (!grid) return KAN_ERR_NULL;
-    // the degree-3 checks of the layer, with any degree 1 .. 5 accepted
-    kan_grid_t g3 = *grid;
     const int degree = grid->degree;
-    if (degree < 1 || degree > 5) return KAN_ERR_UNSUPPORTED;
-    g3.degree = 3;
-    int st = grid_check(g3, kMaxG);
+    int st = grid_check(*grid, kMaxG, true);
     if (st != KAN_OK) return st;
     if (n < 0) return KAN_ERR_SHAPE;
     if (dtype != KAN_F32 && dtype != KAN_BF16) return KAN_ERR_DTYPE;
@@ -490,6 +495,7 @@ int kan_surface_backward(const kan_surface_desc_t* desc, const void* x, const vo
 // Validates a grouped activation; on success *gk and *K describe the grid.
 static int group_check(const kan_group_desc_t* d, GridK* gk, int* K, int* esize) {
     if (!d) return KAN_ERR_NULL;
+    if (d->grid.degree != 3) return KAN_ERR_UNSUPPORTED;          // the grouped kernels are cubic
     kan_desc_t ld;
     memset(&ld, 0, sizeof(ld));
     ld.N = 1;

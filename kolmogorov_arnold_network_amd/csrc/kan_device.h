@@ -93,6 +93,38 @@ __device__ __forceinline__ void dpieces(float u, float scale, float& d0, float& 
     d3 = (u * u) * hs;
 }
 
+// The D + 1 non-zero uniform B-splines of degree D (1 <= D <= 5, a runtime
+// value uniform across the wave) on a knot span with local coordinate u, and
+// their x-derivatives: value r belongs to basis function s - D + r.  The
+// degree-by-degree recurrence on uniform knots,
+//     N^q_r = ((u + q - r) N^{q-1}_{r-1} + (r + 1 - u) N^{q-1}_r) / q,
+// adds non-negative terms only on [0, 1]; dN^D_r/dx = (N^{D-1}_{r-1} -
+// N^{D-1}_r) / h.  Entries r > D are zero.
+__device__ __forceinline__ void local_basis_rt(float u, float scale, int D, float b[6], float d[6]) {
+    float N[6] = {1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 6; ++r) d[r] = 0.0f;
+#pragma unroll
+    for (int q = 1; q <= 5; ++q) {
+        if (q > D) break;
+        if (q == D) {
+#pragma unroll
+            for (int r = 0; r < 6; ++r)
+                if (r <= q) d[r] = ((r >= 1 ? N[r - 1] : 0.0f) - (r <= q - 1 ? N[r] : 0.0f)) * scale;
+        }
+        const float inv = 1.0f / (float)q;
+#pragma unroll
+        for (int r = 5; r >= 0; --r) {
+            if (r > q) continue;
+            float v = r >= 1 ? (u + (float)(q - r)) * N[r - 1] : 0.0f;
+            if (r <= q - 1) v = __builtin_fmaf((float)(r + 1) - u, N[r], v);
+            N[r] = v * inv;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 6; ++r) b[r] = N[r];
+}
+
 // silu(x) = x * sigmoid(x) and its derivative sigmoid(x) * (1 + x (1 - sigmoid(x))).
 __device__ __forceinline__ float silu(float x) {
     const float e = __expf(-x);

@@ -32,6 +32,8 @@ struct Plan {
     // xI = I.
     int pair;
     int64_t xI;
+    int degree;          // spline degree, 1 .. 5 (the gather kernels, the sparse
+                         // forward and the 2-D layer are cubic only)
     int variant_fwd;     // resolved per pass: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
     int variant_bwd;
     int esize;           // bytes per stored element (4 or 2)

@@ -144,6 +144,7 @@ struct GemmArgs {
     GridK g;
     int N, I, O, K, Kb, base;
     int xI;              // x row width: I, or 2P for the pairs of the 2-D layer
+    int deg;             // spline degree (the K-variant operands; the cubic ones assume 3)
     int64_t IKb;
     float* out0;         // y, dx or dC
     float* out1;         // dW_base, or the dx partial sums
@@ -571,6 +572,152 @@ struct GenB2 {
     }
 };
 
+// ---- layers of spline degree D != 3: the same operands with D + 1 values ----
+// GenAK / GenBK / EpiDXK are GenA / GenB / EpiDX with the D + 1 non-zero
+// basis values (and derivatives) of local_basis_rt in place of the 4 cubic
+// pieces; a.K = G + D and a.g places t_0 = lo - D h.  Spans past K + D hold
+// no index < K and are clamped there.
+template <typename TS, int NIN>
+struct GenAK {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int ES = Traits<TS>::ES;
+    static constexpr int PPT = 256 * NIN / NTHR;
+    static constexpr int NPART = PPT;
+    static constexpr int DEPTH = 2;
+    static constexpr int RSTEP = NTHR / NIN;
+    static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
+    const TS* x;
+    int q, row0;
+    int64_t xrow[PPT];
+    float xs[2][PPT];
+    int is[2];
+    __device__ GenAK(const GemmArgs& a, int tm, int) {
+        x = static_cast<const TS*>(a.x);
+        q = threadIdx.x % NIN;
+        row0 = threadIdx.x / NIN;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+            xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        is[SL] = (unsigned)(kt * BK) / (unsigned)a.Kb + q;
+        const int i = min(is[SL], a.I - 1);
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) xs[SL][j] = load_f(x, xrow[j] + i);
+    }
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* row = S + (row0 + RSTEP * j) * PITCH;
+#pragma unroll
+        for (int c = 0; c < (8 + NIN - 1) / NIN; ++c) {
+            const int chunk = q * ((8 + NIN - 1) / NIN) + c;
+            *reinterpret_cast<uint4*>(row + (chunk < 8 ? 16 * chunk : BK * ES)) = make_uint4(0, 0, 0, 0);
+        }
+        const int D = a.deg;
+        const int i = is[SL];
+        const int cb = i * a.Kb - kt * BK;
+        const int lo = max(0, -cb);
+        const int n = i < a.I ? max(0, min(a.K, BK - cb) - lo) : 0;
+        const int cs = cb + a.K;
+        const bool vs = (a.base != 0) & (i < a.I) & ((unsigned)cs < (unsigned)BK);
+        const float xv = xs[SL][j];
+        float u;
+        const int s = min(span_u(xv, a.g, u), a.K + D);
+        float b[6], dd[6];
+        local_basis_rt(u, a.g.scale, D, b, dd);
+        char* pad = row + BK * ES;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const bool v = (r <= D) & ((unsigned)(s - D - lo + r) < (unsigned)n);
+            Traits<TS>::put(v ? row + (cb + s - D + r) * ES : pad, b[r]);
+        }
+        Traits<TS>::put(vs ? row + cs * ES : pad, silu(xv));
+        if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
+    }
+};
+
+template <typename TS, int NQW, int ZR>
+struct GenBK {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    static constexpr int BK = Traits<TS>::BK;
+    static constexpr int ES = Traits<TS>::ES;
+    static constexpr int PPL = BK * NQW / 64;
+    static constexpr int NPART = 1 + PPL;
+    static constexpr int DEPTH = 2;
+    static_assert(BK * NQW % 64 == 0, "whole pairs per lane");
+    const TS* x;
+    int n0, i0, wave, lane;
+    int bl[PPL], il[PPL];
+    int off[PPL], lo[PPL], cnt[PPL], soff[PPL];
+    float xs[2][PPL];
+    __device__ GenBK(const GemmArgs& a, int, int tn) {
+        x = static_cast<const TS*>(a.x);
+        n0 = tn * 256;
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        i0 = (unsigned)n0 / (unsigned)a.Kb + wave * NQW;
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const int pp = lane + 64 * j;
+            bl[j] = pp / NQW;
+            il[j] = pp % NQW;
+            const int i = i0 + il[j];
+            const int rb = i * a.Kb - n0;
+            off[j] = rb * PITCH + bl[j] * ES;
+            lo[j] = max(0, -rb);
+            cnt[j] = i < a.I ? max(0, min(a.K, 256 - rb) - lo[j]) : 0;
+            const int rs = rb + a.K;
+            soff[j] = ((a.base != 0) & (i < a.I) & ((unsigned)rs < 256u)) ? rs * PITCH + bl[j] * ES : 128;
+        }
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+            const int64_t brow = (int64_t)min(kt * BK + bl[j], a.N - 1) * a.I;
+            xs[SL][j] = load_f(x, brow + min(i0 + il[j], a.I - 1));
+        }
+    }
+    template <int SL, bool RF, int p>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        if constexpr (p == 0) {
+#pragma unroll
+            for (int e = 0; e < NQW; ++e) {
+                const int rb = (i0 + e) * a.Kb - n0;
+#pragma unroll
+                for (int z = 0; z < ZR; ++z) {
+                    const int rr = 8 * z + (lane >> 3);
+                    const int row = rb + rr;
+                    const bool v = (rr < a.Kb) & (row >= 0) & (row < 256);
+                    *reinterpret_cast<uint4*>(v ? S + row * PITCH + (lane & 7) * 16 : S + 128) =
+                        make_uint4(0, 0, 0, 0);
+                }
+            }
+            return;
+        } else {
+        constexpr int j = p - 1;
+        const int D = a.deg;
+        const float xv = xs[SL][j];
+        float u;
+        const int s = min(span_u(xv, a.g, u), a.K + D);
+        float b[6], dd[6];
+        local_basis_rt(u, a.g.scale, D, b, dd);
+        const int first = off[j] + (s - D) * PITCH;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const bool v = (r <= D) & ((unsigned)(s - D - lo[j] + r) < (unsigned)cnt[j]);
+            Traits<TS>::put(S + (v ? first + r * PITCH : 128 + r * PITCH), b[r]);
+        }
+        Traits<TS>::put(S + soff[j], silu(xv));
+        if constexpr (RF && p == NPART - 1) fetch<SL>(a, ktn);
+        }
+    }
+};
+
 // Forward A operand in 2:4 structured-sparse form (bf16 only), in the column
 // order of kan_sparse.h; the coefficient operand is packed in the same order
 // (pack_fwd_sparse).
@@ -925,6 +1072,56 @@ struct EpiDX2 {
                         pp[0] = v1;
                         pp[1] = v2;
                     }
+                }
+            }
+            __syncthreads();
+        }
+    }
+};
+
+// dx of a degree-D layer: EpiDX with the D + 1 derivatives of local_basis_rt.
+struct EpiDXK {
+    template <typename TS>
+    __device__ static void run(const GemmArgs& a, Acc& acc, int tm, int tn, char* lds) {
+        float* P = reinterpret_cast<float*>(lds);
+        const TS* x = static_cast<const TS*>(a.x);
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        const int D = a.deg;
+        const int c0 = tn * 256;
+        const int i_lo = c0 / a.Kb;
+        const int nin = min((c0 + 255) / a.Kb, a.I - 1) - i_lo + 1;
+        const int cw = (wave & 1) * 128 + (lane & 31);
+        const int rw = (wave >> 1) * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    P[(rw + acc_row(0, r)) * DX_PITCH + cw + 32 * fj] = acc[h][fj][r];
+            __syncthreads();
+#pragma unroll 1
+            for (int e = t; e < 128 * nin; e += NTHR) {
+                const int rl = e / nin, il = e - rl * nin;
+                const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
+                const int i = i_lo + il;
+                const int cb = i * a.Kb - c0;
+                if (b < a.N) {
+                    const float xv = load_f(x, (int64_t)b * a.I + i);
+                    float u;
+                    const int s = min(span_u(xv, a.g, u), a.K + D);
+                    float bb[6], d[6];
+                    local_basis_rt(u, a.g.scale, D, bb, d);
+                    const float* prow = P + rl * DX_PITCH;
+                    const int cs = cb + a.K;
+                    float v = (a.base && cs >= 0 && cs < 256) ? prow[cs] * silu_prime(xv) : 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 6; ++r) {
+                        const int m = s - D + r, c = cb + m;
+                        if (r <= D && m >= 0 && m < a.K && c >= 0 && c < 256) v = __builtin_fmaf(prow[c], d[r], v);
+                    }
+                    if (cb >= 0 && cb + a.Kb <= 256) a.out0[(int64_t)b * a.I + i] = v;
+                    else a.out1[((int64_t)b * a.tiles_n + tn) * 2 + (cb < 0 ? 0 : 1)] = v;
                 }
             }
             __syncthreads();
@@ -1298,6 +1495,7 @@ GemmArgs base_args(const Plan& p, const void* x) {
     a.N = (int)p.N;
     a.I = (int)p.I;
     a.xI = (int)p.xI;
+    a.deg = p.degree;
     a.O = (int)p.O;
     a.K = p.K;
     a.Kb = p.Kb;
@@ -1423,7 +1621,29 @@ static hipError_t dc_dispatch_pair(const Plan& p, const GemmArgs& a, hipStream_t
     return run_gemm<TS, LoadA, GenB2<TS, N1, 32>, EpiDC>(a, s);
 }
 
+template <typename TS>
+static hipError_t fwd_dispatch_deg(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    const int n = fwd_nin(p);
+    if (n <= 2) return run_gemm<TS, GenAK<TS, 2>, LoadB, EpiY>(a, s);
+    if (n <= 4) return run_gemm<TS, GenAK<TS, 4>, LoadB, EpiY>(a, s);
+    if (n <= 8) return run_gemm<TS, GenAK<TS, 8>, LoadB, EpiY>(a, s);
+    if (n <= 16) return run_gemm<TS, GenAK<TS, 16>, LoadB, EpiY>(a, s);
+    return run_gemm<TS, GenAK<TS, 32>, LoadB, EpiY>(a, s);
+}
+
+template <typename TS>
+static hipError_t dc_dispatch_deg(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    const int zr = (p.Kb + 7) / 8;
+    const int nq = dc_nqw(p);
+    if (zr <= 1 && nq <= 10) return run_gemm<TS, LoadA, GenBK<TS, 10, 1>, EpiDC>(a, s);
+    if (zr <= 2 && nq <= 4) return run_gemm<TS, LoadA, GenBK<TS, 4, 2>, EpiDC>(a, s);
+    if (zr <= 4 && nq <= 2) return run_gemm<TS, LoadA, GenBK<TS, 2, 4>, EpiDC>(a, s);
+    if (zr <= 7 && nq <= 2) return run_gemm<TS, LoadA, GenBK<TS, 2, 7>, EpiDC>(a, s);
+    return run_gemm<TS, LoadA, GenBK<TS, 2, 32>, EpiDC>(a, s);
+}
+
 static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
+    if (p.degree != 3) return p.dtype == KAN_F32 ? fwd_dispatch_deg<float>(p, a, s) : fwd_dispatch_deg<uint16_t>(p, a, s);
     if (p.pair) {
         if (p.sparse) return run_gemm<uint16_t, GenS2, LoadB, EpiY>(a, s);
         return p.dtype == KAN_F32 ? fwd_dispatch_pair<float>(p, a, s) : fwd_dispatch_pair<uint16_t>(p, a, s);
@@ -1469,6 +1689,15 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     // both operands are copied and equally large per tile: 8 x 4 tiles per
     // 32 resident workgroups of an XCD share each dy and each C'^T tile
     a.group_m = 8;
+    if (p.degree != 3) {
+        hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDXK>(a, s)
+                                          : run_gemm<uint16_t, LoadA, LoadB, EpiDXK>(a, s);
+        if (e != hipSuccess || p.tiles_dx < 2) return e;
+        hipLaunchKernelGGL(dx_fixup_kernel,
+                           dim3((unsigned)std::min<int64_t>((p.N * (p.tiles_dx - 1) + 255) / 256, 16384)),
+                           dim3(256), 0, s, part, dx, (int64_t)p.N, (int)p.I, p.Kb, (int)p.tiles_dx);
+        return hipGetLastError();
+    }
     if (p.pair) {
         hipError_t e = p.dtype == KAN_F32 ? run_gemm<float, LoadA, LoadB, EpiDX2>(a, s)
                                           : run_gemm<uint16_t, LoadA, LoadB, EpiDX2>(a, s);
@@ -1499,6 +1728,7 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.out1 = dW;
     a.group_m = 2;
     auto dispatch = [&]() {
+        if (p.degree != 3) return p.dtype == KAN_F32 ? dc_dispatch_deg<float>(p, a, s) : dc_dispatch_deg<uint16_t>(p, a, s);
         if (p.pair) return p.dtype == KAN_F32 ? dc_dispatch_pair<float>(p, a, s) : dc_dispatch_pair<uint16_t>(p, a, s);
         return p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
     };

@@ -41,17 +41,20 @@ def _check_tensor(t, name, dtypes, device=None):
 
 
 def layer_desc(x, C, W, grid, variant="auto", flags=0):
-    """``kan_desc_t`` for ``x [N, I]``, ``C [O, I, G+3]``, ``W [O, I]`` or None."""
+    """``kan_desc_t`` for ``x [N, I]``, ``C [O, I, G+D]``, ``W [O, I]`` or None;
+    the spline degree D (1 .. 5, 3 for the pages' cubic layer) is read off C."""
     lo, hi, G = grid
     N, I = x.shape
     O, I2, K = C.shape
-    if I2 != I or K != G + 3:
-        raise ValueError("C must be [O, I, G+3] = [%d, %d, %d], got %s" % (O, I, G + 3, tuple(C.shape)))
+    if I2 != I or not 1 <= K - G <= 5:
+        raise ValueError("C must be [O, I, G+D] = [%d, %d, %d+D], D in 1..5, got %s"
+                         % (O, I, G, tuple(C.shape)))
     if W is not None and tuple(W.shape) != (O, I):
         raise ValueError("W_base must be [O, I]")
     if x.dtype != C.dtype or (W is not None and W.dtype != C.dtype):
         raise ValueError("x, C and W_base must share one dtype")
-    return L.make_desc(N, I, O, lo, hi, G, _DTYPES[x.dtype], W is not None, _variant(variant), flags)
+    return L.make_desc(N, I, O, lo, hi, G, _DTYPES[x.dtype], W is not None, _variant(variant), flags,
+                       degree=K - G)
 
 
 def kan_workspace_size(desc, pass_):

@@ -55,23 +55,25 @@ class CastBF16(torch.autograd.Function):
 class KANLayer(torch.nn.Module):
     """One KAN layer: ``y_j = sum_i phi_ji(x_i)`` with cubic B-spline ``phi_ji``.
 
-    Parameters: ``coef [out, in, grid_size + 3]`` and, with ``base=True``,
+    Parameters: ``coef [out, in, grid_size + degree]`` and, with ``base=True``,
     ``base_weight [out, in]`` for the ``W_base * silu(x)`` branch.  ``dtype``
     (float32 or bfloat16) is the storage of inputs and parameters; outputs
-    and gradients are computed in float32.
+    and gradients are computed in float32.  ``degree`` (1 .. 5) is the spline
+    degree, 3 (cubic) by default.
     """
 
     def __init__(self, in_features, out_features, grid_size=8, grid_range=(-1.0, 1.0), base=True,
-                 dtype=torch.float32, device=None, variant="auto", coef_std=0.1):
+                 dtype=torch.float32, device=None, variant="auto", coef_std=0.1, degree=3):
         super().__init__()
         self.in_features = int(in_features)
         self.out_features = int(out_features)
         self.grid_size = int(grid_size)
         self.grid_range = (float(grid_range[0]), float(grid_range[1]))
         self.variant = variant
+        self.degree = int(degree)
         fk = dict(dtype=dtype, device=device)
         self.coef = torch.nn.Parameter(
-            torch.randn(out_features, in_features, grid_size + 3, **fk) * coef_std)
+            torch.randn(out_features, in_features, grid_size + self.degree, **fk) * coef_std)
         if base:
             self.base_weight = torch.nn.Parameter(
                 torch.randn(out_features, in_features, **fk) / math.sqrt(in_features))
@@ -93,8 +95,8 @@ class KANLayer(torch.nn.Module):
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self):
-        return "in=%d, out=%d, grid_size=%d, range=%s, base=%s, dtype=%s" % (
-            self.in_features, self.out_features, self.grid_size, self.grid_range,
+        return "in=%d, out=%d, grid_size=%d, degree=%d, range=%s, base=%s, dtype=%s" % (
+            self.in_features, self.out_features, self.grid_size, self.degree, self.grid_range,
             self.base_weight is not None, self.coef.dtype)
 
 

@@ -133,7 +133,7 @@ def coef_grad_pairs(x, dy, pairs, lo, hi, G, with_base):
     return dCp, dWp
 
 
-def network_forward(x, layers, lo, hi, G, bf16_between=False):
+def network_forward(x, layers, lo, hi, G, bf16_between=False, k=3):
     """Activations of a chain of KAN layers.
 
     ``layers`` is a list of ``(C, W_base)``.  Layers compose with nothing in
@@ -144,14 +144,14 @@ def network_forward(x, layers, lo, hi, G, bf16_between=False):
     """
     acts = [np.asarray(x, dtype=np.float64)]
     for li, (C, W) in enumerate(layers):
-        y = layer_forward(acts[-1], C, W, lo, hi, G)
+        y = layer_forward(acts[-1], C, W, lo, hi, G, k=k)
         if bf16_between and li + 1 < len(layers):
             y = round_bf16(y)
         acts.append(y)
     return acts
 
 
-def network_backward(acts, layers, dy, lo, hi, G):
+def network_backward(acts, layers, dy, lo, hi, G, k=3):
     """Gradients of a chain of KAN layers by the chain rule.
 
     ``acts`` is the output of ``network_forward``.  A rounding cast between
@@ -162,7 +162,7 @@ def network_backward(acts, layers, dy, lo, hi, G):
     g = np.asarray(dy, dtype=np.float64)
     for li in range(len(layers) - 1, -1, -1):
         C, W = layers[li]
-        dx, dC, dW = layer_backward(acts[li], C, W, g, lo, hi, G)
+        dx, dC, dW = layer_backward(acts[li], C, W, g, lo, hi, G, k=k)
         grads[li] = (dC, dW)
         g = dx
     return g, grads

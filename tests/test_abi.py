@@ -84,7 +84,10 @@ def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
     (dict(N=-1), "SHAPE"), (dict(I=0), "SHAPE"), (dict(O=0), "SHAPE"), (dict(N=1 << 40), "SHAPE"),
     (dict(G=0), "GRID"), (dict(G=126), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
     (dict(lo=2.0, hi=1.0), "GRID"), (dict(lo=float("nan")), "GRID"), (dict(hi=float("inf")), "GRID"),
-    (dict(degree=2), "UNSUPPORTED"), (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
+    (dict(degree=0), "UNSUPPORTED"), (dict(degree=6), "UNSUPPORTED"),
+    (dict(degree=2, variant=2), "UNSUPPORTED"),                 # degree != 3: matrix cores only
+    (dict(degree=1, G=1, has_base=0), "UNSUPPORTED"),           # 2 columns per input: too few
+    (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
     (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
 ])
 def test_bad_descriptors(L, kw, code):
@@ -204,6 +207,28 @@ def test_workspace_sizes(L):
     assert wb(N=63, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0  # below: gather
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ws(variant=L.KAN_VARIANT_MFMA,
                                                                    dtype=L.KAN_BF16) > 0
+
+
+def test_workspace_sizes_other_degrees(L):
+    """Degree D != 3: K = G + D columns per input, both passes on the matrix
+    cores whatever the variant asked (AUTO), never the structured-sparse
+    forward, otherwise the cubic layout."""
+    r = lambda a, b: (a + b - 1) // b * b
+    for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
+        for (N, I, O, G, base, D) in [(64, 16, 8, 8, 1, 1), (1000, 77, 300, 20, 0, 5), (12608, 768, 3072, 5, 1, 2),
+                                      (5, 3, 2, 1, 1, 4)]:
+            Kb = G + D + base
+            Op, Np = r(O, 256), r(N, 256)
+            kf = r(I * Kb, bk)
+            P, _ = k_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
+            want_f = r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
+            tiles = (I * Kb + 255) // 256
+            want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
+            Pd, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)
+            want_b += r(Pd * O * I * Kb * 4, 256) if Pd > 1 else 0
+            d = desc(L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, degree=D, variant=L.KAN_VARIANT_AUTO)
+            assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == want_f
+            assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == want_b
 
 
 def test_prepare_checks(L):

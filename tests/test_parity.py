@@ -211,6 +211,33 @@ SPARSE = [
 ]
 
 
+# Layers of spline degree D != 3 (the FlashKAN page's degree-k basis): both
+# passes on the matrix cores, against the degree-D oracle; the layer's
+# tolerances.
+DEG_CASES = [(70, 29, 33, 8, 1), (70, 29, 33, 8, 2), (50, 40, 17, 5, 4), (40, 13, 300, 20, 5), (33, 9, 5, 1, 4)]
+
+
+@pytest.mark.parametrize("N,I,O,G,D", DEG_CASES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("base", [True, False])
+def test_layer_general_degree(F, N, I, O, G, D, dtype, base):
+    say("degree-%d layer %dx(%d->%d) G=%d %s base=%s" % (D, N, I, O, G, dtype, base))
+    d = wl.random_layer(N, I, O, G, dtype=dtype, base=base, seed=D, degree=D)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], G)
+    xt, Ct, Wt, dyt = to_dev(x, dtype), to_dev(C, dtype), to_dev(W, dtype), to_dev(dy, "f32")
+    y = F.kan_forward(xt, Ct, Wt, grid)
+    dx, dC, dW = F.kan_backward(xt, Ct, Wt, dyt, grid)
+    ry = oracle.layer_forward(x, C, W, *grid, k=D)
+    rdx, rdC, rdW = oracle.layer_backward(x, C, W, dy, *grid, k=D)
+    err, tol = metric(dtype)
+    assert err(_np(y), ry) <= tol
+    assert err(_np(dx), rdx) <= tol
+    assert err(_np(dC), rdC) <= tol
+    if base:
+        assert err(_np(dW), rdW) <= tol
+
+
 @pytest.mark.parametrize("shape", SPARSE, ids=["x".join(map(str, s)) for s in SPARSE])
 def test_sparse_forward(F, shape):
     """The structured-sparse forward against the oracle, and against the

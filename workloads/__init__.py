@@ -98,13 +98,14 @@ def _draw_x(rng, shape, kind, clamp):
     return x
 
 
-def make_workload(name, G=None, N=None):
+def make_workload(name, G=None, N=None, degree=3):
     """Inputs of one workload as a dict of NumPy float32 arrays.
 
     Keys: ``name, N, widths, G, lo, hi, dtype, base, x, layers`` (list of
     ``(C [O, I, G+3], W [O, I] or None)``) and ``dy [N, O_last]``.  ``G``
     selects the grid for ``c3``; ``N`` may shrink the batch (the first ``N``
-    rows are drawn from the same streams, for quick tests).
+    rows are drawn from the same streams, for quick tests).  ``degree`` other
+    than 3 gives ``C [O, I, G + degree]`` from the same streams.
     """
     spec = dict(CONFIGS[name])
     if G is None:
@@ -124,7 +125,7 @@ def make_workload(name, G=None, N=None):
     for l in range(nl):
         I, O = widths[l], widths[l + 1]
         C = np.random.default_rng(kids[1 + 2 * l]).standard_normal(
-            (O, I, G + 3), dtype=np.float32) * np.float32(spec["c_std"])
+            (O, I, G + degree), dtype=np.float32) * np.float32(spec["c_std"])
         W = None
         if spec["base"]:
             W = np.random.default_rng(kids[2 + 2 * l]).standard_normal(
@@ -139,29 +140,31 @@ def make_workload(name, G=None, N=None):
 
 
 def random_layer(N, I, O, G, dtype="f32", base=True, seed=0, lo=-1.0, hi=1.0,
-                 x_scale=1.0, special=True):
+                 x_scale=1.0, special=True, degree=3):
     """A small random layer for parity tests.
 
     ``x`` is drawn ~U(-x_scale, x_scale) * (hi - lo) / 2 around the grid
     centre.  With ``special`` a share of the entries is replaced by points
     the span logic must get right: every knot of the extended grid, ``lo``,
     ``hi``, points just inside/outside them, and points far outside the
-    extended grid.
+    extended grid.  ``degree`` other than 3 draws ``C [O, I, G + degree]`` and
+    takes the knots of that grid (extended by ``degree`` per side).
     """
-    rng = np.random.default_rng(np.random.SeedSequence([7, seed, N, I, O, G]))
+    seq = [7, seed, N, I, O, G] + ([] if degree == 3 else [degree])
+    rng = np.random.default_rng(np.random.SeedSequence(seq))
     mid, half = 0.5 * (lo + hi), 0.5 * (hi - lo)
     x = (mid + half * x_scale * (2 * rng.random((N, I)) - 1)).astype(np.float32)
     if special and N * I > 0:
         h = (hi - lo) / G
-        pts = [lo + (r - 3) * h for r in range(G + 7)]
+        pts = [lo + (r - degree) * h for r in range(G + 2 * degree + 1)]
         pts += [lo, hi, np.nextafter(np.float32(hi), np.float32(-np.inf)),
                 np.nextafter(np.float32(hi), np.float32(np.inf)),
                 np.nextafter(np.float32(lo), np.float32(-np.inf)),
-                lo - 3 * h - 1e-3, hi + 3 * h + 1e-3, lo - 10.0, hi + 10.0, 0.0]
+                lo - degree * h - 1e-3, hi + degree * h + 1e-3, lo - 10.0, hi + 10.0, 0.0]
         pts = np.asarray(pts, dtype=np.float32)
         mask = rng.random((N, I)) < 0.25
         x[mask] = pts[rng.integers(0, len(pts), size=int(mask.sum()))]
-    C = (rng.standard_normal((O, I, G + 3)) * 0.1).astype(np.float32)
+    C = (rng.standard_normal((O, I, G + degree)) * 0.1).astype(np.float32)
     W = (rng.standard_normal((O, I)) / math.sqrt(I)).astype(np.float32) if base else None
     dy = rng.standard_normal((N, O)).astype(np.float32)
     if dtype == "bf16":
