@@ -64,6 +64,8 @@ def parse():
                     help="spline degree (1 .. 5) of the layer workloads and of --basis-forms")
     ap.add_argument("--basis-forms", type=int, default=0, metavar="POINTS",
                     help="time the local-span and truncated-power basis evaluations on POINTS inputs")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="time plain bf16 torch.matmul on the c5 contraction shapes and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES bytes (HBM counter calibration)")
     args = ap.parse_args()
@@ -107,6 +109,34 @@ def basis_forms(n, steps, degree=3):
     print(json.dumps({"basis_forms": res, "points": n, "steps": steps, "degree": degree}))
 
 
+def blas_reference(steps):
+    """Plain bf16 GEMMs of the c5 contraction shapes (forward, dx, dC) through
+    torch.matmul, the vendor BLAS, on random data: the rate a library GEMM of
+    the same size reaches on this GPU, for comparison with the fused
+    contraction kernels."""
+    import torch
+    res = []
+    for name, (M, N, K) in (("fwd", (65536, 4096, 98304)), ("dx", (65536, 98304, 4096)),
+                            ("dC", (4096, 98304, 65536))):
+        a = torch.randn(M, K, device="cuda:0", dtype=torch.bfloat16)
+        b = torch.randn(K, N, device="cuda:0", dtype=torch.bfloat16)
+        c = torch.empty(M, N, device="cuda:0", dtype=torch.bfloat16)
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res.append({"gemm": name, "M": M, "N": N, "K": K, "ms": ms,
+                    "TFLOP_per_s": 2.0 * M * N * K / ms / 1e9})
+        del a, b, c
+        torch.cuda.empty_cache()
+    print(json.dumps({"blas_reference": res, "steps": steps}))
+
+
 def copy_probe(nbytes):
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -133,6 +163,9 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.blas_reference:
+        blas_reference(args.steps)
         return
     if args.basis_forms:
         basis_forms(args.basis_forms, args.steps, args.degree)
