@@ -40,6 +40,29 @@ def _check_tensor(t, name, dtypes, device=None):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _check_out(t, name, shape, device):
+    """A caller's output tensor: float32, contiguous, on ``device``, of ``shape``."""
+    _check_tensor(t, name, (torch.float32,), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_ws(ws, device):
+    """A caller's ``(buffer, bytes)`` workspace: the buffer must hold the bytes
+    it declares (the library trusts the declared size)."""
+    buf, n = ws
+    n = int(n)
+    if n < 0:
+        raise ValueError("workspace size must be >= 0")
+    if n > 0:
+        if buf is None or not buf.is_cuda or buf.device != device or not buf.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor on %s" % device)
+        if buf.numel() * buf.element_size() < n:
+            raise ValueError("workspace holds %d bytes, %d declared"
+                             % (buf.numel() * buf.element_size(), n))
+    return buf, n
+
+
 def layer_desc(x, C, W, grid, variant="auto", flags=0):
     """``kan_desc_t`` for ``x [N, I]``, ``C [O, I, G+D]``, ``W [O, I]`` or None;
     the spline degree D (1 .. 5, 3 for the pages' cubic layer) is read off C."""
@@ -72,10 +95,15 @@ def workspace(desc, pass_, device):
 
 def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None, dense_forward=False):
     """Packs the pass's operands into a workspace; returns ``(ws, ws_bytes)``."""
+    _check_tensor(C, "C", _DTYPES)
+    _check_tensor(W, "W_base", _DTYPES, C.device)
+    _check_tensor(dy, "dy", (torch.float32,), C.device)
     desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
+    if dy is not None and tuple(dy.shape) != (x.shape[0], C.shape[0]):
+        raise ValueError("dy must be [N, O]")
     if ws is None:
         ws = workspace(desc, pass_, C.device)
-    buf, n = ws
+    buf, n = _check_ws(ws, C.device)
     L.check(L.lib().kan_prepare(ctypes.byref(desc), int(pass_), _ptr(C), _ptr(W), _ptr(dy),
                                 _ptr(buf), n, _stream(C)), "kan_prepare")
     return ws
@@ -92,10 +120,10 @@ def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None
     desc = layer_desc(x, C, W, grid, variant, flags)
     if ws is None:
         ws = workspace(desc, L.KAN_PASS_FORWARD, x.device)
-    buf, n = ws
+    buf, n = _check_ws(ws, x.device)
     y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
                                                 device=x.device)
-    _check_tensor(y, "y", (torch.float32,), x.device)
+    _check_out(y, "y", (x.shape[0], C.shape[0]), x.device)
     L.check(L.lib().kan_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(W), _ptr(y), _ptr(buf),
                                 n, _stream(x)), "kan_forward")
     return y
@@ -113,7 +141,7 @@ def kan_backward(x, C, W, dy, grid, need_dx=True, need_dC=True, need_dW=True, va
         raise ValueError("dy must be [N, O]")
     if ws is None:
         ws = workspace(desc, L.KAN_PASS_BACKWARD, x.device)
-    buf, n = ws
+    buf, n = _check_ws(ws, x.device)
     f32 = dict(dtype=torch.float32, device=x.device)
     dx = torch.empty(x.shape, **f32) if need_dx else None
     dC = torch.empty(C.shape, **f32) if need_dC else None
@@ -168,7 +196,7 @@ def kan_group_forward(x, C, grid, out=None):
     _check_tensor(C, "C", _DTYPES, x.device)
     desc = group_desc(x, C, grid)
     y = out if out is not None else torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    _check_tensor(y, "y", (torch.float32,), x.device)
+    _check_out(y, "y", x.shape, x.device)
     L.check(L.lib().kan_group_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(y), _stream(x)),
             "kan_group_forward")
     return y
@@ -185,7 +213,7 @@ def kan_group_backward(x, C, dy, grid, need_dx=True, need_dC=True, ws=None):
     if ws is None:
         n = kan_group_workspace_size(desc) if need_dC else 0
         ws = (torch.empty(max(n, 1), dtype=torch.uint8, device=x.device), n)
-    buf, n = ws
+    buf, n = _check_ws(ws, x.device)
     f32 = dict(dtype=torch.float32, device=x.device)
     dx = torch.empty(x.shape, **f32) if need_dx else None
     dC = torch.empty(C.shape, **f32) if need_dC else None
@@ -228,10 +256,10 @@ def kan_surface_forward(x, C, grid, ws=None, out=None, dense_forward=False):
     desc = surface_desc(x, C, grid)
     if dense_forward:
         desc.flags = L.KAN_FLAG_DENSE_FORWARD
-    buf, n = ws if ws is not None else _surface_ws(desc, L.KAN_PASS_FORWARD, x.device)
+    buf, n = _check_ws(ws if ws is not None else _surface_ws(desc, L.KAN_PASS_FORWARD, x.device), x.device)
     y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
                                                 device=x.device)
-    _check_tensor(y, "y", (torch.float32,), x.device)
+    _check_out(y, "y", (x.shape[0], C.shape[0]), x.device)
     L.check(L.lib().kan_surface_forward(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(y), _ptr(buf), n,
                                         _stream(x)), "kan_surface_forward")
     return y
@@ -245,7 +273,7 @@ def kan_surface_backward(x, C, dy, grid, need_dx=True, need_dC=True, ws=None):
     desc = surface_desc(x, C, grid)
     if tuple(dy.shape) != (x.shape[0], C.shape[0]):
         raise ValueError("dy must be [N, O]")
-    buf, n = ws if ws is not None else _surface_ws(desc, L.KAN_PASS_BACKWARD, x.device)
+    buf, n = _check_ws(ws if ws is not None else _surface_ws(desc, L.KAN_PASS_BACKWARD, x.device), x.device)
     f32 = dict(dtype=torch.float32, device=x.device)
     dx = torch.empty(x.shape, **f32) if need_dx else None
     dC = torch.empty(C.shape, **f32) if need_dC else None

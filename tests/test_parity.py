@@ -330,6 +330,59 @@ def test_empty_batch(F, variant):
     assert torch.count_nonzero(dC) == 0 and torch.count_nonzero(dW) == 0
 
 
+def test_binding_rejects_bad_outputs_and_workspaces(F):
+    """The Python binding refuses, before any launch, an ``out`` tensor of the
+    wrong shape and a workspace smaller than the bytes it declares (the
+    library trusts the declared size), for the layer, the grouped activation
+    and the 2-D layer."""
+    import torch
+    from kolmogorov_arnold_network_amd import _lib as L
+    say("binding checks")
+    dev = "cuda:0"
+    grid = (-1.0, 1.0, 5)
+    x = torch.rand(40, 6, device=dev) * 2 - 1
+    C = torch.randn(3, 6, 8, device=dev)
+    W = torch.randn(3, 6, device=dev)
+    desc = F.layer_desc(x, C, W, grid, "mfma")
+    n = F.kan_workspace_size(desc, L.KAN_PASS_FORWARD)
+    assert n > 0
+    with pytest.raises(ValueError, match="y must be"):
+        F.kan_forward(x, C, W, grid, "mfma", out=torch.empty(40, 2, device=dev))
+    with pytest.raises(ValueError, match="declared"):
+        F.kan_forward(x, C, W, grid, "mfma", ws=(torch.empty(n - 1, dtype=torch.uint8, device=dev), n))
+    nb = F.kan_workspace_size(desc, L.KAN_PASS_BACKWARD)
+    with pytest.raises(ValueError, match="declared"):
+        F.kan_backward(x, C, W, torch.randn(40, 3, device=dev), grid, variant="mfma",
+                       ws=(torch.empty(nb // 2, dtype=torch.uint8, device=dev), nb))
+    with pytest.raises(ValueError, match="device tensor"):
+        F.kan_forward(x, C, W, grid, "mfma", ws=(torch.empty(n, dtype=torch.uint8), n))
+    with pytest.raises(ValueError, match="dy must be"):
+        F.kan_prepare(x, C, W, grid, L.KAN_PASS_BACKWARD, dy=torch.randn(40, 4, device=dev), variant="mfma")
+    Cg = torch.randn(2, 8, device=dev)
+    with pytest.raises(ValueError, match="y must be"):
+        F.kan_group_forward(x, Cg, grid, out=torch.empty(40, 5, device=dev))
+    gd = F.group_desc(x, Cg, grid)
+    ng = F.kan_group_workspace_size(gd)
+    with pytest.raises(ValueError, match="declared"):
+        F.kan_group_backward(x, Cg, torch.randn(40, 6, device=dev), grid,
+                             ws=(torch.empty(max(ng - 4, 1), dtype=torch.uint8, device=dev), ng))
+    Cs = torch.randn(3, 3, 8, 8, device=dev)
+    with pytest.raises(ValueError, match="y must be"):
+        F.kan_surface_forward(x, Cs, grid, out=torch.empty(39, 3, device=dev))
+    sd = F.surface_desc(x, Cs, grid)
+    ns = F.kan_surface_workspace_size(sd, L.KAN_PASS_BACKWARD)
+    with pytest.raises(ValueError, match="declared"):
+        F.kan_surface_backward(x, Cs, torch.randn(40, 3, device=dev), grid,
+                               ws=(torch.empty(max(ns - 256, 1), dtype=torch.uint8, device=dev), ns))
+    # correct outputs and workspaces still work
+    y = torch.empty(40, 3, device=dev)
+    F.kan_forward(x, C, W, grid, "mfma", out=y, ws=(torch.empty(n, dtype=torch.uint8, device=dev), n))
+    _sync()
+    ref = oracle.layer_forward(_np(x).astype(np.float64), _np(C).astype(np.float64),
+                               _np(W).astype(np.float64), -1.0, 1.0, 5)
+    assert rel_inf(_np(y), ref) <= TOL_F32
+
+
 @pytest.mark.parametrize("variant", ["mfma", "gather"])
 def test_output_guards_and_nonfinite_inputs(F, variant):
     """Outputs written exactly in place (NaN canaries around them stay NaN);
