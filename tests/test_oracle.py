@@ -282,6 +282,43 @@ def test_out_of_grid(G):
     np.testing.assert_allclose(dx, dx_ref, rtol=1e-13, atol=0)
 
 
+@pytest.mark.parametrize("D", [1, 3])
+@pytest.mark.parametrize("G", [1, 2, 5, 8, 20, 50, 125])
+def test_span_decision_near_knots(G, D):
+    """The knot span is an integer decided by floating point.  The oracle's
+    half-open degree-0 intervals compare x with float64 knots; the kernels take
+    the largest s with fma(x, scale, shift - s) >= 0, whose sign is that of
+    the exact real x * scale + shift - s for the float32 constants scale =
+    G / (hi - lo) and shift = D - lo * scale.  On [-1, 1] both constants are
+    exact in float32, and the two rules must pick the same span for every
+    float32 input near every knot, where the degree-1 derivative jumps.  The
+    kernel rule is evaluated here in exact rational arithmetic."""
+    lo, hi = -1.0, 1.0
+    t = obs.knots(lo, hi, G, D)
+    scale = np.float32(G / (hi - lo))
+    shift = np.float32(D - lo * G / (hi - lo))
+    assert float(scale) == G / (hi - lo) and float(shift) == D - lo * G / (hi - lo)
+    fs, fh = Fraction(float(scale)), Fraction(float(shift))
+    xs = []
+    for tr in t:
+        f = np.float32(tr)
+        for direction in (-np.inf, np.inf):
+            v = f
+            for _ in range(3):
+                xs.append(v)
+                v = np.nextafter(v, np.float32(direction))
+    xs = np.unique(np.array(xs, dtype=np.float32))
+    ind = obs.cox_de_boor(xs.astype(np.float64), t, 0)        # [n, G + 2D]
+    inside = ind.sum(axis=1) == 1.0
+    assert inside.sum() > len(t)
+    for x, row, ok in zip(xs, ind, inside):
+        s_kernel = math.floor(Fraction(float(x)) * fs + fh)
+        if ok:
+            assert s_kernel == int(np.argmax(row)), (G, D, float(x))
+        else:
+            assert s_kernel < 0 or s_kernel >= G + 2 * D, (G, D, float(x))
+
+
 def test_silu_closed_forms():
     x = np.array([-3.0, -1.0, 0.0, 0.5, 2.0, 10.0])
     np.testing.assert_allclose(oracle.silu(x), x * (1 + np.tanh(x / 2)) / 2, rtol=1e-14)
