@@ -63,7 +63,10 @@ extern "C" {
 typedef enum {
     KAN_OK = 0,
     KAN_ERR_NULL = -1,        /* a required pointer is NULL, or a forbidden one is not */
-    KAN_ERR_SHAPE = -2,       /* N < 0, I < 1, O < 1, or a size beyond the index range */
+    KAN_ERR_SHAPE = -2,       /* N < 0, I < 1, O < 1, or a size beyond the index range: N, O,
+                               * 2P and a row's I*(G+D+has_base) columns must each stay below
+                               * 2^31 - 4096 (whole tensors may exceed 2^31 elements; addresses
+                               * are 64-bit); the basis entry points bound n*K the same way */
     KAN_ERR_GRID = -3,        /* G < 1 or G > 125 (2-D layer: 13), lo >= hi, or lo / hi not finite */
     KAN_ERR_DTYPE = -4,       /* dtype not KAN_F32 / KAN_BF16 */
     KAN_ERR_ALIGN = -5,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
