@@ -128,7 +128,7 @@ def _tp_scale(D, power):
 
 
 @pytest.mark.parametrize("D", [1, 2, 4, 5])
-@pytest.mark.parametrize("G", [1, 5, 20])
+@pytest.mark.parametrize("G", [1, 5, 20, 125])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_basis_general_degree(F, D, G, dtype):
     lo, hi = -1.0, 1.0
@@ -214,7 +214,9 @@ SPARSE = [
 # Layers of spline degree D != 3 (the FlashKAN page's degree-k basis): both
 # passes on the matrix cores, against the degree-D oracle; the layer's
 # tolerances.
-DEG_CASES = [(70, 29, 33, 8, 1), (70, 29, 33, 8, 2), (50, 40, 17, 5, 4), (40, 13, 300, 20, 5), (33, 9, 5, 1, 4)]
+DEG_CASES = [(70, 29, 33, 8, 1), (70, 29, 33, 8, 2), (50, 40, 17, 5, 4), (40, 13, 300, 20, 5), (33, 9, 5, 1, 4),
+             # the largest grid: 126 (degree 1) and 130 (degree 5) coefficients per edge
+             (19, 4, 5, 125, 1), (21, 3, 7, 125, 5)]
 
 
 @pytest.mark.parametrize("N,I,O,G,D", DEG_CASES)
