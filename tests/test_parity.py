@@ -158,6 +158,7 @@ def test_basis_general_degree(F, D, G, dtype):
 SMALL = [  # N, I, O, G, base
     (1, 1, 1, 1, True), (37, 5, 3, 8, False), (300, 29, 17, 5, True), (513, 64, 260, 20, True),
     (100, 13, 7, 50, False), (257, 40, 300, 8, True), (64, 256, 31, 3, True), (20, 3, 513, 12, False),
+    (40, 5, 70, 125, True),     # the largest grid: K = 128, the gather kernels' LDS bound
 ]
 
 
