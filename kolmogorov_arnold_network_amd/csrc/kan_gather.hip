@@ -6,6 +6,8 @@
 // pieces b0..b3 are formed; the contraction then gathers the coefficients
 // C[j, i, s-3 .. s].  All arithmetic is float32 and every reduction runs in a
 // fixed order without atomics.
+#include <type_traits>
+
 #include "kan_internal.h"
 
 namespace kan {
@@ -268,7 +270,10 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
     // Loads are issued unconditionally from addresses clamped in bounds (a
     // guarded load into a register that was zeroed first makes the compiler
     // wait for every earlier load); invalid values are zeroed when stored.
-    float cp[MAXQ];
+    float cp[std::is_same<TS, float>::value ? 1 : MAXQ];
+    constexpr int NV = (MAXQ + 3) / 4;               // float32: 16-byte pieces per thread
+    float4 cp4[std::is_same<TS, float>::value ? NV : 1];
+    const int nv = (ICK + 15) / 16;
     float wp[2], xp[2];
     const bool jc_ok = j0 + jc < O;
     auto load = [&](int c) {
@@ -277,9 +282,19 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         // does not exist); indices past the chunk's last input are clamped
         const TS* row = C + (jc_ok ? ((int64_t)(j0 + jc) * I + i0) * K : 0);
         const int last = jc_ok ? nic * K - 1 : 0;
+        if constexpr (std::is_same<TS, float>::value) {
+            // 16-byte pieces k = rc + 4 q of the output's chunk row, each
+            // clamped to start inside it (a clamped piece repeats values)
 #pragma unroll
-        for (int q = 0; q < MAXQ; ++q)
-            if (q < nq) cp[q] = load_f(row, min(rc + 4 * q, last));
+            for (int q = 0; q < NV; ++q) {
+                const int s = jc_ok ? min(4 * (rc + 4 * q), last - 3) : 0;
+                if (q < nv) __builtin_memcpy(&cp4[q], row + s, 16);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < MAXQ; ++q)
+                if (q < nq) cp[q] = load_f(row, min(rc + 4 * q, last));
+        }
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
             const bool okw = has_pair[v] && base && j0 + pj[v] < O && pi[v] < nic;
@@ -295,10 +310,24 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         RecF* Rs = reinterpret_cast<RecF*>(Ws + wsz);
         const int i0 = c * IC, nic = min(IC, I - i0);
         const int lim = jc_ok ? nic * K : 0;         // valid coefficients of this output
+        if constexpr (std::is_same<TS, float>::value) {
 #pragma unroll
-        for (int q = 0; q < MAXQ; ++q) {
-            const int rem = rc + 4 * q;
-            if (q < nq && rem < ICK) Cs[rem * GF_TJ + jc] = rem < lim ? cp[q] : 0.0f;
+            for (int q = 0; q < NV; ++q) {
+                const int s = jc_ok ? min(4 * (rc + 4 * q), lim - 4) : 0;
+                if (q < nv && jc_ok) {
+                    Cs[(s + 0) * GF_TJ + jc] = cp4[q].x;
+                    Cs[(s + 1) * GF_TJ + jc] = cp4[q].y;
+                    Cs[(s + 2) * GF_TJ + jc] = cp4[q].z;
+                    Cs[(s + 3) * GF_TJ + jc] = cp4[q].w;
+                }
+            }
+            for (int rem = lim + rc; rem < ICK; rem += 4) Cs[rem * GF_TJ + jc] = 0.0f;
+        } else {
+#pragma unroll
+            for (int q = 0; q < MAXQ; ++q) {
+                const int rem = rc + 4 * q;
+                if (q < nq && rem < ICK) Cs[rem * GF_TJ + jc] = rem < lim ? cp[q] : 0.0f;
+            }
         }
 #pragma unroll
         for (int v = 0; v < 2; ++v) {

@@ -957,28 +957,46 @@ struct EpiDX {
                 for (int r = 0; r < 16; ++r)
                     P[(rw + acc_row(0, r)) * DX_PITCH + cw + 32 * fj] = acc[h][fj][r];
             __syncthreads();
+            // 4 items per pass: their x loads go out together (addresses
+            // clamped in bounds, values of items past the end unused)
+            const int total = 128 * nin;
+            const float inv = 1.0f / (float)nin;   // (e + 0.5) / nin stays 1 / (2 nin) off an integer
 #pragma unroll 1
-            for (int e = t; e < 128 * nin; e += NTHR) {
-                const int rl = e / nin, il = e - rl * nin;
-                const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
-                const int i = i_lo + il;
-                const int cb = i * a.Kb - c0;            // tile column of (i, m = 0)
-                if (b < a.N) {
-                    const float xv = load_f(x, (int64_t)b * a.I + i);
-                    float u;
-                    const int s = span_u(xv, a.g, u);
-                    float d[4];
-                    dpieces(u, a.g.scale, d[0], d[1], d[2], d[3]);
-                    const float* prow = P + rl * DX_PITCH;
-                    const int cs = cb + a.K;
-                    float v = (a.base && cs >= 0 && cs < 256) ? prow[cs] * silu_prime(xv) : 0.0f;
+            for (int e0 = t; e0 < total; e0 += 4 * NTHR) {
+                float xq[4];
+                int rlq[4], ilq[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int m = s - 3 + r, c = cb + m;
-                        if (m >= 0 && m < a.K && c >= 0 && c < 256) v = __builtin_fmaf(prow[c], d[r], v);
+                for (int q = 0; q < 4; ++q) {
+                    const int e = min(e0 + q * NTHR, total - 1);
+                    const int rl = (int)(((float)e + 0.5f) * inv), il = e - rl * nin;
+                    const int b = min(tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31), a.N - 1);
+                    rlq[q] = rl;
+                    ilq[q] = il;
+                    xq[q] = load_f(x, (int64_t)b * a.I + i_lo + il);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = rlq[q], il = ilq[q];
+                    const int b = tm * 256 + (rl >> 5) * 64 + 32 * h + (rl & 31);
+                    const int i = i_lo + il;
+                    const int cb = i * a.Kb - c0;            // tile column of (i, m = 0)
+                    if (e0 + q * NTHR < total && b < a.N) {
+                        const float xv = xq[q];
+                        float u;
+                        const int s = span_u(xv, a.g, u);
+                        float d[4];
+                        dpieces(u, a.g.scale, d[0], d[1], d[2], d[3]);
+                        const float* prow = P + rl * DX_PITCH;
+                        const int cs = cb + a.K;
+                        float v = (a.base && cs >= 0 && cs < 256) ? prow[cs] * silu_prime(xv) : 0.0f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int m = s - 3 + r, c = cb + m;
+                            if (m >= 0 && m < a.K && c >= 0 && c < 256) v = __builtin_fmaf(prow[c], d[r], v);
+                        }
+                        if (cb >= 0 && cb + a.Kb <= 256) a.out0[(int64_t)b * a.I + i] = v;
+                        else a.out1[((int64_t)b * a.tiles_n + tn) * 2 + (cb < 0 ? 0 : 1)] = v;
                     }
-                    if (cb >= 0 && cb + a.Kb <= 256) a.out0[(int64_t)b * a.I + i] = v;
-                    else a.out1[((int64_t)b * a.tiles_n + tn) * 2 + (cb < 0 ? 0 : 1)] = v;
                 }
             }
             __syncthreads();
