@@ -27,8 +27,9 @@
  *   fastest; W_base [O, I]; y, dy [N, O]; dx [N, I]; dC [O, I, G+3];
  *   dW_base [O, I].
  * - x, C and W_base share one storage dtype (KAN_F32 or KAN_BF16); y, dy, dx,
- *   dC and dW_base are always float32.  Arithmetic accumulates in float32 (the
- *   float32 gather forward adds its per-input partials in float64).
+ *   dC and dW_base are always float32.  Arithmetic accumulates in float32
+ *   (the float32 forwards add their partial sums in float64; see
+ *   kan_variant_t).
  * - Tensor pointers are DEVICE pointers, 16-byte aligned.  `desc` and `grid`
  *   are HOST pointers, read during the call only.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
@@ -79,27 +80,32 @@ typedef enum {
 typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
 
 /* Kernel family.  MFMA runs the contraction over the dense basis
- * (I*(G+3+has_base) wide) on the matrix cores, with the basis generated in LDS
- * and never written to memory; it needs G+3+has_base <= 256.  GATHER touches
- * only the 4 non-zero basis functions per input (InKAN page, "Why InKAN?":
- * local 4-basis lookup) on the vector ALUs.  AUTO picks per pass: bf16 runs
- * both passes on MFMA; float32 runs the forward on GATHER (float64 addition
- * across inputs) and the backward on MFMA once N*I*O >= 2^16 (GATHER below);
+ * (I*(G+D+has_base) wide) on the matrix cores, with the basis generated in LDS
+ * and never written to memory; it needs G+D+has_base <= 256, and at least 4
+ * for a degree D other than 3.  A float32 MFMA forward adds its contraction
+ * in fixed slices of at most 1024 (i, m) terms whose float32 partial sums are
+ * added in float64, so that its rounding stays small enough for a following
+ * layer's B' (which amplifies it about tenfold) to keep a chain of layers
+ * within 1e-5.  GATHER touches only the D+1 non-zero basis functions per input
+ * (InKAN page, "Why InKAN?": local 4-basis lookup) on the vector ALUs; its
+ * forward adds the partial sums of chunks of at most 8 inputs in float64.
+ * AUTO picks per pass: bf16 runs both passes on MFMA; float32 runs the forward
+ * on GATHER and the backward on MFMA once N*I*O >= 2^16 (GATHER below);
  * GATHER wherever MFMA does not fit. */
 typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 2 } kan_variant_t;
 
 typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;
 
-/* Grid: G intervals on [lo, hi], 1 <= G <= 125 (the G+3 coefficients of an
+/* Grid: G intervals on [lo, hi], 1 <= G <= 125 (the G+D coefficients of an
  * input for a tile of outputs are staged in LDS), and the spline degree.  The
  * pages' layer is cubic (InKAN page) and 3 is the default everywhere; the
  * layer also takes degree D = 1 .. 5 (FlashKAN page: the degree-k form of the
  * basis), with the grid extended by D knots on each side (t_r = lo + (r - D) h)
  * and K = G + D coefficients per edge, so C is [O, I, G+D] and the formulas
- * at the top hold with B_m of degree D.  A layer of degree other than 3 runs
- * both passes on the matrix cores (variant GATHER and the structured-sparse
- * forward are cubic only) and needs G + D + has_base >= 4.  The grouped
- * activation and the 2-D layer are cubic only. */
+ * at the top hold with B_m of degree D.  Every variant takes every degree,
+ * except that MFMA needs G + D + has_base >= 4 when D != 3 and the
+ * structured-sparse forward is cubic only.  The grouped activation and the
+ * 2-D layer are cubic only. */
 typedef struct {
     float lo;
     float hi;
@@ -144,11 +150,15 @@ int kan_abi_version(void);
 /* Static description of a status code (never NULL). */
 const char* kan_status_string(int status);
 
-/* Bytes of workspace a pass needs (0 when the pass runs on GATHER; SIZE_MAX
- * if `desc` is invalid).  `pass` is kan_pass_t.  Besides the packed operands
- * of kan_prepare it holds, for a contraction with too few output tiles to fill
- * the GPU, the float32 partial outputs of its k-range slices (the forward's
- * y, dC and dW_base over batch slices), which are added in slice order. */
+/* Bytes of workspace a pass needs (SIZE_MAX if `desc` is invalid).  `pass`
+ * is kan_pass_t.  On MFMA it holds the packed operands of kan_prepare and the
+ * float32 partial outputs of k-range slices (the forward's y, slices of at
+ * most 1024 terms in float32 and otherwise where too few output tiles fill
+ * the GPU; dC and dW_base over batch slices), which are added in slice
+ * order.  The GATHER forward needs it only when too few blocks of rows and
+ * outputs fill the GPU: its inputs are then split into slices whose float64
+ * partial outputs [slices][N][O] are added in slice order.  The GATHER
+ * backward needs none (0). */
 size_t kan_workspace_size(const kan_desc_t* desc, int pass);
 
 /* Packs what a pass reads into the workspace: for a pass on MFMA the

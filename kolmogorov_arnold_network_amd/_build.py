@@ -1,8 +1,13 @@
-"""Builds the HIP library ``libkan_mi355x.so`` in-tree with hipcc for gfx950."""
+"""Builds the HIP library ``libkan_mi355x.so`` in-tree with hipcc for gfx950.
+
+Each source is compiled to its own object in parallel (no device code crosses
+a translation unit), then the objects are linked into the shared library.
+"""
 
 import os
 import shutil
 import subprocess
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
@@ -15,7 +20,7 @@ SOURCES = ["kan_api.cpp", "kan_gather.hip", "kan_grouped.hip", "kan_mfma.hip"]
 
 # -packed-fp32-ops off: the compiler must not form packed float32 ALU ops.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
@@ -27,18 +32,39 @@ def hipcc():
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
+def _filter(text):
+    return "\n".join(l for l in text.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
+
+
 def build_library(verbose=False):
     """Compile every source for gfx950 into ``LIB_PATH`` (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-o", tmp] + srcs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                     if "packed-fp32-ops' is not a recognized feature" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + msgs)
-    if verbose and msgs.strip():
-        print(msgs)
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="kanbuild") as tmpdir:
+        jobs = []
+        for s in SOURCES:
+            obj = os.path.join(tmpdir, s + ".o")
+            cmd = [cc] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", "-o", obj,
+                                        os.path.join(CSRC, s)]
+            jobs.append((cmd, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                    stderr=subprocess.STDOUT, text=True)))
+        msgs, failed = [], []
+        for cmd, obj, proc in jobs:
+            out, _ = proc.communicate()
+            out = _filter(out)
+            if out.strip():
+                msgs.append(out)
+            if proc.returncode != 0:
+                failed.append(" ".join(cmd) + "\n" + out)
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n\n".join(failed))
+        tmp = LIB_PATH + ".tmp"
+        cmd = [cc] + HIPCC_FLAGS + ["-shared", "-o", tmp] + [obj for _, obj, _ in jobs]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + _filter(res.stdout + res.stderr))
+    if verbose and msgs:
+        print("\n".join(msgs))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

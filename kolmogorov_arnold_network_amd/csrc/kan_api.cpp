@@ -15,6 +15,7 @@ namespace {
 
 constexpr int64_t kIndexLimit = (int64_t(1) << 31) - 4096;  // keeps 32-bit tile math safe
 constexpr int kMaxG = 125;                                      // K = G + 3 <= 128
+constexpr int64_t kF32SliceTiles = 32;                          // float32 forward: k-tiles per slice
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -92,6 +93,14 @@ void plan_layout(Plan& q, bool dense_forward) {
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
     q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
                            &q.nks_fwd);
+    // A float32 forward sums its contraction in slices of at most 32 k-tiles
+    // (1024 terms): a float32 running sum over the whole basis row (9408
+    // terms at 784 inputs) loses accuracy that the next layer's B' amplifies;
+    // the slices' partials are added in float64.
+    if (q.dtype == KAN_F32 && q.nks_fwd > kF32SliceTiles) {
+        q.nks_fwd = kF32SliceTiles;
+        q.split_fwd = (int)((nkt_fwd + kF32SliceTiles - 1) / kF32SliceTiles);
+    }
     if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
     q.ws_fwd = q.variant_fwd == KAN_VARIANT_MFMA ? off : 0;
     off = 0;
@@ -180,24 +189,18 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     q.esize = d->dtype == KAN_F32 ? 4 : 2;
     if (q.N > kIndexLimit || q.O > kIndexLimit || q.I * q.Kb > kIndexLimit) return KAN_ERR_SHAPE;
 
-    // An input's Kb columns must fit one 256-wide tile on the matrix cores.
+    // An input's Kb columns must fit one 256-wide tile on the matrix cores,
+    // and a degree other than 3 needs at least 4 columns per input (the
+    // operand generators' instances cover that many inputs per tile).
     // AUTO: bf16 runs both passes on the matrix cores.  float32 runs the
-    // forward on the local gather kernel, which adds the per-input partials in
-    // float64: in a chain of layers the next layer's B' amplifies forward
-    // rounding about tenfold, beyond what the float32 matrix instruction's
-    // rounding leaves room for.  Its backward (dx, dC) feeds no B', so it runs
-    // on the matrix cores, several times faster than the gather backward once
-    // the layer has at least 2^16 edge-rows (N I O); below that the packing
-    // and launches of the matrix-core path cost more than the work.
-    // Degrees other than 3 run on the matrix cores only (the gather kernels
-    // are cubic), with at least 4 columns per input (the operand generators'
-    // instances cover that many inputs per tile).
+    // forward on the local gather kernel, whose sums over inputs are float64
+    // and which touches only the D + 1 non-zero basis functions; its backward
+    // (dx, dC) feeds no B', so it runs on the matrix cores once the layer has
+    // at least 2^16 edge-rows (N I O); below that the packing and launches of
+    // the matrix-core path cost more than the work.
     const bool mfma_ok = q.Kb <= kTileN && (q.degree == 3 || q.Kb >= 4);
     if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
-    if (q.degree != 3) {
-        if (d->variant == KAN_VARIANT_GATHER || !mfma_ok) return KAN_ERR_UNSUPPORTED;
-        q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
-    } else if (d->variant == KAN_VARIANT_GATHER) {
+    if (d->variant == KAN_VARIANT_GATHER) {
         q.variant_fwd = q.variant_bwd = KAN_VARIANT_GATHER;
     } else if (d->variant == KAN_VARIANT_MFMA) {
         q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
@@ -208,6 +211,10 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     }
 
     plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
+    if (q.variant_fwd == KAN_VARIANT_GATHER) {
+        q.gf = gather_fwd_plan(q.N, q.I, q.O, q.K, q.degree, q.base);
+        q.ws_fwd = q.gf.ws;
+    }
     *p = q;
     return KAN_OK;
 }
@@ -248,7 +255,6 @@ static int pass_variant(const Plan& p, int pass) {
 }
 
 static int check_ws(const Plan& p, int pass, const void* ws, size_t ws_bytes) {
-    if (pass_variant(p, pass) != KAN_VARIANT_MFMA) return KAN_OK;
     const size_t need = pass == KAN_PASS_FORWARD ? p.ws_fwd : p.ws_bwd;
     if (ws_bytes < need) return KAN_ERR_WORKSPACE;
     if (need > 0 && !ws) return KAN_ERR_NULL;
@@ -319,7 +325,7 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (p.variant_fwd == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, s));
+    if (p.variant_fwd == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, ws, s));
     if (!(desc->flags & KAN_FLAG_PREPARED)) {
         st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
         if (st != KAN_OK) return st;

@@ -1,11 +1,12 @@
-// Local 4-basis kernels on the vector ALUs (gfx950), plus the standalone basis
+// Local-basis kernels on the vector ALUs (gfx950), plus the standalone basis
 // evaluation, the bf16 cast and a zero fill.
 //
 // "Local 4-basis lookup instead of dense K-basis computation" (InKAN project
-// page, "Why InKAN?"): for each (row b, input i) only the span s and the four
-// pieces b0..b3 are formed; the contraction then gathers the coefficients
-// C[j, i, s-3 .. s].  All arithmetic is float32 and every reduction runs in a
-// fixed order without atomics.
+// page, "Why InKAN?"): for each (row b, input i) only the span s and the D + 1
+// non-zero pieces of degree D (4 for the cubic layer) are formed; the
+// contractions then gather the coefficients C[j, i, s-D .. s].  Arithmetic is
+// float32 (the forward adds its partial sums in float64) and every reduction
+// runs in a fixed order without atomics.
 #include <type_traits>
 
 #include "kan_internal.h"
@@ -13,33 +14,6 @@
 namespace kan {
 
 namespace {
-
-// Per (b, i): span-relative coefficient index base and the four weights with
-// the out-of-range ones set to zero, so the inner loops can clamp the index
-// and multiply unconditionally.
-struct Rec {
-    int m0;          // s - 3: index of the coefficient that b0 multiplies
-    float w[4];      // b_r (or derivative) for m = m0 + r; 0 where m is outside [0, K-1]
-    float base;      // silu(x) or silu'(x)
-};
-
-template <bool DERIV>
-__device__ __forceinline__ Rec make_rec(float xv, const GridK& g) {
-    Rec r;
-    float u;
-    const int s = span_u(xv, g, u);
-    float w0, w1, w2, w3;
-    if (DERIV) dpieces(u, g.scale, w0, w1, w2, w3);
-    else pieces(u, w0, w1, w2, w3);
-    r.m0 = s - 3;
-    const int K = g.G + 3;
-    r.w[0] = (r.m0 >= 0 && r.m0 < K) ? w0 : 0.0f;
-    r.w[1] = (r.m0 + 1 >= 0 && r.m0 + 1 < K) ? w1 : 0.0f;
-    r.w[2] = (r.m0 + 2 >= 0 && r.m0 + 2 < K) ? w2 : 0.0f;
-    r.w[3] = (r.m0 + 3 >= 0 && r.m0 + 3 < K) ? w3 : 0.0f;
-    r.base = DERIV ? silu_prime(xv) : silu(xv);
-    return r;
-}
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
@@ -74,7 +48,7 @@ __global__ void basis_eval_kernel(GridK g, int64_t n, const TS* __restrict__ x,
     }
 }
 
-// ---- basis functions of degree D != 3 (basis evaluation only) ----
+// ---- basis functions of degree D (the layer kernels' pieces for D != 3) ----
 // The D + 1 non-zero uniform B-splines of degree D on a knot span, by local
 // coordinate u in [0, 1]: value r belongs to basis function s - D + r.  They
 // come from the degree-by-degree recurrence on uniform knots,
@@ -182,170 +156,233 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  Block: 64 rows x 64 outputs; thread: 4 rows x 4 consecutive outputs.
-// Inputs advance in chunks of IC inputs, as many (up to 7) as keep both chunk
-// buffers within 40 KB of LDS, so that 4 blocks share a CU; a chunk's
-// coefficients for the 64 outputs are then at most 20 values per thread (32
-// for K > 80, with one input per chunk).  They sit
-// in LDS as Cs[i][m][j], so that C[j..j+3, i, m] is one 16-byte read.  LDS
-// holds two chunk buffers: while one chunk is multiplied, the next chunk's
-// coefficients, W_base and x are loaded into registers, and are then written
-// (x as its span record) to the other buffer.  Global latency overlaps the
-// arithmetic, and each chunk costs one barrier.  Each input's five-term
-// partial phi_ji(x_i) is formed in float32 and added into a float64
-// accumulator: a chain of KAN layers feeds y through B' of the next layer,
-// which amplifies forward rounding error about tenfold, and float64 adds cost
-// the same as float32 FMAs on the vector ALU.
-constexpr int GF_TB = 64, GF_TJ = 64;
-
-// A (row, input) pair of the forward chunk: the LDS index of its first
-// coefficient row Cs[ii][mb][0], with mb = s - 3 clamped to [0, K - 4] so that
-// rows mb .. mb + 3 all exist, and the four weights of those rows (the spline
-// pieces shifted by the clamp, zero where a basis index is out of range).
-struct RecF {
-    int cb;
-    float w[4];
-    float base;
+// Layer kernels.  Per (b, i): span-relative coefficient index base and the
+// D + 1 weights with the out-of-range ones set to zero, so the inner loops can
+// clamp the index and multiply unconditionally.
+template <int D>
+struct RecD {
+    int m0;              // s - D: index of the coefficient that piece 0 multiplies
+    float w[D + 1];      // piece r (or its derivative) for m = m0 + r; 0 where m is outside [0, K-1]
+    float base;          // silu(x) or silu'(x)
 };
 
-__device__ __forceinline__ RecF make_recf(float xv, const GridK& g, int ii, int base) {
-    const Rec r = make_rec<false>(xv, g);
-    const int K = g.G + 3;
-    const int mb = clampi(r.m0, 0, K - 4);
-    RecF f;
+template <bool DERIV, int D>
+__device__ __forceinline__ RecD<D> make_rec(float xv, const GridK& g) {
+    RecD<D> r;
+    float u;
+    const int s = span_u(xv, g, u);
+    float w[D + 1];
+    if constexpr (D == 3) {
+        if (DERIV) dpieces(u, g.scale, w[0], w[1], w[2], w[3]);
+        else pieces(u, w[0], w[1], w[2], w[3]);
+    } else {
+        float b[D + 1], d[D + 1];
+        local_basis<D>(u, g.scale, b, d);
+#pragma unroll
+        for (int q = 0; q <= D; ++q) w[q] = DERIV ? d[q] : b[q];
+    }
+    r.m0 = s - D;
+    const int K = g.G + D;
+#pragma unroll
+    for (int q = 0; q <= D; ++q) r.w[q] = (r.m0 + q >= 0 && r.m0 + q < K) ? w[q] : 0.0f;
+    r.base = DERIV ? silu_prime(xv) : silu(xv);
+    return r;
+}
+
+template <int D>
+__device__ __forceinline__ RecD<D> zero_rec() {
+    RecD<D> r;
+    r.m0 = 0;
+#pragma unroll
+    for (int q = 0; q <= D; ++q) r.w[q] = 0.0f;
+    r.base = 0.0f;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  A block computes R = NT / 4 rows by 64 outputs over one slice of
+// the inputs: thread t takes the 4 outputs 4 (t % 16) .. +3 of the rows
+// t / 16 + (NT / 16) p, p < 4.  Inputs advance in chunks of IC <= 8 held in
+// LDS: the chunk's coefficients for the block's 64 outputs as Cs[ii][m][j]
+// (4 outputs of one coefficient row are one 16-byte read), its W_base as
+// Ws[ii][j], and one span record per (row, input).  There are two chunk
+// buffers: while one chunk is multiplied, the next chunk's coefficients,
+// W_base and x are loaded into registers, then written (x as its span record)
+// to the other buffer, with one barrier per chunk.
+//
+// - A thread's sums over one chunk are float32; each chunk's sum is added
+//   into a float64 accumulator.  In a chain of layers the next layer's B'
+//   amplifies forward rounding about tenfold, so the long sum over inputs
+//   is kept out of float32.
+// - All R rows of the block share one staged chunk, so the coefficient
+//   traffic per row, the part of the work that grows with G, falls as R
+//   grows.
+// - With too few blocks to fill the GPU the inputs are split into slices.
+//   Each slice writes float64 partial outputs, which gather_sum_kernel adds
+//   in slice order.
+constexpr int GF_TJ = 64;
+
+template <int D>
+struct alignas(8) RecF {
+    int cb;              // LDS index of coefficient row mb of the pair's input, Cs[ii][mb][0]
+    float w[D + 1];      // weights of rows mb .. mb + D
+    float base;          // silu(x); 0 without the base branch
+};
+
+// mb = s - D clamped to [0, K - D - 1], so that rows mb .. mb + D all exist,
+// and the pieces shifted by the clamp (zero where a basis index is out of
+// range or the span lies off the grid).
+template <int D>
+__device__ __forceinline__ RecF<D> make_recf(float xv, const GridK& g, int ii, bool base) {
+    const RecD<D> r = make_rec<false, D>(xv, g);
+    const int K = g.G + D;
+    const int mb = clampi(r.m0, 0, K - D - 1);
+    RecF<D> f;
     f.cb = (ii * K + mb) * GF_TJ;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q <= D; ++q) {
         const int k = mb + q - r.m0;                 // which piece multiplies row mb + q
-        f.w[q] = k == 0 ? r.w[0] : k == 1 ? r.w[1] : k == 2 ? r.w[2] : k == 3 ? r.w[3] : 0.0f;
+        float v = 0.0f;
+#pragma unroll
+        for (int e = 0; e <= D; ++e) v = k == e ? r.w[e] : v;
+        f.w[q] = v;
     }
     f.base = base ? r.base : 0.0f;
     return f;
 }
 
-__host__ __device__ inline int gather_fwd_ic(int K) {
-    const int ic = 5120 / (GF_TJ * K + GF_TJ + GF_TB * (int)(sizeof(RecF) / 4));
-    return ic < 1 ? 1 : (ic > 7 ? 7 : ic);
-}
-__host__ __device__ inline int gather_fwd_buf_floats(int K) {
-    const int ic = gather_fwd_ic(K);
-    return ic * K * GF_TJ + ic * GF_TJ + ic * GF_TB * (int)(sizeof(RecF) / 4);
-}
-
-template <typename TS, int MAXQ>
-__global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, int O, int base,
-                                                         const TS* __restrict__ x,
-                                                         const TS* __restrict__ C,
-                                                         const TS* __restrict__ W,
-                                                         float* __restrict__ y) {
+template <typename TS, int D, bool BASE, int NT, int MAXQ>
+__global__ __launch_bounds__(NT) void gather_fwd_kernel(GatherFwdArgs a) {
+    constexpr int R = NT / 4;                        // rows per block
+    constexpr int RS = NT / 16;                      // row stride of a thread's 4 rows
+    constexpr int NPC = NT / 64;                     // threads sharing one output's coefficient loads
+    constexpr int RW = (int)(sizeof(RecF<D>) / 4);
+    constexpr int XV = (R * 8 + NT - 1) / NT;        // x loads per thread (IC <= 8)
+    constexpr int WV = (GF_TJ * 8 + NT - 1) / NT;    // W_base loads per thread
+    constexpr int PG = NT == 1024 ? 1 : 4;           // rows whose LDS reads overlap
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
-    const int K = g.G + 3;
-    const int IC = gather_fwd_ic(K);
-    const int ICK = IC * K;                          // coefficients of one output in a chunk
-    const int csz = ICK * GF_TJ, wsz = IC * GF_TJ;
-    const int bufsz = gather_fwd_buf_floats(K);      // floats per buffer: Cs, Ws, Rs
+    const TS* __restrict__ x = static_cast<const TS*>(a.x);
+    const TS* __restrict__ C = static_cast<const TS*>(a.C);
+    const TS* __restrict__ W = static_cast<const TS*>(a.W);
+    const GridK g = a.g;
+    const int K = g.G + D, IC = a.IC, I = a.I, N = a.N, O = a.O;
+    const int csz = IC * K * GF_TJ, wsz = BASE ? IC * GF_TJ : 0;
+    const int bufsz = csz + wsz + IC * R * RW;       // floats per chunk buffer
     const int t = threadIdx.x;
-    const int jq = t % 16, rq = t / 16;
-    const int b0 = blockIdx.x * GF_TB, j0 = blockIdx.y * GF_TJ;
-    const int nch = (I + IC - 1) / IC;
 
-    // this thread's coefficient loads: output jc = t / 4 of the tile, and of
-    // that output's ICK chunk coefficients (rem = ii * K + m, contiguous in
-    // C) those with rem = t % 4 + 4 q
-    const int jc = t >> 2, rc = t & 3;
-    const int nq = (ICK + 3) / 4;                    // <= MAXQ
-    // W_base and x: the 64 IC (output or row, input) pairs of a chunk, pair
-    // u = t + 256 v (v < 2, as IC <= 7) at pair index pj = u / IC, pi = u % IC
-    int pj[2], pi[2];
-    bool has_pair[2];
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-        const int u = t + 256 * v;
-        has_pair[v] = u < IC * 64;
-        pj[v] = u / IC;
-        pi[v] = u % IC;
-    }
+    // block -> (row block, output block).  Workgroups are dealt to the 8 XCDs
+    // in turn; consecutive ids go to one XCD with row blocks fastest, so the
+    // blocks an XCD runs together share one output block's coefficients in
+    // its L2.
+    const int T = a.RB * a.OB;
+    const int bid = blockIdx.x, nfull = T / 8, rem = T % 8, xcd = bid % 8;
+    const int id = xcd * nfull + min(xcd, rem) + bid / 8;
+    const int rb = id % a.RB, ob = id / a.RB;
+    const int b0 = rb * R, j0 = ob * GF_TJ;
+    const int slice = blockIdx.y;
+    const int ib = slice * a.IS, ie = min(I, ib + a.IS);
+    const int nch = (ie - ib + IC - 1) / IC;
 
-    // Loads are issued unconditionally from addresses clamped in bounds (a
-    // guarded load into a register that was zeroed first makes the compiler
-    // wait for every earlier load); invalid values are zeroed when stored.
-    float cp[std::is_same<TS, float>::value ? 1 : MAXQ];
-    constexpr int NV = (MAXQ + 3) / 4;               // float32: 16-byte pieces per thread
-    float4 cp4[std::is_same<TS, float>::value ? NV : 1];
-    const int nv = (ICK + 15) / 16;
-    float wp[2], xp[2];
-    const bool jc_ok = j0 + jc < O;
+    // Coefficient loads: output jl = t % 64 of the block (an output past O
+    // reads output O - 1; its sums are never stored), 4-element pieces
+    // k = t / 64 + NPC q of that output's chunk row C[j, i0 .. i0+nic-1, :],
+    // each clamped to start inside the row.  Consecutive lanes hold
+    // consecutive outputs, so the LDS stores are free of bank conflicts.
+    // Loads are issued unconditionally from addresses clamped in bounds where
+    // possible (a guarded load into a register that was zeroed first makes
+    // the compiler wait for every earlier load); invalid values are zeroed
+    // when stored.
+    const int jl = t % 64, pc = t / 64;
+    const TS* crow = C + (int64_t)min(j0 + jl, O - 1) * I * K;
+    float4 cp[MAXQ];
+    float xp[XV], wp[WV];
     auto load = [&](int c) {
-        const int i0 = c * IC, nic = min(IC, I - i0);
-        // row of output j0 + jc from input i0 on (output 0 when the output
-        // does not exist); indices past the chunk's last input are clamped
-        const TS* row = C + (jc_ok ? ((int64_t)(j0 + jc) * I + i0) * K : 0);
-        const int last = jc_ok ? nic * K - 1 : 0;
-        if constexpr (std::is_same<TS, float>::value) {
-            // 16-byte pieces k = rc + 4 q of the output's chunk row, each
-            // clamped to start inside it (a clamped piece repeats values)
+        const int i0 = ib + c * IC, nic = min(IC, ie - i0);
+        const int ick = nic * K;
+        const TS* src = crow + (int64_t)i0 * K;
 #pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                const int s = jc_ok ? min(4 * (rc + 4 * q), last - 3) : 0;
-                if (q < nv) __builtin_memcpy(&cp4[q], row + s, 16);
+        for (int q = 0; q < MAXQ; ++q) {
+            const int k = pc + NPC * q;
+            if (4 * k < ick) {
+                if (std::is_same<TS, float>::value && ick >= 4) {
+                    __builtin_memcpy(&cp[q], reinterpret_cast<const float*>(src) + min(4 * k, ick - 4), 16);
+                } else {
+                    const int s = ick >= 4 ? min(4 * k, ick - 4) : 0;
+                    cp[q].x = load_f(src, min(s + 0, ick - 1));
+                    cp[q].y = load_f(src, min(s + 1, ick - 1));
+                    cp[q].z = load_f(src, min(s + 2, ick - 1));
+                    cp[q].w = load_f(src, min(s + 3, ick - 1));
+                }
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < MAXQ; ++q)
-                if (q < nq) cp[q] = load_f(row, min(rc + 4 * q, last));
         }
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const bool okw = has_pair[v] && base && j0 + pj[v] < O && pi[v] < nic;
-            const bool okx = has_pair[v] && b0 + pj[v] < N && pi[v] < nic;
-            wp[v] = load_f(W ? W : x, okw ? (int64_t)(j0 + pj[v]) * I + i0 + pi[v] : 0);
-            xp[v] = load_f(x, okx ? (int64_t)(b0 + pj[v]) * I + i0 + pi[v] : 0);
-            wp[v] = okw ? wp[v] : 0.0f;
+        for (int v = 0; v < XV; ++v) {
+            const int u = t + NT * v, row = u / IC, ii = u - row * IC;
+            const bool ok = u < R * IC && b0 + row < N && ii < nic;
+            xp[v] = load_f(x, ok ? (int64_t)(b0 + row) * I + i0 + ii : 0);
+        }
+        if constexpr (BASE) {
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int u = t + NT * v, jj = u / IC, ii = u - jj * IC;
+                const bool ok = u < GF_TJ * IC && j0 + jj < O && ii < nic;
+                wp[v] = load_f(W, ok ? (int64_t)(j0 + jj) * I + i0 + ii : 0);
+            }
         }
     };
     auto store = [&](int c, int buf) {
         float* Cs = smem + buf * bufsz;
         float* Ws = Cs + csz;
-        RecF* Rs = reinterpret_cast<RecF*>(Ws + wsz);
-        const int i0 = c * IC, nic = min(IC, I - i0);
-        const int lim = jc_ok ? nic * K : 0;         // valid coefficients of this output
-        if constexpr (std::is_same<TS, float>::value) {
+        RecF<D>* Rs = reinterpret_cast<RecF<D>*>(Ws + wsz);
+        const int i0 = ib + c * IC, nic = min(IC, ie - i0);
+        const int ick = nic * K;
 #pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                const int s = jc_ok ? min(4 * (rc + 4 * q), lim - 4) : 0;
-                if (q < nv && jc_ok) {
-                    Cs[(s + 0) * GF_TJ + jc] = cp4[q].x;
-                    Cs[(s + 1) * GF_TJ + jc] = cp4[q].y;
-                    Cs[(s + 2) * GF_TJ + jc] = cp4[q].z;
-                    Cs[(s + 3) * GF_TJ + jc] = cp4[q].w;
-                }
-            }
-            for (int rem = lim + rc; rem < ICK; rem += 4) Cs[rem * GF_TJ + jc] = 0.0f;
-        } else {
+        for (int q = 0; q < MAXQ; ++q) {
+            const int k = pc + NPC * q;
+            if (4 * k < ick) {
+                const int s = ick >= 4 ? min(4 * k, ick - 4) : 0;
+                const float vv[4] = {cp[q].x, cp[q].y, cp[q].z, cp[q].w};
 #pragma unroll
-            for (int q = 0; q < MAXQ; ++q) {
-                const int rem = rc + 4 * q;
-                if (q < nq && rem < ICK) Cs[rem * GF_TJ + jc] = rem < lim ? cp[q] : 0.0f;
+                for (int e = 0; e < 4; ++e)
+                    if (s + e < ick) Cs[(s + e) * GF_TJ + jl] = vv[e];
             }
         }
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            if (!has_pair[v]) continue;
-            Ws[pi[v] * GF_TJ + pj[v]] = wp[v];
-            RecF r;
-            if (b0 + pj[v] < N && pi[v] < nic) {
-                r = make_recf(xp[v], g, pi[v], base);
-            } else {
-                r.cb = pi[v] * K * GF_TJ;
-                r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0.0f;
-                r.base = 0.0f;
+        for (int v = 0; v < XV; ++v) {
+            const int u = t + NT * v, row = u / IC, ii = u - row * IC;
+            if (u < R * IC && ii < nic) {
+                RecF<D> r;
+                if (b0 + row < N) {
+                    r = make_recf<D>(xp[v], g, ii, BASE);
+                } else {                             // a row past N: valid index, no weight
+                    r.cb = ii * K * GF_TJ;
+#pragma unroll
+                    for (int q = 0; q <= D; ++q) r.w[q] = 0.0f;
+                    r.base = 0.0f;
+                }
+                Rs[ii * R + row] = r;
             }
-            Rs[pi[v] * GF_TB + pj[v]] = r;
+        }
+        if constexpr (BASE) {
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int u = t + NT * v, jj = u / IC, ii = u - jj * IC;
+                if (u < GF_TJ * IC && ii < nic) Ws[ii * GF_TJ + jj] = j0 + jj < O ? wp[v] : 0.0f;
+            }
         }
     };
 
-    double acc[4][4] = {};
+    const int jq = t & 15, rq = t >> 4;
+    float acc[4][4];
+    double accd[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[p][q] = 0.0f;
+            accd[p][q] = 0.0;
+        }
     load(0);
     store(0, 0);
     __syncthreads();
@@ -354,48 +391,88 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
         if (more) load(c + 1);
         const float* Cs = smem + (c & 1) * bufsz;
         const float* Ws = Cs + csz;
-        const RecF* Rs = reinterpret_cast<const RecF*>(Ws + wsz);
-        const int nic = min(IC, I - c * IC);
+        const RecF<D>* Rs = reinterpret_cast<const RecF<D>*>(Ws + wsz);
+        const int nic = min(IC, ie - (ib + c * IC));
         for (int ii = 0; ii < nic; ++ii) {
-            const float4 wv = *reinterpret_cast<const float4*>(&Ws[ii * GF_TJ + 4 * jq]);
-            RecF rr[4];
+            float4 wv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if constexpr (BASE) wv = *reinterpret_cast<const float4*>(&Ws[ii * GF_TJ + 4 * jq]);
+            RecF<D> rr[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) rr[p] = Rs[ii * GF_TB + rq + 16 * p];
+            for (int p = 0; p < 4; ++p) rr[p] = Rs[ii * R + rq + RS * p];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const RecF& r = rr[p];
-                const float* crow = Cs + r.cb + 4 * jq;
-                // the row's four coefficient reads go out together, ahead of
-                // the FMAs that use them
-                float4 cv[4];
+                const RecF<D>& r = rr[p];
+                const float* cr = Cs + r.cb + 4 * jq;
+                // the row's coefficient reads go out together, ahead of the
+                // FMAs that use them; at most PG rows' reads are in flight
+                // (more would not fit the registers of 1024-thread blocks)
+                float4 cv[D + 1];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) cv[q] = *reinterpret_cast<const float4*>(crow + q * GF_TJ);
-                float a0 = r.base * wv.x, a1 = r.base * wv.y, a2 = r.base * wv.z, a3 = r.base * wv.w;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    a0 = __builtin_fmaf(r.w[q], cv[q].x, a0);
-                    a1 = __builtin_fmaf(r.w[q], cv[q].y, a1);
-                    a2 = __builtin_fmaf(r.w[q], cv[q].z, a2);
-                    a3 = __builtin_fmaf(r.w[q], cv[q].w, a3);
+                for (int q = 0; q <= D; ++q) cv[q] = *reinterpret_cast<const float4*>(cr + q * GF_TJ);
+                if constexpr (BASE) {
+                    acc[p][0] = __builtin_fmaf(r.base, wv.x, acc[p][0]);
+                    acc[p][1] = __builtin_fmaf(r.base, wv.y, acc[p][1]);
+                    acc[p][2] = __builtin_fmaf(r.base, wv.z, acc[p][2]);
+                    acc[p][3] = __builtin_fmaf(r.base, wv.w, acc[p][3]);
                 }
-                acc[p][0] += (double)a0;
-                acc[p][1] += (double)a1;
-                acc[p][2] += (double)a2;
-                acc[p][3] += (double)a3;
+#pragma unroll
+                for (int q = 0; q <= D; ++q) {
+                    acc[p][0] = __builtin_fmaf(r.w[q], cv[q].x, acc[p][0]);
+                    acc[p][1] = __builtin_fmaf(r.w[q], cv[q].y, acc[p][1]);
+                    acc[p][2] = __builtin_fmaf(r.w[q], cv[q].z, acc[p][2]);
+                    acc[p][3] = __builtin_fmaf(r.w[q], cv[q].w, acc[p][3]);
+                }
+                if (PG < 4 && p % PG == PG - 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                accd[p][q] += (double)acc[p][q];
+                acc[p][q] = 0.0f;
+            }
         if (more) store(c + 1, (c + 1) & 1);
         __syncthreads();
     }
+    const bool vec = (O & 3) == 0;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int b = b0 + rq + 16 * p;
-        if (b >= N) continue;
+        const int b = b0 + rq + RS * p;
+        const int j = j0 + 4 * jq;
+        if (b >= N || j >= O) continue;
+        if (a.part) {
+            double* dst = a.part + ((int64_t)slice * N + b) * O + j;
+            if (vec) {
+                *reinterpret_cast<double2*>(dst) = make_double2(accd[p][0], accd[p][1]);
+                *reinterpret_cast<double2*>(dst + 2) = make_double2(accd[p][2], accd[p][3]);
+            } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = j0 + 4 * jq + q;
-            if (j < O) y[(int64_t)b * O + j] = (float)acc[p][q];
+                for (int q = 0; q < 4; ++q)
+                    if (j + q < O) dst[q] = accd[p][q];
+            }
+        } else {
+            float* dst = a.y + (int64_t)b * O + j;
+            if (vec) {
+                *reinterpret_cast<float4*>(dst) = make_float4((float)accd[p][0], (float)accd[p][1],
+                                                              (float)accd[p][2], (float)accd[p][3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (j + q < O) dst[q] = (float)accd[p][q];
+            }
         }
+    }
+}
+
+// y[e] = the float64 sum over slices s = 0 .. S-1, in that order, of
+// part[s n + e], rounded once to float32
+__global__ void gather_sum_kernel(const double* __restrict__ part, float* __restrict__ y, int64_t n, int S) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        double v = part[e];
+        for (int s = 1; s < S; ++s) v += part[s * n + e];
+        y[e] = (float)v;
     }
 }
 
@@ -404,7 +481,7 @@ __global__ __launch_bounds__(256) void gather_fwd_kernel(GridK g, int N, int I, 
 // runs over outputs j in chunks of 16 with dy and C staged in LDS.
 constexpr int GX_TB = 64, GX_TI = 16, GX_JC = 16;
 
-template <typename TS>
+template <typename TS, int D>
 __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, int O, int base,
                                                         const TS* __restrict__ x,
                                                         const TS* __restrict__ C,
@@ -413,7 +490,7 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, i
                                                         float* __restrict__ dx) {
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
-    const int K = g.G + 3;
+    const int K = g.G + D;
     float* Ds = smem;                               // [TB][JC]
     float* Cs = Ds + GX_TB * GX_JC;                  // [TI][K][JC]
     float* Ws = Cs + GX_TI * K * GX_JC;              // [TI][JC]
@@ -422,23 +499,25 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, i
     const int il = t % GX_TI, rq = t / GX_TI;
     const int b0 = blockIdx.x * GX_TB, i0 = blockIdx.y * GX_TI;
     const int i = i0 + il;
-    Rec rec[4];
-    int mi[4][4];
+    RecD<D> rec[4];
+    int mi[4][D + 1];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int b = b0 + rq + 16 * p;
         if (b < N && i < I) {
-            rec[p] = make_rec<true>(load_f(x, (int64_t)b * I + i), g);
+            rec[p] = make_rec<true, D>(load_f(x, (int64_t)b * I + i), g);
             if (!base) rec[p].base = 0.0f;
         } else {
-            rec[p].m0 = 0;
-            rec[p].w[0] = rec[p].w[1] = rec[p].w[2] = rec[p].w[3] = 0.0f;
-            rec[p].base = 0.0f;
+            rec[p] = zero_rec<D>();
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mi[p][q] = clampi(rec[p].m0 + q, 0, K - 1);
+        for (int q = 0; q <= D; ++q) mi[p][q] = clampi(rec[p].m0 + q, 0, K - 1);
     }
-    float Q[4][5] = {};
+    float Q[4][D + 2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < D + 2; ++q) Q[p][q] = 0.0f;
     for (int jc = 0; jc < O; jc += GX_JC) {
         __syncthreads();
         for (int e = t; e < GX_TB * GX_JC; e += 256) {
@@ -466,17 +545,17 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, i
             for (int p = 0; p < 4; ++p) {
                 const float4 d = *reinterpret_cast<const float4*>(&Ds[(rq + 16 * p) * GX_JC + jj]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q <= D; ++q) {
                     const float4 c = *reinterpret_cast<const float4*>(&Cs[(il * K + mi[p][q]) * GX_JC + jj]);
                     Q[p][q] = __builtin_fmaf(d.x, c.x, Q[p][q]);
                     Q[p][q] = __builtin_fmaf(d.y, c.y, Q[p][q]);
                     Q[p][q] = __builtin_fmaf(d.z, c.z, Q[p][q]);
                     Q[p][q] = __builtin_fmaf(d.w, c.w, Q[p][q]);
                 }
-                Q[p][4] = __builtin_fmaf(d.x, wv.x, Q[p][4]);
-                Q[p][4] = __builtin_fmaf(d.y, wv.y, Q[p][4]);
-                Q[p][4] = __builtin_fmaf(d.z, wv.z, Q[p][4]);
-                Q[p][4] = __builtin_fmaf(d.w, wv.w, Q[p][4]);
+                Q[p][D + 1] = __builtin_fmaf(d.x, wv.x, Q[p][D + 1]);
+                Q[p][D + 1] = __builtin_fmaf(d.y, wv.y, Q[p][D + 1]);
+                Q[p][D + 1] = __builtin_fmaf(d.z, wv.z, Q[p][D + 1]);
+                Q[p][D + 1] = __builtin_fmaf(d.w, wv.w, Q[p][D + 1]);
             }
         }
     }
@@ -484,9 +563,9 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, i
     for (int p = 0; p < 4; ++p) {
         const int b = b0 + rq + 16 * p;
         if (b >= N || i >= I) continue;
-        float v = Q[p][4] * rec[p].base;
+        float v = Q[p][D + 1] * rec[p].base;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v = __builtin_fmaf(Q[p][q], rec[p].w[q], v);
+        for (int q = 0; q <= D; ++q) v = __builtin_fmaf(Q[p][q], rec[p].w[q], v);
         dx[(int64_t)b * I + i] = v;
     }
 }
@@ -495,10 +574,12 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, i
 // dC, dW_base.  Block owns 16 inputs x 16 outputs and sweeps every row in a
 // fixed order; thread (i, j) keeps its K spline accumulators in a private LDS
 // column (no other thread touches them, so there is no atomic and the sum
-// order is the row order).
-constexpr int GC_TI = 16, GC_TJ = 16, GC_RB = 64;
+// order is the row order).  Rows are staged GC_RB at a time (32 above degree
+// 3, whose larger records would push G = 125 past the 160 KB of LDS).
+constexpr int GC_TI = 16, GC_TJ = 16;
+template <int D> constexpr int gc_rb() { return D > 3 ? 32 : 64; }
 
-template <typename TS>
+template <typename TS, int D>
 __global__ __launch_bounds__(256) void gather_dc_kernel(GridK g, int N, int I, int O, int base,
                                                         const TS* __restrict__ x,
                                                         const float* __restrict__ dy,
@@ -506,10 +587,11 @@ __global__ __launch_bounds__(256) void gather_dc_kernel(GridK g, int N, int I, i
                                                         float* __restrict__ dW) {
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
-    const int K = g.G + 3;
+    const int K = g.G + D;
     float* Acc = smem;                                // [K][256]
     float* Ds = Acc + K * 256;                        // [RB][TJ]
-    Rec* Rs = reinterpret_cast<Rec*>(Ds + GC_RB * GC_TJ);  // [RB][TI]
+    constexpr int GC_RB = gc_rb<D>();
+    RecD<D>* Rs = reinterpret_cast<RecD<D>*>(Ds + GC_RB * GC_TJ);  // [RB][TI]
 
     const int t = threadIdx.x;
     const int il = t % GC_TI, jl = t / GC_TI;
@@ -526,24 +608,17 @@ __global__ __launch_bounds__(256) void gather_dc_kernel(GridK g, int N, int I, i
         for (int e = t; e < GC_RB * GC_TI; e += 256) {
             const int bb = e / GC_TI, ii = e % GC_TI;
             const int b = r0 + bb, i = i0 + ii;
-            Rec r;
-            if (b < N && i < I) {
-                r = make_rec<false>(load_f(x, (int64_t)b * I + i), g);
-            } else {
-                r.m0 = 0;
-                r.w[0] = r.w[1] = r.w[2] = r.w[3] = 0.0f;
-                r.base = 0.0f;
-            }
-            Rs[bb * GC_TI + ii] = r;
+            Rs[bb * GC_TI + ii] = (b < N && i < I) ? make_rec<false, D>(load_f(x, (int64_t)b * I + i), g)
+                                                   : zero_rec<D>();
         }
         __syncthreads();
         const int nb = min(GC_RB, N - r0);
         for (int bb = 0; bb < nb; ++bb) {
             const float d = Ds[bb * GC_TJ + jl];
-            const Rec r = Rs[bb * GC_TI + il];
+            const RecD<D> r = Rs[bb * GC_TI + il];
             accw = __builtin_fmaf(d, r.base, accw);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q <= D; ++q) {
                 const int m = clampi(r.m0 + q, 0, K - 1);
                 Acc[m * 256 + t] = __builtin_fmaf(d, r.w[q], Acc[m * 256 + t]);
             }
@@ -568,6 +643,38 @@ hipError_t allow_lds(Kern k, size_t bytes) {
 }
 
 }  // namespace
+
+GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int base) {
+    GatherFwdPlan q;
+    const int64_t ob = (O + GF_TJ - 1) / GF_TJ;
+    // 256-row blocks of 1024 threads when they still make 64 or more blocks
+    // (or when K is large, where staging dominates); 64-row blocks of 256
+    // threads for small batches
+    q.nt = ((N + 255) / 256 * ob >= 64 || K > 32) ? 1024 : 256;
+    const int R = q.nt / 4;
+    const int rw = ((D + 3) + 1) & ~1;                       // words of a span record
+    const int64_t per_in = (int64_t)GF_TJ * K + (base ? GF_TJ : 0) + (int64_t)R * rw;
+    // both chunk buffers within 150 KB (1024 threads, one block per CU) or
+    // 64 KB (256 threads, two or more per CU); a chunk row of at most 256 / 128
+    // coefficients per output, which the prefetch registers hold
+    const int64_t budget = (q.nt == 1024 ? 150 * 1024 : 64 * 1024) / 4;
+    const int lim = q.nt == 1024 ? 256 : 128;
+    int64_t ic = std::min<int64_t>(8, budget / (2 * per_in));
+    ic = std::min<int64_t>(ic, lim / K);
+    q.ic = (int)std::max<int64_t>(ic, 1);
+    q.lds = (size_t)(2 * q.ic * per_in * 4);
+    q.rb = (N + R - 1) / R;
+    q.ob = ob;
+    // fewer blocks than CUs: split the inputs, at least 8 per slice
+    const int64_t T = q.rb * q.ob;
+    int64_t S = 1;
+    if (N * I * O >= (int64_t(1) << 16) && T < 256)
+        S = std::max<int64_t>(1, std::min<int64_t>((256 + T - 1) / T, (I + 7) / 8));
+    q.is = (I + S - 1) / S;
+    q.split = (int)((I + q.is - 1) / q.is);
+    q.ws = q.split > 1 ? (size_t)round_up((int64_t)q.split * N * O * 8, 256) : 0;
+    return q;
+}
 
 template <int D>
 static hipError_t basis_deg_run(const GridK& g, int64_t n, int dtype, const void* x, float* B, float* dB,
@@ -614,67 +721,118 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TS, int MAXQ>
-static hipError_t gather_fwd_run(const Plan& p, const void* x, const void* C, const void* W, float* y,
-                                 hipStream_t s) {
-    const size_t lds = (size_t)2 * gather_fwd_buf_floats(p.K) * 4;   // two chunk buffers
-    dim3 grid((unsigned)((p.N + GF_TB - 1) / GF_TB), (unsigned)((p.O + GF_TJ - 1) / GF_TJ));
-    hipError_t e = allow_lds(gather_fwd_kernel<TS, MAXQ>, lds);
+// ---- layer launchers: degree, base branch and block size as template arguments ----
+template <typename TS, int D, bool BASE, int NT>
+static hipError_t gather_fwd_run(const Plan& p, const GatherFwdArgs& a, hipStream_t s) {
+    constexpr int MAXQ = NT == 1024 ? 4 : 8;        // ceil(IC K / 4 / (NT / 64)) at the plan's limits
+    auto k = gather_fwd_kernel<TS, D, BASE, NT, MAXQ>;
+    hipError_t e = allow_lds(k, p.gf.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gather_fwd_kernel<TS, MAXQ>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
-                       (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
-                       static_cast<const TS*>(W), y);
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.gf.rb * p.gf.ob), (unsigned)p.gf.split), dim3(NT), p.gf.lds, s, a);
     return hipGetLastError();
 }
 
-// prefetch registers per thread: ceil(64 IC K / 256) coefficients
-template <typename TS>
-static hipError_t gather_fwd_t(const Plan& p, const void* x, const void* C, const void* W,
-                               float* y, hipStream_t s) {
-    const int nq = (gather_fwd_ic(p.K) * p.K * GF_TJ + 255) / 256;
-    if (nq <= 20) return gather_fwd_run<TS, 20>(p, x, C, W, y, s);
-    return gather_fwd_run<TS, 32>(p, x, C, W, y, s);
+template <typename TS, int D>
+static hipError_t gather_fwd_nt(const Plan& p, const GatherFwdArgs& a, hipStream_t s) {
+    if (p.gf.nt == 1024)
+        return p.base ? gather_fwd_run<TS, D, true, 1024>(p, a, s) : gather_fwd_run<TS, D, false, 1024>(p, a, s);
+    return p.base ? gather_fwd_run<TS, D, true, 256>(p, a, s) : gather_fwd_run<TS, D, false, 256>(p, a, s);
 }
 
 template <typename TS>
-static hipError_t gather_dx_t(const Plan& p, const void* x, const void* C, const void* W,
-                              const float* dy, float* dx, hipStream_t s) {
+static hipError_t gather_fwd_deg(const Plan& p, const GatherFwdArgs& a, hipStream_t s) {
+    switch (p.degree) {
+        case 1: return gather_fwd_nt<TS, 1>(p, a, s);
+        case 2: return gather_fwd_nt<TS, 2>(p, a, s);
+        case 4: return gather_fwd_nt<TS, 4>(p, a, s);
+        case 5: return gather_fwd_nt<TS, 5>(p, a, s);
+        default: return gather_fwd_nt<TS, 3>(p, a, s);
+    }
+}
+
+hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
+                             float* y, void* ws, hipStream_t s) {
+    GatherFwdArgs a;
+    a.g = p.gk;
+    a.N = (int)p.N;
+    a.I = (int)p.I;
+    a.O = (int)p.O;
+    a.IC = p.gf.ic;
+    a.IS = (int)p.gf.is;
+    a.RB = (int)p.gf.rb;
+    a.OB = (int)p.gf.ob;
+    a.x = x;
+    a.C = C;
+    a.W = W;
+    a.y = y;
+    a.part = p.gf.split > 1 ? static_cast<double*>(ws) : nullptr;
+    hipError_t e = p.dtype == KAN_F32 ? gather_fwd_deg<float>(p, a, s) : gather_fwd_deg<uint16_t>(p, a, s);
+    if (e != hipSuccess || p.gf.split <= 1) return e;
+    const int64_t n = p.N * p.O;
+    hipLaunchKernelGGL(gather_sum_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 16384)), dim3(256),
+                       0, s, a.part, y, n, p.gf.split);
+    return hipGetLastError();
+}
+
+template <typename TS, int D>
+static hipError_t gather_dx_run(const Plan& p, const void* x, const void* C, const void* W,
+                                const float* dy, float* dx, hipStream_t s) {
     const size_t lds = (size_t)(GX_TB * GX_JC + GX_TI * p.K * GX_JC + GX_TI * GX_JC) * 4;
     dim3 grid((unsigned)((p.N + GX_TB - 1) / GX_TB), (unsigned)((p.I + GX_TI - 1) / GX_TI));
-    hipError_t e = allow_lds(gather_dx_kernel<TS>, lds);
+    hipError_t e = allow_lds(gather_dx_kernel<TS, D>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_dx_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+    hipLaunchKernelGGL((gather_dx_kernel<TS, D>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
                        (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
                        static_cast<const TS*>(W), dy, dx);
     return hipGetLastError();
 }
 
-template <typename TS>
-static hipError_t gather_dc_t(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
-                              hipStream_t s) {
-    const size_t lds = (size_t)(p.K * 256 + GC_RB * GC_TJ) * 4 + GC_RB * GC_TI * sizeof(Rec);
+template <typename TS, int D>
+static hipError_t gather_dc_run(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
+                                hipStream_t s) {
+    constexpr int GC_RB = gc_rb<D>();
+    const size_t lds = (size_t)(p.K * 256 + GC_RB * GC_TJ) * 4 + GC_RB * GC_TI * sizeof(RecD<D>);
     dim3 grid((unsigned)((p.I + GC_TI - 1) / GC_TI), (unsigned)((p.O + GC_TJ - 1) / GC_TJ));
-    hipError_t e = allow_lds(gather_dc_kernel<TS>, lds);
+    hipError_t e = allow_lds(gather_dc_kernel<TS, D>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_dc_kernel<TS>, grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
+    hipLaunchKernelGGL((gather_dc_kernel<TS, D>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
                        (int)p.O, p.base, static_cast<const TS*>(x), dy, dC, dW);
     return hipGetLastError();
 }
 
-hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
-                             float* y, hipStream_t s) {
-    return p.dtype == KAN_F32 ? gather_fwd_t<float>(p, x, C, W, y, s)
-                              : gather_fwd_t<uint16_t>(p, x, C, W, y, s);
+template <typename TS>
+static hipError_t gather_dx_deg(const Plan& p, const void* x, const void* C, const void* W,
+                                const float* dy, float* dx, hipStream_t s) {
+    switch (p.degree) {
+        case 1: return gather_dx_run<TS, 1>(p, x, C, W, dy, dx, s);
+        case 2: return gather_dx_run<TS, 2>(p, x, C, W, dy, dx, s);
+        case 4: return gather_dx_run<TS, 4>(p, x, C, W, dy, dx, s);
+        case 5: return gather_dx_run<TS, 5>(p, x, C, W, dy, dx, s);
+        default: return gather_dx_run<TS, 3>(p, x, C, W, dy, dx, s);
+    }
 }
+
+template <typename TS>
+static hipError_t gather_dc_deg(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
+                                hipStream_t s) {
+    switch (p.degree) {
+        case 1: return gather_dc_run<TS, 1>(p, x, dy, dC, dW, s);
+        case 2: return gather_dc_run<TS, 2>(p, x, dy, dC, dW, s);
+        case 4: return gather_dc_run<TS, 4>(p, x, dy, dC, dW, s);
+        case 5: return gather_dc_run<TS, 5>(p, x, dy, dC, dW, s);
+        default: return gather_dc_run<TS, 3>(p, x, dy, dC, dW, s);
+    }
+}
+
 hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
                             const float* dy, float* dx, hipStream_t s) {
-    return p.dtype == KAN_F32 ? gather_dx_t<float>(p, x, C, W, dy, dx, s)
-                              : gather_dx_t<uint16_t>(p, x, C, W, dy, dx, s);
+    return p.dtype == KAN_F32 ? gather_dx_deg<float>(p, x, C, W, dy, dx, s)
+                              : gather_dx_deg<uint16_t>(p, x, C, W, dy, dx, s);
 }
 hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
                             hipStream_t s) {
-    return p.dtype == KAN_F32 ? gather_dc_t<float>(p, x, dy, dC, dW, s)
-                              : gather_dc_t<uint16_t>(p, x, dy, dC, dW, s);
+    return p.dtype == KAN_F32 ? gather_dc_deg<float>(p, x, dy, dC, dW, s)
+                              : gather_dc_deg<uint16_t>(p, x, dy, dC, dW, s);
 }
 
 }  // namespace kan

@@ -21,6 +21,29 @@ constexpr int kTileKBytes = 128;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// Local-gather forward: blocks of nt threads compute nt / 4 rows by 64
+// outputs, staging ic inputs per chunk in lds bytes of LDS; the inputs are
+// cut into `split` slices of `is` inputs (split > 1: float64 partial outputs
+// [split][N][O] in a workspace of ws bytes, added in slice order).
+struct GatherFwdPlan {
+    int nt, ic, split;
+    int64_t is, rb, ob;
+    size_t lds, ws;
+};
+GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int base);
+
+struct GatherFwdArgs {
+    GridK g;
+    int N, I, O;
+    int IC, IS;          // inputs per chunk and per slice
+    int RB, OB;          // row blocks and output blocks of one slice
+    const void* x;
+    const void* C;
+    const void* W;
+    float* y;            // one slice: the output
+    double* part;        // several slices: their partial outputs [slice][N][O]
+};
+
 struct Plan {
     int64_t N, I, O;
     int G, K, Kb;        // K = G+3 spline functions; Kb = K + has_base columns per input
@@ -32,8 +55,8 @@ struct Plan {
     // xI = I.
     int pair;
     int64_t xI;
-    int degree;          // spline degree, 1 .. 5 (the gather kernels, the sparse
-                         // forward and the 2-D layer are cubic only)
+    int degree;          // spline degree, 1 .. 5 (the sparse forward and the 2-D
+                         // layer are cubic only)
     int variant_fwd;     // resolved per pass: KAN_VARIANT_MFMA or KAN_VARIANT_GATHER
     int variant_bwd;
     int esize;           // bytes per stored element (4 or 2)
@@ -71,6 +94,8 @@ struct Plan {
     size_t off_yp, sz_yp;      // forward slices' partial y: [split_fwd][N][O] float (split_fwd > 1)
     size_t off_dcp, sz_dcp;    // dC slices' partials: [split_dc][O][I][K] then [split_dc][O][I] float
     size_t ws_fwd, ws_bwd;
+
+    GatherFwdPlan gf;    // the local-gather forward (variant_fwd == GATHER)
 };
 
 // Builds the plan; returns KAN_OK or the validation error for `desc` alone.
@@ -86,7 +111,7 @@ hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
-                             float* y, hipStream_t s);
+                             float* y, void* ws, hipStream_t s);
 hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
                             const float* dy, float* dx, hipStream_t s);
 hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,

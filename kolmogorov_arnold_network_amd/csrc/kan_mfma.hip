@@ -1487,14 +1487,15 @@ hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// out[e] = sum over slices s = 0 .. P-1, in that order, of part[s n + e]
+// out[e] = sum over slices s = 0 .. P-1, in that order, of part[s n + e],
+// added in float64 and rounded once
 __global__ void sum_slices_kernel(const float* __restrict__ part, float* __restrict__ out, int64_t n,
                                   int P) {
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
          e += (int64_t)gridDim.x * blockDim.x) {
-        float v = part[e];
-        for (int q = 1; q < P; ++q) v += part[q * n + e];
-        out[e] = v;
+        double v = part[e];
+        for (int q = 1; q < P; ++q) v += (double)part[q * n + e];
+        out[e] = (float)v;
     }
 }
 

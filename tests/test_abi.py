@@ -85,8 +85,8 @@ def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
     (dict(G=0), "GRID"), (dict(G=126), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
     (dict(lo=2.0, hi=1.0), "GRID"), (dict(lo=float("nan")), "GRID"), (dict(hi=float("inf")), "GRID"),
     (dict(degree=0), "UNSUPPORTED"), (dict(degree=6), "UNSUPPORTED"),
-    (dict(degree=2, variant=2), "UNSUPPORTED"),                 # degree != 3: matrix cores only
-    (dict(degree=1, G=1, has_base=0), "UNSUPPORTED"),           # 2 columns per input: too few
+    (dict(degree=1, G=1, has_base=0), "UNSUPPORTED"),           # MFMA: 2 columns per input, too few
+    (dict(degree=1, G=1, has_base=0, dtype=1), "UNSUPPORTED"),  # the same in bf16
     (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
     (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
 ])
@@ -164,6 +164,31 @@ def k_slices(tiles, nkt, out_bytes, esize):
     return (nkt + nks - 1) // nks, nks
 
 
+def gather_fwd_ws(N, I, O, K, D, base):
+    """Workspace of the local-gather forward: float64 partial outputs of its
+    input slices, used when its blocks (R rows x 64 outputs) are fewer than
+    the 256 CUs and the layer has at least 2^16 edge-rows."""
+    ob = (O + 63) // 64
+    nt = 1024 if ((N + 255) // 256 * ob >= 64 or K > 32) else 256
+    R = nt // 4
+    T = (N + R - 1) // R * ob
+    S = 1
+    if N * I * O >= 1 << 16 and T < 256:
+        S = max(1, min((256 + T - 1) // T, (I + 7) // 8))
+    IS = (I + S - 1) // S
+    S = (I + IS - 1) // IS
+    return (S * N * O * 8 + 255) // 256 * 256 if S > 1 else 0
+
+
+def fwd_slices(nt_tiles, nkt, out_bytes, es):
+    """k-slices of the MFMA forward: the occupancy split, and for float32 at
+    most 32 k-tiles per slice."""
+    P, nks = k_slices(nt_tiles, nkt, out_bytes, es)
+    if es == 4 and nks > 32:
+        P = (nkt + 31) // 32
+    return P
+
+
 def test_workspace_sizes(L):
     ws = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 0)
     wb = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 1)
@@ -183,7 +208,7 @@ def test_workspace_sizes(L):
 
             def fwd_bytes(kf, nkt):
                 # packed C', then the partial y of a split forward
-                P, _ = k_slices((Np // 256) * (Op // 256), nkt, N * O * 4, es)
+                P = fwd_slices((Np // 256) * (Op // 256), nkt, N * O * 4, es)
                 return r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
             kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
             assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == fwd_bytes(kf, kf // (64 if sparse else bk))
@@ -200,8 +225,15 @@ def test_workspace_sizes(L):
     # backward on the matrix cores
     assert ws(G=125, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) > 0      # largest grid: MFMA fits
     assert ws(G=126, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ctypes.c_size_t(-1).value
-    # float32 AUTO: gather forward (no workspace), matrix-core backward
+    # float32 AUTO: gather forward (no workspace unless it splits its
+    # inputs), matrix-core backward
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0
+    for (N, I, O, G, base) in [(1024, 784, 64, 8, 1), (1024, 64, 10, 8, 1), (32, 8, 4, 8, 0), (8192, 1024, 1024, 50, 0),
+                               (300, 5000, 7, 20, 1), (1, 100000, 1, 3, 0)]:
+        for v in (L.KAN_VARIANT_AUTO, L.KAN_VARIANT_GATHER):
+            assert ws(N=N, I=I, O=O, G=G, has_base=base, variant=v, dtype=L.KAN_F32) == \
+                gather_fwd_ws(N, I, O, G + 3, 3, base)
+    assert gather_fwd_ws(1024, 784, 64, 11, 3, 1) > 0            # the 784-wide quick-start layer splits
     assert wb(N=64, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == wb(
         N=64, I=32, O=32, variant=L.KAN_VARIANT_MFMA, dtype=L.KAN_F32) > 0          # 2^16 edge-rows
     assert wb(N=63, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0  # below: gather
@@ -210,25 +242,37 @@ def test_workspace_sizes(L):
 
 
 def test_workspace_sizes_other_degrees(L):
-    """Degree D != 3: K = G + D columns per input, both passes on the matrix
-    cores whatever the variant asked (AUTO), never the structured-sparse
-    forward, otherwise the cubic layout."""
+    """Degree D != 3: K = G + D columns per input and the cubic layer's
+    choice of kernels (AUTO: bf16 on the matrix cores; float32 forward on the
+    gather kernel, backward on the matrix cores from 2^16 edge-rows), never
+    the structured-sparse forward, otherwise the cubic layout."""
     r = lambda a, b: (a + b - 1) // b * b
     for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
         for (N, I, O, G, base, D) in [(64, 16, 8, 8, 1, 1), (1000, 77, 300, 20, 0, 5), (12608, 768, 3072, 5, 1, 2),
-                                      (5, 3, 2, 1, 1, 4)]:
+                                      (5, 3, 2, 1, 1, 4), (1024, 784, 64, 8, 1, 2)]:
             Kb = G + D + base
             Op, Np = r(O, 256), r(N, 256)
             kf = r(I * Kb, bk)
-            P, _ = k_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
+            P = fwd_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
             want_f = r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
             tiles = (I * Kb + 255) // 256
             want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
             Pd, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)
             want_b += r(Pd * O * I * Kb * 4, 256) if Pd > 1 else 0
-            d = desc(L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, degree=D, variant=L.KAN_VARIANT_AUTO)
-            assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == want_f
-            assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == want_b
+            for v in (L.KAN_VARIANT_AUTO, L.KAN_VARIANT_MFMA, L.KAN_VARIANT_GATHER):
+                d = desc(L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, degree=D, variant=v)
+                gather_f = v == L.KAN_VARIANT_GATHER or (v == L.KAN_VARIANT_AUTO and dt == L.KAN_F32)
+                gather_b = v == L.KAN_VARIANT_GATHER or (v == L.KAN_VARIANT_AUTO and dt == L.KAN_F32
+                                                         and N * I * O < 1 << 16)
+                assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == (
+                    gather_fwd_ws(N, I, O, G + D, D, base) if gather_f else want_f)
+                assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == (0 if gather_b else want_b)
+    # too few columns for the matrix cores (degree 1, G = 1, no base branch:
+    # 2 per input): AUTO takes the gather kernels in both dtypes
+    for dt in (L.KAN_F32, L.KAN_BF16):
+        d = desc(L, N=64, I=16, O=8, G=1, has_base=0, dtype=dt, degree=1, variant=L.KAN_VARIANT_AUTO)
+        assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == 0
+        assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == 0
 
 
 def test_prepare_checks(L):
@@ -362,7 +406,7 @@ def test_surface_workspace_sizes(L):
             Kb = (G + 3) ** 2
             Op, Np = r(O, 256), r(N, 256)
             kf = r(P * Kb, bk)
-            Pf, _ = k_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
+            Pf = fwd_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
             want_f = r(Op * kf * es, 256) + (r(Pf * N * O * 4, 256) if Pf > 1 else 0)
             tiles = (P * Kb + 255) // 256
             want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 4 * 4, 256)
