@@ -83,7 +83,7 @@ typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
  * (I*(G+D+has_base) wide) on the matrix cores, with the basis generated in LDS
  * and never written to memory; it needs G+D+has_base <= 256, and at least 4
  * for a degree D other than 3.  A float32 MFMA forward adds its contraction
- * in fixed slices of at most 1024 (i, m) terms whose float32 partial sums are
+ * in fixed slices of at most 256 (i, m) terms whose float32 partial sums are
  * added in float64, so that its rounding stays small enough for a following
  * layer's B' (which amplifies it about tenfold) to keep a chain of layers
  * within 1e-5.  GATHER touches only the D+1 non-zero basis functions per input
@@ -153,7 +153,7 @@ const char* kan_status_string(int status);
 /* Bytes of workspace a pass needs (SIZE_MAX if `desc` is invalid).  `pass`
  * is kan_pass_t.  On MFMA it holds the packed operands of kan_prepare and the
  * float32 partial outputs of k-range slices (the forward's y, slices of at
- * most 1024 terms in float32 and otherwise where too few output tiles fill
+ * most 256 terms in float32 and otherwise where too few output tiles fill
  * the GPU; dC and dW_base over batch slices), which are added in slice
  * order.  The GATHER forward needs it only when too few blocks of rows and
  * outputs fill the GPU: its inputs are then split into slices whose float64

@@ -15,7 +15,7 @@ namespace {
 
 constexpr int64_t kIndexLimit = (int64_t(1) << 31) - 4096;  // keeps 32-bit tile math safe
 constexpr int kMaxG = 125;                                      // K = G + 3 <= 128
-constexpr int64_t kF32SliceTiles = 32;                          // float32 forward: k-tiles per slice
+constexpr int64_t kF32SliceTiles = 8;                           // float32 forward: k-tiles per slice
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -93,8 +93,8 @@ void plan_layout(Plan& q, bool dense_forward) {
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
     q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
                            &q.nks_fwd);
-    // A float32 forward sums its contraction in slices of at most 32 k-tiles
-    // (1024 terms): a float32 running sum over the whole basis row (9408
+    // A float32 forward sums its contraction in slices of at most 8 k-tiles
+    // (256 terms): a float32 running sum over the whole basis row (9408
     // terms at 784 inputs) loses accuracy that the next layer's B' amplifies;
     // the slices' partials are added in float64.
     if (q.dtype == KAN_F32 && q.nks_fwd > kF32SliceTiles) {

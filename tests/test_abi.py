@@ -182,10 +182,10 @@ def gather_fwd_ws(N, I, O, K, D, base):
 
 def fwd_slices(nt_tiles, nkt, out_bytes, es):
     """k-slices of the MFMA forward: the occupancy split, and for float32 at
-    most 32 k-tiles per slice."""
+    most 8 k-tiles per slice."""
     P, nks = k_slices(nt_tiles, nkt, out_bytes, es)
-    if es == 4 and nks > 32:
-        P = (nkt + 31) // 32
+    if es == 4 and nks > 8:
+        P = (nkt + 7) // 8
     return P
 
 
