@@ -176,6 +176,26 @@ int kan_prepare(const kan_desc_t* desc, int pass, const void* C, const void* W_b
 int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
                 float* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Forward without a caller workspace --------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * forward as kan_forward (same kernels, same bits), with the workspace taken
+ * from a fixed array of KAN_STATIC_SCRATCH_BYTES of device memory inside the
+ * library.  Every GPU the library runs on holds its own copy of that array
+ * from the first call until the process ends; the call itself allocates and
+ * frees nothing.  A layer whose forward workspace (kan_workspace_size) is
+ * larger returns KAN_ERR_WORKSPACE before any work; KAN_FLAG_PREPARED is
+ * refused (KAN_ERR_UNSUPPORTED).  The array keeps the last call's contents
+ * and nothing in it has to start at zero.  All calls on one GPU share the
+ * array, so calls that overlap in time on one GPU (on different streams or
+ * from different threads) race and must be ordered by the caller; calls
+ * queued on one stream are ordered by the stream.  `stream` must belong to
+ * the current device.  Other arguments, validation and errors as for
+ * kan_forward. */
+#define KAN_STATIC_SCRATCH_BYTES (32u << 20)
+int kan_forward_static(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
+                       float* y, void* stream);
+
 /* Backward.  dy [N, O] float32 in.  dx [N, I], dC [O, I, G+3] and dW_base
  * [O, I] are float32 outputs; each may be NULL to skip it (dW_base must be
  * NULL when has_base == 0).  dC and dW_base are sums over all N rows, reduced

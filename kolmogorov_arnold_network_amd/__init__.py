@@ -12,7 +12,7 @@ package binds that ABI (``functional``) and wraps it as torch modules
 """
 
 from . import _lib
-from .functional import (kan_forward, kan_backward, kan_prepare, kan_basis_eval, kan_basis_eval_tp,
+from .functional import (kan_forward, kan_forward_static, kan_backward, kan_prepare, kan_basis_eval, kan_basis_eval_tp,
                          kan_cast_f32_to_bf16, kan_workspace_size, layer_desc, workspace,
                          kan_group_forward, kan_group_backward, kan_group_workspace_size, group_desc,
                          kan_surface_forward, kan_surface_backward, kan_surface_workspace_size,
@@ -20,7 +20,7 @@ from .functional import (kan_forward, kan_backward, kan_prepare, kan_basis_eval,
 from .modules import (KANLayer, KANNetwork, KANFunction, KANGroupedActivation, KANSurfaceLayer,
                       GroupedFunction, SurfaceFunction)
 
-__all__ = ["kan_forward", "kan_backward", "kan_prepare", "kan_basis_eval", "kan_basis_eval_tp",
+__all__ = ["kan_forward", "kan_forward_static", "kan_backward", "kan_prepare", "kan_basis_eval", "kan_basis_eval_tp",
            "kan_cast_f32_to_bf16",
            "kan_workspace_size", "layer_desc", "workspace", "KANLayer", "KANNetwork", "KANFunction",
            "kan_group_forward", "kan_group_backward", "kan_group_workspace_size", "group_desc",

@@ -33,11 +33,13 @@ KAN_PASS_BACKWARD = 1
 KAN_FLAG_PREPARED = 1
 KAN_FLAG_DENSE_FORWARD = 2
 
+KAN_STATIC_SCRATCH_BYTES = 32 << 20     # kan_forward_static's device array
+
 ABI_VERSION = 1
 
 # every symbol include/kan.h declares
 EXPORTS = ("kan_abi_version", "kan_status_string", "kan_workspace_size", "kan_prepare",
-           "kan_forward", "kan_backward", "kan_basis_eval", "kan_basis_eval_tp", "kan_cast_f32_to_bf16",
+           "kan_forward", "kan_forward_static", "kan_backward", "kan_basis_eval", "kan_basis_eval_tp", "kan_cast_f32_to_bf16",
            "kan_group_workspace_size", "kan_group_forward", "kan_group_backward",
            "kan_surface_workspace_size", "kan_surface_forward", "kan_surface_backward")
 
@@ -96,6 +98,8 @@ def lib():
     L.kan_prepare.argtypes = [P(kan_desc_t), ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]
     L.kan_forward.restype = ctypes.c_int
     L.kan_forward.argtypes = [P(kan_desc_t), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.kan_forward_static.restype = ctypes.c_int
+    L.kan_forward_static.argtypes = [P(kan_desc_t), _vp, _vp, _vp, _vp, _vp]
     L.kan_backward.restype = ctypes.c_int
     L.kan_backward.argtypes = [P(kan_desc_t), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     for f in (L.kan_basis_eval, L.kan_basis_eval_tp):

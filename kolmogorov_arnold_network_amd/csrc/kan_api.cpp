@@ -307,32 +307,51 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
     Plan p;
     int st = make_plan(desc, &p);
     if (st != KAN_OK) return st;
+    if ((st = forward_validate(p, x, C, W_base, y, ws, ws_bytes, false)) != KAN_OK) return st;
+    return forward_launch(p, desc->flags, x, C, W_base, y, ws, stream);
+}
+
+}  // extern "C"
+
+namespace kan {
+
+int forward_validate(const Plan& p, const void* x, const void* C, const void* W_base, const float* y,
+                     const void* ws, size_t ws_bytes, bool own_ws) {
+    int st;
     if (!C || (p.N > 0 && (!x || !y))) return KAN_ERR_NULL;
     if ((W_base != nullptr) != (p.base == 1)) return KAN_ERR_NULL;
     const void* fptrs[] = {x, C, W_base, y};
     for (const void* q : fptrs)
         if (q && !aligned(q, 16)) return KAN_ERR_ALIGN;
-    if ((st = check_ws(p, KAN_PASS_FORWARD, ws, ws_bytes)) != KAN_OK) return st;
+    if (!own_ws && (st = check_ws(p, KAN_PASS_FORWARD, ws, ws_bytes)) != KAN_OK) return st;
     const Range out{y, (size_t)(p.N * p.O) * 4};
-    const Range wr{ws, p.ws_fwd};
+    const Range wr{own_ws ? nullptr : ws, p.ws_fwd};
     const Range in[] = {{x, (size_t)(p.N * p.I) * p.esize},
                         {C, (size_t)(p.O * p.I * p.K) * p.esize},
                         {W_base, (size_t)(p.O * p.I) * p.esize}};
     for (const Range& r : in)
         if (overlap(out, r) || overlap(wr, r)) return KAN_ERR_ALIAS;
     if (overlap(out, wr)) return KAN_ERR_ALIAS;
-    if (p.N == 0) return KAN_OK;
+    return KAN_OK;
+}
 
+int forward_launch(const Plan& p, int flags, const void* x, const void* C, const void* W_base, float* y,
+                   void* ws, void* stream) {
+    if (p.N == 0) return KAN_OK;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (p.variant_fwd == KAN_VARIANT_GATHER) return status_of(launch_gather_fwd(p, x, C, W_base, y, ws, s));
-    if (!(desc->flags & KAN_FLAG_PREPARED)) {
-        st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
+    if (!(flags & KAN_FLAG_PREPARED)) {
+        const int st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
         if (st != KAN_OK) return st;
     }
     return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
                                      reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
 }
+
+}  // namespace kan
+
+extern "C" {
 
 int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const void* W_base,
                  const float* dy, float* dx, float* dC, float* dW, void* ws, size_t ws_bytes,

@@ -103,6 +103,15 @@ int make_plan(const kan_desc_t* desc, Plan* p);
 // The plan of a 2-D tensor-product layer (always on the matrix cores).
 int make_plan_surface(const kan_surface_desc_t* desc, Plan* p);
 
+// The forward pass of a plan built by make_plan, shared by kan_forward and
+// kan_forward_static: pointer, alignment, workspace and overlap checks (with
+// own_ws the workspace is the library's own array and is not checked), then
+// the launches.
+int forward_validate(const Plan& p, const void* x, const void* C, const void* W_base, const float* y,
+                     const void* ws, size_t ws_bytes, bool own_ws);
+int forward_launch(const Plan& p, int flags, const void* x, const void* C, const void* W_base, float* y,
+                   void* ws, void* stream);
+
 // ---- launchers (return hipError_t of the launch) ----
 // degree 1 .. 5; g built for that degree (t_0 = lo - degree h)
 hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x, float* B,

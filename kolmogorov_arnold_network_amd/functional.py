@@ -129,6 +129,22 @@ def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None
     return y
 
 
+def kan_forward_static(x, C, W, grid, variant="auto", out=None, dense_forward=False):
+    """``y [N, O]`` float32 of one KAN layer with the library's own static
+    device workspace (no workspace argument, nothing allocated but ``y``
+    when ``out`` is not given)."""
+    _check_tensor(x, "x", _DTYPES)
+    _check_tensor(C, "C", _DTYPES, x.device)
+    _check_tensor(W, "W_base", _DTYPES, x.device)
+    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
+    y = out if out is not None else torch.empty((x.shape[0], C.shape[0]), dtype=torch.float32,
+                                                device=x.device)
+    _check_out(y, "y", (x.shape[0], C.shape[0]), x.device)
+    L.check(L.lib().kan_forward_static(ctypes.byref(desc), _ptr(x), _ptr(C), _ptr(W), _ptr(y), _stream(x)),
+            "kan_forward_static")
+    return y
+
+
 def kan_backward(x, C, W, dy, grid, need_dx=True, need_dC=True, need_dW=True, variant="auto",
                  ws=None, prepared=False):
     """``(dx [N, I], dC [O, I, G+3], dW_base [O, I])`` float32; unrequested ones are None."""

@@ -98,6 +98,30 @@ def test_bad_descriptors(L, kw, code):
     assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == ctypes.c_size_t(-1).value
 
 
+def test_static_forward_checks(L):
+    """kan_forward_static validates like kan_forward and, before touching
+    the GPU, refuses a layer whose forward workspace exceeds its static
+    array and the prepared flag (the array is shared by every call)."""
+    lib = L.lib()
+    stat = lambda d, **kw: lib.kan_forward_static(ctypes.byref(d), kw.get("x", X), kw.get("c", C),
+                                                  kw.get("w", W), kw.get("y", Y), None)
+    assert lib.kan_forward_static(None, X, C, W, Y, None) == L.KAN_ERR_NULL
+    assert stat(desc(L, G=0)) == L.KAN_ERR_GRID
+    assert stat(desc(L, variant=9)) == L.KAN_ERR_UNSUPPORTED
+    assert stat(desc(L, flags=L.KAN_FLAG_PREPARED)) == L.KAN_ERR_UNSUPPORTED
+    big = desc(L, N=65536, I=4096, O=4096, G=20, dtype=L.KAN_BF16)        # 0.8 GB of packed C'
+    assert lib.kan_workspace_size(ctypes.byref(big), 0) > L.KAN_STATIC_SCRATCH_BYTES
+    assert stat(big) == L.KAN_ERR_WORKSPACE
+    assert stat(desc(L), w=None) == L.KAN_ERR_NULL                       # base branch needs W_base
+    assert stat(desc(L), x=X + 4) == L.KAN_ERR_ALIGN
+    assert stat(desc(L), y=X) == L.KAN_ERR_ALIAS
+    # the quick-start layers fit the array on every variant
+    for v in (L.KAN_VARIANT_AUTO, L.KAN_VARIANT_MFMA, L.KAN_VARIANT_GATHER):
+        for (N, I, O) in [(1024, 784, 64), (1024, 64, 10)]:
+            d = desc(L, N=N, I=I, O=O, variant=v)
+            assert 0 < lib.kan_workspace_size(ctypes.byref(d), 0) <= L.KAN_STATIC_SCRATCH_BYTES
+
+
 def test_null_desc(L):
     lib = L.lib()
     assert lib.kan_forward(None, X, C, W, Y, WS, 1 << 30, None) == L.KAN_ERR_NULL
