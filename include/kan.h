@@ -90,8 +90,11 @@ typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
  * (InKAN page, "Why InKAN?": local 4-basis lookup) on the vector ALUs; its
  * forward adds the partial sums of chunks of at most 8 inputs in float64.
  * AUTO picks per pass: bf16 runs both passes on MFMA; float32 runs the forward
- * on GATHER and the backward on MFMA once N*I*O >= 2^16 (GATHER below);
- * GATHER wherever MFMA does not fit. */
+ * on GATHER and the backward on whichever family is estimated faster: GATHER
+ * (about N*I*O / 2.5e12 s, independent of G) or MFMA (about
+ * 2*N*I*O*(G+D+has_base) / 110e12 s + 75 us), that is GATHER for small
+ * layers and from about 22 columns per input up; GATHER wherever MFMA does
+ * not fit. */
 typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 2 } kan_variant_t;
 
 typedef enum { KAN_PASS_FORWARD = 0, KAN_PASS_BACKWARD = 1 } kan_pass_t;
@@ -155,10 +158,11 @@ const char* kan_status_string(int status);
  * float32 partial outputs of k-range slices (the forward's y, slices of at
  * most 256 terms in float32 and otherwise where too few output tiles fill
  * the GPU; dC and dW_base over batch slices), which are added in slice
- * order.  The GATHER forward needs it only when too few blocks of rows and
- * outputs fill the GPU: its inputs are then split into slices whose float64
- * partial outputs [slices][N][O] are added in slice order.  The GATHER
- * backward needs none (0). */
+ * order.  GATHER needs it only when too few blocks fill the GPU: the
+ * forward then splits its inputs into slices whose float64 partial outputs
+ * [slices][N][O] are added in slice order, the backward splits dx over
+ * output slices and dC / dW_base over row slices, with float32 partials
+ * added in slice order (in float64). */
 size_t kan_workspace_size(const kan_desc_t* desc, int pass);
 
 /* Packs what a pass reads into the workspace: for a pass on MFMA the

@@ -194,10 +194,13 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     // operand generators' instances cover that many inputs per tile).
     // AUTO: bf16 runs both passes on the matrix cores.  float32 runs the
     // forward on the local gather kernel, whose sums over inputs are float64
-    // and which touches only the D + 1 non-zero basis functions; its backward
-    // (dx, dC) feeds no B', so it runs on the matrix cores once the layer has
-    // at least 2^16 edge-rows (N I O); below that the packing and launches of
-    // the matrix-core path cost more than the work.
+    // and which touches only the D + 1 non-zero basis functions.  Its
+    // backward takes whichever of the two kernel families the measured rates
+    // make faster: the gather dx / dC do about 2.5e12 edge-rows (N I O) per
+    // second whatever K is; the dense float32 contractions execute 2 N I O Kb
+    // flops at about 110 TFLOP/s, plus about 75 us of packing, epilogue and
+    // launches per pass.  So the gather backward wins from Kb of about 22 up,
+    // and on small layers at any Kb.
     const bool mfma_ok = q.Kb <= kTileN && (q.degree == 3 || q.Kb >= 4);
     if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
     if (d->variant == KAN_VARIANT_GATHER) {
@@ -206,14 +209,20 @@ int make_plan(const kan_desc_t* d, Plan* p) {
         q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
     } else {
         q.variant_fwd = (mfma_ok && q.dtype == KAN_BF16) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
-        const bool big = q.N * q.I * q.O >= (int64_t(1) << 16);
-        q.variant_bwd = mfma_ok && (q.dtype == KAN_BF16 || big) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
+        const double nio = (double)q.N * (double)q.I * (double)q.O;
+        const double t_gather = nio / 2.5e12, t_mfma = 2.0 * nio * q.Kb / 110e12 + 75e-6;
+        q.variant_bwd = mfma_ok && (q.dtype == KAN_BF16 || t_mfma < t_gather) ? KAN_VARIANT_MFMA
+                                                                               : KAN_VARIANT_GATHER;
     }
 
     plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
     if (q.variant_fwd == KAN_VARIANT_GATHER) {
         q.gf = gather_fwd_plan(q.N, q.I, q.O, q.K, q.degree, q.base);
         q.ws_fwd = q.gf.ws;
+    }
+    if (q.variant_bwd == KAN_VARIANT_GATHER) {
+        q.gb = gather_bwd_plan(q.N, q.I, q.O, q.K, q.base);
+        q.ws_bwd = q.gb.ws;
     }
     *p = q;
     return KAN_OK;
@@ -391,8 +400,8 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
     }
     if (p.variant_bwd == KAN_VARIANT_GATHER) {
         hipError_t e = hipSuccess;
-        if (dx) e = launch_gather_dx(p, x, C, W_base, dy, dx, s);
-        if (e == hipSuccess && (dC || dW)) e = launch_gather_dc(p, x, dy, dC, dW, s);
+        if (dx) e = launch_gather_dx(p, x, C, W_base, dy, dx, ws, s);
+        if (e == hipSuccess && (dC || dW)) e = launch_gather_dc(p, x, dy, dC, dW, ws, s);
         return status_of(e);
     }
     if (!(desc->flags & KAN_FLAG_PREPARED)) {

@@ -477,158 +477,376 @@ __global__ void gather_sum_kernel(const double* __restrict__ part, float* __rest
 }
 
 // ---------------------------------------------------------------------------
-// dx.  Block: 64 rows x 16 inputs; thread: 4 rows x 1 input.  The reduction
-// runs over outputs j in chunks of 16 with dy and C staged in LDS.
-constexpr int GX_TB = 64, GX_TI = 16, GX_JC = 16;
+// dx.  A block of 1024 threads computes 256 rows x 16 inputs: thread t takes
+// input t % 16 and rows t / 16 + 64 p, p < 4, whose D + 1 basis derivatives
+// and silu' it forms once.  The sum over outputs j runs in chunks of JC held
+// in LDS: dy[rows][JC], the chunk's coefficients for the block's 16 inputs as
+// Cs[ii][m][j] and W_base as Ws[ii][j] (rows padded to JC + 4 floats, so
+// that the transposing stores of consecutive pieces fall in different
+// banks).  There are two chunk buffers: the next chunk is loaded into
+// registers while the current one is read, with one barrier per chunk.  All
+// 256 rows share a staged chunk, which keeps the coefficient staging (the
+// part that grows with G) small next to the arithmetic.  With too few
+// blocks to fill the GPU the outputs are split into slices whose partial dx
+// are added in slice order (gather_sum_f32_kernel).
+constexpr int GX_NT = 1024, GX_R = 256, GX_TI = 16;
 
-template <typename TS, int D>
-__global__ __launch_bounds__(256) void gather_dx_kernel(GridK g, int N, int I, int O, int base,
-                                                        const TS* __restrict__ x,
-                                                        const TS* __restrict__ C,
-                                                        const TS* __restrict__ W,
-                                                        const float* __restrict__ dy,
-                                                        float* __restrict__ dx) {
+template <typename TS, int D, int JC>
+__global__ __launch_bounds__(GX_NT) void gather_dx_kernel(GatherDxArgs a) {
+    constexpr int JP = JC + 4;                       // padded LDS row (floats)
+    constexpr int NPC = GX_NT / JC;                  // threads sharing one output's coefficient loads
+    constexpr int MAXQ = 3;                          // ceil(K JC / 256) at the plan's K bound for JC
+    constexpr int NDY = GX_R * JC / 4;               // float4 pieces of a dy chunk (<= GX_NT)
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
-    const int K = g.G + D;
-    float* Ds = smem;                               // [TB][JC]
-    float* Cs = Ds + GX_TB * GX_JC;                  // [TI][K][JC]
-    float* Ws = Cs + GX_TI * K * GX_JC;              // [TI][JC]
-
+    const TS* __restrict__ x = static_cast<const TS*>(a.x);
+    const TS* __restrict__ C = static_cast<const TS*>(a.C);
+    const TS* __restrict__ W = static_cast<const TS*>(a.W);
+    const float* __restrict__ dy = a.dy;
+    const GridK g = a.g;
+    const int K = g.G + D, N = a.N, I = a.I, O = a.O;
+    const int dsz = GX_R * JC, csz = GX_TI * K * JP;
+    const int bufsz = dsz + csz + GX_TI * JP;        // floats per chunk buffer
     const int t = threadIdx.x;
+
+    // block -> (row block, input block), row blocks fastest on an XCD: the
+    // blocks an XCD runs together share one input block's coefficients
+    const int T = a.RB * a.IB;
+    const int bid = blockIdx.x, nfull = T / 8, rem = T % 8, xcd = bid % 8;
+    const int id = xcd * nfull + min(xcd, rem) + bid / 8;
+    const int rb = id % a.RB, ibk = id / a.RB;
+    const int b0 = rb * GX_R, i0 = ibk * GX_TI;
+    const int nin = min(GX_TI, I - i0);
+    const int slice = blockIdx.y;
+    const int js = slice * a.JS, je = min(O, js + a.JS);
+    const int nch = (je - js + JC - 1) / JC;
+
     const int il = t % GX_TI, rq = t / GX_TI;
-    const int b0 = blockIdx.x * GX_TB, i0 = blockIdx.y * GX_TI;
     const int i = i0 + il;
-    RecD<D> rec[4];
-    int mi[4][D + 1];
+    // per row: the LDS index of coefficient row mb = s - D clamped to
+    // [0, K - D - 1] of this thread's input, and the derivative pieces
+    // shifted by the clamp (as in the forward's records), then silu'
+    int cb[4];
+    float wd[4][D + 1], bs[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int b = b0 + rq + 16 * p;
-        if (b < N && i < I) {
-            rec[p] = make_rec<true, D>(load_f(x, (int64_t)b * I + i), g);
-            if (!base) rec[p].base = 0.0f;
-        } else {
-            rec[p] = zero_rec<D>();
-        }
+        const int b = b0 + rq + 64 * p;
+        const RecD<D> r = (b < N && i < I) ? make_rec<true, D>(load_f(x, (int64_t)b * I + i), g) : zero_rec<D>();
+        const int mb = clampi(r.m0, 0, K - D - 1);
+        cb[p] = (il * K + mb) * JP;
 #pragma unroll
-        for (int q = 0; q <= D; ++q) mi[p][q] = clampi(rec[p].m0 + q, 0, K - 1);
+        for (int q = 0; q <= D; ++q) {
+            const int k = mb + q - r.m0;
+            float v = 0.0f;
+#pragma unroll
+            for (int e = 0; e <= D; ++e) v = k == e ? r.w[e] : v;
+            wd[p][q] = v;
+        }
+        bs[p] = a.base ? r.base : 0.0f;
     }
+
+    // loads of one chunk: dy piece t (row t / (JC/4), columns 4 (t % (JC/4))
+    // .. +3), coefficient pieces k = t / JC + NPC q of output j = t % JC's
+    // run C[j, i0 .. i0+nin-1, :], and W_base[j, i0 + ii] for t < 16 JC.
+    // Indices are clamped in bounds; values outside the chunk are zeroed when
+    // stored.
+    const bool vec = (O & 3) == 0;
+    const int dyr = t / (JC / 4), dyc = 4 * (t % (JC / 4));
+    const int jj = t % JC, pc = t / JC;
+    const int ick = nin * K;
+    float4 dp, cp[MAXQ];
+    float wp;
+    auto load = [&](int c) {
+        const int j0 = js + c * JC;
+        if (t < NDY) {
+            const int b = min(b0 + dyr, N - 1), j = j0 + dyc;
+            const float* row = dy + (int64_t)b * O;
+            if (vec) {
+                __builtin_memcpy(&dp, row + min(j, O - 4), 16);
+            } else {
+                dp.x = row[min(j + 0, O - 1)];
+                dp.y = row[min(j + 1, O - 1)];
+                dp.z = row[min(j + 2, O - 1)];
+                dp.w = row[min(j + 3, O - 1)];
+            }
+        }
+        const TS* src = C + ((int64_t)min(j0 + jj, O - 1) * I + i0) * K;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            const int k = pc + NPC * q;
+            if (4 * k < ick) {
+                if (std::is_same<TS, float>::value && ick >= 4) {
+                    __builtin_memcpy(&cp[q], reinterpret_cast<const float*>(src) + min(4 * k, ick - 4), 16);
+                } else {
+                    const int s = ick >= 4 ? min(4 * k, ick - 4) : 0;
+                    cp[q].x = load_f(src, min(s + 0, ick - 1));
+                    cp[q].y = load_f(src, min(s + 1, ick - 1));
+                    cp[q].z = load_f(src, min(s + 2, ick - 1));
+                    cp[q].w = load_f(src, min(s + 3, ick - 1));
+                }
+            }
+        }
+        if (t < GX_TI * JC) {
+            const int wj = t / GX_TI, wi = t % GX_TI;
+            wp = a.base ? load_f(W, (int64_t)min(j0 + wj, O - 1) * I + i0 + min(wi, nin - 1)) : 0.0f;
+        }
+    };
+    auto store = [&](int c, int buf) {
+        float* Ds = smem + buf * bufsz;
+        float* Cs = Ds + dsz;
+        float* Ws = Cs + csz;
+        const int j0 = js + c * JC;
+        if (t < NDY) {
+            const int j = j0 + dyc;
+            float4 v;
+            if (vec && j < je) {
+                v = dp;                                   // j .. j+3 < O, inside the slice (JS % JC == 0)
+            } else {
+                v.x = j + 0 < je ? dp.x : 0.0f;
+                v.y = j + 1 < je ? dp.y : 0.0f;
+                v.z = j + 2 < je ? dp.z : 0.0f;
+                v.w = j + 3 < je ? dp.w : 0.0f;
+            }
+            if (b0 + dyr >= N) v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            *reinterpret_cast<float4*>(Ds + dyr * JC + dyc) = v;
+        }
+        const bool jok = j0 + jj < je;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            const int k = pc + NPC * q;
+            if (4 * k < ick) {
+                const int s = ick >= 4 ? min(4 * k, ick - 4) : 0;
+                const float vv[4] = {cp[q].x, cp[q].y, cp[q].z, cp[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (s + e < ick) Cs[(s + e) * JP + jj] = jok ? vv[e] : 0.0f;
+            }
+        }
+        if (t < GX_TI * JC) {
+            const int wj = t / GX_TI, wi = t % GX_TI;
+            Ws[wi * JP + wj] = (j0 + wj < je && wi < nin) ? wp : 0.0f;
+        }
+    };
+
     float Q[4][D + 2];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int q = 0; q < D + 2; ++q) Q[p][q] = 0.0f;
-    for (int jc = 0; jc < O; jc += GX_JC) {
-        __syncthreads();
-        for (int e = t; e < GX_TB * GX_JC; e += 256) {
-            const int bb = e / GX_JC, jj = e % GX_JC;
-            const int b = b0 + bb, j = jc + jj;
-            Ds[bb * GX_JC + jj] = (b < N && j < O) ? dy[(int64_t)b * O + j] : 0.0f;
-        }
-        for (int e = t; e < GX_JC * GX_TI * K; e += 256) {
-            const int jj = e / (GX_TI * K), rem = e % (GX_TI * K);
-            const int ii = rem / K, m = rem % K;
-            const int j = jc + jj, ig = i0 + ii;
-            Cs[(ii * K + m) * GX_JC + jj] =
-                (j < O && ig < I) ? load_f(C, ((int64_t)j * I + ig) * K + m) : 0.0f;
-        }
-        for (int e = t; e < GX_JC * GX_TI; e += 256) {
-            const int jj = e / GX_TI, ii = e % GX_TI;
-            const int j = jc + jj, ig = i0 + ii;
-            Ws[ii * GX_JC + jj] = (base && j < O && ig < I) ? load_f(W, (int64_t)j * I + ig) : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int jj = 0; jj < GX_JC; jj += 4) {
-            const float4 wv = *reinterpret_cast<const float4*>(&Ws[il * GX_JC + jj]);
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const bool more = c + 1 < nch;
+        if (more) load(c + 1);
+        const float* Ds = smem + (c & 1) * bufsz;
+        const float* Cs = Ds + dsz;
+        const float* Ws = Cs + csz;
+        // keep the chunk's arithmetic apart from the prefetch and the stores
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+        for (int jq = 0; jq < JC; jq += 4) {
+            const float4 wv = *reinterpret_cast<const float4*>(&Ws[il * JP + jq]);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const float4 d = *reinterpret_cast<const float4*>(&Ds[(rq + 16 * p) * GX_JC + jj]);
+                const float4 d = *reinterpret_cast<const float4*>(&Ds[(rq + 64 * p) * JC + jq]);
+                float4 cv[D + 1];
+#pragma unroll
+                for (int q = 0; q <= D; ++q) cv[q] = *reinterpret_cast<const float4*>(&Cs[cb[p] + q * JP + jq]);
 #pragma unroll
                 for (int q = 0; q <= D; ++q) {
-                    const float4 c = *reinterpret_cast<const float4*>(&Cs[(il * K + mi[p][q]) * GX_JC + jj]);
-                    Q[p][q] = __builtin_fmaf(d.x, c.x, Q[p][q]);
-                    Q[p][q] = __builtin_fmaf(d.y, c.y, Q[p][q]);
-                    Q[p][q] = __builtin_fmaf(d.z, c.z, Q[p][q]);
-                    Q[p][q] = __builtin_fmaf(d.w, c.w, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.x, cv[q].x, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.y, cv[q].y, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.z, cv[q].z, Q[p][q]);
+                    Q[p][q] = __builtin_fmaf(d.w, cv[q].w, Q[p][q]);
                 }
                 Q[p][D + 1] = __builtin_fmaf(d.x, wv.x, Q[p][D + 1]);
                 Q[p][D + 1] = __builtin_fmaf(d.y, wv.y, Q[p][D + 1]);
                 Q[p][D + 1] = __builtin_fmaf(d.z, wv.z, Q[p][D + 1]);
                 Q[p][D + 1] = __builtin_fmaf(d.w, wv.w, Q[p][D + 1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) store(c + 1, (c + 1) & 1);
+        __syncthreads();
     }
+    float* out = a.part ? a.part + (int64_t)slice * N * I : a.dx;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int b = b0 + rq + 16 * p;
+        const int b = b0 + rq + 64 * p;
         if (b >= N || i >= I) continue;
-        float v = Q[p][D + 1] * rec[p].base;
+        float v = Q[p][D + 1] * bs[p];
 #pragma unroll
-        for (int q = 0; q <= D; ++q) v = __builtin_fmaf(Q[p][q], rec[p].w[q], v);
-        dx[(int64_t)b * I + i] = v;
+        for (int q = 0; q <= D; ++q) v = __builtin_fmaf(Q[p][q], wd[p][q], v);
+        out[(int64_t)b * I + i] = v;
+    }
+}
+
+// out[e] = the float64 sum over slices s = 0 .. S-1, in that order, of
+// part[s n + e], rounded once to float32
+__global__ void gather_sum_f32_kernel(const float* __restrict__ part, float* __restrict__ out, int64_t n,
+                                      int S) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        double v = part[e];
+        for (int s = 1; s < S; ++s) v += (double)part[s * n + e];
+        out[e] = (float)v;
     }
 }
 
 // ---------------------------------------------------------------------------
-// dC, dW_base.  Block owns 16 inputs x 16 outputs and sweeps every row in a
-// fixed order; thread (i, j) keeps its K spline accumulators in a private LDS
-// column (no other thread touches them, so there is no atomic and the sum
-// order is the row order).  Rows are staged GC_RB at a time (32 above degree
-// 3, whose larger records would push G = 125 past the 160 KB of LDS).
-constexpr int GC_TI = 16, GC_TJ = 16;
-template <int D> constexpr int gc_rb() { return D > 3 ? 32 : 64; }
+// dC, dW_base.  Wave w of a block owns input i = (NT / 64) ib + w and its
+// lanes the block's 64 outputs j; every lane keeps the K sums dC[j, i, m] of
+// its (j, i) in registers (KMAX of them).  Rows come in chunks of 64: the
+// block stages dy[rows][64 outputs] in LDS, and lane l of each wave forms the
+// span and D + 1 weights of row l for the wave's input.  A row's span is then
+// the same in every lane of the wave, so the wave walks the spans
+// s = 0 .. K + D - 1 as a compile-time loop: a ballot selects the chunk's rows
+// whose span is s, and each adds dy[b, j] times its weights into the sums
+// m = s - D .. s, registers named at compile time.  Rows off the grid add
+// only their silu term.  There are no atomics and no shared accumulators;
+// the order of each sum is fixed by the data (rows by span, then by index).
+// With too few blocks to fill the GPU the rows are split into slices whose
+// partial sums are added in slice order.  Two chunk buffers, one barrier per
+// chunk.
+template <int N0, int N1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N0 < N1) {
+        f(std::integral_constant<int, N0>());
+        static_for<N0 + 1, N1>(f);
+    }
+}
 
-template <typename TS, int D>
-__global__ __launch_bounds__(256) void gather_dc_kernel(GridK g, int N, int I, int O, int base,
-                                                        const TS* __restrict__ x,
-                                                        const float* __restrict__ dy,
-                                                        float* __restrict__ dC,
-                                                        float* __restrict__ dW) {
+constexpr int GC_RW = 8;                             // floats of a row record: w[0 .. D], silu at 7
+
+template <int D, bool BASE, int KMAX, int NT>
+__global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
+    constexpr int NW = NT / 64;                      // inputs (waves) per block
+    constexpr int DSZ = 64 * 64, WSZ = NW * 64 * GC_RW;
+    constexpr int DV = DSZ / 4 / NT;                 // float4 dy pieces per thread
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
-    const int K = g.G + D;
-    float* Acc = smem;                                // [K][256]
-    float* Ds = Acc + K * 256;                        // [RB][TJ]
-    constexpr int GC_RB = gc_rb<D>();
-    RecD<D>* Rs = reinterpret_cast<RecD<D>*>(Ds + GC_RB * GC_TJ);  // [RB][TI]
+    const GridK g = a.g;
+    const int K = g.G + D, N = a.N, I = a.I, O = a.O;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
-    const int t = threadIdx.x;
-    const int il = t % GC_TI, jl = t / GC_TI;
-    const int i0 = blockIdx.x * GC_TI, j0 = blockIdx.y * GC_TJ;
-    for (int m = 0; m < K; ++m) Acc[m * 256 + t] = 0.0f;
-    float accw = 0.0f;
-    for (int r0 = 0; r0 < N; r0 += GC_RB) {
-        __syncthreads();
-        for (int e = t; e < GC_RB * GC_TJ; e += 256) {
-            const int bb = e / GC_TJ, jj = e % GC_TJ;
-            const int b = r0 + bb, j = j0 + jj;
-            Ds[bb * GC_TJ + jj] = (b < N && j < O) ? dy[(int64_t)b * O + j] : 0.0f;
-        }
-        for (int e = t; e < GC_RB * GC_TI; e += 256) {
-            const int bb = e / GC_TI, ii = e % GC_TI;
-            const int b = r0 + bb, i = i0 + ii;
-            Rs[bb * GC_TI + ii] = (b < N && i < I) ? make_rec<false, D>(load_f(x, (int64_t)b * I + i), g)
-                                                   : zero_rec<D>();
-        }
-        __syncthreads();
-        const int nb = min(GC_RB, N - r0);
-        for (int bb = 0; bb < nb; ++bb) {
-            const float d = Ds[bb * GC_TJ + jl];
-            const RecD<D> r = Rs[bb * GC_TI + il];
-            accw = __builtin_fmaf(d, r.base, accw);
+    const int T = a.IBN * a.OB;
+    const int bid = blockIdx.x, nfull = T / 8, rem = T % 8, xcd = bid % 8;
+    const int id = xcd * nfull + min(xcd, rem) + bid / 8;
+    const int ibk = id % a.IBN, ob = id / a.IBN;
+    const int i = ibk * NW + wave, j0 = ob * 64, j = j0 + lane;
+    const int slice = blockIdx.y;
+    const int rs = slice * a.RS, re = min(N, rs + a.RS);
+    const int nch = (re - rs + 63) / 64;
+    const bool vec = (O & 3) == 0;
+    const int ic = min(i, I - 1);
+
+    float4 dp[DV];
+    float xp;
+    auto load = [&](int c) {
+        const int r0 = rs + 64 * c;
 #pragma unroll
-            for (int q = 0; q <= D; ++q) {
-                const int m = clampi(r.m0 + q, 0, K - 1);
-                Acc[m * 256 + t] = __builtin_fmaf(d, r.w[q], Acc[m * 256 + t]);
+        for (int v = 0; v < DV; ++v) {
+            const int u = t + NT * v, row = u / 16, col = 4 * (u % 16);
+            const float* src = a.dy + (int64_t)min(r0 + row, N - 1) * O;
+            if (vec) {
+                __builtin_memcpy(&dp[v], src + min(j0 + col, O - 4), 16);
+            } else {
+                dp[v].x = src[min(j0 + col + 0, O - 1)];
+                dp[v].y = src[min(j0 + col + 1, O - 1)];
+                dp[v].z = src[min(j0 + col + 2, O - 1)];
+                dp[v].w = src[min(j0 + col + 3, O - 1)];
             }
         }
+        const int64_t xi = (int64_t)min(r0 + lane, N - 1) * I + ic;
+        xp = a.bf16 ? load_f(static_cast<const uint16_t*>(a.x), xi) : load_f(static_cast<const float*>(a.x), xi);
+    };
+    int span = -1;                                   // this lane's row's span in the current chunk
+    bool live = false;                               // this lane's row exists
+    auto store = [&](int c, int buf) {
+        float* Ds = smem + buf * (DSZ + WSZ);
+        float* Wr = Ds + DSZ + wave * 64 * GC_RW;
+        const int r0 = rs + 64 * c;
+#pragma unroll
+        for (int v = 0; v < DV; ++v) {
+            const int u = t + NT * v, row = u / 16, col = 4 * (u % 16);
+            float4 d = dp[v];
+            const int jc = j0 + col;
+            if (!vec || jc + 3 >= O) {
+                d.x = jc + 0 < O ? d.x : 0.0f;
+                d.y = jc + 1 < O ? d.y : 0.0f;
+                d.z = jc + 2 < O ? d.z : 0.0f;
+                d.w = jc + 3 < O ? d.w : 0.0f;
+            }
+            if (r0 + row >= re) d = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            *reinterpret_cast<float4*>(Ds + row * 64 + col) = d;
+        }
+        live = r0 + lane < re && i < I;
+        const RecD<D> r = make_rec<false, D>(xp, g);
+        span = live ? r.m0 + D : -1;
+        float wr[GC_RW] = {};
+#pragma unroll
+        for (int q = 0; q <= D; ++q) wr[q] = r.w[q];
+        wr[7] = BASE ? r.base : 0.0f;
+        *reinterpret_cast<float4*>(Wr + lane * GC_RW) = make_float4(wr[0], wr[1], wr[2], wr[3]);
+        *reinterpret_cast<float4*>(Wr + lane * GC_RW + 4) = make_float4(wr[4], wr[5], wr[6], wr[7]);
+    };
+
+    float acc[KMAX];
+#pragma unroll
+    for (int m = 0; m < KMAX; ++m) acc[m] = 0.0f;
+    float accw = 0.0f;
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const bool more = c + 1 < nch;
+        if (more) load(c + 1);
+        const float* Ds = smem + (c & 1) * (DSZ + WSZ);
+        const float* Wr = Ds + DSZ + wave * 64 * GC_RW;
+        const int cur = span;
+        static_for<0, KMAX + D>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            if (s < K + D) {
+                uint64_t mask = __ballot(cur == s);
+                while (mask) {
+                    const int l = __builtin_ctzll(mask);
+                    mask &= mask - 1;
+                    const float d = Ds[l * 64 + lane];
+                    const float4 w0 = *reinterpret_cast<const float4*>(Wr + l * GC_RW);
+                    const float4 w1 = *reinterpret_cast<const float4*>(Wr + l * GC_RW + 4);
+                    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                    static_for<0, D + 1>([&](auto rc) {
+                        constexpr int r = decltype(rc)::value, m = s - D + r;
+                        if constexpr (m >= 0 && m < KMAX) acc[m] = __builtin_fmaf(d, w[r], acc[m]);
+                    });
+                    if constexpr (BASE) accw = __builtin_fmaf(d, w[7], accw);
+                }
+            }
+        });
+        if constexpr (BASE) {
+            // rows whose span lies off the grid: the silu term only
+            uint64_t mask = __ballot(live && (cur < 0 || cur >= K + D));
+            while (mask) {
+                const int l = __builtin_ctzll(mask);
+                mask &= mask - 1;
+                accw = __builtin_fmaf(Ds[l * 64 + lane], Wr[l * GC_RW + 7], accw);
+            }
+        }
+        if (more) store(c + 1, (c + 1) & 1);
+        __syncthreads();
     }
-    const int i = i0 + il, j = j0 + jl;
     if (i < I && j < O) {
-        if (dC)
-            for (int m = 0; m < K; ++m) dC[((int64_t)j * I + i) * K + m] = Acc[m * 256 + t];
-        if (dW && base) dW[(int64_t)j * I + i] = accw;
+        float* dC = a.cpart ? a.cpart + (int64_t)slice * O * I * K : a.dC;
+        float* dW = a.wpart ? a.wpart + (int64_t)slice * O * I : a.dW;
+        if (dC) {
+            float* dst = dC + ((int64_t)j * I + i) * K;
+#pragma unroll
+            for (int m = 0; m < KMAX; ++m)
+                if (m < K) dst[m] = acc[m];
+        }
+        if (BASE && dW) dW[(int64_t)j * I + i] = accw;
     }
 }
 
@@ -774,65 +992,162 @@ hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const 
     return hipGetLastError();
 }
 
-template <typename TS, int D>
-static hipError_t gather_dx_run(const Plan& p, const void* x, const void* C, const void* W,
-                                const float* dy, float* dx, hipStream_t s) {
-    const size_t lds = (size_t)(GX_TB * GX_JC + GX_TI * p.K * GX_JC + GX_TI * GX_JC) * 4;
-    dim3 grid((unsigned)((p.N + GX_TB - 1) / GX_TB), (unsigned)((p.I + GX_TI - 1) / GX_TI));
-    hipError_t e = allow_lds(gather_dx_kernel<TS, D>, lds);
+GatherBwdPlan gather_bwd_plan(int64_t N, int64_t I, int64_t O, int K, int base) {
+    GatherBwdPlan q;
+    const int64_t target = 256;                       // blocks that fill the CUs once
+    const bool big = N * I * O >= (int64_t(1) << 16);
+    // dx: the widest output chunk whose two buffers fit in 150 KB of LDS
+    q.jc = 4;
+    for (int jc : {16, 8}) {
+        const int64_t floats = 2 * ((int64_t)GX_R * jc + (int64_t)GX_TI * K * (jc + 4) + GX_TI * (jc + 4));
+        if (floats * 4 <= 150 * 1024) { q.jc = jc; break; }
+    }
+    q.lds_dx = (size_t)(2 * ((int64_t)GX_R * q.jc + (int64_t)GX_TI * K * (q.jc + 4) + GX_TI * (q.jc + 4)) * 4);
+    q.rb = (N + GX_R - 1) / GX_R;
+    q.ib = (I + GX_TI - 1) / GX_TI;
+    int64_t sx = 1;
+    if (big && q.rb * q.ib < target)
+        sx = std::max<int64_t>(1, std::min((target + q.rb * q.ib - 1) / (q.rb * q.ib), (O + 4 * q.jc - 1) / (4 * q.jc)));
+    q.js = ((O + sx - 1) / sx + q.jc - 1) / q.jc * q.jc;
+    q.sx = (int)((O + q.js - 1) / q.js);
+    // dC: KMAX register sums per lane; waves of one block share a dy chunk
+    q.kmax = K <= 16 ? 16 : K <= 32 ? 32 : K <= 64 ? 64 : 132;    // K <= 125 + 5
+    q.nt_dc = q.kmax <= 64 ? 1024 : 512;
+    const int nw = q.nt_dc / 64;
+    q.ibn = (I + nw - 1) / nw;
+    q.ob = (O + 63) / 64;
+    q.lds_dc = (size_t)(2 * (64 * 64 + nw * 64 * GC_RW) * 4);
+    int64_t sc = 1;
+    if (big && q.ibn * q.ob < target)
+        sc = std::max<int64_t>(1, std::min((target + q.ibn * q.ob - 1) / (q.ibn * q.ob), (N + 127) / 128));
+    q.rs = std::max<int64_t>(64, ((N + sc - 1) / sc + 63) / 64 * 64);
+    q.sc = (int)std::max<int64_t>(1, (N + q.rs - 1) / q.rs);
+    // workspace: dx partials, then dC and dW_base partials
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (size_t)round_up((int64_t)bytes, 256);
+        return o;
+    };
+    q.off_dxp = q.sx > 1 ? take((size_t)q.sx * N * I * 4) : 0;
+    q.off_dcp = q.sc > 1 ? take((size_t)q.sc * O * I * K * 4) : 0;
+    q.off_dwp = q.sc > 1 && base ? take((size_t)q.sc * O * I * 4) : 0;
+    q.ws = off;
+    return q;
+}
+
+template <typename TS, int D, int JC>
+static hipError_t gather_dx_run(const Plan& p, const GatherDxArgs& a, hipStream_t s) {
+    auto k = gather_dx_kernel<TS, D, JC>;
+    hipError_t e = allow_lds(k, p.gb.lds_dx);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gather_dx_kernel<TS, D>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
-                       (int)p.O, p.base, static_cast<const TS*>(x), static_cast<const TS*>(C),
-                       static_cast<const TS*>(W), dy, dx);
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.gb.rb * p.gb.ib), (unsigned)p.gb.sx), dim3(GX_NT), p.gb.lds_dx, s, a);
     return hipGetLastError();
 }
 
 template <typename TS, int D>
-static hipError_t gather_dc_run(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
-                                hipStream_t s) {
-    constexpr int GC_RB = gc_rb<D>();
-    const size_t lds = (size_t)(p.K * 256 + GC_RB * GC_TJ) * 4 + GC_RB * GC_TI * sizeof(RecD<D>);
-    dim3 grid((unsigned)((p.I + GC_TI - 1) / GC_TI), (unsigned)((p.O + GC_TJ - 1) / GC_TJ));
-    hipError_t e = allow_lds(gather_dc_kernel<TS, D>, lds);
+static hipError_t gather_dx_jc(const Plan& p, const GatherDxArgs& a, hipStream_t s) {
+    if (p.gb.jc == 16) return gather_dx_run<TS, D, 16>(p, a, s);
+    if (p.gb.jc == 8) return gather_dx_run<TS, D, 8>(p, a, s);
+    return gather_dx_run<TS, D, 4>(p, a, s);
+}
+
+template <typename TS>
+static hipError_t gather_dx_deg(const Plan& p, const GatherDxArgs& a, hipStream_t s) {
+    switch (p.degree) {
+        case 1: return gather_dx_jc<TS, 1>(p, a, s);
+        case 2: return gather_dx_jc<TS, 2>(p, a, s);
+        case 4: return gather_dx_jc<TS, 4>(p, a, s);
+        case 5: return gather_dx_jc<TS, 5>(p, a, s);
+        default: return gather_dx_jc<TS, 3>(p, a, s);
+    }
+}
+
+template <int D, bool BASE, int KMAX>
+static hipError_t gather_dc_run(const Plan& p, const GatherDcArgs& a, hipStream_t s) {
+    constexpr int NT = KMAX <= 64 ? 1024 : 512;
+    auto k = gather_dc_kernel<D, BASE, KMAX, NT>;
+    hipError_t e = allow_lds(k, p.gb.lds_dc);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gather_dc_kernel<TS, D>), grid, dim3(256), lds, s, p.gk, (int)p.N, (int)p.I,
-                       (int)p.O, p.base, static_cast<const TS*>(x), dy, dC, dW);
+    hipLaunchKernelGGL(k, dim3((unsigned)(p.gb.ibn * p.gb.ob), (unsigned)p.gb.sc), dim3(NT), p.gb.lds_dc, s, a);
     return hipGetLastError();
 }
 
-template <typename TS>
-static hipError_t gather_dx_deg(const Plan& p, const void* x, const void* C, const void* W,
-                                const float* dy, float* dx, hipStream_t s) {
-    switch (p.degree) {
-        case 1: return gather_dx_run<TS, 1>(p, x, C, W, dy, dx, s);
-        case 2: return gather_dx_run<TS, 2>(p, x, C, W, dy, dx, s);
-        case 4: return gather_dx_run<TS, 4>(p, x, C, W, dy, dx, s);
-        case 5: return gather_dx_run<TS, 5>(p, x, C, W, dy, dx, s);
-        default: return gather_dx_run<TS, 3>(p, x, C, W, dy, dx, s);
+template <int D, bool BASE>
+static hipError_t gather_dc_kmax(const Plan& p, const GatherDcArgs& a, hipStream_t s) {
+    switch (p.gb.kmax) {
+        case 16: return gather_dc_run<D, BASE, 16>(p, a, s);
+        case 32: return gather_dc_run<D, BASE, 32>(p, a, s);
+        case 64: return gather_dc_run<D, BASE, 64>(p, a, s);
+        default: return gather_dc_run<D, BASE, 132>(p, a, s);
     }
 }
 
-template <typename TS>
-static hipError_t gather_dc_deg(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
-                                hipStream_t s) {
-    switch (p.degree) {
-        case 1: return gather_dc_run<TS, 1>(p, x, dy, dC, dW, s);
-        case 2: return gather_dc_run<TS, 2>(p, x, dy, dC, dW, s);
-        case 4: return gather_dc_run<TS, 4>(p, x, dy, dC, dW, s);
-        case 5: return gather_dc_run<TS, 5>(p, x, dy, dC, dW, s);
-        default: return gather_dc_run<TS, 3>(p, x, dy, dC, dW, s);
-    }
+template <int D>
+static hipError_t gather_dc_base(const Plan& p, const GatherDcArgs& a, hipStream_t s) {
+    return p.base ? gather_dc_kmax<D, true>(p, a, s) : gather_dc_kmax<D, false>(p, a, s);
+}
+
+static hipError_t sum_f32(const float* part, float* out, int64_t n, int S, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_sum_f32_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 16384)), dim3(256),
+                       0, s, part, out, n, S);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
-                            const float* dy, float* dx, hipStream_t s) {
-    return p.dtype == KAN_F32 ? gather_dx_deg<float>(p, x, C, W, dy, dx, s)
-                              : gather_dx_deg<uint16_t>(p, x, C, W, dy, dx, s);
+                            const float* dy, float* dx, void* ws, hipStream_t s) {
+    GatherDxArgs a;
+    a.g = p.gk;
+    a.N = (int)p.N;
+    a.I = (int)p.I;
+    a.O = (int)p.O;
+    a.base = p.base;
+    a.RB = (int)p.gb.rb;
+    a.IB = (int)p.gb.ib;
+    a.JS = (int)p.gb.js;
+    a.x = x;
+    a.C = C;
+    a.W = W;
+    a.dy = dy;
+    a.dx = dx;
+    a.part = p.gb.sx > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.gb.off_dxp) : nullptr;
+    hipError_t e = p.dtype == KAN_F32 ? gather_dx_deg<float>(p, a, s) : gather_dx_deg<uint16_t>(p, a, s);
+    if (e != hipSuccess || p.gb.sx <= 1) return e;
+    return sum_f32(a.part, dx, p.N * p.I, p.gb.sx, s);
 }
+
 hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
-                            hipStream_t s) {
-    return p.dtype == KAN_F32 ? gather_dc_deg<float>(p, x, dy, dC, dW, s)
-                              : gather_dc_deg<uint16_t>(p, x, dy, dC, dW, s);
+                            void* ws, hipStream_t s) {
+    GatherDcArgs a;
+    a.g = p.gk;
+    a.N = (int)p.N;
+    a.I = (int)p.I;
+    a.O = (int)p.O;
+    a.IBN = (int)p.gb.ibn;
+    a.OB = (int)p.gb.ob;
+    a.RS = (int)p.gb.rs;
+    a.bf16 = p.dtype == KAN_BF16;
+    a.x = x;
+    a.dy = dy;
+    a.dC = dC;
+    a.dW = dW;
+    const bool split = p.gb.sc > 1;
+    char* w = static_cast<char*>(ws);
+    a.cpart = split && dC ? reinterpret_cast<float*>(w + p.gb.off_dcp) : nullptr;
+    a.wpart = split && dW ? reinterpret_cast<float*>(w + p.gb.off_dwp) : nullptr;
+    hipError_t e;
+    switch (p.degree) {
+        case 1: e = gather_dc_base<1>(p, a, s); break;
+        case 2: e = gather_dc_base<2>(p, a, s); break;
+        case 4: e = gather_dc_base<4>(p, a, s); break;
+        case 5: e = gather_dc_base<5>(p, a, s); break;
+        default: e = gather_dc_base<3>(p, a, s); break;
+    }
+    if (e != hipSuccess || !split) return e;
+    if (dC) e = sum_f32(a.cpart, dC, p.O * p.I * p.K, p.gb.sc, s);
+    if (e == hipSuccess && dW) e = sum_f32(a.wpart, dW, p.O * p.I, p.gb.sc, s);
+    return e;
 }
 
 }  // namespace kan

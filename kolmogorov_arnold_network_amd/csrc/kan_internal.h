@@ -32,6 +32,47 @@ struct GatherFwdPlan {
 };
 GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int base);
 
+// Local-gather backward.  dx: blocks of 1024 threads compute 256 rows by 16
+// inputs (rb x ib blocks), summing over outputs in chunks of jc staged in
+// lds_dx bytes; the outputs are cut into sx slices of js (sx > 1: float32
+// partial dx [sx][N][I] at off_dxp).  dC: blocks of nt_dc threads, one input
+// per wave and 64 outputs (ibn x ob blocks), kmax register sums per lane,
+// lds_dc bytes; the rows are cut into sc slices of rs (sc > 1: partial dC
+// [sc][O][I][K] at off_dcp and dW_base [sc][O][I] at off_dwp).
+struct GatherBwdPlan {
+    int jc, sx, kmax, nt_dc, sc;
+    int64_t rb, ib, js, ibn, ob, rs;
+    size_t lds_dx, lds_dc, off_dxp, off_dcp, off_dwp, ws;
+};
+GatherBwdPlan gather_bwd_plan(int64_t N, int64_t I, int64_t O, int K, int base);
+
+struct GatherDxArgs {
+    GridK g;
+    int N, I, O, base;
+    int RB, IB;          // row blocks, input blocks
+    int JS;              // outputs per slice (a multiple of the chunk)
+    const void* x;
+    const void* C;
+    const void* W;
+    const float* dy;
+    float* dx;           // one slice: the output
+    float* part;         // several slices: their partial dx [slice][N][I]
+};
+
+struct GatherDcArgs {
+    GridK g;
+    int N, I, O;
+    int IBN, OB;         // input blocks, output blocks
+    int RS;              // rows per slice (a multiple of 64)
+    int bf16;            // x stored as bf16
+    const void* x;
+    const float* dy;
+    float* dC;           // one slice: the outputs (either may be NULL)
+    float* dW;
+    float* cpart;        // several slices: partial dC [slice][O][I][K]
+    float* wpart;        // and dW_base [slice][O][I]
+};
+
 struct GatherFwdArgs {
     GridK g;
     int N, I, O;
@@ -96,6 +137,7 @@ struct Plan {
     size_t ws_fwd, ws_bwd;
 
     GatherFwdPlan gf;    // the local-gather forward (variant_fwd == GATHER)
+    GatherBwdPlan gb;    // the local-gather backward (variant_bwd == GATHER)
 };
 
 // Builds the plan; returns KAN_OK or the validation error for `desc` alone.
@@ -122,9 +164,9 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const void* W,
                              float* y, void* ws, hipStream_t s);
 hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const void* W,
-                            const float* dy, float* dx, hipStream_t s);
+                            const float* dy, float* dx, void* ws, hipStream_t s);
 hipError_t launch_gather_dc(const Plan& p, const void* x, const float* dy, float* dC, float* dW,
-                            hipStream_t s);
+                            void* ws, hipStream_t s);
 
 hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
 hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);

@@ -161,7 +161,20 @@ def test_backward_pointer_checks(L):
 
 
 def test_empty_batch_forward_returns_ok_without_launch(L):
-    assert fwd(L, desc(L, N=0)) == L.KAN_OK
+    """N = 0 on every variant, dtype and degree: the plans (workspace sizes
+    of both passes) are well defined and the forwards return without a
+    launch."""
+    for v in (L.KAN_VARIANT_AUTO, L.KAN_VARIANT_MFMA, L.KAN_VARIANT_GATHER):
+        for dt in (L.KAN_F32, L.KAN_BF16):
+            for deg in (1, 3, 5):
+                for G in (1, 8, 125):
+                    if v == L.KAN_VARIANT_MFMA and deg != 3 and G + deg + 1 < 4:
+                        continue                             # too few columns for the matrix cores
+                    d = desc(L, N=0, variant=v, dtype=dt, degree=deg, G=G)
+                    for ps in (0, 1):
+                        assert L.lib().kan_workspace_size(ctypes.byref(d), ps) != ctypes.c_size_t(-1).value
+                    assert fwd(L, d) == L.KAN_OK
+                    assert L.lib().kan_forward_static(ctypes.byref(d), X, C, W, Y, None) == L.KAN_OK
 
 
 def k_slices(tiles, nkt, out_bytes, esize):
@@ -204,6 +217,41 @@ def gather_fwd_ws(N, I, O, K, D, base):
     return (S * N * O * 8 + 255) // 256 * 256 if S > 1 else 0
 
 
+def gather_bwd_ws(N, I, O, K, base):
+    """Workspace of the local-gather backward: float32 partial dx of its
+    output slices (256-row x 16-input blocks) and partial dC / dW_base of its
+    row slices (one input per wave, 64 outputs), each used when its blocks
+    are fewer than the 256 CUs and the layer has at least 2^16 edge-rows."""
+    big = N * I * O >= 1 << 16
+    r = lambda a, b: (a + b - 1) // b * b
+    jc = 4
+    for c in (16, 8):
+        if 2 * (256 * c + 16 * K * (c + 4) + 16 * (c + 4)) * 4 <= 150 * 1024:
+            jc = c
+            break
+    T = (N + 255) // 256 * ((I + 15) // 16)
+    sx = max(1, min((256 + T - 1) // T, (O + 4 * jc - 1) // (4 * jc))) if big and T < 256 else 1
+    js = r((O + sx - 1) // sx, jc)
+    sx = (O + js - 1) // js
+    kmax = 16 if K <= 16 else 32 if K <= 32 else 64 if K <= 64 else 132
+    nw = (1024 if kmax <= 64 else 512) // 64
+    T = (I + nw - 1) // nw * ((O + 63) // 64)
+    sc = max(1, min((256 + T - 1) // T, (N + 127) // 128)) if big and T < 256 else 1
+    rs = max(64, r((N + sc - 1) // sc, 64))
+    sc = max(1, (N + rs - 1) // rs)
+    ws = r(sx * N * I * 4, 256) if sx > 1 else 0
+    if sc > 1:
+        ws += r(sc * O * I * K * 4, 256) + (r(sc * O * I * 4, 256) if base else 0)
+    return ws
+
+
+def auto_bwd_gather(N, I, O, Kb):
+    """float32 AUTO backward: gather when its estimate (N I O / 2.5e12 s) is
+    below the dense contraction's (2 N I O Kb / 110e12 s + 75 us)."""
+    nio = float(N) * I * O
+    return not (2.0 * nio * Kb / 110e12 + 75e-6 < nio / 2.5e12)
+
+
 def fwd_slices(nt_tiles, nkt, out_bytes, es):
     """k-slices of the MFMA forward: the occupancy split, and for float32 at
     most 8 k-tiles per slice."""
@@ -217,6 +265,11 @@ def test_workspace_sizes(L):
     ws = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 0)
     wb = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 1)
     assert ws(variant=L.KAN_VARIANT_GATHER) == 0 and wb(variant=L.KAN_VARIANT_GATHER) == 0
+    for (N, I, O, G, base) in [(1024, 784, 64, 8, 1), (1024, 64, 10, 8, 1), (8192, 1024, 1024, 50, 0),
+                               (300, 5000, 7, 20, 1), (5000, 3, 300, 125, 1), (64, 16, 8, 8, 1)]:
+        assert wb(N=N, I=I, O=O, G=G, has_base=base, variant=L.KAN_VARIANT_GATHER) == \
+            gather_bwd_ws(N, I, O, G + 3, base)
+    assert gather_bwd_ws(1024, 784, 64, 11, 1) > 0                # the quick-start layer splits
     # MFMA forward: packed C' [O padded to 256][I*Kb padded to the k-tile]
     r = lambda a, b: (a + b - 1) // b * b
     for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
@@ -258,9 +311,17 @@ def test_workspace_sizes(L):
             assert ws(N=N, I=I, O=O, G=G, has_base=base, variant=v, dtype=L.KAN_F32) == \
                 gather_fwd_ws(N, I, O, G + 3, 3, base)
     assert gather_fwd_ws(1024, 784, 64, 11, 3, 1) > 0            # the 784-wide quick-start layer splits
-    assert wb(N=64, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == wb(
-        N=64, I=32, O=32, variant=L.KAN_VARIANT_MFMA, dtype=L.KAN_F32) > 0          # 2^16 edge-rows
-    assert wb(N=63, I=32, O=32, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == 0  # below: gather
+    # float32 AUTO backward by the cost estimate: gather for the quick-start
+    # layers and the G = 20 / 50 grid sweep, matrix cores for the 1024-wide
+    # layer at G = 8
+    for (N, I, O, G, base) in [(1024, 784, 64, 8, 1), (1024, 64, 10, 8, 1), (32, 8, 4, 8, 0),
+                               (8192, 1024, 1024, 8, 0), (8192, 1024, 1024, 20, 0), (8192, 1024, 1024, 50, 0)]:
+        g = auto_bwd_gather(N, I, O, G + 3 + base)
+        want = wb(N=N, I=I, O=O, G=G, has_base=base, dtype=L.KAN_F32,
+                  variant=L.KAN_VARIANT_GATHER if g else L.KAN_VARIANT_MFMA)
+        assert wb(N=N, I=I, O=O, G=G, has_base=base, variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_F32) == want
+    assert auto_bwd_gather(1024, 784, 64, 12) and auto_bwd_gather(8192, 1024, 1024, 23)
+    assert not auto_bwd_gather(8192, 1024, 1024, 11)
     assert ws(variant=L.KAN_VARIANT_AUTO, dtype=L.KAN_BF16) == ws(variant=L.KAN_VARIANT_MFMA,
                                                                    dtype=L.KAN_BF16) > 0
 
@@ -287,10 +348,11 @@ def test_workspace_sizes_other_degrees(L):
                 d = desc(L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, degree=D, variant=v)
                 gather_f = v == L.KAN_VARIANT_GATHER or (v == L.KAN_VARIANT_AUTO and dt == L.KAN_F32)
                 gather_b = v == L.KAN_VARIANT_GATHER or (v == L.KAN_VARIANT_AUTO and dt == L.KAN_F32
-                                                         and N * I * O < 1 << 16)
+                                                         and auto_bwd_gather(N, I, O, Kb))
                 assert L.lib().kan_workspace_size(ctypes.byref(d), 0) == (
                     gather_fwd_ws(N, I, O, G + D, D, base) if gather_f else want_f)
-                assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == (0 if gather_b else want_b)
+                assert L.lib().kan_workspace_size(ctypes.byref(d), 1) == (
+                    gather_bwd_ws(N, I, O, G + D, base) if gather_b else want_b)
     # too few columns for the matrix cores (degree 1, G = 1, no base branch:
     # 2 per input): AUTO takes the gather kernels in both dtypes
     for dt in (L.KAN_F32, L.KAN_BF16):
