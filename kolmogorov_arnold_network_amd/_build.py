@@ -16,7 +16,7 @@ INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libkan_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["kan_api.cpp", "kan_gather.hip", "kan_grouped.hip", "kan_mfma.hip", "kan_static.hip"]
+SOURCES = ["kan_api.cpp", "kan_plan.cpp", "kan_gather.hip", "kan_grouped.hip", "kan_mfma.hip", "kan_static.hip"]
 
 # -packed-fp32-ops off: the compiler must not form packed float32 ALU ops.
 HIPCC_FLAGS = [

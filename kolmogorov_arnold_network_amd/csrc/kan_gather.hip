@@ -220,7 +220,7 @@ __device__ __forceinline__ RecD<D> zero_rec() {
 // - With too few blocks to fill the GPU the inputs are split into slices.
 //   Each slice writes float64 partial outputs, which gather_sum_kernel adds
 //   in slice order.
-constexpr int GF_TJ = 64;
+constexpr int GF_TJ = kGatherFwdOutputs;
 
 template <int D>
 struct alignas(8) RecF {
@@ -489,7 +489,7 @@ __global__ void gather_sum_kernel(const double* __restrict__ part, float* __rest
 // part that grows with G) small next to the arithmetic.  With too few
 // blocks to fill the GPU the outputs are split into slices whose partial dx
 // are added in slice order (gather_sum_f32_kernel).
-constexpr int GX_NT = 1024, GX_R = 256, GX_TI = 16;
+constexpr int GX_NT = 1024, GX_R = kGatherDxRows, GX_TI = kGatherDxInputs;
 
 template <typename TS, int D, int JC>
 __global__ __launch_bounds__(GX_NT) void gather_dx_kernel(GatherDxArgs a) {
@@ -696,20 +696,21 @@ __global__ void gather_sum_f32_kernel(const float* __restrict__ part, float* __r
 }
 
 // ---------------------------------------------------------------------------
-// dC, dW_base.  Wave w of a block owns input i = (NT / 64) ib + w and its
-// lanes the block's 64 outputs j; every lane keeps the K sums dC[j, i, m] of
-// its (j, i) in registers (KMAX of them).  Rows come in chunks of 64: the
-// block stages dy[rows][64 outputs] in LDS, and lane l of each wave forms the
-// span and D + 1 weights of row l for the wave's input.  A row's span is then
-// the same in every lane of the wave, so the wave walks the spans
-// s = 0 .. K + D - 1 as a compile-time loop: a ballot selects the chunk's rows
-// whose span is s, and each adds dy[b, j] times its weights into the sums
-// m = s - D .. s, registers named at compile time.  Rows off the grid add
-// only their silu term.  There are no atomics and no shared accumulators;
-// the order of each sum is fixed by the data (rows by span, then by index).
-// With too few blocks to fill the GPU the rows are split into slices whose
-// partial sums are added in slice order.  Two chunk buffers, one barrier per
-// chunk.
+// dC, dW_base.  Wave w of a block owns input i = (NT / 64) ib + w and each of
+// its lanes OPL consecutive outputs j of the block's 64 OPL; every lane keeps
+// the K sums dC[j, i, m] of its (j, i) pairs in registers (KMAX of them per
+// output).  Rows come in chunks of 64: the block stages dy[rows][64 OPL
+// outputs] in LDS, and lane l of each wave forms the span and D + 1 weights
+// of row l for the wave's input.  A row's span is then the same in every lane
+// of the wave, so the wave walks the spans s = 0 .. K + D - 1 as a
+// compile-time loop: a ballot selects the chunk's rows whose span is s, and
+// each adds dy[b, j] times its weights into the sums m = s - D .. s,
+// registers named at compile time; the reads of a span's next row are issued
+// before the current row's FMAs.  Rows off the grid add only their silu term.
+// There are no atomics and no shared accumulators; the order of each sum is
+// fixed by the data (rows by span, then by index).  With too few blocks to
+// fill the GPU the rows are split into slices whose partial sums are added in
+// slice order.  Two chunk buffers, one barrier per chunk.
 template <int N0, int N1, class F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (N0 < N1) {
@@ -718,13 +719,15 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-constexpr int GC_RW = 8;                             // floats of a row record: w[0 .. D], silu at 7
+constexpr int GC_RW = kGatherDcRecord;               // floats of a row record: w[0 .. D], silu at 7
 
-template <int D, bool BASE, int KMAX, int NT>
+template <int D, bool BASE, int KMAX, int OPL, int NT>
 __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
     constexpr int NW = NT / 64;                      // inputs (waves) per block
-    constexpr int DSZ = 64 * 64, WSZ = NW * 64 * GC_RW;
+    constexpr int OB = 64 * OPL;                     // outputs per block
+    constexpr int DSZ = 64 * OB, WSZ = NW * 64 * GC_RW;
     constexpr int DV = DSZ / 4 / NT;                 // float4 dy pieces per thread
+    typedef float vecO __attribute__((ext_vector_type(OPL)));
     extern __shared__ float4 smem4[];
     float* smem = reinterpret_cast<float*>(smem4);
     const GridK g = a.g;
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
     const int bid = blockIdx.x, nfull = T / 8, rem = T % 8, xcd = bid % 8;
     const int id = xcd * nfull + min(xcd, rem) + bid / 8;
     const int ibk = id % a.IBN, ob = id / a.IBN;
-    const int i = ibk * NW + wave, j0 = ob * 64, j = j0 + lane;
+    const int i = ibk * NW + wave, j0 = ob * OB, jl = j0 + OPL * lane;
     const int slice = blockIdx.y;
     const int rs = slice * a.RS, re = min(N, rs + a.RS);
     const int nch = (re - rs + 63) / 64;
@@ -748,7 +751,7 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
         const int r0 = rs + 64 * c;
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
-            const int u = t + NT * v, row = u / 16, col = 4 * (u % 16);
+            const int u = t + NT * v, row = u / (OB / 4), col = 4 * (u % (OB / 4));
             const float* src = a.dy + (int64_t)min(r0 + row, N - 1) * O;
             if (vec) {
                 __builtin_memcpy(&dp[v], src + min(j0 + col, O - 4), 16);
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
         const int r0 = rs + 64 * c;
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
-            const int u = t + NT * v, row = u / 16, col = 4 * (u % 16);
+            const int u = t + NT * v, row = u / (OB / 4), col = 4 * (u % (OB / 4));
             float4 d = dp[v];
             const int jc = j0 + col;
             if (!vec || jc + 3 >= O) {
@@ -780,7 +783,7 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
                 d.w = jc + 3 < O ? d.w : 0.0f;
             }
             if (r0 + row >= re) d = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            *reinterpret_cast<float4*>(Ds + row * 64 + col) = d;
+            *reinterpret_cast<float4*>(Ds + row * OB + col) = d;
         }
         live = r0 + lane < re && i < I;
         const RecD<D> r = make_rec<false, D>(xp, g);
@@ -793,10 +796,14 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
         *reinterpret_cast<float4*>(Wr + lane * GC_RW + 4) = make_float4(wr[4], wr[5], wr[6], wr[7]);
     };
 
-    float acc[KMAX];
+    float acc[OPL][KMAX];
 #pragma unroll
-    for (int m = 0; m < KMAX; ++m) acc[m] = 0.0f;
-    float accw = 0.0f;
+    for (int o = 0; o < OPL; ++o)
+#pragma unroll
+        for (int m = 0; m < KMAX; ++m) acc[o][m] = 0.0f;
+    float accw[OPL];
+#pragma unroll
+    for (int o = 0; o < OPL; ++o) accw[o] = 0.0f;
     load(0);
     store(0, 0);
     __syncthreads();
@@ -806,22 +813,43 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
         const float* Ds = smem + (c & 1) * (DSZ + WSZ);
         const float* Wr = Ds + DSZ + wave * 64 * GC_RW;
         const int cur = span;
+        // one row's dy (this lane's outputs) and weights
+        auto rd = [&](int l, vecO& d, float4& w0, float4& w1) {
+            d = *reinterpret_cast<const vecO*>(Ds + l * OB + OPL * lane);
+            w0 = *reinterpret_cast<const float4*>(Wr + l * GC_RW);
+            w1 = *reinterpret_cast<const float4*>(Wr + l * GC_RW + 4);
+        };
         static_for<0, KMAX + D>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
             if (s < K + D) {
                 uint64_t mask = __ballot(cur == s);
-                while (mask) {
-                    const int l = __builtin_ctzll(mask);
+                if (mask) {
+                    int l = __builtin_ctzll(mask);
                     mask &= mask - 1;
-                    const float d = Ds[l * 64 + lane];
-                    const float4 w0 = *reinterpret_cast<const float4*>(Wr + l * GC_RW);
-                    const float4 w1 = *reinterpret_cast<const float4*>(Wr + l * GC_RW + 4);
-                    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-                    static_for<0, D + 1>([&](auto rc) {
-                        constexpr int r = decltype(rc)::value, m = s - D + r;
-                        if constexpr (m >= 0 && m < KMAX) acc[m] = __builtin_fmaf(d, w[r], acc[m]);
-                    });
-                    if constexpr (BASE) accw = __builtin_fmaf(d, w[7], accw);
+                    vecO d;
+                    float4 w0, w1;
+                    rd(l, d, w0, w1);
+                    while (true) {
+                        const bool next = mask != 0;
+                        const int ln = next ? __builtin_ctzll(mask) : l;
+                        mask &= mask - 1;
+                        vecO dn;
+                        float4 w0n, w1n;
+                        rd(ln, dn, w0n, w1n);        // ahead of this row's FMAs
+                        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                        for (int o = 0; o < OPL; ++o) {
+                            static_for<0, D + 1>([&](auto rc) {
+                                constexpr int r = decltype(rc)::value, m = s - D + r;
+                                if constexpr (m >= 0 && m < KMAX) acc[o][m] = __builtin_fmaf(d[o], w[r], acc[o][m]);
+                            });
+                            if constexpr (BASE) accw[o] = __builtin_fmaf(d[o], w[7], accw[o]);
+                        }
+                        if (!next) break;
+                        d = dn;
+                        w0 = w0n;
+                        w1 = w1n;
+                    }
                 }
             }
         });
@@ -831,22 +859,30 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
             while (mask) {
                 const int l = __builtin_ctzll(mask);
                 mask &= mask - 1;
-                accw = __builtin_fmaf(Ds[l * 64 + lane], Wr[l * GC_RW + 7], accw);
+                const vecO d = *reinterpret_cast<const vecO*>(Ds + l * OB + OPL * lane);
+                const float sv = Wr[l * GC_RW + 7];
+#pragma unroll
+                for (int o = 0; o < OPL; ++o) accw[o] = __builtin_fmaf(d[o], sv, accw[o]);
             }
         }
         if (more) store(c + 1, (c + 1) & 1);
         __syncthreads();
     }
-    if (i < I && j < O) {
+    if (i < I) {
         float* dC = a.cpart ? a.cpart + (int64_t)slice * O * I * K : a.dC;
         float* dW = a.wpart ? a.wpart + (int64_t)slice * O * I : a.dW;
-        if (dC) {
-            float* dst = dC + ((int64_t)j * I + i) * K;
 #pragma unroll
-            for (int m = 0; m < KMAX; ++m)
-                if (m < K) dst[m] = acc[m];
+        for (int o = 0; o < OPL; ++o) {
+            const int j = jl + o;
+            if (j >= O) continue;
+            if (dC) {
+                float* dst = dC + ((int64_t)j * I + i) * K;
+#pragma unroll
+                for (int m = 0; m < KMAX; ++m)
+                    if (m < K) dst[m] = acc[o][m];
+            }
+            if (BASE && dW) dW[(int64_t)j * I + i] = accw[o];
         }
-        if (BASE && dW) dW[(int64_t)j * I + i] = accw;
     }
 }
 
@@ -861,38 +897,6 @@ hipError_t allow_lds(Kern k, size_t bytes) {
 }
 
 }  // namespace
-
-GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int base) {
-    GatherFwdPlan q;
-    const int64_t ob = (O + GF_TJ - 1) / GF_TJ;
-    // 256-row blocks of 1024 threads when they still make 64 or more blocks
-    // (or when K is large, where staging dominates); 64-row blocks of 256
-    // threads for small batches
-    q.nt = ((N + 255) / 256 * ob >= 64 || K > 32) ? 1024 : 256;
-    const int R = q.nt / 4;
-    const int rw = ((D + 3) + 1) & ~1;                       // words of a span record
-    const int64_t per_in = (int64_t)GF_TJ * K + (base ? GF_TJ : 0) + (int64_t)R * rw;
-    // both chunk buffers within 150 KB (1024 threads, one block per CU) or
-    // 64 KB (256 threads, two or more per CU); a chunk row of at most 256 / 128
-    // coefficients per output, which the prefetch registers hold
-    const int64_t budget = (q.nt == 1024 ? 150 * 1024 : 64 * 1024) / 4;
-    const int lim = q.nt == 1024 ? 256 : 128;
-    int64_t ic = std::min<int64_t>(8, budget / (2 * per_in));
-    ic = std::min<int64_t>(ic, lim / K);
-    q.ic = (int)std::max<int64_t>(ic, 1);
-    q.lds = (size_t)(2 * q.ic * per_in * 4);
-    q.rb = (N + R - 1) / R;
-    q.ob = ob;
-    // fewer blocks than CUs: split the inputs, at least 8 per slice
-    const int64_t T = q.rb * q.ob;
-    int64_t S = 1;
-    if (N * I * O >= (int64_t(1) << 16) && T < 256)
-        S = std::max<int64_t>(1, std::min<int64_t>((256 + T - 1) / T, (I + 7) / 8));
-    q.is = (I + S - 1) / S;
-    q.split = (int)((I + q.is - 1) / q.is);
-    q.ws = q.split > 1 ? (size_t)round_up((int64_t)q.split * N * O * 8, 256) : 0;
-    return q;
-}
 
 template <int D>
 static hipError_t basis_deg_run(const GridK& g, int64_t n, int dtype, const void* x, float* B, float* dB,
@@ -992,50 +996,6 @@ hipError_t launch_gather_fwd(const Plan& p, const void* x, const void* C, const 
     return hipGetLastError();
 }
 
-GatherBwdPlan gather_bwd_plan(int64_t N, int64_t I, int64_t O, int K, int base) {
-    GatherBwdPlan q;
-    const int64_t target = 256;                       // blocks that fill the CUs once
-    const bool big = N * I * O >= (int64_t(1) << 16);
-    // dx: the widest output chunk whose two buffers fit in 150 KB of LDS
-    q.jc = 4;
-    for (int jc : {16, 8}) {
-        const int64_t floats = 2 * ((int64_t)GX_R * jc + (int64_t)GX_TI * K * (jc + 4) + GX_TI * (jc + 4));
-        if (floats * 4 <= 150 * 1024) { q.jc = jc; break; }
-    }
-    q.lds_dx = (size_t)(2 * ((int64_t)GX_R * q.jc + (int64_t)GX_TI * K * (q.jc + 4) + GX_TI * (q.jc + 4)) * 4);
-    q.rb = (N + GX_R - 1) / GX_R;
-    q.ib = (I + GX_TI - 1) / GX_TI;
-    int64_t sx = 1;
-    if (big && q.rb * q.ib < target)
-        sx = std::max<int64_t>(1, std::min((target + q.rb * q.ib - 1) / (q.rb * q.ib), (O + 4 * q.jc - 1) / (4 * q.jc)));
-    q.js = ((O + sx - 1) / sx + q.jc - 1) / q.jc * q.jc;
-    q.sx = (int)((O + q.js - 1) / q.js);
-    // dC: KMAX register sums per lane; waves of one block share a dy chunk
-    q.kmax = K <= 16 ? 16 : K <= 32 ? 32 : K <= 64 ? 64 : 132;    // K <= 125 + 5
-    q.nt_dc = q.kmax <= 64 ? 1024 : 512;
-    const int nw = q.nt_dc / 64;
-    q.ibn = (I + nw - 1) / nw;
-    q.ob = (O + 63) / 64;
-    q.lds_dc = (size_t)(2 * (64 * 64 + nw * 64 * GC_RW) * 4);
-    int64_t sc = 1;
-    if (big && q.ibn * q.ob < target)
-        sc = std::max<int64_t>(1, std::min((target + q.ibn * q.ob - 1) / (q.ibn * q.ob), (N + 127) / 128));
-    q.rs = std::max<int64_t>(64, ((N + sc - 1) / sc + 63) / 64 * 64);
-    q.sc = (int)std::max<int64_t>(1, (N + q.rs - 1) / q.rs);
-    // workspace: dx partials, then dC and dW_base partials
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t o = off;
-        off += (size_t)round_up((int64_t)bytes, 256);
-        return o;
-    };
-    q.off_dxp = q.sx > 1 ? take((size_t)q.sx * N * I * 4) : 0;
-    q.off_dcp = q.sc > 1 ? take((size_t)q.sc * O * I * K * 4) : 0;
-    q.off_dwp = q.sc > 1 && base ? take((size_t)q.sc * O * I * 4) : 0;
-    q.ws = off;
-    return q;
-}
-
 template <typename TS, int D, int JC>
 static hipError_t gather_dx_run(const Plan& p, const GatherDxArgs& a, hipStream_t s) {
     auto k = gather_dx_kernel<TS, D, JC>;
@@ -1063,10 +1023,10 @@ static hipError_t gather_dx_deg(const Plan& p, const GatherDxArgs& a, hipStream_
     }
 }
 
-template <int D, bool BASE, int KMAX>
+template <int D, bool BASE, int KMAX, int OPL>
 static hipError_t gather_dc_run(const Plan& p, const GatherDcArgs& a, hipStream_t s) {
-    constexpr int NT = KMAX <= 64 ? 1024 : 512;
-    auto k = gather_dc_kernel<D, BASE, KMAX, NT>;
+    constexpr int NT = KMAX * OPL <= 64 ? 1024 : 512;
+    auto k = gather_dc_kernel<D, BASE, KMAX, OPL, NT>;
     hipError_t e = allow_lds(k, p.gb.lds_dc);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)(p.gb.ibn * p.gb.ob), (unsigned)p.gb.sc), dim3(NT), p.gb.lds_dc, s, a);
@@ -1075,11 +1035,12 @@ static hipError_t gather_dc_run(const Plan& p, const GatherDcArgs& a, hipStream_
 
 template <int D, bool BASE>
 static hipError_t gather_dc_kmax(const Plan& p, const GatherDcArgs& a, hipStream_t s) {
+    const bool two = p.gb.opl == 2;
     switch (p.gb.kmax) {
-        case 16: return gather_dc_run<D, BASE, 16>(p, a, s);
-        case 32: return gather_dc_run<D, BASE, 32>(p, a, s);
-        case 64: return gather_dc_run<D, BASE, 64>(p, a, s);
-        default: return gather_dc_run<D, BASE, 132>(p, a, s);
+        case 16: return two ? gather_dc_run<D, BASE, 16, 2>(p, a, s) : gather_dc_run<D, BASE, 16, 1>(p, a, s);
+        case 32: return two ? gather_dc_run<D, BASE, 32, 2>(p, a, s) : gather_dc_run<D, BASE, 32, 1>(p, a, s);
+        case 64: return gather_dc_run<D, BASE, 64, 1>(p, a, s);
+        default: return gather_dc_run<D, BASE, 132, 1>(p, a, s);
     }
 }
 

@@ -32,11 +32,11 @@ namespace kan {
 
 namespace {
 
-constexpr int GP_C = 64;                // channels per block (one per lane)
-constexpr int GP_W = 4;                 // row waves per block
+constexpr int GP_C = kGroupChannels;    // channels per block (one per lane)
+constexpr int GP_W = kGroupWaves;       // row waves per block
 constexpr int GP_T = GP_C * GP_W;       // threads per block
-constexpr int GP_UF = 16;               // rows whose loads a forward thread issues together
-constexpr int GP_UB = 8;                // the same, backward
+constexpr int GP_UF = kGroupRowsFwd;    // rows whose loads a forward thread issues together
+constexpr int GP_UB = kGroupRowsBwd;    // the same, backward
 constexpr size_t kTabLimit = 32 * 1024; // LDS bytes for the per-span table
 
 // p[i] for a wave-uniform row base p and a lane's channel i, as a 32-bit
@@ -417,27 +417,6 @@ hipError_t bwd_t(const GridK& g, const GroupPlan& gp, int64_t N, int64_t I, int 
 }
 
 }  // namespace
-
-// Row chunks.  The forward aims at 2048 blocks (8 per CU, one round).  The
-// backward aims at 1024 (4 per CU) and gives every chunk at least
-// max(64, 24 K) rows, so that the partials (K floats per channel per chunk,
-// written and read back) stay within about 1/30 of the traffic of x, dy and
-// dx.  Chunks are whole multiples of the rows a block's waves take per step.
-GroupPlan grouped_plan(int64_t N, int64_t I, int K) {
-    GroupPlan gp;
-    gp.xb = (I + GP_C - 1) / GP_C;
-    auto chunk = [&](int64_t blocks, int64_t rmin, int64_t step) {
-        const int64_t gy = std::max<int64_t>(1, blocks / gp.xb);
-        return round_up(std::max<int64_t>(rmin, (N + gy - 1) / gy), step);
-    };
-    gp.rows_fwd = chunk(2048, 1, GP_W * GP_UF);
-    gp.rows_bwd = chunk(1024, std::max<int64_t>(64, 24 * (int64_t)K), GP_W * GP_UB);
-    gp.gy_fwd = (N + gp.rows_fwd - 1) / gp.rows_fwd;
-    gp.gy_bwd = (N + gp.rows_bwd - 1) / gp.rows_bwd;
-    gp.part_floats = gp.gy_bwd * K * I;
-    gp.red_floats = (int64_t)K * I;
-    return gp;
-}
 
 hipError_t launch_grouped_fwd(const GridK& g, int64_t N, int64_t I, int groups, int dtype,
                               const void* x, const void* C, float* y, hipStream_t s) {

@@ -21,6 +21,17 @@ constexpr int kTileKBytes = 128;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// Block geometry of the vector-ALU kernels, shared with their host plans
+// (kan_plan.cpp).
+constexpr int kGatherFwdOutputs = 64;   // local-gather forward: outputs per block
+constexpr int kGatherDxRows = 256;      // local-gather dx: rows per block
+constexpr int kGatherDxInputs = 16;     // local-gather dx: inputs per block
+constexpr int kGatherDcRecord = 8;      // local-gather dC: floats of a row's weight record
+constexpr int kGroupChannels = 64;      // grouped activation: channels per block (one per lane)
+constexpr int kGroupWaves = 4;          // grouped activation: row waves per block
+constexpr int kGroupRowsFwd = 16;       // grouped forward: rows whose loads a thread issues together
+constexpr int kGroupRowsBwd = 8;        // grouped backward: the same
+
 // Local-gather forward: blocks of nt threads compute nt / 4 rows by 64
 // outputs, staging ic inputs per chunk in lds bytes of LDS; the inputs are
 // cut into `split` slices of `is` inputs (split > 1: float64 partial outputs
@@ -36,11 +47,11 @@ GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int
 // inputs (rb x ib blocks), summing over outputs in chunks of jc staged in
 // lds_dx bytes; the outputs are cut into sx slices of js (sx > 1: float32
 // partial dx [sx][N][I] at off_dxp).  dC: blocks of nt_dc threads, one input
-// per wave and 64 outputs (ibn x ob blocks), kmax register sums per lane,
+// per wave and 64 opl outputs (ibn x ob blocks), kmax register sums per output,
 // lds_dc bytes; the rows are cut into sc slices of rs (sc > 1: partial dC
 // [sc][O][I][K] at off_dcp and dW_base [sc][O][I] at off_dwp).
 struct GatherBwdPlan {
-    int jc, sx, kmax, nt_dc, sc;
+    int jc, sx, kmax, opl, nt_dc, sc;
     int64_t rb, ib, js, ibn, ob, rs;
     size_t lds_dx, lds_dc, off_dxp, off_dcp, off_dwp, ws;
 };

@@ -80,7 +80,9 @@ def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
     return L.lib().kan_backward(ctypes.byref(d), x, c, w, dy, dx, dc, dw, ws, nbytes, None)
 
 
-@pytest.mark.parametrize("kw,code", [
+# Layer descriptors every entry point must reject, with the status.  Also
+# the cases tests/test_host_sanitize.py runs through the sanitizer build.
+BAD_DESCS = [
     (dict(N=-1), "SHAPE"), (dict(I=0), "SHAPE"), (dict(O=0), "SHAPE"), (dict(N=1 << 40), "SHAPE"),
     (dict(G=0), "GRID"), (dict(G=126), "GRID"), (dict(G=5000), "GRID"), (dict(lo=1.0, hi=1.0), "GRID"),
     (dict(lo=2.0, hi=1.0), "GRID"), (dict(lo=float("nan")), "GRID"), (dict(hi=float("inf")), "GRID"),
@@ -89,7 +91,27 @@ def bwd(L, d, x=X, c=C, w=W, dy=DY, dx=DX, dc=DC, dw=DW, ws=WS, nbytes=None):
     (dict(degree=1, G=1, has_base=0, dtype=1), "UNSUPPORTED"),  # the same in bf16
     (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
     (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
-])
+]
+
+# Pointer, alignment, workspace and overlap errors of one valid layer
+# (desc() changes, call changes, status).
+FWD_POINTER_CASES = [
+    ({}, dict(x=None), "NULL"), ({}, dict(y=None), "NULL"), ({}, dict(c=None), "NULL"),
+    ({}, dict(w=None), "NULL"),                                 # has_base=1 needs W
+    (dict(has_base=0), {}, "NULL"),                             # has_base=0 forbids W
+    ({}, dict(x=X + 8), "ALIGN"), ({}, dict(y=Y + 4), "ALIGN"), ({}, dict(ws=WS + 128), "ALIGN"),
+    ({}, dict(nbytes=16), "WORKSPACE"), ({}, dict(ws=None), "NULL"),
+    ({}, dict(y=X + 64), "ALIAS"), ({}, dict(y=C), "ALIAS"), ({}, dict(ws=Y), "ALIAS"),
+]
+BWD_POINTER_CASES = [
+    ({}, dict(dy=None), "NULL"), ({}, dict(x=None), "NULL"),
+    (dict(has_base=0), dict(w=None), "NULL"),                   # dW given without base
+    ({}, dict(dy=DY + 2), "ALIGN"), ({}, dict(dc=DC + 4), "ALIGN"), ({}, dict(nbytes=0), "WORKSPACE"),
+    ({}, dict(dx=DC), "ALIAS"), ({}, dict(dw=DY), "ALIAS"), ({}, dict(dc=X), "ALIAS"), ({}, dict(ws=DX), "ALIAS"),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DESCS)
 def test_bad_descriptors(L, kw, code):
     d = desc(L, **kw)
     want = getattr(L, "KAN_ERR_" + code)
@@ -130,34 +152,13 @@ def test_null_desc(L):
 
 
 def test_forward_pointer_checks(L):
-    d = desc(L)
-    assert fwd(L, d, x=None) == L.KAN_ERR_NULL
-    assert fwd(L, d, y=None) == L.KAN_ERR_NULL
-    assert fwd(L, d, c=None) == L.KAN_ERR_NULL
-    assert fwd(L, d, w=None) == L.KAN_ERR_NULL                     # has_base=1 needs W
-    assert fwd(L, desc(L, has_base=0)) == L.KAN_ERR_NULL          # has_base=0 forbids W
-    assert fwd(L, d, x=X + 8) == L.KAN_ERR_ALIGN
-    assert fwd(L, d, y=Y + 4) == L.KAN_ERR_ALIGN
-    assert fwd(L, d, ws=WS + 128) == L.KAN_ERR_ALIGN
-    assert fwd(L, d, nbytes=16) == L.KAN_ERR_WORKSPACE
-    assert fwd(L, d, ws=None) == L.KAN_ERR_NULL
-    assert fwd(L, d, y=X + 64) == L.KAN_ERR_ALIAS
-    assert fwd(L, d, y=C) == L.KAN_ERR_ALIAS
-    assert fwd(L, d, ws=Y) == L.KAN_ERR_ALIAS
+    for dkw, ckw, code in FWD_POINTER_CASES:
+        assert fwd(L, desc(L, **dkw), **ckw) == getattr(L, "KAN_ERR_" + code), (dkw, ckw)
 
 
 def test_backward_pointer_checks(L):
-    d = desc(L)
-    assert bwd(L, d, dy=None) == L.KAN_ERR_NULL
-    assert bwd(L, d, x=None) == L.KAN_ERR_NULL
-    assert bwd(L, desc(L, has_base=0), w=None) == L.KAN_ERR_NULL  # dW given without base
-    assert bwd(L, d, dy=DY + 2) == L.KAN_ERR_ALIGN
-    assert bwd(L, d, dc=DC + 4) == L.KAN_ERR_ALIGN
-    assert bwd(L, d, nbytes=0) == L.KAN_ERR_WORKSPACE
-    assert bwd(L, d, dx=DC) == L.KAN_ERR_ALIAS
-    assert bwd(L, d, dw=DY) == L.KAN_ERR_ALIAS
-    assert bwd(L, d, dc=X) == L.KAN_ERR_ALIAS
-    assert bwd(L, d, ws=DX) == L.KAN_ERR_ALIAS
+    for dkw, ckw, code in BWD_POINTER_CASES:
+        assert bwd(L, desc(L, **dkw), **ckw) == getattr(L, "KAN_ERR_" + code), (dkw, ckw)
 
 
 def test_empty_batch_forward_returns_ok_without_launch(L):
@@ -234,8 +235,9 @@ def gather_bwd_ws(N, I, O, K, base):
     js = r((O + sx - 1) // sx, jc)
     sx = (O + js - 1) // js
     kmax = 16 if K <= 16 else 32 if K <= 32 else 64 if K <= 64 else 132
-    nw = (1024 if kmax <= 64 else 512) // 64
-    T = (I + nw - 1) // nw * ((O + 63) // 64)
+    opl = 2 if kmax <= 32 and O > 64 else 1
+    nw = (1024 if kmax * opl <= 64 else 512) // 64
+    T = (I + nw - 1) // nw * ((O + 64 * opl - 1) // (64 * opl))
     sc = max(1, min((256 + T - 1) // T, (N + 127) // 128)) if big and T < 256 else 1
     rs = max(64, r((N + sc - 1) // sc, 64))
     sc = max(1, (N + rs - 1) // rs)
@@ -435,10 +437,13 @@ def test_group_workspace_sizes(L):
     assert f(gdesc(L, N=10, I=(1 << 31) // 11, groups=1, G=8)) == bad     # I * (G+3) beyond the index range
 
 
-@pytest.mark.parametrize("kw,code", [
+GROUP_BAD_DESCS = [
     (dict(N=-1), -2), (dict(I=0), -2), (dict(groups=0), -2), (dict(groups=301), -2),
     (dict(N=1 << 40), -2), (dict(G=0), -3), (dict(G=126), -3), (dict(lo=1.0, hi=1.0), -3),
-    (dict(lo=float("nan")), -3), (dict(dtype=2), -4), (dict(degree=2), -8)])
+    (dict(lo=float("nan")), -3), (dict(dtype=2), -4), (dict(degree=2), -8)]
+
+
+@pytest.mark.parametrize("kw,code", GROUP_BAD_DESCS)
 def test_group_bad_descriptors(L, kw, code):
     d = gdesc(L, **kw)
     lib = L.lib()
@@ -506,10 +511,13 @@ def test_surface_workspace_sizes(L):
     assert L.lib().kan_surface_workspace_size(None, 0) == bad
 
 
-@pytest.mark.parametrize("kw,code", [
+SURFACE_BAD_DESCS = [
     (dict(N=-1), -2), (dict(P=0), -2), (dict(O=0), -2), (dict(G=0), -3), (dict(G=14), -3),
     (dict(lo=1.0, hi=0.5), -3), (dict(hi=float("inf")), -3), (dict(dtype=5), -4), (dict(degree=1), -8),
-    (dict(flags=4), -8), (dict(P=1 << 30), -2)])
+    (dict(flags=4), -8), (dict(P=1 << 30), -2)]
+
+
+@pytest.mark.parametrize("kw,code", SURFACE_BAD_DESCS)
 def test_surface_bad_descriptors(L, kw, code):
     d = sdesc(L, **kw)
     lib = L.lib()
