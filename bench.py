@@ -311,7 +311,20 @@ def main():
     I, O = widths[dl], widths[dl + 1]
     alg_dom = 2.0 * N * I * O * (D + 1 + (1 if base else 0))
     exe_dom = 2.0 * N * I * O * (fwd_cols if dom.endswith(".fwd") else Kb)
-    mfma_path = args.variant == "mfma" or (args.variant == "auto" and (dt == "bf16" or D != 3))
+    # which kernel family ran the dominant stage: the variant asked for, or
+    # AUTO's rule (include/kan.h, kan_variant_t): bf16 on the matrix cores;
+    # float32 forward on the gather kernel, float32 backward by its cost estimate
+    Kb_dom = G + D + (1 if base else 0)
+    mfma_ok = Kb_dom <= 256 and (D == 3 or Kb_dom >= 4)
+    if args.variant != "auto":
+        mfma_path = args.variant == "mfma"
+    elif dt == "bf16":
+        mfma_path = mfma_ok
+    elif dom.endswith(".fwd"):
+        mfma_path = False
+    else:
+        nio = float(N) * I * O
+        mfma_path = mfma_ok and 4.0 * nio * Kb_dom / 110e12 + 150e-6 < nio / 1.6e12
     peak = PEAK_TFLOPS[dt]
     t_dom = stage_ms[dom] * 1e-3
     roof = {
@@ -653,28 +666,46 @@ def read_traffic(workload, kernel, files=MFMA_FILES):
         return None
 
 
-def cpu_baseline(d, rows=None):
-    """The float64 NumPy oracle on a bounded sample of the same workload: y, dx
-    and the sample rows' own dC / dW_base contributions, timed on the host."""
-    import numpy as np
+# rows per oracle sample: the sizes the parity tests check each workload on
+# (c1, c2: every row; c3: 512; c4: 256; c5: 128)
+SAMPLE_ROWS = {"c1": 32, "c2": 1024, "c3": 512, "c4": 256, "c5": 128}
+
+
+def cpu_baseline(d, rows=None, budget_s=10.0):
+    """The float64 NumPy oracle on bounded samples of the same workload: y, dx
+    and the sample rows' own dC / dW_base contributions, timed on the host.
+    Seeded subsets of the parity sample size are run one after another until
+    about ``budget_s`` seconds have passed, with BLAS on every host thread;
+    then one subset again with BLAS on a single thread."""
     import oracle
     import workloads as wl
-    cores = _cpu_threads()
+    from threadpoolctl import threadpool_limits
     N = d["N"]
-    default_rows = {"c1": 32, "c2": 1024, "c3": 1024, "c4": 1024, "c5": 2048}
-    n = min(N, rows or default_rows[d["name"]])
-    R = wl.sample_indices(N, n, 99)
+    n = min(N, rows or SAMPLE_ROWS[d["name"]])
     lo, hi, G = d["lo"], d["hi"], d["G"]
     bf = d["dtype"] == "bf16"
-    t0 = time.perf_counter()
     k = d["layers"][0][0].shape[2] - G                     # spline degree
-    acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf, k=k)
-    oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G, k=k)
-    dt = time.perf_counter() - t0
+
+    def one(seed):
+        R = wl.sample_indices(N, n, seed)
+        t0 = time.perf_counter()
+        acts = oracle.network_forward(d["x"][R], d["layers"], lo, hi, G, bf16_between=bf, k=k)
+        oracle.network_backward(acts, d["layers"], d["dy"][R], lo, hi, G, k=k)
+        return time.perf_counter() - t0
+
+    cores = _cpu_threads()
+    total, reps = 0.0, 0
+    while reps == 0 or (total < budget_s and reps < 64):
+        total += one(99 + reps)
+        reps += 1
+    with threadpool_limits(limits=1):
+        t1 = one(99)
     model = _cpu_model()
-    return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d rows: forward and backward (dx, and the rows' own dC/dW_base "
-                      "contributions) in float64 NumPy, %.1f s; CPU %s" % (n, N, dt, model)}
+    return {"value": reps * n / total, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "single_core_value": n / t1,
+            "sample": "%d seeded subset(s) of %d of %d rows (forward and backward: dx, and the rows' own "
+                      "dC/dW_base contributions) in float64 NumPy, %.1f s on %d threads; one subset on 1 "
+                      "thread, %.1f s; CPU %s" % (reps, n, N, total, cores, t1, model)}
 
 
 if __name__ == "__main__":

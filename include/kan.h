@@ -91,9 +91,9 @@ typedef enum { KAN_F32 = 0, KAN_BF16 = 1 } kan_dtype_t;
  * forward adds the partial sums of chunks of at most 8 inputs in float64.
  * AUTO picks per pass: bf16 runs both passes on MFMA; float32 runs the forward
  * on GATHER and the backward on whichever family is estimated faster: GATHER
- * (about N*I*O / 2.5e12 s, independent of G) or MFMA (about
- * 2*N*I*O*(G+D+has_base) / 110e12 s + 75 us), that is GATHER for small
- * layers and from about 22 columns per input up; GATHER wherever MFMA does
+ * (about N*I*O / 1.6e12 s, independent of G) or MFMA (about
+ * 4*N*I*O*(G+D+has_base) / 110e12 s + 150 us), that is GATHER for small
+ * layers and from about 17 columns per input up; GATHER wherever MFMA does
  * not fit. */
 typedef enum { KAN_VARIANT_AUTO = 0, KAN_VARIANT_MFMA = 1, KAN_VARIANT_GATHER = 2 } kan_variant_t;
 

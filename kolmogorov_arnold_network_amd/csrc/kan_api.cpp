@@ -196,11 +196,11 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     // forward on the local gather kernel, whose sums over inputs are float64
     // and which touches only the D + 1 non-zero basis functions.  Its
     // backward takes whichever of the two kernel families the measured rates
-    // make faster: the gather dx / dC do about 2.5e12 edge-rows (N I O) per
-    // second whatever K is; the dense float32 contractions execute 2 N I O Kb
-    // flops at about 110 TFLOP/s, plus about 75 us of packing, epilogue and
-    // launches per pass.  So the gather backward wins from Kb of about 22 up,
-    // and on small layers at any Kb.
+    // make faster: the gather dx and dC together do about 1.6e12 edge-rows
+    // (N I O) per second whatever K is; the two dense float32 contractions
+    // execute 4 N I O Kb flops at about 110 TFLOP/s, plus about 150 us of
+    // packing, epilogues and launches.  So the gather backward wins from Kb of
+    // about 17 up, and on small layers at any Kb.
     const bool mfma_ok = q.Kb <= kTileN && (q.degree == 3 || q.Kb >= 4);
     if (d->variant == KAN_VARIANT_MFMA && !mfma_ok) return KAN_ERR_UNSUPPORTED;
     if (d->variant == KAN_VARIANT_GATHER) {
@@ -210,7 +210,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     } else {
         q.variant_fwd = (mfma_ok && q.dtype == KAN_BF16) ? KAN_VARIANT_MFMA : KAN_VARIANT_GATHER;
         const double nio = (double)q.N * (double)q.I * (double)q.O;
-        const double t_gather = nio / 2.5e12, t_mfma = 2.0 * nio * q.Kb / 110e12 + 75e-6;
+        const double t_gather = nio / 1.6e12, t_mfma = 4.0 * nio * q.Kb / 110e12 + 150e-6;
         q.variant_bwd = mfma_ok && (q.dtype == KAN_BF16 || t_mfma < t_gather) ? KAN_VARIANT_MFMA
                                                                                : KAN_VARIANT_GATHER;
     }

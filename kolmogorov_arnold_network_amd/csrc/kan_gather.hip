@@ -705,8 +705,8 @@ __global__ void gather_sum_f32_kernel(const float* __restrict__ part, float* __r
 // of the wave, so the wave walks the spans s = 0 .. K + D - 1 as a
 // compile-time loop: a ballot selects the chunk's rows whose span is s, and
 // each adds dy[b, j] times its weights into the sums m = s - D .. s,
-// registers named at compile time; the reads of a span's next row are issued
-// before the current row's FMAs.  Rows off the grid add only their silu term.
+// registers named at compile time.  Rows off the grid add only their silu
+// term.
 // There are no atomics and no shared accumulators; the order of each sum is
 // fixed by the data (rows by span, then by index).  With too few blocks to
 // fill the GPU the rows are split into slices whose partial sums are added in
@@ -823,32 +823,20 @@ __global__ __launch_bounds__(NT) void gather_dc_kernel(GatherDcArgs a) {
             constexpr int s = decltype(sc)::value;
             if (s < K + D) {
                 uint64_t mask = __ballot(cur == s);
-                if (mask) {
-                    int l = __builtin_ctzll(mask);
+                while (mask) {
+                    const int l = __builtin_ctzll(mask);
                     mask &= mask - 1;
                     vecO d;
                     float4 w0, w1;
                     rd(l, d, w0, w1);
-                    while (true) {
-                        const bool next = mask != 0;
-                        const int ln = next ? __builtin_ctzll(mask) : l;
-                        mask &= mask - 1;
-                        vecO dn;
-                        float4 w0n, w1n;
-                        rd(ln, dn, w0n, w1n);        // ahead of this row's FMAs
-                        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                        for (int o = 0; o < OPL; ++o) {
-                            static_for<0, D + 1>([&](auto rc) {
-                                constexpr int r = decltype(rc)::value, m = s - D + r;
-                                if constexpr (m >= 0 && m < KMAX) acc[o][m] = __builtin_fmaf(d[o], w[r], acc[o][m]);
-                            });
-                            if constexpr (BASE) accw[o] = __builtin_fmaf(d[o], w[7], accw[o]);
-                        }
-                        if (!next) break;
-                        d = dn;
-                        w0 = w0n;
-                        w1 = w1n;
+                    for (int o = 0; o < OPL; ++o) {
+                        static_for<0, D + 1>([&](auto rc) {
+                            constexpr int r = decltype(rc)::value, m = s - D + r;
+                            if constexpr (m >= 0 && m < KMAX) acc[o][m] = __builtin_fmaf(d[o], w[r], acc[o][m]);
+                        });
+                        if constexpr (BASE) accw[o] = __builtin_fmaf(d[o], w[7], accw[o]);
                     }
                 }
             }

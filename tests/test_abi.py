@@ -248,10 +248,10 @@ def gather_bwd_ws(N, I, O, K, base):
 
 
 def auto_bwd_gather(N, I, O, Kb):
-    """float32 AUTO backward: gather when its estimate (N I O / 2.5e12 s) is
-    below the dense contraction's (2 N I O Kb / 110e12 s + 75 us)."""
+    """float32 AUTO backward: gather when its estimate (N I O / 1.6e12 s) is
+    below the dense contractions' (4 N I O Kb / 110e12 s + 150 us)."""
     nio = float(N) * I * O
-    return not (2.0 * nio * Kb / 110e12 + 75e-6 < nio / 2.5e12)
+    return not (4.0 * nio * Kb / 110e12 + 150e-6 < nio / 1.6e12)
 
 
 def fwd_slices(nt_tiles, nkt, out_bytes, es):
