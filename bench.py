@@ -64,6 +64,9 @@ def parse():
                     help="spline degree (1 .. 5) of the layer workloads and of --basis-forms")
     ap.add_argument("--basis-forms", type=int, default=0, metavar="POINTS",
                     help="time the local-span and truncated-power basis evaluations on POINTS inputs")
+    ap.add_argument("--forward-forms", action="store_true",
+                    help="time the bf16 matrix-core forward with its three operand generators "
+                         "(2:4 sparse, span-based dense, truncated-power dense) on the bf16 layer shapes")
     ap.add_argument("--blas-reference", action="store_true",
                     help="time plain bf16 torch.matmul on the c5 contraction shapes and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -107,6 +110,54 @@ def basis_forms(n, steps, degree=3):
                                           "output_GB_per_s": out_bytes / (ms * 1e-3) / 1e9,
                                           "hbm_frac": out_bytes / (ms * 1e-3) / 8e12}
     print(json.dumps({"basis_forms": res, "points": n, "steps": steps, "degree": degree}))
+
+
+def forward_forms(steps):
+    """The bf16 layer forward on the matrix cores with each of its three A
+    operand generators -- the 2:4 structured-sparse one (default), the dense
+    span-based one (KAN_FLAG_DENSE_FORWARD) and the dense truncated-power one
+    (KAN_FLAG_TP_FORWARD) -- on the layer shapes of the bf16 workloads and of
+    the grid sweep at bf16: ms per forward and the output's relative Frobenius
+    distance from the span-based dense forward.  Inputs are drawn on the
+    device: x ~ U(-1, 1), C ~ N(0, 0.02), W_base ~ N(0, 1/in)."""
+    import torch
+    from kolmogorov_arnold_network_amd import _lib as L
+    from kolmogorov_arnold_network_amd import functional as F
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    res = []
+    for name, N, I, O, G in (("768->3072 (12608 rows, G=5)", 12608, 768, 3072, 5),
+                             ("3072->768 (12608 rows, G=5)", 12608, 3072, 768, 5),
+                             ("1024->1024 (8192 rows, G=8)", 8192, 1024, 1024, 8),
+                             ("1024->1024 (8192 rows, G=20)", 8192, 1024, 1024, 20),
+                             ("1024->1024 (8192 rows, G=50)", 8192, 1024, 1024, 50),
+                             ("4096->4096 (65536 rows, G=20)", 65536, 4096, 4096, 20)):
+        x = (torch.rand(N, I, device=dev, generator=g) * 2 - 1).to(torch.bfloat16)
+        C = (torch.randn(O, I, G + 3, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        W = (torch.randn(O, I, device=dev, generator=g) / I ** 0.5).to(torch.bfloat16)
+        grid = (-1.0, 1.0, G)
+        row = {"layer": name}
+        ys = {}
+        for form, kw in (("sparse", {}), ("dense", {"dense_forward": True}), ("tp", {"tp_forward": True})):
+            flags = F._fwd_flags(kw.get("dense_forward", False), kw.get("tp_forward", False))
+            ws = F.workspace(F.layer_desc(x, C, W, grid, "mfma", flags), L.KAN_PASS_FORWARD, dev)
+            y = F.kan_forward(x, C, W, grid, "mfma", ws=ws, **kw)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                F.kan_forward(x, C, W, grid, "mfma", ws=ws, out=y, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            row[form + "_ms"] = e0.elapsed_time(e1) / steps
+            ys[form] = y
+        for form in ("sparse", "tp"):
+            row[form + "_vs_dense"] = float((ys[form] - ys["dense"]).norm() / ys["dense"].norm())
+        res.append(row)
+        print(json.dumps(row), flush=True)
+        del x, C, W, ys, y, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"forward_forms": res, "steps": steps}))
 
 
 def blas_reference(steps):
@@ -166,6 +217,9 @@ def main():
         return
     if args.blas_reference:
         blas_reference(args.steps)
+        return
+    if args.forward_forms:
+        forward_forms(args.steps)
         return
     if args.basis_forms:
         basis_forms(args.basis_forms, args.steps, args.degree)

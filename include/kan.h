@@ -126,7 +126,7 @@ typedef struct {
     int32_t dtype;     /* kan_dtype_t: storage of x, C, W_base */
     int32_t has_base;  /* 0 or 1 */
     int32_t variant;   /* kan_variant_t */
-    int32_t flags;     /* 0, or KAN_FLAG_PREPARED and/or KAN_FLAG_DENSE_FORWARD */
+    int32_t flags;     /* 0, or KAN_FLAG_PREPARED, KAN_FLAG_DENSE_FORWARD, KAN_FLAG_TP_FORWARD */
 } kan_desc_t;
 
 /* The workspace already holds this pass's packed operands, written by
@@ -146,6 +146,22 @@ typedef struct {
  * combined with KAN_FLAG_PREPARED; both passes of a prepared pair must agree
  * on it. */
 #define KAN_FLAG_DENSE_FORWARD 2
+
+/* The dense bf16 forward on the matrix cores (implies KAN_FLAG_DENSE_FORWARD)
+ * with its basis tile generated by the truncated-power form instead of the
+ * knot span (FlashKAN project page: a degree-k B-spline is a combination of
+ * k+2 shifted truncated powers of the normalised coordinate, clamped to
+ * [0, k+1]): every column (i, m) of the tile is B(x/h + shift - m) on its own,
+ * with no span lookup, zero fill or scatter.  The values are rounded to bf16
+ * like the span form's (their float32 cancellation error, ~1e-6, is far
+ * below bf16's rounding).  Only for bf16 storage, degree 3, and a forward
+ * that runs on MFMA (KAN_ERR_UNSUPPORTED otherwise); both passes of a
+ * prepared pair must agree on it.  It costs G+3+has_base basis evaluations
+ * per (row, input) where the span form costs one, and on MI355X, whose bf16
+ * matrix rate is 16x its vector float32 rate, that vector work outlasts the
+ * contraction: the forward is 2.5x to 8x slower than the span form.  It is
+ * an independent construction of the same operand, not a fast path. */
+#define KAN_FLAG_TP_FORWARD 4
 
 /* KAN_ABI_VERSION of the loaded library. */
 int kan_abi_version(void);

@@ -32,6 +32,7 @@ KAN_PASS_BACKWARD = 1
 
 KAN_FLAG_PREPARED = 1
 KAN_FLAG_DENSE_FORWARD = 2
+KAN_FLAG_TP_FORWARD = 4
 
 KAN_STATIC_SCRATCH_BYTES = 32 << 20     # kan_forward_static's device array
 

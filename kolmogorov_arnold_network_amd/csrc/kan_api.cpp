@@ -173,7 +173,8 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     if (d->dtype != KAN_F32 && d->dtype != KAN_BF16) return KAN_ERR_DTYPE;
     if (d->has_base != 0 && d->has_base != 1) return KAN_ERR_UNSUPPORTED;
     if (d->variant < KAN_VARIANT_AUTO || d->variant > KAN_VARIANT_GATHER) return KAN_ERR_UNSUPPORTED;
-    if (d->flags & ~(KAN_FLAG_PREPARED | KAN_FLAG_DENSE_FORWARD)) return KAN_ERR_UNSUPPORTED;
+    if (d->flags & ~(KAN_FLAG_PREPARED | KAN_FLAG_DENSE_FORWARD | KAN_FLAG_TP_FORWARD))
+        return KAN_ERR_UNSUPPORTED;
 
     Plan q;
     memset(&q, 0, sizeof(q));
@@ -215,7 +216,14 @@ int make_plan(const kan_desc_t* d, Plan* p) {
                                                                                : KAN_VARIANT_GATHER;
     }
 
-    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
+    // the truncated-power generator: the dense bf16 forward of a cubic layer
+    // on the matrix cores (in float32 its alternating sum loses ~2e-6 per
+    // basis value, more than a chain of layers leaves room for)
+    const bool tp = (d->flags & KAN_FLAG_TP_FORWARD) != 0;
+    if (tp && (q.dtype != KAN_BF16 || q.degree != 3 || q.variant_fwd != KAN_VARIANT_MFMA))
+        return KAN_ERR_UNSUPPORTED;
+    q.tp = tp;
+    plan_layout(q, tp || (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
     if (q.variant_fwd == KAN_VARIANT_GATHER) {
         q.gf = gather_fwd_plan(q.N, q.I, q.O, q.K, q.degree, q.base);
         q.ws_fwd = q.gf.ws;

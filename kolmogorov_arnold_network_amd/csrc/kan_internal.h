@@ -124,6 +124,8 @@ struct Plan {
 
     // structured-sparse forward (bf16): each input's Kb columns become NG
     // groups of 4 (Kb8 = 4 NG columns) in the column order of kan_sparse.h
+    int tp;              // 1: the dense bf16 forward generates its basis by the
+                         // truncated-power form (KAN_FLAG_TP_FORWARD)
     int sparse;          // 1: the forward uses the sparse layout
     int NG, Kb8;
     int64_t Kfs;         // sparse forward contraction length: I * Kb8 rounded up to 64

@@ -309,6 +309,70 @@ struct GenA {
     }
 };
 
+// Forward A operand of a bf16 layer from the truncated-power form (FlashKAN
+// project page: a cubic B-spline is a combination of five shifted truncated
+// cubes of the normalised coordinate, clamped to [0, 4]).  Every tile column
+// (i, m) is evaluated on its own from u = x / h + (shift - m): there is no
+// span, no zero fill and no scatter.  Pairs and lanes as in GenA (NIN
+// adjacent lanes per row, one input each); a lane writes every tile column of
+// its input, the silu column included, and zeros for inputs past the last
+// one, so the tile is complete without a fill.  Columns whose u lies outside
+// (0, 4) come out exactly 0 (all terms vanish, or cancel exactly at u = 4).
+template <int NIN>
+struct GenT {
+    static constexpr bool SPARSE = false;
+    __device__ __forceinline__ void init(const GemmArgs&, uint4*) {}
+    static constexpr int BK = Traits<uint16_t>::BK;
+    static constexpr int ES = Traits<uint16_t>::ES;
+    static constexpr int PPT = 256 * NIN / NTHR;       // pairs per thread
+    static constexpr int NPART = PPT;                  // part j: pair j (its row)
+    static constexpr int DEPTH = 2;                    // two slots of x values
+    static constexpr int RSTEP = NTHR / NIN;           // rows between a thread's pairs
+    static_assert(NIN >= 2 && (NIN & (NIN - 1)) == 0 && NIN <= 32, "NIN: power of two");
+    const uint16_t* x;
+    int q, row0;
+    int64_t xrow[PPT];
+    float xs[2][PPT];
+    int is[2];
+    __device__ GenT(const GemmArgs& a, int tm, int) {
+        x = static_cast<const uint16_t*>(a.x);
+        q = threadIdx.x % NIN;
+        row0 = threadIdx.x / NIN;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+            xrow[j] = (int64_t)min(tm * 256 + row0 + RSTEP * j, a.N - 1) * a.I;
+    }
+    template <int SL>
+    __device__ __forceinline__ void fetch(const GemmArgs& a, int kt) {
+        is[SL] = (unsigned)(kt * BK) / (unsigned)a.Kb + q;
+        const int i = min(is[SL], a.I - 1);
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) xs[SL][j] = load_f(x, xrow[j] + i);
+    }
+    template <int SL, bool RF, int j>
+    __device__ __forceinline__ void part(const GemmArgs& a, char* S, int kt, int ktn) {
+        char* row = S + (row0 + RSTEP * j) * PITCH;
+        const int i = is[SL];
+        const int cb = i * a.Kb - kt * BK;             // tile column of (i, 0)
+        const bool live = i < a.I;
+        const float xv = xs[SL][j];
+        const float sx = live && a.base ? silu(xv) : 0.0f;
+        const float u0 = __builtin_fmaf(xv, a.g.scale, a.g.shift);
+        char* pad = row + BK * ES;
+        // a trip count uniform over the block: columns outside the tile go
+        // to the row's pad bytes
+#pragma nounroll
+        for (int m = 0; m < a.Kb; ++m) {
+            const int c = cb + m;
+            float b = sx, d;
+            tp_basis(u0 - (float)m, a.g.scale, b, d);
+            if (m >= a.K) b = sx;
+            Traits<uint16_t>::put((unsigned)c < (unsigned)BK ? row + c * ES : pad, live ? b : 0.0f);
+        }
+        if constexpr (RF && j == NPART - 1) fetch<SL>(a, ktn);
+    }
+};
+
 // dC B operand Phi'^T[(i, m), b]: tile rows are the 256 packed columns
 // n0 .. n0+255 of Phi', k runs over the batch.  Wave w owns the NQW tile
 // inputs w NQW .. w NQW + NQW - 1: it zero-fills their tile rows and then
@@ -1588,6 +1652,16 @@ hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, 
 // Inputs that can meet one k-tile of the forward: ceil((BK - 1) / Kb) + 1.
 static int fwd_nin(const Plan& p) { return (p.BK - 1 + p.Kb - 1) / p.Kb + 1; }
 
+// the truncated-power generator (bf16, KAN_FLAG_TP_FORWARD)
+static hipError_t fwd_dispatch_tp(const Plan& p, const GemmArgs& a, hipStream_t s) {
+    const int n = fwd_nin(p);
+    if (n <= 2) return run_gemm<uint16_t, GenT<2>, LoadB, EpiY>(a, s);
+    if (n <= 4) return run_gemm<uint16_t, GenT<4>, LoadB, EpiY>(a, s);
+    if (n <= 8) return run_gemm<uint16_t, GenT<8>, LoadB, EpiY>(a, s);
+    if (n <= 16) return run_gemm<uint16_t, GenT<16>, LoadB, EpiY>(a, s);
+    return run_gemm<uint16_t, GenT<32>, LoadB, EpiY>(a, s);
+}
+
 template <typename TS>
 static hipError_t fwd_dispatch(const Plan& p, const GemmArgs& a, hipStream_t s) {
     const int n = fwd_nin(p);           // rounded up to a power of two
@@ -1673,6 +1747,7 @@ static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
         return run_gemm<uint16_t, GenS<8>, LoadB, EpiY>(a, s);
     }
     if (p.dtype == KAN_F32) return fwd_dispatch<float>(p, a, s);
+    if (p.tp) return fwd_dispatch_tp(p, a, s);
     return fwd_dispatch<uint16_t>(p, a, s);
 }
 

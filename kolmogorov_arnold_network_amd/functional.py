@@ -93,12 +93,16 @@ def workspace(desc, pass_, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
-def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None, dense_forward=False):
+def _fwd_flags(dense_forward, tp_forward):
+    return (L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0) | (L.KAN_FLAG_TP_FORWARD if tp_forward else 0)
+
+
+def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None, dense_forward=False, tp_forward=False):
     """Packs the pass's operands into a workspace; returns ``(ws, ws_bytes)``."""
     _check_tensor(C, "C", _DTYPES)
     _check_tensor(W, "W_base", _DTYPES, C.device)
     _check_tensor(dy, "dy", (torch.float32,), C.device)
-    desc = layer_desc(x, C, W, grid, variant, L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
+    desc = layer_desc(x, C, W, grid, variant, _fwd_flags(dense_forward, tp_forward))
     if dy is not None and tuple(dy.shape) != (x.shape[0], C.shape[0]):
         raise ValueError("dy must be [N, O]")
     if ws is None:
@@ -110,13 +114,15 @@ def kan_prepare(x, C, W, grid, pass_, dy=None, variant="auto", ws=None, dense_fo
 
 
 def kan_forward(x, C, W, grid, variant="auto", ws=None, prepared=False, out=None,
-                dense_forward=False):
+                dense_forward=False, tp_forward=False):
     """``y [N, O]`` float32 of one KAN layer.  ``dense_forward`` turns off the
-    structured-sparse forward of bf16 layers (``KAN_FLAG_DENSE_FORWARD``)."""
+    structured-sparse forward of bf16 layers (``KAN_FLAG_DENSE_FORWARD``);
+    ``tp_forward`` generates the dense bf16 basis tile by the truncated-power
+    form (``KAN_FLAG_TP_FORWARD``)."""
     _check_tensor(x, "x", _DTYPES)
     _check_tensor(C, "C", _DTYPES, x.device)
     _check_tensor(W, "W_base", _DTYPES, x.device)
-    flags = (L.KAN_FLAG_PREPARED if prepared else 0) | (L.KAN_FLAG_DENSE_FORWARD if dense_forward else 0)
+    flags = (L.KAN_FLAG_PREPARED if prepared else 0) | _fwd_flags(dense_forward, tp_forward)
     desc = layer_desc(x, C, W, grid, variant, flags)
     if ws is None:
         ws = workspace(desc, L.KAN_PASS_FORWARD, x.device)

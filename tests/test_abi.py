@@ -90,7 +90,10 @@ BAD_DESCS = [
     (dict(degree=1, G=1, has_base=0), "UNSUPPORTED"),           # MFMA: 2 columns per input, too few
     (dict(degree=1, G=1, has_base=0, dtype=1), "UNSUPPORTED"),  # the same in bf16
     (dict(dtype=7), "DTYPE"), (dict(has_base=2), "UNSUPPORTED"),
-    (dict(variant=9), "UNSUPPORTED"), (dict(flags=4), "UNSUPPORTED"),
+    (dict(variant=9), "UNSUPPORTED"), (dict(flags=8), "UNSUPPORTED"),
+    # the truncated-power forward: bf16, cubic, on the matrix cores only
+    (dict(flags=4), "UNSUPPORTED"), (dict(flags=4, dtype=1, degree=2), "UNSUPPORTED"),
+    (dict(flags=4, dtype=1, variant=2), "UNSUPPORTED"),
 ]
 
 # Pointer, alignment, workspace and overlap errors of one valid layer
@@ -291,6 +294,11 @@ def test_workspace_sizes(L):
                 return r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
             kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
             assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == fwd_bytes(kf, kf // (64 if sparse else bk))
+            if dt == L.KAN_BF16:
+                # the truncated-power forward packs the dense operand
+                assert L.lib().kan_workspace_size(ctypes.byref(desc(
+                    L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_TP_FORWARD)), 0) == \
+                    fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk)
             if sparse:
                 assert L.lib().kan_workspace_size(ctypes.byref(desc(
                     L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)), 0) == \

@@ -265,6 +265,31 @@ def test_sparse_forward(F, shape):
     assert rel_inf(y_s, y_d) <= 1e-5
 
 
+# Truncated-power forward generator: the SPARSE shapes plus the two bf16
+# workloads' grids (G = 5: 9 columns per input; G = 20: 24).
+TP_CASES = SPARSE + [(300, 40, 70, 5, True), (129, 70, 33, 20, True)]
+
+
+@pytest.mark.parametrize("shape", TP_CASES, ids=["x".join(map(str, s)) for s in TP_CASES])
+def test_tp_forward(F, shape):
+    """The dense forward with its operand built from truncated powers, against
+    the oracle at the bf16 bar and against the span-based dense forward (the
+    two round different float32 basis values to bf16)."""
+    N, I, O, G, base = shape
+    say("truncated-power forward %s" % (shape,))
+    d = wl.random_layer(N, I, O, G, dtype="bf16", base=base, seed=5 * N + I + O + G)
+    (C, W), x = d["layers"][0], d["x"]
+    grid = (d["lo"], d["hi"], G)
+    xt, Ct, Wt = to_dev(x, "bf16"), to_dev(C, "bf16"), to_dev(W, "bf16")
+    y_t = F.kan_forward(xt, Ct, Wt, grid, "mfma", tp_forward=True)
+    y_d = F.kan_forward(xt, Ct, Wt, grid, "mfma", dense_forward=True)
+    _sync()
+    y_t, y_d = _np(y_t), _np(y_d)
+    ref = oracle.layer_forward(x, C, W, *grid)
+    assert rel_fro(y_t, ref) <= TOL_BF16
+    assert rel_fro(y_t, y_d) <= TOL_BF16
+
+
 def test_deterministic_and_prepared(F):
     import torch
     d = wl.random_layer(700, 48, 300, 8, dtype="bf16", base=True, seed=5)
