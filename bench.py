@@ -46,6 +46,8 @@ SURFACE_METRIC = "2-D tensor-product KAN layer fwd+bwd rows/sec; % of MFMA roofl
 GROUPED_METRIC = "grouped spline activation fwd+bwd elements/sec; % of HBM roofline, 1 GPU"
 MFMA_FILES = ("kan_mfma.hip", "kan_device.h", "kan_sparse.h", "kan_internal.h", "kan_api.cpp")
 GROUPED_FILES = ("kan_grouped.hip", "kan_device.h", "kan_internal.h", "kan_api.cpp")
+GATHER_FILES = ("kan_gather.hip", "kan_device.h", "kan_internal.h", "kan_plan.cpp", "kan_api.cpp")
+DIGEST_FILES = {"mfma": MFMA_FILES, "grouped": GROUPED_FILES, "gather": GATHER_FILES}
 
 
 def parse():
@@ -58,7 +60,7 @@ def parse():
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None)
-    ap.add_argument("--code-digest", nargs="?", const="mfma", default=None, choices=["mfma", "grouped"],
+    ap.add_argument("--code-digest", nargs="?", const="mfma", default=None, choices=sorted(DIGEST_FILES),
                     help="print the digest that ties a counter summary to the kernel source")
     ap.add_argument("--degree", type=int, default=3,
                     help="spline degree (1 .. 5) of the layer workloads and of --basis-forms")
@@ -210,7 +212,7 @@ def stage_names(nl):
 def main():
     args = parse()
     if args.code_digest:
-        print(kernel_code_digest(GROUPED_FILES if args.code_digest == "grouped" else MFMA_FILES))
+        print(kernel_code_digest(DIGEST_FILES[args.code_digest]))
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -393,7 +395,7 @@ def main():
         "executed_frac": exe_dom / t_dom / 1e12 / peak if mfma_path else None,
         "dominant_ms": stage_ms[dom],
     }
-    tr = read_traffic(args.workload, dom.split(".")[1])
+    tr = read_traffic(args.workload, dom.split(".")[1], MFMA_FILES if mfma_path else GATHER_FILES)
     if tr is not None:
         roof["traffic"] = tr
     out = {
