@@ -481,9 +481,12 @@ __global__ void gather_sum_kernel(const double* __restrict__ part, float* __rest
 // input t % 16 and rows t / 16 + 64 p, p < 4, whose D + 1 basis derivatives
 // and silu' it forms once.  The sum over outputs j runs in chunks of JC held
 // in LDS: dy[rows][JC], the chunk's coefficients for the block's 16 inputs as
-// Cs[ii][m][j] and W_base as Ws[ii][j] (rows padded to JC + 4 floats, so
-// that the transposing stores of consecutive pieces fall in different
-// banks).  There are two chunk buffers: the next chunk is loaded into
+// Cs[m][ii][j] and W_base as Ws[ii][j], rows padded to JP = JC + 4 floats.
+// A wave reads the coefficient rows of 16 inputs at once, each at its own
+// data-dependent m; with ii the faster index and JP / 4 odd, the 16-byte
+// pieces of the 16 inputs fall in distinct bank groups whatever the m (in the
+// layout Cs[ii][m][j] the random m made most of these reads conflict).
+// There are two chunk buffers: the next chunk is loaded into
 // registers while the current one is read, with one barrier per chunk.  All
 // 256 rows share a staged chunk, which keeps the coefficient staging (the
 // part that grows with G) small next to the arithmetic.  With too few
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(GX_NT) void gather_dx_kernel(GatherDxArgs a) {
         const int b = b0 + rq + 64 * p;
         const RecD<D> r = (b < N && i < I) ? make_rec<true, D>(load_f(x, (int64_t)b * I + i), g) : zero_rec<D>();
         const int mb = clampi(r.m0, 0, K - D - 1);
-        cb[p] = (il * K + mb) * JP;
+        cb[p] = (mb * GX_TI + il) * JP;
 #pragma unroll
         for (int q = 0; q <= D; ++q) {
             const int k = mb + q - r.m0;
@@ -615,11 +618,17 @@ __global__ __launch_bounds__(GX_NT) void gather_dx_kernel(GatherDxArgs a) {
         for (int q = 0; q < MAXQ; ++q) {
             const int k = pc + NPC * q;
             if (4 * k < ick) {
+                // element s + e of the run is (ii, m) = divmod(s + e, K),
+                // stored at (m GX_TI + ii) JP + jj; the quotient of the
+                // small integer s by K is exact in float
                 const int s = ick >= 4 ? min(4 * k, ick - 4) : 0;
+                int ii = (int)(((float)s + 0.5f) * a.invK), m = s - ii * K;
                 const float vv[4] = {cp[q].x, cp[q].y, cp[q].z, cp[q].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (s + e < ick) Cs[(s + e) * JP + jj] = jok ? vv[e] : 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    if (s + e < ick) Cs[(m * GX_TI + ii) * JP + jj] = jok ? vv[e] : 0.0f;
+                    if (++m == K) m = 0, ++ii;
+                }
             }
         }
         if (t < GX_TI * JC) {
@@ -652,7 +661,7 @@ __global__ __launch_bounds__(GX_NT) void gather_dx_kernel(GatherDxArgs a) {
                 const float4 d = *reinterpret_cast<const float4*>(&Ds[(rq + 64 * p) * JC + jq]);
                 float4 cv[D + 1];
 #pragma unroll
-                for (int q = 0; q <= D; ++q) cv[q] = *reinterpret_cast<const float4*>(&Cs[cb[p] + q * JP + jq]);
+                for (int q = 0; q <= D; ++q) cv[q] = *reinterpret_cast<const float4*>(&Cs[cb[p] + q * (GX_TI * JP) + jq]);
 #pragma unroll
                 for (int q = 0; q <= D; ++q) {
                     Q[p][q] = __builtin_fmaf(d.x, cv[q].x, Q[p][q]);
@@ -1055,6 +1064,7 @@ hipError_t launch_gather_dx(const Plan& p, const void* x, const void* C, const v
     a.RB = (int)p.gb.rb;
     a.IB = (int)p.gb.ib;
     a.JS = (int)p.gb.js;
+    a.invK = 1.0f / (float)p.K;
     a.x = x;
     a.C = C;
     a.W = W;

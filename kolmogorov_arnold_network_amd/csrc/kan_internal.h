@@ -62,6 +62,7 @@ struct GatherDxArgs {
     int N, I, O, base;
     int RB, IB;          // row blocks, input blocks
     int JS;              // outputs per slice (a multiple of the chunk)
+    float invK;          // 1 / K, rounded
     const void* x;
     const void* C;
     const void* W;
