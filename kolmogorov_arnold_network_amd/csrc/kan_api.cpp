@@ -32,29 +32,6 @@ bool overlap(const Range& a, const Range& b) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 
-// Slices of the k range for a contraction of `tiles` output tiles over `nkt`
-// k-tiles with `out_bytes` of fp32 output.  The contraction kernel runs one
-// workgroup per CU, so its time is estimated as the rounds of kCUs
-// workgroups times the k-tiles each runs; a split adds its partial outputs,
-// written and then summed (2 P + 1 passes over out_bytes).  The split with
-// the least estimate is taken if it saves at least 1/16; each slice keeps
-// at least 8 k-tiles.  Returns the slice count; *nks = k-tiles per slice.
-int k_slices(int64_t tiles, int64_t nkt, int64_t out_bytes, int esize, int64_t* nks) {
-    constexpr int64_t kCUs = 256;                         // MI355X compute units
-    const int64_t kt_ns = esize == 2 ? 2000 : 8000;       // one k-tile of one workgroup
-    constexpr int64_t kBytesPerNs = 4000;                 // streaming rate of the partials
-    auto est = [&](int64_t P) {
-        const int64_t per = (nkt + P - 1) / P, rounds = (tiles * P + kCUs - 1) / kCUs;
-        return rounds * per * kt_ns + (P > 1 ? (2 * P + 1) * out_bytes / kBytesPerNs : 0);
-    };
-    int64_t best = 1, tb = est(1);
-    for (int64_t P = 2; P <= 8 && (nkt + P - 1) / P >= 8; ++P)
-        if (est(P) < tb) best = P, tb = est(P);
-    if (tb > est(1) - est(1) / 16) best = 1;
-    *nks = (nkt + best - 1) / best;
-    return (int)((nkt + *nks - 1) / *nks);
-}
-
 // Matrix-core geometry and workspace layout of a plan whose shape, K, Kb,
 // base, dtype and per-pass variants are set.
 void plan_layout(Plan& q, bool dense_forward) {
@@ -91,26 +68,34 @@ void plan_layout(Plan& q, bool dense_forward) {
     q.Kfs = round_up(q.I * q.Kb8, 64);
     take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
-    q.split_fwd = k_slices((q.Npad / kTileM) * (q.Opad / kTileN), nkt_fwd, q.N * q.O * 4, q.esize,
-                           &q.nks_fwd);
+    const KSplit kf = k_split(q.Npad / kTileM, q.Opad / kTileN, nkt_fwd, q.N, q.O * 4, q.esize);
+    q.split_fwd = kf.P;
+    q.nks_fwd = kf.nks;
+    q.tail_fwd = kf.tail;
     // A float32 forward sums its contraction in slices of at most 8 k-tiles
     // (256 terms): a float32 running sum over the whole basis row (9408
     // terms at 784 inputs) loses accuracy that the next layer's B' amplifies;
     // the slices' partials are added in float64.
-    if (q.dtype == KAN_F32 && q.nks_fwd > kF32SliceTiles) {
+    const bool sliced = q.split_fwd > 1 && q.tail_fwd == q.Npad / kTileM && q.nks_fwd <= kF32SliceTiles;
+    if (q.dtype == KAN_F32 && nkt_fwd > kF32SliceTiles && !sliced) {
         q.nks_fwd = kF32SliceTiles;
         q.split_fwd = (int)((nkt_fwd + kF32SliceTiles - 1) / kF32SliceTiles);
+        q.tail_fwd = q.Npad / kTileM;
     }
-    if (q.split_fwd > 1) take((size_t)(q.split_fwd * q.N * q.O) * 4, &q.off_yp, &q.sz_yp);
+    if (q.split_fwd > 1)
+        take((size_t)(q.split_fwd * fwd_tail_rows(q) * q.O) * 4, &q.off_yp, &q.sz_yp);
     q.ws_fwd = q.variant_fwd == KAN_VARIANT_MFMA ? off : 0;
     off = 0;
     take((size_t)(q.tiles_dx * kTileN * q.Opad) * q.esize, &q.off_cpt, &q.sz_cpt);
     take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
     take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
     take((size_t)(q.Npad * q.tiles_dx * 2 * (q.pair ? 2 : 1)) * 4, &q.off_part, &q.sz_part);
-    q.split_dc = k_slices((q.Opad / kTileM) * ((q.IKb + kTileN - 1) / kTileN), q.Npad / q.BK,
-                          q.O * q.I * q.Kb * 4, q.esize, &q.nks_dc);
-    if (q.split_dc > 1) take((size_t)(q.split_dc * q.O * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
+    const KSplit kc = k_split(q.Opad / kTileM, (q.IKb + kTileN - 1) / kTileN, q.Npad / q.BK, q.O, q.I * q.Kb * 4,
+                              q.esize);
+    q.split_dc = kc.P;
+    q.nks_dc = kc.nks;
+    q.tail_dc = kc.tail;
+    if (q.split_dc > 1) take((size_t)(q.split_dc * dc_tail_rows(q) * q.I * q.Kb) * 4, &q.off_dcp, &q.sz_dcp);
     q.ws_bwd = q.variant_bwd == KAN_VARIANT_MFMA ? off : 0;
 }
 

@@ -131,11 +131,15 @@ struct Plan {
     int NG, Kb8;
     int64_t Kfs;         // sparse forward contraction length: I * Kb8 rounded up to 64
 
-    // k-split of launches with too few output tiles: the forward (over its
-    // k-tiles) and dC (over the batch) run as split_* slices of nks_* k-tiles
-    // that write fp32 partial outputs, summed afterwards in slice order
+    // k-split of launches whose output tiles leave CUs idle: the forward
+    // (over its k-tiles) and dC (over the batch).  The last tail_* tile rows
+    // (every row, or the few that would run in a final, mostly idle round)
+    // run as split_* slices of nks_* k-tiles that write fp32 partial outputs,
+    // summed afterwards in slice order; the other tile rows run whole and
+    // write their outputs directly.
     int split_fwd, split_dc;
     int64_t nks_fwd, nks_dc;
+    int64_t tail_fwd, tail_dc;
 
     // workspace layout (bytes); forward uses [off_cp, +sz_cp).  Every array is
     // blocked: 256-row tiles, each cut into k-tiles of 256 x BK contiguous
@@ -146,13 +150,29 @@ struct Plan {
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
                                // (pairs: [Npad][tiles_dx][2][2], both inputs of the pair)
-    size_t off_yp, sz_yp;      // forward slices' partial y: [split_fwd][N][O] float (split_fwd > 1)
-    size_t off_dcp, sz_dcp;    // dC slices' partials: [split_dc][O][I][K] then [split_dc][O][I] float
+    size_t off_yp, sz_yp;      // forward slices' partial y of the tail rows: [split_fwd][fwd_tail_rows][O] float
+    size_t off_dcp, sz_dcp;    // dC slices' partials of the tail rows j: [split_dc][dc_tail_rows][I][K], then
+                               // [split_dc][dc_tail_rows][I] float
     size_t ws_fwd, ws_bwd;
 
     GatherFwdPlan gf;    // the local-gather forward (variant_fwd == GATHER)
     GatherBwdPlan gb;    // the local-gather backward (variant_bwd == GATHER)
 };
+
+// Output rows of the sliced tail tiles: y rows b >= first_fwd_row(p), dC rows
+// j >= first_dc_row(p).
+inline int64_t first_fwd_row(const Plan& p) { return (p.Npad / 256 - p.tail_fwd) * 256; }
+inline int64_t first_dc_row(const Plan& p) { return (p.Opad / 256 - p.tail_dc) * 256; }
+inline int64_t fwd_tail_rows(const Plan& p) { return p.N - first_fwd_row(p); }
+inline int64_t dc_tail_rows(const Plan& p) { return p.O - first_dc_row(p); }
+
+// A k-split: P slices of nks k-tiles each, taken by the last `tail` tile rows.
+struct KSplit {
+    int P;
+    int64_t nks;
+    int64_t tail;
+};
+KSplit k_split(int64_t tiles_m, int64_t tiles_n, int64_t nkt, int64_t rows_out, int64_t row_bytes, int esize);
 
 // Builds the plan; returns KAN_OK or the validation error for `desc` alone.
 int make_plan(const kan_desc_t* desc, Plan* p);

@@ -148,29 +148,45 @@ struct GemmArgs {
     int64_t IKb;
     float* out0;         // y, dx or dC
     float* out1;         // dW_base, or the dx partial sums
-    // k-split: slice blockIdx.y runs k-tiles [nks * slice, min(nkt, nks * (slice + 1)))
-    // and writes its epilogue output at out0 + slice * ostride0 (out1 likewise)
-    int nks;
-    int64_t ostride0, ostride1;
+    // k-split of the last `tail` tile rows (0: none): slice s of such a tile
+    // runs k-tiles [nks s, min(nkt, nks (s + 1))) and writes its epilogue
+    // output to part0 + s * ostride0 - oshift0 in place of out0 (part1,
+    // ostride1, oshift1 in place of out1): the partial arrays hold the tail
+    // rows only, and oshift* is the output offset of the first tail row
+    int tail, nks;
+    float* part0;
+    float* part1;
+    int64_t ostride0, ostride1, oshift0, oshift1;
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2.  Give every XCD a contiguous range of tile ids, and walk
 // ids in groups of `group_m` tile rows so that the workgroups resident on one
-// XCD share their B tiles (and their A tiles across the group).
-__device__ __forceinline__ void tile_coords(const GemmArgs& a, int& tm, int& tn) {
-    const int total = a.tiles_m * a.tiles_n;
-    const int bid = blockIdx.x;
+// XCD share their B tiles (and their A tiles across the group).  The grid
+// holds the whole tiles of the first tiles_m - tail tile rows, then slice 0
+// of every tail tile, slice 1, and so on; returns the slice.
+__device__ __forceinline__ int tile_coords(const GemmArgs& a, int& tm, int& tn) {
+    int bid = blockIdx.x, slice = 0, row0 = 0, rows = a.tiles_m - a.tail;
+    const int head = rows * a.tiles_n;
+    if (bid >= head) {
+        bid -= head;
+        row0 = rows;
+        rows = a.tail;
+        slice = bid / (rows * a.tiles_n);
+        bid -= slice * rows * a.tiles_n;
+    }
+    const int total = rows * a.tiles_n;
     const int nfull = total / 8, rem = total % 8;
     const int xcd = bid % 8, slot = bid / 8;
     const int id = xcd * nfull + min(xcd, rem) + slot;
     const int per_group = a.group_m * a.tiles_n;
     const int grp = id / per_group;
     const int first_m = grp * a.group_m;
-    const int gm = min(a.tiles_m - first_m, a.group_m);
+    const int gm = min(rows - first_m, a.group_m);
     const int r = id - grp * per_group;
-    tm = first_m + r % gm;
+    tm = row0 + first_m + r % gm;
     tn = r / gm;
+    return slice;
 }
 
 // ---- operands ----
@@ -1238,12 +1254,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     extern __shared__ uint4 lds4[];
     char* lds = reinterpret_cast<char*>(lds4);
     int tm, tn;
-    tile_coords(args, tm, tn);
-    // this workgroup's slice of the k range (the whole range unless split)
-    const int slice = blockIdx.y;
-    const int kb = slice * args.nks, ke = min(args.nkt, kb + args.nks);
-    if (args.out0) args.out0 += slice * args.ostride0;
-    if (args.out1) args.out1 += slice * args.ostride1;
+    const int slice = tile_coords(args, tm, tn);
+    // this workgroup's slice of the k range: the whole range, or one slice
+    // of a tail tile, whose output goes to the partial arrays
+    int kb = 0, ke = args.nkt;
+    if (tm >= args.tiles_m - args.tail) {
+        kb = slice * args.nks;
+        ke = min(args.nkt, kb + args.nks);
+        args.out0 = args.part0 ? args.part0 + (slice * args.ostride0 - args.oshift0) : nullptr;
+        args.out1 = args.part1 ? args.part1 + (slice * args.ostride1 - args.oshift1) : nullptr;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     AOp A(args, tm, tn);
@@ -1546,8 +1566,9 @@ hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    const unsigned slices = (unsigned)((a.nkt + a.nks - 1) / a.nks);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.tiles_m * a.tiles_n), slices), dim3(NTHR), LDS_BYTES, s, a);
+    const int64_t slices = a.tail > 0 ? (a.nkt + a.nks - 1) / a.nks : 0;
+    const int64_t blocks = (int64_t)(a.tiles_m - a.tail) * a.tiles_n + (int64_t)a.tail * a.tiles_n * slices;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -1585,7 +1606,7 @@ GemmArgs base_args(const Plan& p, const void* x) {
     a.base = p.base;
     a.IKb = p.IKb;
     a.group_m = 16;
-    a.nks = 1 << 30;     // one slice unless a launcher splits the k range
+    a.nks = 1 << 30;     // no tail: every tile runs its whole k range
     return a;
 }
 
@@ -1761,11 +1782,15 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
     a.out0 = y;
     if (p.split_fwd <= 1) return fwd_run(p, a, s);
-    a.out0 = ypart;
+    // the tail rows in split_fwd slices: partials, then a sum in slice order
+    const int64_t r0 = first_fwd_row(p), n = fwd_tail_rows(p) * p.O;
+    a.tail = (int)p.tail_fwd;
     a.nks = (int)p.nks_fwd;
-    a.ostride0 = p.N * p.O;
+    a.part0 = ypart;
+    a.ostride0 = n;
+    a.oshift0 = r0 * p.O;
     hipError_t e = fwd_run(p, a, s);
-    return e != hipSuccess ? e : sum_slices(ypart, y, p.N * p.O, p.split_fwd, s);
+    return e != hipSuccess ? e : sum_slices(ypart, y + r0 * p.O, n, p.split_fwd, s);
 }
 
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
@@ -1827,17 +1852,22 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
         return p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);
     };
     if (p.split_dc <= 1) return dispatch();
-    // the batch in split_dc fixed slices: partials, then a sum in slice order
-    const int64_t nc = p.O * p.I * p.K, nw = p.O * p.I;
+    // the tail rows j with the batch in split_dc fixed slices: partials,
+    // then a sum in slice order
+    const int64_t j0 = first_dc_row(p), rows = dc_tail_rows(p);
+    const int64_t nc = rows * p.I * p.K, nw = rows * p.I;
     float* wpart = cpart + p.split_dc * nc;
-    a.out0 = dC ? cpart : nullptr;
-    a.out1 = dW ? wpart : nullptr;
+    a.tail = (int)p.tail_dc;
     a.nks = (int)p.nks_dc;
+    a.part0 = dC ? cpart : nullptr;
+    a.part1 = dW ? wpart : nullptr;
     a.ostride0 = nc;
     a.ostride1 = nw;
+    a.oshift0 = j0 * p.I * p.K;
+    a.oshift1 = j0 * p.I;
     hipError_t e = dispatch();
-    if (e == hipSuccess && dC) e = sum_slices(cpart, dC, nc, p.split_dc, s);
-    if (e == hipSuccess && dW) e = sum_slices(wpart, dW, nw, p.split_dc, s);
+    if (e == hipSuccess && dC) e = sum_slices(cpart, dC + j0 * p.I * p.K, nc, p.split_dc, s);
+    if (e == hipSuccess && dW) e = sum_slices(wpart, dW + j0 * p.I, nw, p.split_dc, s);
     return e;
 }
 

@@ -1,6 +1,6 @@
-// Host-side launch plans of the vector-ALU kernels: block counts, chunk
-// sizes, slices and workspace layouts of the local-gather layer kernels and
-// of the grouped activation.  Pure host code (no device code, no HIP calls),
+// Host-side launch plans: the k-split of the matrix-core contractions, and
+// the block counts, chunk sizes, slices and workspace layouts of the
+// local-gather layer kernels and of the grouped activation.  Pure host code (no device code, no HIP calls),
 // so the validation and planning path can also be built on its own for the
 // host sanitizers.
 #include <algorithm>
@@ -8,6 +8,52 @@
 #include "kan_internal.h"
 
 namespace kan {
+
+// Slices of the k range for a contraction of tiles_m x tiles_n output tiles
+// over nkt k-tiles whose fp32 output has rows_out rows of row_bytes (a tile
+// row covers 256 of them).  The contraction kernel runs one workgroup per
+// CU, so its time is estimated as the rounds of kCUs workgroups times the
+// k-tiles each runs; cut k ranges add their partial outputs, written and
+// then summed (2 P + 1 passes over those bytes).  Two forms are weighed:
+//  - every tile cut into P slices (the launch has too few tiles for the CUs);
+//  - the first tile rows whole, in as many full rounds as the tiles fill,
+//    and only the last tile rows cut into P slices that fill the final
+//    round instead of leaving most of its CUs idle.
+// The least estimate is taken if it saves at least 1/16; each slice keeps at
+// least 8 k-tiles.
+KSplit k_split(int64_t tiles_m, int64_t tiles_n, int64_t nkt, int64_t rows_out, int64_t row_bytes, int esize) {
+    constexpr int64_t kCUs = 256;                         // MI355X compute units
+    const int64_t kt_ns = esize == 2 ? 2000 : 8000;       // one k-tile of one workgroup
+    constexpr int64_t kBytesPerNs = 4000;                 // streaming rate of the partials
+    const int64_t tiles = tiles_m * tiles_n;
+    auto est = [&](int64_t P) {
+        const int64_t per = (nkt + P - 1) / P, rounds = (tiles * P + kCUs - 1) / kCUs;
+        return rounds * per * kt_ns + (P > 1 ? (2 * P + 1) * rows_out * row_bytes / kBytesPerNs : 0);
+    };
+    KSplit r{1, nkt, 0};
+    const int64_t e1 = est(1);
+    int64_t tb = e1;
+    for (int64_t P = 2; P <= 8 && (nkt + P - 1) / P >= 8; ++P)
+        if (est(P) < tb) r = KSplit{(int)P, 0, tiles_m}, tb = est(P);
+    const int64_t full = tiles / kCUs;
+    if (full >= 1) {
+        const int64_t h = full * kCUs / tiles_n, t = tiles_m - h, tt = t * tiles_n;
+        const int64_t P = t > 0 ? std::min<int64_t>(std::min<int64_t>(8, kCUs / tt), nkt / 8) : 0;
+        if (P >= 2) {
+            const int64_t per = (nkt + P - 1) / P;
+            const int64_t tail_bytes = std::max<int64_t>(0, rows_out - 256 * h) * row_bytes;
+            const int64_t e = (h * tiles_n + kCUs - 1) / kCUs * nkt * kt_ns + per * kt_ns +
+                              (2 * P + 1) * tail_bytes / kBytesPerNs;
+            if (e < tb) r = KSplit{(int)P, 0, t}, tb = e;
+        }
+    }
+    if (tb > e1 - e1 / 16) r = KSplit{1, nkt, 0};
+    if (r.P > 1) {
+        r.nks = (nkt + r.P - 1) / r.P;
+        r.P = (int)((nkt + r.nks - 1) / r.nks);
+    }
+    return r;
+}
 
 GatherFwdPlan gather_fwd_plan(int64_t N, int64_t I, int64_t O, int K, int D, int base) {
     GatherFwdPlan q;

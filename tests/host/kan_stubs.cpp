@@ -94,6 +94,11 @@ hipError_t launch_prep_dy(const Plan&, const float* dy, void* dyp, void* dyt, hi
 hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y, hipStream_t) {
     need(x && cp && y, "mfma forward pointers");
     need(p.split_fwd >= 1 && (p.split_fwd == 1 || ypart), "mfma forward slices");
+    need(p.split_fwd == 1 || (p.tail_fwd >= 1 && p.tail_fwd <= p.Npad / 256 && fwd_tail_rows(p) >= 1 &&
+                              p.nks_fwd * (p.split_fwd - 1) < (p.sparse ? p.Kfs / 64 : p.Kf / p.BK)),
+         "mfma forward tail");
+    if (p.split_fwd > 1)
+        need(p.off_yp + (size_t)p.split_fwd * fwd_tail_rows(p) * p.O * 4 <= p.ws_fwd, "forward partials in the workspace");
     ++g_launches;
     return hipSuccess;
 }
@@ -106,6 +111,11 @@ hipError_t launch_mfma_dx(const Plan&, const void* x, const void* dyp, const voi
 hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float*, float*,
                           hipStream_t) {
     need(x && dyt && (p.split_dc == 1 || cpart), "mfma dC pointers");
+    need(p.split_dc == 1 || (p.tail_dc >= 1 && p.tail_dc <= p.Opad / 256 && dc_tail_rows(p) >= 1 &&
+                             p.nks_dc * (p.split_dc - 1) < p.Npad / p.BK),
+         "mfma dC tail");
+    if (p.split_dc > 1)
+        need(p.off_dcp + (size_t)p.split_dc * dc_tail_rows(p) * p.I * p.Kb * 4 <= p.ws_bwd, "dC partials in the workspace");
     ++g_launches;
     return hipSuccess;
 }

@@ -181,28 +181,59 @@ def test_empty_batch_forward_returns_ok_without_launch(L):
                     assert L.lib().kan_forward_static(ctypes.byref(d), X, C, W, Y, None) == L.KAN_OK
 
 
-def k_slices(tiles, nkt, out_bytes, esize):
+def k_split(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize):
     """The planner's k-split rule, restated: slices of the k range for a
-    contraction of `tiles` output tiles over `nkt` k-tiles with `out_bytes`
-    of fp32 output (estimate: rounds of 256 one-per-CU workgroups x k-tiles
-    per workgroup at 2 us (bf16) or 8 us (fp32), plus 2P + 1 passes over
-    the partials at 4 bytes/ns; taken when it saves >= 1/16, >= 8 k-tiles a
-    slice).  Returns (slices, k-tiles per slice)."""
+    contraction of tiles_m x tiles_n output tiles over `nkt` k-tiles whose
+    fp32 output has rows_out rows of row_bytes.  Estimate: rounds of 256
+    one-per-CU workgroups x k-tiles per workgroup at 2 us (bf16) or 8 us
+    (fp32), plus 2P + 1 passes over the partials at 4 bytes/ns.  Either every
+    tile row is cut into P slices, or the tile rows that fill whole rounds run
+    whole and only the last `tail` rows are cut, into P slices that fit the
+    final round.  Taken when it saves >= 1/16, >= 8 k-tiles a slice.
+    Returns (slices, k-tiles per slice, tail tile rows)."""
     kt_ns = 2000 if esize == 2 else 8000
+    tiles = tiles_m * tiles_n
 
     def est(P):
         per, rounds = (nkt + P - 1) // P, (tiles * P + 255) // 256
-        return rounds * per * kt_ns + ((2 * P + 1) * out_bytes // 4000 if P > 1 else 0)
-    best, tb = 1, est(1)
+        return rounds * per * kt_ns + ((2 * P + 1) * rows_out * row_bytes // 4000 if P > 1 else 0)
+    e1 = est(1)
+    best, tb = (1, 0), e1
     P = 2
     while P <= 8 and (nkt + P - 1) // P >= 8:
         if est(P) < tb:
-            best, tb = P, est(P)
+            best, tb = (P, tiles_m), est(P)
         P += 1
-    if tb > est(1) - est(1) // 16:
-        best = 1
-    nks = (nkt + best - 1) // best
-    return (nkt + nks - 1) // nks, nks
+    full = tiles // 256
+    if full >= 1:
+        h = full * 256 // tiles_n
+        t = tiles_m - h
+        P = min(8, 256 // (t * tiles_n), nkt // 8) if t > 0 else 0
+        if P >= 2:
+            per = (nkt + P - 1) // P
+            e = ((h * tiles_n + 255) // 256 * nkt * kt_ns + per * kt_ns
+                 + (2 * P + 1) * max(0, rows_out - 256 * h) * row_bytes // 4000)
+            if e < tb:
+                best, tb = (P, t), e
+    if tb > e1 - e1 // 16:
+        best = (1, 0)
+    if best[0] == 1:
+        return 1, nkt, 0
+    nks = (nkt + best[0] - 1) // best[0]
+    return (nkt + nks - 1) // nks, nks, best[1]
+
+
+def split_bytes(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize, f32_forward=False):
+    """Bytes of the partial outputs of a k-split contraction (0 when not
+    split): P slices of the tail rows' output.  A float32 forward sums in
+    slices of at most 8 k-tiles on every tile row."""
+    P, nks, tail = k_split(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize)
+    if f32_forward and nkt > 8 and not (P > 1 and tail == tiles_m and nks <= 8):
+        P, tail = (nkt + 7) // 8, tiles_m
+    if P <= 1:
+        return 0
+    rows = rows_out - (tiles_m - tail) * 256
+    return (P * rows * row_bytes + 255) // 256 * 256
 
 
 def gather_fwd_ws(N, I, O, K, D, base):
@@ -257,15 +288,6 @@ def auto_bwd_gather(N, I, O, Kb):
     return not (4.0 * nio * Kb / 110e12 + 150e-6 < nio / 1.6e12)
 
 
-def fwd_slices(nt_tiles, nkt, out_bytes, es):
-    """k-slices of the MFMA forward: the occupancy split, and for float32 at
-    most 8 k-tiles per slice."""
-    P, nks = k_slices(nt_tiles, nkt, out_bytes, es)
-    if es == 4 and nks > 8:
-        P = (nkt + 7) // 8
-    return P
-
-
 def test_workspace_sizes(L):
     ws = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 0)
     wb = lambda **kw: L.lib().kan_workspace_size(ctypes.byref(desc(L, **kw)), 1)
@@ -290,8 +312,7 @@ def test_workspace_sizes(L):
 
             def fwd_bytes(kf, nkt):
                 # packed C', then the partial y of a split forward
-                P = fwd_slices((Np // 256) * (Op // 256), nkt, N * O * 4, es)
-                return r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
+                return r(Op * kf * es, 256) + split_bytes(Np // 256, Op // 256, nkt, N, O * 4, es, es == 4)
             kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
             assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == fwd_bytes(kf, kf // (64 if sparse else bk))
             if dt == L.KAN_BF16:
@@ -305,8 +326,7 @@ def test_workspace_sizes(L):
                     fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk)
             tiles = (I * Kb + 255) // 256           # dx tiles of 256 P columns
             want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
-            P, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)   # dC over batch slices
-            want += r(P * O * I * Kb * 4, 256) if P > 1 else 0
+            want += split_bytes(Op // 256, tiles, Np // bk, O, I * Kb * 4, es)   # dC over batch slices
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores; float32 forward on the gather kernel and
     # backward on the matrix cores
@@ -348,12 +368,10 @@ def test_workspace_sizes_other_degrees(L):
             Kb = G + D + base
             Op, Np = r(O, 256), r(N, 256)
             kf = r(I * Kb, bk)
-            P = fwd_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
-            want_f = r(Op * kf * es, 256) + (r(P * N * O * 4, 256) if P > 1 else 0)
+            want_f = r(Op * kf * es, 256) + split_bytes(Np // 256, Op // 256, kf // bk, N, O * 4, es, es == 4)
             tiles = (I * Kb + 255) // 256
             want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
-            Pd, _ = k_slices((Op // 256) * tiles, Np // bk, O * I * Kb * 4, es)
-            want_b += r(Pd * O * I * Kb * 4, 256) if Pd > 1 else 0
+            want_b += split_bytes(Op // 256, tiles, Np // bk, O, I * Kb * 4, es)
             for v in (L.KAN_VARIANT_AUTO, L.KAN_VARIANT_MFMA, L.KAN_VARIANT_GATHER):
                 d = desc(L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, degree=D, variant=v)
                 gather_f = v == L.KAN_VARIANT_GATHER or (v == L.KAN_VARIANT_AUTO and dt == L.KAN_F32)
@@ -505,12 +523,10 @@ def test_surface_workspace_sizes(L):
             Kb = (G + 3) ** 2
             Op, Np = r(O, 256), r(N, 256)
             kf = r(P * Kb, bk)
-            Pf = fwd_slices((Np // 256) * (Op // 256), kf // bk, N * O * 4, es)
-            want_f = r(Op * kf * es, 256) + (r(Pf * N * O * 4, 256) if Pf > 1 else 0)
+            want_f = r(Op * kf * es, 256) + split_bytes(Np // 256, Op // 256, kf // bk, N, O * 4, es, es == 4)
             tiles = (P * Kb + 255) // 256
             want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 4 * 4, 256)
-            Pd, _ = k_slices((Op // 256) * tiles, Np // bk, O * P * Kb * 4, es)
-            want_b += r(Pd * O * P * Kb * 4, 256) if Pd > 1 else 0
+            want_b += split_bytes(Op // 256, tiles, Np // bk, O, P * Kb * 4, es)
             d = sdesc(L, N=N, P=P, O=O, G=G, dtype=dt)
             assert L.lib().kan_surface_workspace_size(ctypes.byref(d), 0) == want_f
             assert L.lib().kan_surface_workspace_size(ctypes.byref(d), 1) == want_b

@@ -347,6 +347,42 @@ def test_split_batch_dc(F, dtype):
         assert err(_np(y), oracle.layer_forward(x, C, W, *grid)) <= tol
 
 
+def test_tail_split(F):
+    """Launches with a little over one round of output tiles: the tile rows
+    that fill whole rounds run their whole k range and write their outputs,
+    and only the last tile rows run in fixed k slices that fill the final
+    round, summed in slice order.  The forward (4252 rows x 4066 outputs:
+    17 x 16 tiles, of which the last tile row is sliced; both the 2:4 and
+    the dense form) and dC (4302 outputs x 342 inputs, Kb = 12: 17 x 17
+    tiles, the last 2 tile rows sliced) against the oracle in full, with
+    ragged edges on every side, and bitwise the same on a second call."""
+    import torch
+    dtype = "bf16"
+    err, tol = metric(dtype)
+    d = wl.random_layer(4252, 128, 4066, 8, dtype=dtype, base=True, seed=31)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, Wt = to_dev(x, dtype), to_dev(C, dtype), to_dev(W, dtype)
+    ry = oracle.layer_forward(x, C, W, *grid)
+    for dense in (False, True):
+        say("tail split forward 4252x128x4066 dense=%d" % dense)
+        y = F.kan_forward(xt, Ct, Wt, grid, "mfma", dense_forward=dense)
+        y2 = F.kan_forward(xt, Ct, Wt, grid, "mfma", dense_forward=dense)
+        _sync()
+        assert torch.equal(y, y2)
+        assert err(_np(y), ry) <= tol
+    d = wl.random_layer(1000, 342, 4302, 8, dtype=dtype, base=True, seed=32)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    xt, Ct, Wt, dyt = to_dev(x, dtype), to_dev(C, dtype), to_dev(W, dtype), to_dev(dy, "f32")
+    say("tail split dC 1000x342x4302")
+    g1 = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+    g2 = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+    _sync()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    _, rdC, rdW = oracle.layer_backward(x, C, W, dy, *grid, need=("dC", "dW"))
+    assert err(_np(g1[1]), rdC) <= tol and err(_np(g1[2]), rdW) <= tol
+
+
 @pytest.mark.parametrize("variant", ["mfma", "gather"])
 def test_empty_batch(F, variant):
     import torch
