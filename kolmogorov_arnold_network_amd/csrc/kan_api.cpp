@@ -32,9 +32,23 @@ bool overlap(const Range& a, const Range& b) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 
+// Whether a dense bf16 cubic layer builds its basis operand once in HBM
+// rather than in every workgroup that needs it.  Inside the contraction
+// every output tile regenerates the basis tiles of its k range; with few
+// columns per input (Kb <= 12: 21 or more inputs per 256-column tile) that
+// generator work exceeds what loading a built tile costs (c4's first layer,
+// Kb = 9: about 2.2 against 1.6 us per k-tile of a workgroup).  Building
+// costs one write of the N x I Kb bf16 basis, repaid when at least 8 output
+// tiles (O > 1792) read each of its tiles; the array is kept within 1 GiB.
+bool materialize_basis(const Plan& q) {
+    const int64_t bytes = q.Npad * round_up(q.IKb, 256) * 2;
+    return q.dtype == KAN_BF16 && q.degree == 3 && !q.pair && !q.tp && q.Kb <= 12 && q.Opad / kTileN >= 8 &&
+           bytes <= (int64_t(1) << 30);
+}
+
 // Matrix-core geometry and workspace layout of a plan whose shape, K, Kb,
 // base, dtype and per-pass variants are set.
-void plan_layout(Plan& q, bool dense_forward) {
+void plan_layout(Plan& q, bool dense_forward, bool materialize) {
     if (q.variant_fwd != KAN_VARIANT_MFMA && q.variant_bwd != KAN_VARIANT_MFMA) return;
     q.BK = kTileKBytes / q.esize;
     q.IKb = q.I * q.Kb;
@@ -67,6 +81,8 @@ void plan_layout(Plan& q, bool dense_forward) {
     }
     q.Kfs = round_up(q.I * q.Kb8, 64);
     take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
+    q.mat_fwd = materialize && !q.sparse && materialize_basis(q);
+    if (q.mat_fwd) take((size_t)(q.Npad * q.Kf) * q.esize, &q.off_phi, &q.sz_phi);
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
     const KSplit kf = k_split(q.Npad / kTileM, q.Opad / kTileN, nkt_fwd, q.N, q.O * 4, q.esize);
     q.split_fwd = kf.P;
@@ -90,6 +106,8 @@ void plan_layout(Plan& q, bool dense_forward) {
     take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
     take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
     take((size_t)(q.Npad * q.tiles_dx * 2 * (q.pair ? 2 : 1)) * 4, &q.off_part, &q.sz_part);
+    q.mat_dc = materialize && materialize_basis(q);
+    if (q.mat_dc) take((size_t)(q.tiles_dx * kTileN * q.Npad) * q.esize, &q.off_phit, &q.sz_phit);
     const KSplit kc = k_split(q.Opad / kTileM, (q.IKb + kTileN - 1) / kTileN, q.Npad / q.BK, q.O, q.I * q.Kb * 4,
                               q.esize);
     q.split_dc = kc.P;
@@ -143,12 +161,12 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     if (q.N > kIndexLimit || q.O > kIndexLimit || q.xI > kIndexLimit || q.I * q.Kb > kIndexLimit)
         return KAN_ERR_SHAPE;
     q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
-    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
+    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0, false);
     *p = q;
     return KAN_OK;
 }
 
-int make_plan(const kan_desc_t* d, Plan* p) {
+int make_plan(const kan_desc_t* d, Plan* p, bool materialize) {
     if (!d || !p) return KAN_ERR_NULL;
     if (d->N < 0 || d->I < 1 || d->O < 1) return KAN_ERR_SHAPE;
     // G <= kMaxG: the gather kernels stage an input's K = G+3 coefficients
@@ -208,7 +226,7 @@ int make_plan(const kan_desc_t* d, Plan* p) {
     if (tp && (q.dtype != KAN_BF16 || q.degree != 3 || q.variant_fwd != KAN_VARIANT_MFMA))
         return KAN_ERR_UNSUPPORTED;
     q.tp = tp;
-    plan_layout(q, tp || (d->flags & KAN_FLAG_DENSE_FORWARD) != 0);
+    plan_layout(q, tp || (d->flags & KAN_FLAG_DENSE_FORWARD) != 0, materialize);
     if (q.variant_fwd == KAN_VARIANT_GATHER) {
         q.gf = gather_fwd_plan(q.N, q.I, q.O, q.K, q.degree, q.base);
         q.ws_fwd = q.gf.ws;
@@ -347,7 +365,7 @@ int forward_launch(const Plan& p, int flags, const void* x, const void* C, const
         const int st = prepare_impl(p, KAN_PASS_FORWARD, C, W_base, nullptr, ws, s);
         if (st != KAN_OK) return st;
     }
-    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
+    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp), ws_at(ws, p.off_phi),
                                      reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
 }
 
@@ -406,8 +424,8 @@ int kan_backward(const kan_desc_t* desc, const void* x, const void* C, const voi
         e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),
                            reinterpret_cast<float*>(ws_at(ws, p.off_part)), dx, s);
     if (e == hipSuccess && (dC || dW))
-        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), reinterpret_cast<float*>(ws_at(ws, p.off_dcp)),
-                           dC, dW, s);
+        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), ws_at(ws, p.off_phit),
+                           reinterpret_cast<float*>(ws_at(ws, p.off_dcp)), dC, dW, s);
     return status_of(e);
 }
 
@@ -477,7 +495,7 @@ int kan_surface_forward(const kan_surface_desc_t* desc, const void* x, const voi
         st = prepare_impl(p, KAN_PASS_FORWARD, C, nullptr, nullptr, ws, s);
         if (st != KAN_OK) return st;
     }
-    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp),
+    return status_of(launch_mfma_fwd(p, x, ws_at(ws, p.off_cp), ws_at(ws, p.off_phi),
                                      reinterpret_cast<float*>(ws_at(ws, p.off_yp)), y, s));
 }
 
@@ -514,7 +532,8 @@ int kan_surface_backward(const kan_surface_desc_t* desc, const void* x, const vo
         e = launch_mfma_dx(p, x, ws_at(ws, p.off_dyp), ws_at(ws, p.off_cpt),
                            reinterpret_cast<float*>(ws_at(ws, p.off_part)), dx, s);
     if (e == hipSuccess && dC)
-        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), reinterpret_cast<float*>(ws_at(ws, p.off_dcp)),
+        e = launch_mfma_dc(p, x, ws_at(ws, p.off_dyt), ws_at(ws, p.off_phit),
+                           reinterpret_cast<float*>(ws_at(ws, p.off_dcp)),
                            dC, nullptr, s);
     return status_of(e);
 }

@@ -143,9 +143,22 @@ __global__ void basis_eval_deg_kernel(GridK g, int64_t n, const TS* __restrict__
     }
 }
 
+// 8 values per lane and step: two 16-byte loads, one 16-byte store (both
+// arrays are 16-byte aligned); the last n % 8 values one by one
 __global__ void cast_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
-    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
-         k += (int64_t)gridDim.x * blockDim.x)
+    const int64_t n8 = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n8; k += stride) {
+        const float4 a = reinterpret_cast<const float4*>(in)[2 * k];
+        const float4 b = reinterpret_cast<const float4*>(in)[2 * k + 1];
+        uint4 o;
+        o.x = (uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16);
+        o.y = (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16);
+        o.z = (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16);
+        o.w = (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16);
+        reinterpret_cast<uint4*>(out)[k] = o;
+    }
+    for (int64_t k = 8 * n8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n; k += stride)
         out[k] = f2bf(in[k]);
 }
 
@@ -930,7 +943,7 @@ hipError_t launch_basis_eval(const GridK& g, int64_t n, int dtype, const void* x
 }
 
 hipError_t launch_cast_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
-    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid1d(n)), dim3(256), 0, s, in, out, n);
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid1d((n + 7) / 8)), dim3(256), 0, s, in, out, n);
     return hipGetLastError();
 }
 

@@ -150,6 +150,12 @@ struct Plan {
     size_t off_dyt, sz_dyt;    // dy^T in storage dtype: rows j < Opad, k = b < Npad
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
                                // (pairs: [Npad][tiles_dx][2][2], both inputs of the pair)
+    // basis operands built once in HBM (bf16 cubic layers with Kb <= 12 and
+    // at least 8 output tiles): the forward's A operand Phi' [Npad][Kf] and
+    // dC's B operand Phi'^T [tiles_dx * 256][Npad], blocked like the others
+    int mat_fwd, mat_dc;
+    size_t off_phi, sz_phi;    // forward workspace
+    size_t off_phit, sz_phit;  // backward workspace
     size_t off_yp, sz_yp;      // forward slices' partial y of the tail rows: [split_fwd][fwd_tail_rows][O] float
     size_t off_dcp, sz_dcp;    // dC slices' partials of the tail rows j: [split_dc][dc_tail_rows][I][K], then
                                // [split_dc][dc_tail_rows][I] float
@@ -175,7 +181,9 @@ struct KSplit {
 KSplit k_split(int64_t tiles_m, int64_t tiles_n, int64_t nkt, int64_t rows_out, int64_t row_bytes, int esize);
 
 // Builds the plan; returns KAN_OK or the validation error for `desc` alone.
-int make_plan(const kan_desc_t* desc, Plan* p);
+// materialize = false keeps every basis operand inside the contractions
+// (for the fixed-size workspace of kan_forward_static).
+int make_plan(const kan_desc_t* desc, Plan* p, bool materialize = true);
 // The plan of a 2-D tensor-product layer (always on the matrix cores).
 int make_plan_surface(const kan_surface_desc_t* desc, Plan* p);
 
@@ -206,11 +214,11 @@ hipError_t launch_pack_fwd(const Plan& p, const void* C, const void* W, void* cp
 hipError_t launch_pack_fwd_sparse(const Plan& p, const void* C, const void* W, void* cp, hipStream_t s);
 hipError_t launch_pack_bwd(const Plan& p, const void* C, const void* W, void* cpt, hipStream_t s);
 hipError_t launch_prep_dy(const Plan& p, const float* dy, void* dyp, void* dyt, hipStream_t s);
-hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y,
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, void* phi, float* ypart, float* y,
                            hipStream_t s);
 hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const void* cpt,
                           float* part, float* dx, hipStream_t s);
-hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float* dC,
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, void* phit, float* cpart, float* dC,
                           float* dW, hipStream_t s);
 
 // Grouped spline activation: blocks of 256 channels by chunks of rows.

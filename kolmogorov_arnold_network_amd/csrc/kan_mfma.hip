@@ -1531,6 +1531,14 @@ __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__
     }
 }
 
+// 4 consecutive stored elements at p (8 bytes of bf16, 16 of float; p aligned to that)
+__device__ __forceinline__ void store4(uint16_t* p, const uint16_t (&o)[4]) {
+    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                              (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+}
+__device__ __forceinline__ void store4(float* p, const float (&o)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+}
 template <typename TS> __device__ __forceinline__ TS to_store(float v);
 template <> __device__ __forceinline__ float to_store<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { return f2bf(v); }
@@ -1541,22 +1549,41 @@ template <> __device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { re
 template <typename TS>
 __global__ void prep_dy_kernel(const float* __restrict__ dy, TS* __restrict__ dyp,
                                TS* __restrict__ dyt, int N, int O, int64_t Npad, int64_t Opad) {
-    __shared__ TS tile[64][65];
+    __shared__ TS tile[64][68];
     constexpr int BK = Traits<TS>::BK;
     const int64_t b0 = (int64_t)blockIdx.x * 64;
     const int64_t j0 = (int64_t)blockIdx.y * 64;
     const int t = threadIdx.x;
-    for (int e = t; e < 64 * 64; e += 256) {
-        const int bb = e / 64, jj = e % 64;
-        const int64_t b = b0 + bb, j = j0 + jj;
-        const TS v = (b < N && j < O) ? to_store<TS>(dy[b * O + j]) : TS(0);
-        dyp[blk<TS>(b, j, Opad / BK)] = v;
-        tile[bb][jj] = v;
+    // 4 consecutive values per lane: one 16-byte load of dy when the row
+    // holds them at a 16-byte boundary, and 4 consecutive packed elements
+    // (one k-tile holds them: BK and the offsets are multiples of 4)
+    const bool vec = (O & 3) == 0;
+    for (int e = t; e < 64 * 16; e += 256) {
+        const int bb = e >> 4, jq = (e & 15) * 4;
+        const int64_t b = b0 + bb, j = j0 + jq;
+        float v[4];
+        if (vec && b < N && j + 3 < O) {
+            const float4 f = *reinterpret_cast<const float4*>(dy + b * O + j);
+            v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = (b < N && j + q < O) ? dy[b * O + j + q] : 0.0f;
+        }
+        TS o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o[q] = to_store<TS>(v[q]);
+            tile[bb][jq + q] = o[q];
+        }
+        store4(dyp + blk<TS>(b, j, Opad / BK), o);
     }
     __syncthreads();
-    for (int e = t; e < 64 * 64; e += 256) {
-        const int jj = e / 64, bb = e % 64;
-        dyt[blk<TS>(j0 + jj, b0 + bb, Npad / BK)] = tile[bb][jj];
+    for (int e = t; e < 64 * 16; e += 256) {
+        const int jj = e >> 4, bq = (e & 15) * 4;
+        TS o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = tile[bq + q][jj];
+        store4(dyt + blk<TS>(j0 + jj, b0 + bq, Npad / BK), o);
     }
 }
 
@@ -1569,6 +1596,40 @@ hipError_t run_gemm(const GemmArgs& a, hipStream_t s) {
     const int64_t slices = a.tail > 0 ? (a.nkt + a.nks - 1) / a.nks : 0;
     const int64_t blocks = (int64_t)(a.tiles_m - a.tail) * a.tiles_n + (int64_t)a.tail * a.tiles_n * slices;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+// The operand a generator would build in LDS, built once and written to
+// HBM in the blocked layout the copied operands read (k-tile kt of 256-row
+// tile T: one contiguous block of 256 rows x 128 bytes at T * tstride + kt *
+// BLOCK_BYTES).  One workgroup per (k-tile, tile): the generator fills one
+// LDS tile exactly as inside the contraction, then the block is copied out,
+// so a contraction that loads it computes the same bits as one that
+// generates it.  AOP: the generator is an A operand (its tile is a row tile
+// tm), else a B operand (its tile is a column tile tn).
+template <typename TS, class Gen, bool AOP>
+__global__ __launch_bounds__(NTHR, 1) void gen_pack_kernel(GemmArgs args, char* __restrict__ out,
+                                                           int64_t tstride) {
+    extern __shared__ uint4 lds4[];
+    char* S = reinterpret_cast<char*>(lds4);
+    const int kt = blockIdx.x, T = blockIdx.y;
+    Gen g(args, AOP ? T : 0, AOP ? 0 : T);
+    g.template fetch<0>(args, kt);
+    static_for<0, Gen::NPART>([&](auto pc) {
+        g.template part<0, false, decltype(pc)::value>(args, S, kt, kt);
+    });
+    __syncthreads();
+    char* dst = out + T * tstride + (int64_t)kt * BLOCK_BYTES;
+#pragma unroll
+    for (int c = threadIdx.x; c < 256 * 8; c += NTHR)     // 16-byte chunk c % 8 of row c / 8
+        *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(S + (c >> 3) * PITCH + (c & 7) * 16);
+}
+
+template <typename TS, class Gen, bool AOP>
+hipError_t run_gen_pack(const GemmArgs& a, int tiles, int nkt, char* out, hipStream_t s) {
+    auto kern = gen_pack_kernel<TS, Gen, AOP>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nkt, (unsigned)tiles), dim3(NTHR), TILE_BYTES, s, a, out,
+                       (int64_t)nkt * BLOCK_BYTES);
     return hipGetLastError();
 }
 
@@ -1772,7 +1833,24 @@ static hipError_t fwd_run(const Plan& p, GemmArgs& a, hipStream_t s) {
     return fwd_dispatch<uint16_t>(p, a, s);
 }
 
-hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y,
+// the dense bf16 forward of a cubic layer with its basis operand built once
+// in HBM (Plan::mat_fwd): the generator as in fwd_dispatch, into a pack
+static hipError_t fwd_mat_run(const Plan& p, GemmArgs& a, void* phi, hipStream_t s) {
+    const int n = fwd_nin(p);
+    char* out = static_cast<char*>(phi);
+    hipError_t e;
+    if (n <= 2) e = run_gen_pack<uint16_t, GenA<uint16_t, 2>, true>(a, a.tiles_m, a.nkt, out, s);
+    else if (n <= 4) e = run_gen_pack<uint16_t, GenA<uint16_t, 4>, true>(a, a.tiles_m, a.nkt, out, s);
+    else if (n <= 8) e = run_gen_pack<uint16_t, GenA<uint16_t, 8>, true>(a, a.tiles_m, a.nkt, out, s);
+    else if (n <= 16) e = run_gen_pack<uint16_t, GenA<uint16_t, 16>, true>(a, a.tiles_m, a.nkt, out, s);
+    else e = run_gen_pack<uint16_t, GenA<uint16_t, 32>, true>(a, a.tiles_m, a.nkt, out, s);
+    if (e != hipSuccess) return e;
+    a.a = out;
+    a.a_tstride = (int64_t)a.nkt * BLOCK_BYTES;
+    return run_gemm<uint16_t, LoadA, LoadB, EpiY>(a, s);
+}
+
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, void* phi, float* ypart, float* y,
                            hipStream_t s) {
     GemmArgs a = base_args(p, x);
     a.tiles_m = (int)(p.Npad / 256);
@@ -1781,7 +1859,8 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.nkt = (int)(p.sparse ? p.Kfs / 64 : p.Kf / p.BK);
     a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
     a.out0 = y;
-    if (p.split_fwd <= 1) return fwd_run(p, a, s);
+    auto run = [&]() { return p.mat_fwd ? fwd_mat_run(p, a, phi, s) : fwd_run(p, a, s); };
+    if (p.split_fwd <= 1) return run();
     // the tail rows in split_fwd slices: partials, then a sum in slice order
     const int64_t r0 = first_fwd_row(p), n = fwd_tail_rows(p) * p.O;
     a.tail = (int)p.tail_fwd;
@@ -1789,7 +1868,7 @@ hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* 
     a.part0 = ypart;
     a.ostride0 = n;
     a.oshift0 = r0 * p.O;
-    hipError_t e = fwd_run(p, a, s);
+    hipError_t e = run();
     return e != hipSuccess ? e : sum_slices(ypart, y + r0 * p.O, n, p.split_fwd, s);
 }
 
@@ -1835,7 +1914,23 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float* dC,
+// dC of a cubic bf16 layer with its basis operand built once in HBM
+// (Plan::mat_dc): the generator as in dc_dispatch, into a pack
+static hipError_t dc_mat_run(const Plan& p, GemmArgs& a, void* phit, hipStream_t s) {
+    const int zr = (p.Kb + 7) / 8;
+    const int nq = dc_nqw(p);
+    char* out = static_cast<char*>(phit);
+    hipError_t e;
+    if (zr <= 1 && nq <= 10) e = run_gen_pack<uint16_t, GenB<uint16_t, 10, 1>, false>(a, a.tiles_n, a.nkt, out, s);
+    else if (zr <= 2 && nq <= 4) e = run_gen_pack<uint16_t, GenB<uint16_t, 4, 2>, false>(a, a.tiles_n, a.nkt, out, s);
+    else return hipErrorInvalidValue;     // the plan materializes Kb <= 12 only
+    if (e != hipSuccess) return e;
+    a.b = out;
+    a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;
+    return run_gemm<uint16_t, LoadA, LoadB, EpiDC>(a, s);
+}
+
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, void* phit, float* cpart, float* dC,
                           float* dW, hipStream_t s) {
     GemmArgs a = base_args(p, x);
     a.tiles_m = (int)(p.Opad / 256);
@@ -1847,6 +1942,7 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* 
     a.out1 = dW;
     a.group_m = 2;
     auto dispatch = [&]() {
+        if (p.mat_dc) return dc_mat_run(p, a, phit, s);
         if (p.degree != 3) return p.dtype == KAN_F32 ? dc_dispatch_deg<float>(p, a, s) : dc_dispatch_deg<uint16_t>(p, a, s);
         if (p.pair) return p.dtype == KAN_F32 ? dc_dispatch_pair<float>(p, a, s) : dc_dispatch_pair<uint16_t>(p, a, s);
         return p.dtype == KAN_F32 ? dc_dispatch<float>(p, a, s) : dc_dispatch<uint16_t>(p, a, s);

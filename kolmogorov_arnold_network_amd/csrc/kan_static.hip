@@ -40,7 +40,7 @@ extern "C" {
 int kan_forward_static(const kan_desc_t* desc, const void* x, const void* C, const void* W_base, float* y,
                        void* stream) {
     kan::Plan p;
-    int st = kan::make_plan(desc, &p);
+    int st = kan::make_plan(desc, &p, false);
     if (st != KAN_OK) return st;
     if (desc->flags & KAN_FLAG_PREPARED) return KAN_ERR_UNSUPPORTED;   // the array is shared by every call
     if (p.ws_fwd > (size_t)KAN_STATIC_SCRATCH_BYTES) return KAN_ERR_WORKSPACE;

@@ -91,8 +91,10 @@ hipError_t launch_prep_dy(const Plan&, const float* dy, void* dyp, void* dyt, hi
     ++g_launches;
     return hipSuccess;
 }
-hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, float* ypart, float* y, hipStream_t) {
-    need(x && cp && y, "mfma forward pointers");
+hipError_t launch_mfma_fwd(const Plan& p, const void* x, const void* cp, void* phi, float* ypart, float* y,
+                           hipStream_t) {
+    need(x && cp && y && (!p.mat_fwd || phi), "mfma forward pointers");
+    if (p.mat_fwd) need(p.off_phi + (size_t)p.Npad * p.Kf * 2 <= p.ws_fwd && !p.sparse, "forward basis in the workspace");
     need(p.split_fwd >= 1 && (p.split_fwd == 1 || ypart), "mfma forward slices");
     need(p.split_fwd == 1 || (p.tail_fwd >= 1 && p.tail_fwd <= p.Npad / 256 && fwd_tail_rows(p) >= 1 &&
                               p.nks_fwd * (p.split_fwd - 1) < (p.sparse ? p.Kfs / 64 : p.Kf / p.BK)),
@@ -108,9 +110,11 @@ hipError_t launch_mfma_dx(const Plan&, const void* x, const void* dyp, const voi
     ++g_launches;
     return hipSuccess;
 }
-hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, float* cpart, float*, float*,
+hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, void* phit, float* cpart, float*, float*,
                           hipStream_t) {
-    need(x && dyt && (p.split_dc == 1 || cpart), "mfma dC pointers");
+    need(x && dyt && (p.split_dc == 1 || cpart) && (!p.mat_dc || phit), "mfma dC pointers");
+    if (p.mat_dc)
+        need(p.off_phit + (size_t)p.tiles_dx * 256 * p.Npad * 2 <= p.ws_bwd && p.Kb <= 12, "dC basis in the workspace");
     need(p.split_dc == 1 || (p.tail_dc >= 1 && p.tail_dc <= p.Opad / 256 && dc_tail_rows(p) >= 1 &&
                              p.nks_dc * (p.split_dc - 1) < p.Npad / p.BK),
          "mfma dC tail");

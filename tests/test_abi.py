@@ -301,7 +301,8 @@ def test_workspace_sizes(L):
     r = lambda a, b: (a + b - 1) // b * b
     for dt, es, bk in [(L.KAN_F32, 4, 32), (L.KAN_BF16, 2, 64)]:
         for (N, I, O, G, base) in [(64, 16, 8, 8, 1), (1000, 777, 300, 20, 0), (5, 3, 2, 1, 1),
-                                   (12608, 768, 3072, 5, 1), (12608, 3072, 768, 5, 1), (8192, 1024, 1024, 50, 0)]:
+                                   (12608, 768, 3072, 5, 1), (12608, 3072, 768, 5, 1), (8192, 1024, 1024, 50, 0),
+                                   (300, 40, 2000, 8, 1), (700, 100, 1793, 3, 0), (65536, 4096, 4096, 5, 1)]:
             Kb = G + 3 + base
             # bf16 forwards with 11 <= Kb <= 32 whose 2:4 layout (NG groups of 4
             # columns per input) costs <= 3/4 of the dense one pack I * 4 NG columns
@@ -309,12 +310,18 @@ def test_workspace_sizes(L):
             ng += ng & 1
             sparse = dt == L.KAN_BF16 and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
             Op, Np = r(O, 256), r(N, 256)
+            # bf16 layers with Kb <= 12 and at least 8 output tiles build the
+            # dense basis operand once (forward: [Np][I Kb padded to 64];
+            # dC: [I Kb padded to 256][Np])
+            mat = dt == L.KAN_BF16 and Kb <= 12 and Op // 256 >= 8 and Np * r(I * Kb, 256) * 2 <= 1 << 30
 
-            def fwd_bytes(kf, nkt):
-                # packed C', then the partial y of a split forward
-                return r(Op * kf * es, 256) + split_bytes(Np // 256, Op // 256, nkt, N, O * 4, es, es == 4)
+            def fwd_bytes(kf, nkt, basis=False):
+                # packed C', the built basis, then the partial y of a split forward
+                return (r(Op * kf * es, 256) + (r(Np * kf * es, 256) if basis else 0)
+                        + split_bytes(Np // 256, Op // 256, nkt, N, O * 4, es, es == 4))
             kf = r(I * 4 * ng, 64) if sparse else r(I * Kb, bk)
-            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == fwd_bytes(kf, kf // (64 if sparse else bk))
+            assert ws(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == \
+                fwd_bytes(kf, kf // (64 if sparse else bk), mat and not sparse)
             if dt == L.KAN_BF16:
                 # the truncated-power forward packs the dense operand
                 assert L.lib().kan_workspace_size(ctypes.byref(desc(
@@ -323,9 +330,10 @@ def test_workspace_sizes(L):
             if sparse:
                 assert L.lib().kan_workspace_size(ctypes.byref(desc(
                     L, N=N, I=I, O=O, G=G, has_base=base, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)), 0) == \
-                    fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk)
+                    fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk, mat)
             tiles = (I * Kb + 255) // 256           # dx tiles of 256 P columns
             want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
+            want += r(tiles * 256 * Np * es, 256) if mat else 0
             want += split_bytes(Op // 256, tiles, Np // bk, O, I * Kb * 4, es)   # dC over batch slices
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores; float32 forward on the gather kernel and

@@ -383,6 +383,36 @@ def test_tail_split(F):
     assert err(_np(g1[1]), rdC) <= tol and err(_np(g1[2]), rdW) <= tol
 
 
+@pytest.mark.parametrize("shape", [(300, 40, 2000, 8, True), (700, 100, 1793, 3, False)])
+def test_materialized_basis(F, shape):
+    """bf16 layers with few columns per input (Kb = 12 and 6) and at least
+    8 output tiles build their dense basis operand once in HBM: the forward
+    (dense form) and dC against the oracle in full, and the forward bitwise
+    equal to kan_forward_static, whose fixed workspace keeps the basis
+    generated inside the contraction (the same LDS tiles, so the same
+    bits)."""
+    import torch
+    N, I, O, G, base = shape
+    dtype = "bf16"
+    err, tol = metric(dtype)
+    d = wl.random_layer(N, I, O, G, dtype=dtype, base=base, seed=33)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, dyt = to_dev(x, dtype), to_dev(C, dtype), to_dev(dy, "f32")
+    Wt = to_dev(W, dtype) if base else None
+    say("materialized basis %dx%dx%d G=%d base=%d" % shape)
+    y = F.kan_forward(xt, Ct, Wt, grid, "mfma", dense_forward=True)
+    ys = F.kan_forward_static(xt, Ct, Wt, grid, "mfma", dense_forward=True)
+    g = F.kan_backward(xt, Ct, Wt, dyt, grid, variant="mfma")
+    _sync()
+    assert torch.equal(y, ys)
+    assert err(_np(y), oracle.layer_forward(x, C, W, *grid)) <= tol
+    rdx, rdC, rdW = oracle.layer_backward(x, C, W, dy, *grid)
+    assert err(_np(g[0]), rdx) <= tol and err(_np(g[1]), rdC) <= tol
+    if base:
+        assert err(_np(g[2]), rdW) <= tol
+
+
 @pytest.mark.parametrize("variant", ["mfma", "gather"])
 def test_empty_batch(F, variant):
     import torch
