@@ -32,18 +32,21 @@ bool overlap(const Range& a, const Range& b) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 
-// Whether a dense bf16 cubic layer builds its basis operand once in HBM
+// Whether a dense bf16 cubic layer builds a basis operand once in HBM
 // rather than in every workgroup that needs it.  Inside the contraction
 // every output tile regenerates the basis tiles of its k range; with few
 // columns per input (Kb <= 12: 21 or more inputs per 256-column tile) that
-// generator work exceeds what loading a built tile costs (c4's first layer,
-// Kb = 9: about 2.2 against 1.6 us per k-tile of a workgroup).  Building
-// costs one write of the N x I Kb bf16 basis, repaid when at least 8 output
-// tiles (O > 1792) read each of its tiles; the array is kept within 1 GiB.
-bool materialize_basis(const Plan& q) {
+// generator work exceeds what loading a built tile costs (c4, Kb = 9: about
+// 2.2 (forward) and 2.5 (dC) against 1.6-1.8 us per k-tile of a
+// workgroup).  Building costs one write of the N x I Kb bf16 basis, repaid
+// when enough output tiles read each of its tiles: measured at c4, the
+// forward gains with 12 reading tiles and loses with 3; dC gains with 12
+// and with 3.  So the forward's operand is built from 8 output tiles
+// (O > 1792) and dC's from 3 (O > 512); the array is kept within 1 GiB.
+bool materialize_basis(const Plan& q, int64_t min_tiles) {
     const int64_t bytes = q.Npad * round_up(q.IKb, 256) * 2;
-    return q.dtype == KAN_BF16 && q.degree == 3 && !q.pair && !q.tp && q.Kb <= 12 && q.Opad / kTileN >= 8 &&
-           bytes <= (int64_t(1) << 30);
+    return q.dtype == KAN_BF16 && q.degree == 3 && !q.pair && !q.tp && q.Kb <= 12 &&
+           q.Opad / kTileN >= min_tiles && bytes <= (int64_t(1) << 30);
 }
 
 // Matrix-core geometry and workspace layout of a plan whose shape, K, Kb,
@@ -81,7 +84,7 @@ void plan_layout(Plan& q, bool dense_forward, bool materialize) {
     }
     q.Kfs = round_up(q.I * q.Kb8, 64);
     take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
-    q.mat_fwd = materialize && !q.sparse && materialize_basis(q);
+    q.mat_fwd = materialize && !q.sparse && materialize_basis(q, 8);
     if (q.mat_fwd) take((size_t)(q.Npad * q.Kf) * q.esize, &q.off_phi, &q.sz_phi);
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
     const KSplit kf = k_split(q.Npad / kTileM, q.Opad / kTileN, nkt_fwd, q.N, q.O * 4, q.esize);
@@ -106,7 +109,7 @@ void plan_layout(Plan& q, bool dense_forward, bool materialize) {
     take((size_t)(q.Npad * q.Opad) * q.esize, &q.off_dyp, &q.sz_dyp);
     take((size_t)(q.Opad * q.Npad) * q.esize, &q.off_dyt, &q.sz_dyt);
     take((size_t)(q.Npad * q.tiles_dx * 2 * (q.pair ? 2 : 1)) * 4, &q.off_part, &q.sz_part);
-    q.mat_dc = materialize && materialize_basis(q);
+    q.mat_dc = materialize && materialize_basis(q, 3);
     if (q.mat_dc) take((size_t)(q.tiles_dx * kTileN * q.Npad) * q.esize, &q.off_phit, &q.sz_phit);
     const KSplit kc = k_split(q.Opad / kTileM, (q.IKb + kTileN - 1) / kTileN, q.Npad / q.BK, q.O, q.I * q.Kb * 4,
                               q.esize);

@@ -223,10 +223,11 @@ __device__ __forceinline__ RecD<D> zero_rec() {
 // W_base and x are loaded into registers, then written (x as its span record)
 // to the other buffer, with one barrier per chunk.
 //
-// - A thread's sums over one chunk are float32; each chunk's sum is added
-//   into a float64 accumulator.  In a chain of layers the next layer's B'
-//   amplifies forward rounding about tenfold, so the long sum over inputs
-//   is kept out of float32.
+// - A thread's sums over a run of at most 8 inputs (one chunk, or several
+//   chunks when K is large and a chunk holds fewer than 8 inputs) are
+//   float32; each run's sum is added into a float64 accumulator.  In a chain
+//   of layers the next layer's B' amplifies forward rounding about tenfold,
+//   so the long sum over inputs is kept out of float32.
 // - All R rows of the block share one staged chunk, so the coefficient
 //   traffic per row, the part of the work that grows with G, falls as R
 //   grows.
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(NT) void gather_fwd_kernel(GatherFwdArgs a) {
     const int slice = blockIdx.y;
     const int ib = slice * a.IS, ie = min(I, ib + a.IS);
     const int nch = (ie - ib + IC - 1) / IC;
+    const int fold = max(1, 8 / IC);                 // chunks per float32 run
 
     // Coefficient loads: output jl = t % 64 of the block (an output past O
     // reads output O - 1; its sums are never stored), 4-element pieces
@@ -438,13 +440,17 @@ __global__ __launch_bounds__(NT) void gather_fwd_kernel(GatherFwdArgs a) {
                 if (PG < 4 && p % PG == PG - 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // float32 sums over runs of at most 8 inputs (one chunk of 8, or
+        // fold chunks of fewer), each folded into the float64 sums
+        if ((c + 1) % fold == 0 || !more) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+            for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                accd[p][q] += (double)acc[p][q];
-                acc[p][q] = 0.0f;
-            }
+                for (int q = 0; q < 4; ++q) {
+                    accd[p][q] += (double)acc[p][q];
+                    acc[p][q] = 0.0f;
+                }
+        }
         if (more) store(c + 1, (c + 1) & 1);
         __syncthreads();
     }

@@ -151,8 +151,9 @@ struct Plan {
     size_t off_part, sz_part;  // dx partial sums of inputs cut by a tile edge: [Npad][tiles_dx][2] float
                                // (pairs: [Npad][tiles_dx][2][2], both inputs of the pair)
     // basis operands built once in HBM (bf16 cubic layers with Kb <= 12 and
-    // at least 8 output tiles): the forward's A operand Phi' [Npad][Kf] and
-    // dC's B operand Phi'^T [tiles_dx * 256][Npad], blocked like the others
+    // at least 8 (forward) or 3 (dC) output tiles): the forward's A operand
+    // Phi' [Npad][Kf] and dC's B operand Phi'^T [tiles_dx * 256][Npad],
+    // blocked like the others
     int mat_fwd, mat_dc;
     size_t off_phi, sz_phi;    // forward workspace
     size_t off_phit, sz_phit;  // backward workspace

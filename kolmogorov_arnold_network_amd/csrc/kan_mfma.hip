@@ -1408,6 +1408,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs args) {
     Epi::template run<TS>(args, acc, tm, tn, lds);
 }
 
+// 4 consecutive stored elements at p (8 bytes of bf16, 16 of float; p aligned to that)
+__device__ __forceinline__ void store4(uint16_t* p, const uint16_t (&o)[4]) {
+    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                              (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+}
+__device__ __forceinline__ void store4(float* p, const float (&o)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+}
+
 // ---- packing ----
 // The loaded operands are stored blocked: element (row r, k) of an operand
 // with nk = K / BK k-tiles sits at ((r / 256) * nk + k / BK) * 256 * BK +
@@ -1429,18 +1438,20 @@ __global__ void pack_fwd_kernel(const TS* __restrict__ C, const TS* __restrict__
     const int64_t IKb = (int64_t)I * Kb;
     const int64_t Kf = nk * Traits<TS>::BK;
     for (int64_t j = blockIdx.y; j < Opad; j += gridDim.y) {
+        // 4 consecutive k of one k-tile (Kf and BK are multiples of 4): one store
         for (int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k0 < Kf;
              k0 += (int64_t)gridDim.x * blockDim.x * 4) {
             int i = (int)(k0 / Kb), m = (int)(k0 - (int64_t)i * Kb);
+            TS v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t k = k0 + e;
-                TS v = TS(0);
+                v[e] = TS(0);
                 if (j < O && k < IKb)
-                    v = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
-                if (k < Kf) cp[blk<TS>(j, k, nk)] = v;
+                    v[e] = m < K ? C[((int64_t)j * I + i) * K + m] : W[(int64_t)j * I + i];
                 if (++m == Kb) { m = 0; ++i; }
             }
+            store4(cp + blk<TS>(j, k0, nk), v);
         }
     }
 }
@@ -1531,14 +1542,6 @@ __global__ void pack_bwd_kernel(const TS* __restrict__ C, const TS* __restrict__
     }
 }
 
-// 4 consecutive stored elements at p (8 bytes of bf16, 16 of float; p aligned to that)
-__device__ __forceinline__ void store4(uint16_t* p, const uint16_t (&o)[4]) {
-    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                              (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-}
-__device__ __forceinline__ void store4(float* p, const float (&o)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
-}
 template <typename TS> __device__ __forceinline__ TS to_store(float v);
 template <> __device__ __forceinline__ float to_store<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t to_store<uint16_t>(float v) { return f2bf(v); }

@@ -310,10 +310,11 @@ def test_workspace_sizes(L):
             ng += ng & 1
             sparse = dt == L.KAN_BF16 and ng <= 8 and Kb >= 11 and 8 * ng <= 3 * Kb
             Op, Np = r(O, 256), r(N, 256)
-            # bf16 layers with Kb <= 12 and at least 8 output tiles build the
-            # dense basis operand once (forward: [Np][I Kb padded to 64];
-            # dC: [I Kb padded to 256][Np])
-            mat = dt == L.KAN_BF16 and Kb <= 12 and Op // 256 >= 8 and Np * r(I * Kb, 256) * 2 <= 1 << 30
+            # bf16 layers with Kb <= 12 build the dense basis operand once:
+            # the forward's ([Np][I Kb padded to 64]) from 8 output tiles,
+            # dC's ([I Kb padded to 256][Np]) from 3
+            fits = dt == L.KAN_BF16 and Kb <= 12 and Np * r(I * Kb, 256) * 2 <= 1 << 30
+            mat, mat_dc = fits and Op // 256 >= 8, fits and Op // 256 >= 3
 
             def fwd_bytes(kf, nkt, basis=False):
                 # packed C', the built basis, then the partial y of a split forward
@@ -333,7 +334,7 @@ def test_workspace_sizes(L):
                     fwd_bytes(r(I * Kb, bk), r(I * Kb, bk) // bk, mat)
             tiles = (I * Kb + 255) // 256           # dx tiles of 256 P columns
             want = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
-            want += r(tiles * 256 * Np * es, 256) if mat else 0
+            want += r(tiles * 256 * Np * es, 256) if mat_dc else 0
             want += split_bytes(Op // 256, tiles, Np // bk, O, I * Kb * 4, es)   # dC over batch slices
             assert wb(N=N, I=I, O=O, G=G, has_base=base, dtype=dt) == want
     # auto: bf16 on the matrix cores; float32 forward on the gather kernel and

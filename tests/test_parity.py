@@ -383,14 +383,14 @@ def test_tail_split(F):
     assert err(_np(g1[1]), rdC) <= tol and err(_np(g1[2]), rdW) <= tol
 
 
-@pytest.mark.parametrize("shape", [(300, 40, 2000, 8, True), (700, 100, 1793, 3, False)])
+@pytest.mark.parametrize("shape", [(300, 40, 2000, 8, True), (700, 100, 1793, 3, False), (500, 60, 600, 5, True)])
 def test_materialized_basis(F, shape):
-    """bf16 layers with few columns per input (Kb = 12 and 6) and at least
-    8 output tiles build their dense basis operand once in HBM: the forward
-    (dense form) and dC against the oracle in full, and the forward bitwise
-    equal to kan_forward_static, whose fixed workspace keeps the basis
-    generated inside the contraction (the same LDS tiles, so the same
-    bits)."""
+    """bf16 layers with few columns per input (Kb = 12, 6 and 9) build their
+    dense basis operands once in HBM, the forward's from 8 output tiles and
+    dC's from 3 (the third shape: dC only): the forward (dense form) and dC
+    against the oracle in full, and the forward bitwise equal to
+    kan_forward_static, whose fixed workspace keeps the basis generated
+    inside the contraction (the same LDS tiles, so the same bits)."""
     import torch
     N, I, O, G, base = shape
     dtype = "bf16"
