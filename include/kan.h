@@ -174,7 +174,11 @@ const char* kan_status_string(int status);
  * float32 partial outputs of k-range slices (the forward's y, slices of at
  * most 256 terms in float32 and otherwise where too few output tiles fill
  * the GPU; dC and dW_base over batch slices), which are added in slice
- * order.  GATHER needs it only when too few blocks fill the GPU: the
+ * order.  A bf16 layer with few columns per input (G + 3 + has_base <= 12)
+ * also gets its dense basis built once from x, in bf16, when enough output
+ * tiles read it: the forward's [N][I*(G+3+has_base)] from O > 1792, dC's
+ * transpose from O > 512 (the 2-D layer's dC pair basis too), each at most
+ * 1 GiB.  kan_forward writes it; it is not part of kan_prepare.  GATHER needs it only when too few blocks fill the GPU: the
  * forward then splits its inputs into slices whose float64 partial outputs
  * [slices][N][O] are added in slice order, the backward splits dx over
  * output slices and dC / dW_base over row slices, with float32 partials
@@ -199,12 +203,14 @@ int kan_forward(const kan_desc_t* desc, const void* x, const void* C, const void
 /* ---- Forward without a caller workspace --------------------------------
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  The same
- * forward as kan_forward (same kernels, same bits), with the workspace taken
- * from a fixed array of KAN_STATIC_SCRATCH_BYTES of device memory inside the
- * library.  Every GPU the library runs on holds its own copy of that array
- * from the first call until the process ends; the call itself allocates and
- * frees nothing.  A layer whose forward workspace (kan_workspace_size) is
- * larger returns KAN_ERR_WORKSPACE before any work; KAN_FLAG_PREPARED is
+ * forward as kan_forward (the same bits), with the workspace taken from a
+ * fixed array of KAN_STATIC_SCRATCH_BYTES of device memory inside the
+ * library.  It never builds the basis in the workspace (kan_workspace_size);
+ * its contraction generates the same basis tiles on chip.  Every GPU the
+ * library runs on holds its own copy of that array from the first call
+ * until the process ends; the call itself allocates and frees nothing.  A
+ * layer whose forward workspace, without the built basis, is larger returns
+ * KAN_ERR_WORKSPACE before any work; KAN_FLAG_PREPARED is
  * refused (KAN_ERR_UNSUPPORTED).  The array keeps the last call's contents
  * and nothing in it has to start at zero.  All calls on one GPU share the
  * array, so calls that overlap in time on one GPU (on different streams or
@@ -342,7 +348,8 @@ typedef struct {
 /* Bytes of workspace a pass of the 2-D layer needs (SIZE_MAX if `desc` is
  * invalid): the packed coefficient operand, and for the backward dy in both
  * orientations and the dx partial sums of pairs cut by a tile edge, plus the
- * float32 partial outputs of k-range slices, as for kan_workspace_size. */
+ * float32 partial outputs of k-range slices and, for a bf16 backward with
+ * O > 512, dC's pair basis built once, as for kan_workspace_size. */
 size_t kan_surface_workspace_size(const kan_surface_desc_t* desc, int pass);
 
 /* Forward: y [N, O] float32. */

@@ -43,9 +43,11 @@ int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 // forward gains with 12 reading tiles and loses with 3; dC gains with 12
 // and with 3.  So the forward's operand is built from 8 output tiles
 // (O > 1792) and dC's from 3 (O > 512); the array is kept within 1 GiB.
+// The 2-D layer's dC generator (16 products per pair) costs more than a
+// load at any pair width, so its dC operand is built by the same rule.
 bool materialize_basis(const Plan& q, int64_t min_tiles) {
     const int64_t bytes = q.Npad * round_up(q.IKb, 256) * 2;
-    return q.dtype == KAN_BF16 && q.degree == 3 && !q.pair && !q.tp && q.Kb <= 12 &&
+    return q.dtype == KAN_BF16 && q.degree == 3 && !q.tp && (q.pair || q.Kb <= 12) &&
            q.Opad / kTileN >= min_tiles && bytes <= (int64_t(1) << 30);
 }
 
@@ -84,7 +86,7 @@ void plan_layout(Plan& q, bool dense_forward, bool materialize) {
     }
     q.Kfs = round_up(q.I * q.Kb8, 64);
     take((size_t)(q.Opad * (q.sparse ? q.Kfs : q.Kf)) * q.esize, &q.off_cp, &q.sz_cp);
-    q.mat_fwd = materialize && !q.sparse && materialize_basis(q, 8);
+    q.mat_fwd = materialize && !q.sparse && !q.pair && materialize_basis(q, 8);
     if (q.mat_fwd) take((size_t)(q.Npad * q.Kf) * q.esize, &q.off_phi, &q.sz_phi);
     const int64_t nkt_fwd = q.sparse ? q.Kfs / 64 : q.Kf / q.BK;
     const KSplit kf = k_split(q.Npad / kTileM, q.Opad / kTileN, nkt_fwd, q.N, q.O * 4, q.esize);
@@ -164,7 +166,7 @@ int make_plan_surface(const kan_surface_desc_t* d, Plan* p) {
     if (q.N > kIndexLimit || q.O > kIndexLimit || q.xI > kIndexLimit || q.I * q.Kb > kIndexLimit)
         return KAN_ERR_SHAPE;
     q.variant_fwd = q.variant_bwd = KAN_VARIANT_MFMA;
-    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0, false);
+    plan_layout(q, (d->flags & KAN_FLAG_DENSE_FORWARD) != 0, true);
     *p = q;
     return KAN_OK;
 }

@@ -1918,15 +1918,26 @@ hipError_t launch_mfma_dx(const Plan& p, const void* x, const void* dyp, const v
 }
 
 // dC of a cubic bf16 layer with its basis operand built once in HBM
-// (Plan::mat_dc): the generator as in dc_dispatch, into a pack
+// (Plan::mat_dc): the generator as in dc_dispatch (dc_dispatch_pair for the
+// 2-D layer), into a pack
 static hipError_t dc_mat_run(const Plan& p, GemmArgs& a, void* phit, hipStream_t s) {
     const int zr = (p.Kb + 7) / 8;
     const int nq = dc_nqw(p);
     char* out = static_cast<char*>(phit);
     hipError_t e;
-    if (zr <= 1 && nq <= 10) e = run_gen_pack<uint16_t, GenB<uint16_t, 10, 1>, false>(a, a.tiles_n, a.nkt, out, s);
-    else if (zr <= 2 && nq <= 4) e = run_gen_pack<uint16_t, GenB<uint16_t, 4, 2>, false>(a, a.tiles_n, a.nkt, out, s);
-    else return hipErrorInvalidValue;     // the plan materializes Kb <= 12 only
+    if (p.pair) {   // the generator dc_dispatch_pair takes for bf16 (one item per lane)
+        if (zr <= 2 && nq <= 4) e = run_gen_pack<uint16_t, GenB2<uint16_t, 4, 2>, false>(a, a.tiles_n, a.nkt, out, s);
+        else if (zr <= 7 && nq <= 2) e = run_gen_pack<uint16_t, GenB2<uint16_t, 2, 7>, false>(a, a.tiles_n, a.nkt, out, s);
+        else if (zr <= 8 && nq <= 1) e = run_gen_pack<uint16_t, GenB2<uint16_t, 1, 8>, false>(a, a.tiles_n, a.nkt, out, s);
+        else if (zr <= 16 && nq <= 1) e = run_gen_pack<uint16_t, GenB2<uint16_t, 1, 16>, false>(a, a.tiles_n, a.nkt, out, s);
+        else e = run_gen_pack<uint16_t, GenB2<uint16_t, 1, 32>, false>(a, a.tiles_n, a.nkt, out, s);
+    } else if (zr <= 1 && nq <= 10) {
+        e = run_gen_pack<uint16_t, GenB<uint16_t, 10, 1>, false>(a, a.tiles_n, a.nkt, out, s);
+    } else if (zr <= 2 && nq <= 4) {
+        e = run_gen_pack<uint16_t, GenB<uint16_t, 4, 2>, false>(a, a.tiles_n, a.nkt, out, s);
+    } else {
+        return hipErrorInvalidValue;      // the plan builds 1-D operands for Kb <= 12 only
+    }
     if (e != hipSuccess) return e;
     a.b = out;
     a.b_tstride = (int64_t)a.nkt * BLOCK_BYTES;

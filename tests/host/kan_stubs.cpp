@@ -114,7 +114,7 @@ hipError_t launch_mfma_dc(const Plan& p, const void* x, const void* dyt, void* p
                           hipStream_t) {
     need(x && dyt && (p.split_dc == 1 || cpart) && (!p.mat_dc || phit), "mfma dC pointers");
     if (p.mat_dc)
-        need(p.off_phit + (size_t)p.tiles_dx * 256 * p.Npad * 2 <= p.ws_bwd && p.Kb <= 12, "dC basis in the workspace");
+        need(p.off_phit + (size_t)p.tiles_dx * 256 * p.Npad * 2 <= p.ws_bwd && (p.Kb <= 12 || p.pair), "dC basis in the workspace");
     need(p.split_dc == 1 || (p.tail_dc >= 1 && p.tail_dc <= p.Opad / 256 && dc_tail_rows(p) >= 1 &&
                              p.nks_dc * (p.split_dc - 1) < p.Npad / p.BK),
          "mfma dC tail");

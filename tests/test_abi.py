@@ -527,7 +527,7 @@ def test_surface_workspace_sizes(L):
     pair cut by a tile edge."""
     r = lambda a, b: (a + b - 1) // b * b
     for dt, es, bk in [(0, 4, 32), (1, 2, 64)]:
-        for (N, P, O, G) in [(100, 8, 20, 5), (8192, 512, 1024, 5), (300, 7, 33, 8), (5, 3, 2, 1),
+        for (N, P, O, G) in [(100, 8, 20, 5), (8192, 512, 1024, 5), (300, 7, 33, 8), (5, 3, 2, 1), (64, 16, 700, 1),
                              (77, 4, 300, 13)]:
             Kb = (G + 3) ** 2
             Op, Np = r(O, 256), r(N, 256)
@@ -535,6 +535,9 @@ def test_surface_workspace_sizes(L):
             want_f = r(Op * kf * es, 256) + split_bytes(Np // 256, Op // 256, kf // bk, N, O * 4, es, es == 4)
             tiles = (P * Kb + 255) // 256
             want_b = r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 4 * 4, 256)
+            # bf16 dC from 3 output tiles: the pair basis built once, [tiles * 256][Np]
+            if dt == 1 and Op // 256 >= 3 and Np * r(P * Kb, 256) * 2 <= 1 << 30:
+                want_b += r(tiles * 256 * Np * es, 256)
             want_b += split_bytes(Op // 256, tiles, Np // bk, O, P * Kb * 4, es)
             d = sdesc(L, N=N, P=P, O=O, G=G, dtype=dt)
             assert L.lib().kan_surface_workspace_size(ctypes.byref(d), 0) == want_f

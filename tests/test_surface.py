@@ -55,6 +55,8 @@ SMALL = [
     (260, 6, 20, 7, "bf16"),            # Kb = 100
     (33, 40, 9, 5, "f32"),              # 40 pairs, 10 dx tiles
     (1, 1, 1, 3, "bf16"),               # smallest
+    (200, 6, 600, 5, "bf16"),           # O > 512 in bf16: dC on the pair basis built once (Kb = 64)
+    (64, 16, 700, 1, "bf16"),           # the same with Kb = 16
 ]
 
 
