@@ -223,6 +223,24 @@ def k_split(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize):
     return (nkt + nks - 1) // nks, nks, best[1]
 
 
+def test_k_split_choices():
+    """The split the rule gives the workloads' launches: c4's first-layer
+    forward (50 x 12 tiles, 108 k-tiles) runs 42 tile rows whole and the
+    last 8 in 2 slices; its dC (12 x 27 tiles, 200 k-tiles) 9 rows whole and
+    3 in 3 slices; the second layer's dC (3 x 108) 2 rows whole and 1 in 2
+    slices; its forward (50 x 3 tiles, 432 k-tiles) every tile in 5 slices;
+    c5's launches fill whole rounds and stay whole; the tail test's dC
+    shapes (17 x 17 tiles) slice their last 2 tile rows."""
+    assert k_split(50, 12, 108, 12608, 3072 * 4, 2) == (2, 54, 8)
+    assert k_split(12, 27, 200, 3072, 768 * 9 * 4, 2) == (3, 67, 3)
+    assert k_split(3, 108, 200, 768, 3072 * 9 * 4, 2) == (2, 100, 1)
+    assert k_split(50, 3, 432, 12608, 768 * 4, 2) == (5, 87, 50)
+    assert k_split(256, 16, 1536, 65536, 4096 * 4, 2) == (1, 1536, 0)
+    assert k_split(16, 384, 1024, 4096, 4096 * 24 * 4, 2) == (1, 1024, 0)
+    assert k_split(17, 17, 16, 4302, 342 * 12 * 4, 2)[2] == 2
+    assert k_split(17, 17, 32, 4302, 342 * 12 * 4, 4)[2] == 2
+
+
 def split_bytes(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize, f32_forward=False):
     """Bytes of the partial outputs of a k-split contraction (0 when not
     split): P slices of the tail rows' output.  A float32 forward sums in

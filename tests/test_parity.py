@@ -383,6 +383,26 @@ def test_tail_split(F):
     assert err(_np(g1[1]), rdC) <= tol and err(_np(g1[2]), rdW) <= tol
 
 
+def test_tail_split_dc_f32(F):
+    """The float32 dC with the same tail split (17 x 17 tiles, the last 2
+    tile rows of outputs in batch slices) against the oracle in full, and
+    bitwise the same on a second call."""
+    import torch
+    dtype = "f32"
+    err, tol = metric(dtype)
+    d = wl.random_layer(1000, 342, 4302, 8, dtype=dtype, base=True, seed=34)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, Wt, dyt = to_dev(x, dtype), to_dev(C, dtype), to_dev(W, dtype), to_dev(dy, "f32")
+    say("tail split dC f32 1000x342x4302")
+    g1 = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+    g2 = F.kan_backward(xt, Ct, Wt, dyt, grid, need_dx=False, variant="mfma")
+    _sync()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    _, rdC, rdW = oracle.layer_backward(x, C, W, dy, *grid, need=("dC", "dW"))
+    assert err(_np(g1[1]), rdC) <= tol and err(_np(g1[2]), rdW) <= tol
+
+
 @pytest.mark.parametrize("shape", [(300, 40, 2000, 8, True), (700, 100, 1793, 3, False), (500, 60, 600, 5, True)])
 def test_materialized_basis(F, shape):
     """bf16 layers with few columns per input (Kb = 12, 6 and 9) build their
