@@ -36,12 +36,12 @@ int status_of(hipError_t e) { return e == hipSuccess ? KAN_OK : KAN_ERR_HIP; }
 // rather than in every workgroup that needs it.  Inside the contraction
 // every output tile regenerates the basis tiles of its k range; with few
 // columns per input (Kb <= 12: 21 or more inputs per 256-column tile) that
-// generator work exceeds what loading a built tile costs (c4, Kb = 9: about
-// 2.2 (forward) and 2.5 (dC) against 1.6-1.8 us per k-tile of a
-// workgroup).  Building costs one write of the N x I Kb bf16 basis, repaid
-// when enough output tiles read each of its tiles: measured at c4, the
-// forward gains with 12 reading tiles and loses with 3; dC gains with 12
-// and with 3.  So the forward's operand is built from 8 output tiles
+// generator work exceeds what loading a built tile costs (the 768 -> 3072
+// -> 768 channel mixer on 12608 rows, Kb = 9: about 2.2 (forward) and 2.5
+// (dC) against 1.6-1.8 us per k-tile of a workgroup).  Building costs one
+// write of the N x I Kb bf16 basis, repaid when enough output tiles read
+// each of its tiles: measured on that mixer, the forward gains with 12
+// reading tiles and loses with 3; dC gains with 12 and with 3.  So the forward's operand is built from 8 output tiles
 // (O > 1792) and dC's from 3 (O > 512); the array is kept within 1 GiB.
 // The 2-D layer's dC generator (16 products per pair) costs more than a
 // load at any pair width, so its dC operand is built by the same rule.

@@ -224,13 +224,15 @@ def k_split(tiles_m, tiles_n, nkt, rows_out, row_bytes, esize):
 
 
 def test_k_split_choices():
-    """The split the rule gives the workloads' launches: c4's first-layer
-    forward (50 x 12 tiles, 108 k-tiles) runs 42 tile rows whole and the
-    last 8 in 2 slices; its dC (12 x 27 tiles, 200 k-tiles) 9 rows whole and
-    3 in 3 slices; the second layer's dC (3 x 108) 2 rows whole and 1 in 2
-    slices; its forward (50 x 3 tiles, 432 k-tiles) every tile in 5 slices;
-    c5's launches fill whole rounds and stay whole; the tail test's dC
-    shapes (17 x 17 tiles) slice their last 2 tile rows."""
+    """The split the rule gives the workloads' launches: the 768 -> 3072
+    layer on 12608 rows (bf16, G = 5, base) runs its forward (50 x 12
+    tiles, 108 k-tiles) as 42 whole tile rows and the last 8 in 2 slices,
+    its dC (12 x 27 tiles, 200 k-tiles) as 9 whole rows and 3 in 3 slices;
+    the 3072 -> 768 layer's dC (3 x 108) as 2 whole rows and 1 in 2
+    slices, its forward (50 x 3 tiles, 432 k-tiles) every tile in 5
+    slices; the 4096 -> 4096 layer on 65536 rows fills whole rounds and
+    stays whole; the tail test's dC shapes (17 x 17 tiles) slice their last
+    2 tile rows."""
     assert k_split(50, 12, 108, 12608, 3072 * 4, 2) == (2, 54, 8)
     assert k_split(12, 27, 200, 3072, 768 * 9 * 4, 2) == (3, 67, 3)
     assert k_split(3, 108, 200, 768, 3072 * 9 * 4, 2) == (2, 100, 1)
