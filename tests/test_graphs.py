@@ -57,6 +57,33 @@ def _layer_step(torch, L, F):
     return step, (y, dx, dC, dW)
 
 
+def _layer_built_step(torch, L, F):
+    """A bf16 layer with 12 columns per input and 2000 outputs (dense forward
+    flag): both passes build their basis operands in the workspace
+    (gen_pack_kernel) before the contractions load them."""
+    d = wl.random_layer(300, 40, 2000, 8, dtype="bf16", base=True, seed=35)
+    (C, W), x, dy = d["layers"][0], d["x"], d["dy"]
+    grid = (d["lo"], d["hi"], d["G"])
+    xt, Ct, Wt = to_dev(x, "bf16"), to_dev(C, "bf16"), to_dev(W, "bf16")
+    dyt = to_dev(dy, "f32")
+    desc = F.layer_desc(xt, Ct, Wt, grid, "mfma", L.KAN_FLAG_DENSE_FORWARD)
+    wsf = F.workspace(desc, L.KAN_PASS_FORWARD, xt.device)
+    wsb = F.workspace(desc, L.KAN_PASS_BACKWARD, xt.device)
+    y = torch.empty(300, 2000, device="cuda:0")
+    dx = torch.empty(300, 40, device="cuda:0")
+    dC = torch.empty(C.shape, device="cuda:0")
+    dW = torch.empty(W.shape, device="cuda:0")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    lib = L.lib()
+
+    def step():
+        S = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        L.check(lib.kan_forward(ctypes.byref(desc), P(xt), P(Ct), P(Wt), P(y), P(wsf[0]), wsf[1], S), "fwd")
+        L.check(lib.kan_backward(ctypes.byref(desc), P(xt), P(Ct), P(Wt), P(dyt), P(dx), P(dC), P(dW),
+                                 P(wsb[0]), wsb[1], S), "bwd")
+    return step, (y, dx, dC, dW)
+
+
 def _grouped_step(torch, L, F):
     d = wl.random_grouped(500, 300, 7, 8, dtype="bf16", seed=32)
     grid = (d["lo"], d["hi"], d["G"])
@@ -101,7 +128,8 @@ def _surface_step(torch, L, F):
     return step, (y, dx, dC)
 
 
-STEPS = {"layer": _layer_step, "grouped": _grouped_step, "surface": _surface_step}
+STEPS = {"layer": _layer_step, "layer_built": _layer_built_step, "grouped": _grouped_step,
+         "surface": _surface_step}
 
 
 @pytest.mark.parametrize("name", sorted(STEPS))
