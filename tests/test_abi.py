@@ -385,6 +385,39 @@ def test_workspace_sizes(L):
                                                                    dtype=L.KAN_BF16) > 0
 
 
+def test_built_basis_thresholds(L):
+    """The built basis operands start exactly where the planner's rule puts
+    them: dC's from 3 output tiles (O = 513), the forward's from 8
+    (O = 1793, dense forward), bf16 only, Kb <= 12 only, and not past
+    1 GiB."""
+    r = lambda a, b: (a + b - 1) // b * b
+
+    def want(N, I, O, G, dt, built):
+        es, bk = (2, 64) if dt == L.KAN_BF16 else (4, 32)
+        Kb = G + 4
+        Op, Np = r(O, 256), r(N, 256)
+        tiles = (I * Kb + 255) // 256
+        kf = r(I * Kb, bk)
+        f = (r(Op * kf * es, 256) + (r(Np * kf * es, 256) if built[0] else 0)
+             + split_bytes(Np // 256, Op // 256, kf // bk, N, O * 4, es, es == 4))
+        b = (r(tiles * 256 * Op * es, 256) + 2 * r(Np * Op * es, 256) + r(Np * tiles * 2 * 4, 256)
+             + (r(tiles * 256 * Np * es, 256) if built[1] else 0)
+             + split_bytes(Op // 256, tiles, Np // bk, O, I * Kb * 4, es))
+        return f, b
+
+    def got(N, I, O, G, dt):
+        d = desc(L, N=N, I=I, O=O, G=G, has_base=1, dtype=dt, flags=L.KAN_FLAG_DENSE_FORWARD)
+        return L.lib().kan_workspace_size(ctypes.byref(d), 0), L.lib().kan_workspace_size(ctypes.byref(d), 1)
+
+    bf, f32 = L.KAN_BF16, L.KAN_F32
+    for O, built in [(512, (False, False)), (513, (False, True)), (1792, (False, True)), (1793, (True, True))]:
+        assert got(1000, 40, O, 8, bf) == want(1000, 40, O, 8, bf, built), O          # Kb = 12
+    assert got(1000, 40, 1793, 9, bf) == want(1000, 40, 1793, 9, bf, (False, False))  # Kb = 13
+    assert got(1000, 40, 1793, 8, f32) == want(1000, 40, 1793, 8, f32, (False, False))
+    # 65536 x 4096 inputs at Kb = 9 is 4.8 GB of basis: past 1 GiB
+    assert got(65536, 4096, 4096, 5, bf) == want(65536, 4096, 4096, 5, bf, (False, False))
+
+
 def test_workspace_sizes_other_degrees(L):
     """Degree D != 3: K = G + D columns per input and the cubic layer's
     choice of kernels (AUTO: bf16 on the matrix cores; float32 forward on the
